@@ -1,0 +1,241 @@
+"""fp64 CPU oracle for jagged attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does; the two
+share no code.  The arithmetic lives in ``jfa_oracle.c`` (plain C, fp64); this
+module only marshals numpy arrays into it.
+
+Conventions (see ``jfa_oracle.c`` for the page citations):
+  q [Tq, H, d], k/v [Tkv, H, d], o like q, lse [H, Tq]; offsets int64 [B+1].
+  mode: "softmax" | "silu" | "gelu"; bias_kind: "none" | "relpos" | "dense".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "jfa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libjfa_oracle.so")
+
+MODES = {"softmax": 0, "silu": 1, "gelu": 2}
+BIAS = {"none": 0, "relpos": 1, "dense": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compiles the oracle with gcc (plain -O2, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp,
+                               "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_double),
+                ("normalize", ctypes.c_int32), ("bias_kind", ctypes.c_int32),
+                ("num_buckets", ctypes.c_int32)]
+
+
+class _SchedParams(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("bq_bm", ctypes.c_int32), ("bq_bn", ctypes.c_int32),
+                ("bk_bn", ctypes.c_int32), ("bk_bm", ctypes.c_int32),
+                ("fuse", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        _lib.ora_offsets.argtypes = [P, ctypes.c_int32, P]
+        _lib.ora_bias_offsets.argtypes = [P, P, ctypes.c_int32, P]
+        _lib.ora_relpos_bucket.argtypes = [ctypes.c_int64, ctypes.c_int32]
+        _lib.ora_relpos_bucket.restype = ctypes.c_int
+        _lib.ora_forward.argtypes = [P] * 10
+        _lib.ora_backward.argtypes = [P] * 12
+        _lib.ora_schedule.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                      P, P, P, P, P, ctypes.c_int64, P]
+        _lib.ora_e4m3_decode.argtypes = [ctypes.c_int]
+        _lib.ora_e4m3_decode.restype = ctypes.c_double
+        _lib.ora_mxfp8_quantize.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+        _lib.ora_mxfp8_dequantize.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
+        _lib.ora_set_threads.argtypes = [ctypes.c_int]
+        _lib.ora_max_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):           # a CPU torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def set_threads(n: int) -> None:
+    lib().ora_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().ora_max_threads())
+
+
+# ------------------------------------------------------------------ offsets
+
+def offsets(lengths) -> np.ndarray:
+    """Exclusive prefix sum of per-sample lengths (int64 [B+1])."""
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    out = np.zeros(ln.shape[0] + 1, dtype=np.int64)
+    if lib().ora_offsets(_ptr(ln), ln.shape[0], _ptr(out)) != 0:
+        raise ValueError("negative length")
+    return out
+
+
+def bias_offsets(q_lens, kv_lens) -> np.ndarray:
+    """Start of each sample's block in a dense jagged bias, in units of H elements."""
+    a = np.ascontiguousarray(q_lens, dtype=np.int32)
+    b = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    out = np.zeros(a.shape[0] + 1, dtype=np.int64)
+    if lib().ora_bias_offsets(_ptr(a), _ptr(b), a.shape[0], _ptr(out)) != 0:
+        raise ValueError("negative length")
+    return out
+
+
+def relpos_bucket(delta: int, num_buckets: int = 64) -> int:
+    return int(lib().ora_relpos_bucket(int(delta), int(num_buckets)))
+
+
+# ------------------------------------------------------------ attention
+
+def _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets):
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if normalize is None:
+        normalize = mode != "softmax"
+    return _Problem(B, H, d, MODES[mode], int(bool(causal)), float(scale), int(bool(normalize)),
+                    BIAS[bias_kind], int(num_buckets))
+
+
+def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
+            bias_kind="none", num_buckets=64, scale=None, normalize=None):
+    """Returns (o [Tq,H,d] fp64, lse [H,Tq] fp64 or None for GDPA)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Tq, H, d = q.shape
+    qo, ko = offsets(q_lens), offsets(kv_lens)
+    B = qo.shape[0] - 1
+    assert qo[-1] == Tq and ko[-1] == k.shape[0] and k.shape == v.shape
+    bo = bias_offsets(q_lens, kv_lens)
+    bias64 = _f64(bias) if bias is not None else None
+    if bias_kind != "none":
+        assert bias64 is not None
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets)
+    o = np.zeros_like(q)
+    lse = np.full((H, Tq), np.nan) if mode == "softmax" else None
+    lib().ora_forward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
+                      _ptr(bias64), _ptr(bo), _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
+             bias_kind="none", num_buckets=64, scale=None, normalize=None):
+    """Returns (dq, dk, dv) in fp64: the gradients of <O, dout>."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Tq, H, d = q.shape
+    qo, ko = offsets(q_lens), offsets(kv_lens)
+    B = qo.shape[0] - 1
+    bo = bias_offsets(q_lens, kv_lens)
+    bias64 = _f64(bias) if bias is not None else None
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    lib().ora_backward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
+                       _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
+
+
+def case_forward(case, **kw):
+    """Oracle forward on a ``jfa_synth.Case`` (values widened exactly to fp64)."""
+    return forward(case.q, case.k, case.v, case.q_lens, case.kv_lens, mode=case.mode,
+                   causal=case.causal, bias=case.bias, bias_kind=case.bias_kind,
+                   num_buckets=case.num_buckets, **kw)
+
+
+def case_backward(case, **kw):
+    return backward(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                    mode=case.mode, causal=case.causal, bias=case.bias,
+                    bias_kind=case.bias_kind, num_buckets=case.num_buckets, **kw)
+
+
+# ------------------------------------------------------------- tile lists
+
+def schedule(q_offsets, kv_offsets, heads: int, causal: bool, *, bm: int, bn: int, slots: int,
+             bq_bm: int, bq_bn: int, bk_bn: int, bk_bm: int, fuse: bool = True) -> dict:
+    """Forward / combine / backward tile lists (see ``ora_schedule`` in the C source)."""
+    qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
+    ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
+    B = qo.shape[0] - 1
+    n = np.diff(qo)
+    m = np.diff(ko)
+    cap = int(np.sum((n + 1)) + np.sum(m + 1) + 64 + 2 * max(slots, 0) + 16)
+    cap += int(np.sum(-(-np.maximum(m, 1) // min(bn, bq_bn, bk_bn)) * (-(-np.maximum(n, 1) // min(bm, bq_bm)))))
+    fwd = np.zeros((cap, 4), np.int32)
+    fslot = np.zeros(cap, np.int32)
+    comb = np.zeros((cap, 4), np.int32)
+    bq = np.zeros((cap, 4), np.int32)
+    bk = np.zeros((cap, 4), np.int32)
+    counts = np.zeros(5, np.int64)
+    sp = _SchedParams(bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, int(bool(fuse)))
+    rc = lib().ora_schedule(_ptr(qo), _ptr(ko), B, heads, int(bool(causal)), ctypes.byref(sp),
+                            _ptr(fwd), _ptr(fslot), _ptr(comb), _ptr(bq), _ptr(bk), cap,
+                            _ptr(counts))
+    if rc == -1:
+        raise ValueError("malformed offsets")
+    if rc != 0:
+        raise RuntimeError(f"ora_schedule failed ({rc})")
+    nf, nc, nq, nk, C = (int(x) for x in counts)
+    return dict(fwd=fwd[:nf].copy(), fwd_slot=fslot[:nf].copy(), combine=comb[:nc].copy(),
+                bwd_q=bq[:nq].copy(), bwd_kv=bk[:nk].copy(), split_threshold=C)
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().ora_e4m3_decode(int(code)))
+
+
+def mxfp8_quantize(x):
+    """x [..., d] -> (codes uint8 [..., d], scales uint8 [..., d/32])."""
+    x = _f64(x)
+    d = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros(x.shape[:-1] + (d // 32,), np.uint8)
+    if lib().ora_mxfp8_quantize(_ptr(x), rows, d, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("d must be a multiple of 32")
+    return codes, scales
+
+
+def mxfp8_dequantize(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    d = codes.shape[-1]
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    out = np.zeros(codes.shape, np.float64)
+    lib().ora_mxfp8_dequantize(_ptr(codes), _ptr(scales), rows, d, _ptr(out))
+    return out

@@ -1,0 +1,440 @@
+"""Pins the fp64 oracle to things other than itself.
+
+Each check here would fail on a plausible mistake in the oracle (a dropped
+term, a wrong sign or index, a transposed operand, a wrong mask alignment):
+  - torch's own scaled_dot_product_attention / autograd / silu / gelu (fp64);
+  - a dense, padded, batched computation (jagged must equal masked-padded);
+  - central finite differences of the forward;
+  - closed forms and hand-computed fixtures under tests/golden/;
+  - brute-force enumeration of tile lists;
+  - torch's float8_e4m3fn for the E4M3 code table.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from jfa_synth import custom_case
+from tests.conftest import GOLDEN
+from tests.helpers import max_abs, rel_l2, torch_reference
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+# ------------------------------------------------------------------ offsets
+
+def test_offsets_match_cumsum(oracle_mod):
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        lens = rng.integers(0, 1000, size=rng.integers(1, 50)).astype(np.int32)
+        off = oracle_mod.offsets(lens)
+        assert off.dtype == np.int64
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(lens.astype(np.int64))]))
+
+
+def test_offsets_reject_negative(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.offsets(np.array([3, -1, 2], np.int32))
+
+
+def test_bias_offsets_are_running_products(oracle_mod):
+    q = np.array([3, 0, 5, 7], np.int32)
+    kv = np.array([2, 4, 0, 9], np.int32)
+    assert list(oracle_mod.bias_offsets(q, kv)) == [0, 6, 6, 6, 69]
+
+
+# ------------------------------------------------------- relative position
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def test_relpos_bucket_golden(oracle_mod):
+    rows = _golden_rows("relpos_buckets.txt")
+    assert len(rows) >= 20
+    for dist, width, want in rows:
+        assert oracle_mod.relpos_bucket(int(dist), int(width)) == int(want), (dist, width)
+
+
+def test_relpos_bucket_invariants(oracle_mod):
+    prev = 0
+    for d in range(0, 70000):
+        bkt = oracle_mod.relpos_bucket(d, 64)
+        assert prev <= bkt <= 63
+        prev = bkt
+    # four buckets per doubling between 16 and 2^15
+    for k in range(4, 15):
+        seen = {oracle_mod.relpos_bucket(d, 64) for d in range(2 ** k, 2 ** (k + 1))}
+        assert len(seen) == 4
+
+
+# -------------------------------------------------------- worked example
+
+def test_worked_example(oracle_mod):
+    s2 = math.sqrt(2.0)
+    q = np.array([[[0.0, 0.0]], [[s2 * math.log(3.0), 0.0]]])
+    k = np.array([[[1.0, 0.0]], [[0.0, 0.0]]])
+    v = np.array([[[4.0, 8.0]], [[0.0, 4.0]]])
+    lens = np.array([2], np.int32)
+    for mode, causal, row, o0, o1, lse in _golden_rows("attention_worked_example.txt"):
+        ev = lambda s: eval(s, {"log": math.log, "nan": float("nan")})  # noqa: E731
+        o, l = oracle_mod.forward(q, k, v, lens, lens, mode=mode, causal=bool(int(causal)))
+        r = int(row)
+        assert abs(o[r, 0, 0] - ev(o0)) < 1e-12 and abs(o[r, 0, 1] - ev(o1)) < 1e-12
+        if mode == "softmax":
+            assert abs(l[0, r] - ev(lse)) < 1e-12
+
+
+# ------------------------------------------- attention vs torch (fp64)
+
+CASES = [
+    # q_lens, kv_lens, H, d
+    ([5, 0, 9, 1, 12], [5, 0, 9, 1, 12], 2, 16),
+    ([4, 7, 3], [9, 2, 3], 2, 8),           # asymmetric, q longer and shorter than kv
+    ([6, 3], [0, 5], 1, 8),                  # an empty key set
+]
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bias_kind", ["none", "relpos", "dense"])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_forward_backward_vs_torch(oracle_mod, mode, causal, bias_kind, ci):
+    ql, kl, H, d = CASES[ci]
+    case = custom_case(ql, kl, H, d, dtype="f32", mode=mode, causal=causal,
+                       bias_kind=bias_kind, num_buckets=64, seed=100 + ci, bias_std=0.5)
+    o, lse = oracle_mod.case_forward(case)
+    dq, dk, dv = oracle_mod.case_backward(case)
+    ref = torch_reference(case.q, case.k, case.v, case.q_lens, case.kv_lens, mode, causal,
+                          case.bias, bias_kind, oracle_mod.relpos_bucket, dout=case.dout)
+    assert max_abs(o, ref["o"]) < 1e-12
+    if mode == "softmax":
+        finite = np.isfinite(ref["lse"])
+        assert np.array_equal(np.isfinite(lse), finite)
+        assert np.all(lse[~finite] == -np.inf)
+        assert max_abs(lse[finite], ref["lse"][finite]) < 1e-12
+    else:
+        assert lse is None
+    for got, want in ((dq, ref["dq"]), (dk, ref["dk"]), (dv, ref["dv"])):
+        assert max_abs(got, want) < 1e-11
+
+
+def test_jagged_equals_masked_padded(oracle_mod):
+    """A padded, batched torch computation with a key-padding mask agrees on valid rows."""
+    ql = np.array([7, 3, 11, 1], np.int32)
+    kl = np.array([9, 3, 4, 6], np.int32)
+    H, d = 3, 8
+    for mode in ("softmax", "silu"):
+        case = custom_case(ql, kl, H, d, dtype="f32", mode=mode, seed=7)
+        o, _ = oracle_mod.case_forward(case)
+        B, Lq, Lk = len(ql), int(ql.max()), int(kl.max())
+        qp = torch.zeros(B, H, Lq, d, dtype=torch.float64)
+        kp = torch.zeros(B, H, Lk, d, dtype=torch.float64)
+        vp = torch.zeros(B, H, Lk, d, dtype=torch.float64)
+        qo = np.concatenate([[0], np.cumsum(ql)])
+        ko = np.concatenate([[0], np.cumsum(kl)])
+        for b in range(B):
+            qp[b, :, :ql[b]] = case.q[qo[b]:qo[b + 1]].double().permute(1, 0, 2)
+            kp[b, :, :kl[b]] = case.k[ko[b]:ko[b + 1]].double().permute(1, 0, 2)
+            vp[b, :, :kl[b]] = case.v[ko[b]:ko[b + 1]].double().permute(1, 0, 2)
+        s = (qp @ kp.transpose(-1, -2)) / math.sqrt(d)
+        keymask = torch.arange(Lk)[None, :] < torch.as_tensor(kl)[:, None]   # [B, Lk]
+        if mode == "softmax":
+            s = s.masked_fill(~keymask[:, None, None, :], -math.inf)
+            op = torch.softmax(s, dim=-1) @ vp
+        else:
+            a = torch.nn.functional.silu(s) * keymask[:, None, None, :]
+            # the true kv_len divides, never the padded length
+            op = (a @ vp) / torch.as_tensor(kl, dtype=torch.float64)[:, None, None, None]
+        for b in range(B):
+            got = o[qo[b]:qo[b + 1]]
+            want = op[b, :, :ql[b]].permute(1, 0, 2).numpy()
+            assert max_abs(got, want) < 1e-12
+
+
+# ---------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal,bias_kind", [(False, "none"), (True, "relpos"), (False, "dense")])
+def test_backward_central_differences(oracle_mod, mode, causal, bias_kind):
+    ql, kl = [3, 6, 2], [4, 6, 5]
+    case = custom_case(ql, kl, 2, 4, dtype="f32", mode=mode, causal=causal, bias_kind=bias_kind,
+                       seed=11, bias_std=0.5)
+    q, k, v = (case.q.double().numpy().copy() for _ in range(1)), None, None
+    q = case.q.double().numpy().copy()
+    k = case.k.double().numpy().copy()
+    v = case.v.double().numpy().copy()
+    dout = case.dout.double().numpy()
+    kw = dict(mode=mode, causal=causal, bias=case.bias, bias_kind=bias_kind)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle_mod.forward(qq, kk, vv, case.q_lens, case.kv_lens, **kw)
+        return float(np.sum(o * dout))
+
+    dq, dk, dv = oracle_mod.backward(q, k, v, dout, case.q_lens, case.kv_lens, **kw)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + h
+            lp = loss(q, k, v)
+            x[idx] = old - h
+            lm = loss(q, k, v)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - g)) / max(1.0, np.max(np.abs(g)))
+        assert err < 1e-6, (name, err)
+
+
+# ----------------------------------------------------------- closed forms
+
+def test_closed_forms_softmax(oracle_mod):
+    ql = np.array([6, 4, 1], np.int32)
+    for causal in (False, True):
+        case = custom_case(ql, ql, 2, 8, dtype="f32", causal=causal, seed=3)
+        # V = 1 -> O = 1 (the weights of every row sum to one)
+        o, _ = oracle_mod.forward(case.q, case.k, torch.ones_like(case.v), ql, ql, causal=causal)
+        assert max_abs(o, np.ones_like(o)) < 1e-13
+        # K = 0, no bias -> O_i = mean of the visible V_j (prefix mean when causal)
+        o, lse = oracle_mod.forward(case.q, torch.zeros_like(case.k), case.v, ql, ql,
+                                    causal=causal)
+        v = case.v.double().numpy()
+        off = 0
+        for n in ql:
+            for i in range(n):
+                upto = i + 1 if causal else n
+                want = v[off:off + upto].mean(axis=0)
+                assert max_abs(o[off + i], want) < 1e-13
+                assert abs(lse[0, off + i] - math.log(upto)) < 1e-13
+            off += n
+    # kv_len = 1 -> O_i = V_0, and dQ = dK = 0 exactly
+    case = custom_case([5, 3], [1, 1], 2, 8, dtype="f32", seed=4)
+    o, _ = oracle_mod.case_forward(case)
+    dq, dk, dv = oracle_mod.case_backward(case)
+    v = case.v.double().numpy()
+    assert max_abs(o[:5], np.broadcast_to(v[0], (5, 2, 8))) < 1e-14
+    assert max_abs(o[5:], np.broadcast_to(v[1], (3, 2, 8))) < 1e-14
+    assert np.all(dq == 0) and np.all(dk == 0)
+    # a per-row constant added to a dense bias leaves softmax output unchanged
+    case = custom_case([4, 5], [6, 3], 2, 8, dtype="f32", bias_kind="dense", seed=5)
+    o1, _ = oracle_mod.case_forward(case)
+    shifted = case.bias.double().clone()
+    off = 0
+    for n, m in zip(case.q_lens, case.kv_lens):
+        blk = shifted[off:off + 2 * n * m].view(2, n, m)
+        blk += torch.arange(n, dtype=torch.float64)[None, :, None] * 3.0
+        off += 2 * n * m
+    o2, _ = oracle_mod.forward(case.q, case.k, case.v, case.q_lens, case.kv_lens,
+                               bias=shifted, bias_kind="dense")
+    assert max_abs(o1, o2) < 1e-13
+
+
+@pytest.mark.parametrize("mode", ["silu", "gelu"])
+def test_closed_forms_gdpa(oracle_mod, mode):
+    ql, kl = np.array([4, 3], np.int32), np.array([5, 2], np.int32)
+    case = custom_case(ql, kl, 2, 8, dtype="f32", mode=mode, seed=6)
+    # Q = 0, no bias -> every score is 0 and act(0) = 0 -> O = 0
+    o, _ = oracle_mod.forward(torch.zeros_like(case.q), case.k, case.v, ql, kl, mode=mode)
+    assert np.all(o == 0)
+    # K = 0 -> scores 0, act'(0) = 1/2: dK_j = (s / (2 m)) sum_i (dO_i . V_j) Q_i
+    dq, dk, dv = oracle_mod.backward(case.q, torch.zeros_like(case.k), case.v, case.dout, ql, kl,
+                                     mode=mode)
+    q, v, do = (t.double().numpy() for t in (case.q, case.v, case.dout))
+    s = 1 / math.sqrt(8)
+    qoff = koff = 0
+    for n, m in zip(ql, kl):
+        for h in range(2):
+            for j in range(m):
+                want = sum((do[qoff + i, h] @ v[koff + j, h]) * q[qoff + i, h] for i in range(n))
+                want = want * s / (2 * m)
+                assert max_abs(dk[koff + j, h], want) < 1e-13
+        qoff += n
+        koff += m
+
+
+def test_zero_length_samples(oracle_mod):
+    ql = np.array([3, 0, 4, 2], np.int32)
+    kl = np.array([0, 5, 3, 2], np.int32)
+    for mode in ("softmax", "silu", "gelu"):
+        case = custom_case(ql, kl, 2, 8, dtype="f32", mode=mode, seed=8)
+        o, lse = oracle_mod.case_forward(case)
+        dq, dk, dv = oracle_mod.case_backward(case)
+        assert np.all(o[:3] == 0) and np.all(dq[:3] == 0)       # sample 0 has no keys
+        if mode == "softmax":
+            assert np.all(lse[:, :3] == -np.inf)
+        assert np.all(dk[:5] == 0) and np.all(dv[:5] == 0)      # sample 1 has no queries
+        assert np.any(o[3:] != 0)
+
+
+# -------------------------------------------------------------- tile lists
+
+def _parse_schedule_golden():
+    cases, cur = [], None
+    for row in _golden_rows("schedule_small.txt"):
+        key = row[0]
+        if key == "case":
+            cur = dict(name=row[1], rec=[], comb=[])
+        elif key == "end":
+            cases.append(cur)
+        elif key in ("rec", "comb"):
+            cur[key].append([int(x) for x in row[1:]])
+        elif key == "q_lens":
+            cur[key] = [int(x) for x in row[1:]]
+        else:
+            cur[key] = int(row[1])
+    return cases
+
+
+def test_schedule_golden(oracle_mod):
+    for c in _parse_schedule_golden():
+        off = oracle_mod.offsets(np.array(c["q_lens"], np.int32))
+        s = oracle_mod.schedule(off, off, c["heads"], bool(c["causal"]), bm=c["bm"], bn=c["bn"],
+                                slots=c["slots"], bq_bm=64, bq_bn=64, bk_bn=64, bk_bm=64)
+        got = np.concatenate([s["fwd"], s["fwd_slot"][:, None]], axis=1).tolist()
+        assert got == c["rec"], c["name"]
+        assert s["combine"].tolist() == c["comb"], c["name"]
+        assert s["split_threshold"] == c["threshold"]
+
+
+def _visible_pairs(n, m, causal, r0, r1, c0, c1):
+    cnt = 0
+    for i in range(r0, min(r1, n)):
+        for j in range(c0, min(c1, m)):
+            if not causal or j <= i + (m - n):
+                cnt += 1
+    return cnt
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_invariants_bruteforce(oracle_mod, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 12))
+    ql = rng.integers(0, 300, size=B).astype(np.int32)
+    kl = ql.copy() if seed % 2 == 0 else rng.integers(0, 300, size=B).astype(np.int32)
+    causal = seed % 3 != 2
+    H, bm, bn = int(rng.integers(1, 5)), 64 * int(rng.integers(1, 3)), 32 * int(rng.integers(1, 3))
+    slots = int(rng.integers(1, 40)) if seed != 5 else 0
+    qo, ko = oracle_mod.offsets(ql), oracle_mod.offsets(kl)
+    s = oracle_mod.schedule(qo, ko, H, causal, bm=bm, bn=bn, slots=slots, bq_bm=64, bq_bn=32,
+                            bk_bn=64, bk_bm=32)
+    fwd, slot = s["fwd"], s["fwd_slot"]
+    cost = np.maximum(1, fwd[:, 3] - fwd[:, 2])
+    # longest first, ties by (b, t, kb): the list is sorted by a total order
+    keys = [(-c, b, t, kb) for c, (b, t, kb, _) in zip(cost, fwd)]
+    assert keys == sorted(keys) and len(set(keys)) == len(keys)
+    # every query tile appears; its chunks tile [0, steps) exactly; steps cover every visible pair
+    C = s["split_threshold"]
+    for b in range(B):
+        n, m = int(ql[b]), int(kl[b])
+        for t in range(-(-n // bm)):
+            parts = sorted([tuple(r[2:]) for r in fwd if r[0] == b and r[1] == t])
+            assert parts[0][0] == 0
+            for a, c in zip(parts, parts[1:]):
+                assert a[1] == c[0]
+            steps = parts[-1][1]
+            # steps is the smallest count covering every visible pair of the tile
+            assert _visible_pairs(n, m, causal, t * bm, (t + 1) * bm, 0, steps * bn) == \
+                _visible_pairs(n, m, causal, t * bm, (t + 1) * bm, 0, m)
+            if steps > 0:
+                assert _visible_pairs(n, m, causal, t * bm, (t + 1) * bm, (steps - 1) * bn,
+                                      steps * bn) > 0
+            if slots > 0 and steps > C:
+                assert len(parts) == -(-steps // C)
+            else:
+                assert len(parts) == 1
+        assert not any(r[0] == b and r[1] >= -(-n // bm) for r in fwd)
+    # split chunks own distinct, dense partial slots
+    used = sorted(slot[slot >= 0].tolist())
+    assert used == list(range(len(used)))
+    # backward classes: one query tile -> q-stationary single pass (owns dK/dV);
+    # else one key tile -> kv-stationary single pass (owns dQ); else both passes.
+    for b in range(B):
+        n, m = int(ql[b]), int(kl[b])
+        one_q = -(-n // 64) == 1
+        one_k = not one_q and -(-m // 64) == 1
+        rq = [r for r in s["bwd_q"] if r[0] == b]
+        rk = [r for r in s["bwd_kv"] if r[0] == b]
+        assert len(rq) == (0 if one_k else -(-n // 64))
+        assert len(rk) == (0 if one_q else -(-m // 64))
+        if one_q:
+            assert rq[0][3] == -(-m // 32)            # visits every key tile
+        for _, u, first, end in rk:
+            assert end == -(-n // 32)
+            if one_k or not causal:
+                assert first == 0                     # visits every query tile
+            elif first < end:
+                # the first query tile is the first one with a visible pair
+                assert _visible_pairs(n, m, causal, 0, first * 32, u * 64, (u + 1) * 64) == 0
+                assert _visible_pairs(n, m, causal, first * 32, (first + 1) * 32, u * 64,
+                                      (u + 1) * 64) > 0
+            else:
+                assert _visible_pairs(n, m, causal, 0, n, u * 64, (u + 1) * 64) == 0
+
+
+def test_schedule_rejects_bad_offsets(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.schedule(np.array([0, 5, 3], np.int64), np.array([0, 5, 8], np.int64), 1,
+                            False, bm=64, bn=64, slots=0, bq_bm=64, bq_bn=64, bk_bn=64, bk_bm=64)
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def test_e4m3_table_matches_torch_float8(oracle_mod):
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        got = oracle_mod.e4m3_decode(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(got), c
+        else:
+            assert got == ref[c], c
+
+
+def test_mxfp8_golden(oracle_mod):
+    for amax, x, scale, code in _golden_rows("mxfp8_cases.txt"):
+        blk = np.zeros(32)
+        blk[0], blk[1] = float(amax), float(x)
+        codes, scales = oracle_mod.mxfp8_quantize(blk[None, :])
+        assert scales[0, 0] == int(scale), (amax, x)
+        assert codes[0, 1] == int(code, 16), (amax, x, hex(codes[0, 1]))
+
+
+def test_mxfp8_against_torch_cast_and_bounds(oracle_mod):
+    rng = np.random.default_rng(9)
+    x = torch.from_numpy(rng.standard_normal((512, 128), dtype=np.float32)).to(torch.bfloat16)
+    x[3, :32] = 0                                       # an all-zero block
+    x[4, 32:64] *= 1e-30                                # tiny magnitudes
+    xd = x.double().numpy()
+    codes, scales = oracle_mod.mxfp8_quantize(xd)
+    deq = oracle_mod.mxfp8_dequantize(codes, scales)
+    for r in range(xd.shape[0]):
+        for blk in range(4):
+            xb = xd[r, 32 * blk:32 * blk + 32]
+            amax = np.max(np.abs(xb))
+            if amax == 0:
+                assert scales[r, blk] == 127 and np.all(codes[r, 32 * blk:32 * blk + 32] == 0)
+                continue
+            e = int(scales[r, blk]) - 127
+            assert 256 <= amax * 2.0 ** -e < 512           # the scale puts amax in the top binade
+            y = xb * 2.0 ** -e
+            inr = np.abs(y) <= 448
+            ref = torch.from_numpy(y[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[r, 32 * blk:32 * blk + 32][inr], ref)
+            assert np.all(codes[r, 32 * blk:32 * blk + 32][~inr] & 127 == 0x7E)
+            big = (np.abs(y) >= 2.0 ** -6) & inr              # normal, unsaturated E4M3 range
+            rel = np.abs(deq[r, 32 * blk:32 * blk + 32][big] - xb[big]) / np.abs(xb[big])
+            assert np.all(rel <= 2.0 ** -4)                   # half an ulp of a 3-bit mantissa
+            sat = ~inr                                        # y in (448, 512) clips to 448
+            rel = np.abs(deq[r, 32 * blk:32 * blk + 32][sat] - xb[sat]) / np.abs(xb[sat])
+            assert np.all(rel < 1.0 / 8)
