@@ -1,0 +1,170 @@
+/*
+ * jfa.h - C ABI of libjfa.so: jagged flash attention (JFA) and generalized
+ * dot-product attention (GDPA), forward and backward, on AMD MI355X (gfx950).
+ *
+ * What is computed (sources: the pages on Meta's GEM training work):
+ *  - "Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a
+ *    Different Stack", section "Bottleneck move 1": attention directly on
+ *    variable-length (jagged) tensors, with custom biases and asymmetric
+ *    query/key-value lengths; GDPA uses GELU or SiLU in place of softmax;
+ *    removing padding exposes tile scheduling and backward accumulation.
+ *  - same page, FAQ "What is a jagged tensor?": values plus offsets.
+ *  - "Meta Enhances GEM Training Efficiency with Advanced LLM-Scale
+ *    Innovations", section "Leveraging Compute Efficiency through Customized
+ *    Kernels": MXFP8 attention.
+ *
+ * For sample b with n = q_len, m = kv_len, query i < n, key j < m, head h:
+ *   S_ij = qk_scale * <Q[qo_b+i,h,:], K[ko_b+j,h,:]> + bias_h(b,i,j)
+ *   visible(i,j) = !causal || j <= i + (m - n)      (bottom-right aligned)
+ *   softmax: O_i = sum_j softmax_j(S_i.) V_j over visible j; LSE_i = log sum_j exp S_ij
+ *   GDPA:    O_i = w * sum_{visible j} act(S_ij) V_j, w = 1/m if kv_len_normalize else 1,
+ *            act = SiLU (x*sigmoid x) or GELU (erf form)
+ * Rows with no visible key: O = 0, LSE = -inf.  Backward returns the
+ * gradients of <O, dO> with respect to Q, K, V.
+ *
+ * Conventions for every entry point:
+ *  - Layout: Q, O, dO, dQ are [total_q, H, d] row-major; K, V, dK, dV are
+ *    [total_kv, H, d]; LSE is fp32 [H, total_q].  Offsets are int32 [B+1],
+ *    off[0] = 0, non-decreasing, off[B] = total rows; q and kv offsets are
+ *    independent (asymmetric lengths).
+ *  - Memory: every pointer except `jfa_problem*`, `status_out` and the
+ *    argument of jfa_tile_config is a DEVICE pointer allocated by the caller,
+ *    16-byte aligned.  The library never allocates or frees device memory and
+ *    keeps no mutable state between calls, except opt-in kernel timing.
+ *  - Streams: `stream` is a hipStream_t (NULL = default stream).  All work is
+ *    enqueued asynchronously; nothing blocks the host except
+ *    jfa_read_device_status and jfa_kernel_timing.
+ *  - Errors: host-checkable mistakes return an error before anything is
+ *    enqueued.  Malformed offsets found on the device set the status word in
+ *    the workspace; the kernels of that call then write nothing, and
+ *    jfa_read_device_status reports JFA_ERR_DEVICE_DATA.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misaligned pointer, bad enum */
+  JFA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (e.g. d not in {64,128}) */
+  JFA_ERR_WORKSPACE = -3,     /* workspace_bytes smaller than jfa_workspace_bytes() */
+  JFA_ERR_LAUNCH = -4,        /* a HIP call failed */
+  JFA_ERR_DEVICE_DATA = -5    /* offsets found malformed on the device */
+} jfa_status;
+
+typedef enum { JFA_MODE_SOFTMAX = 0, JFA_MODE_SILU = 1, JFA_MODE_GELU = 2 } jfa_mode;
+typedef enum { JFA_F32 = 0, JFA_BF16 = 1, JFA_MXFP8_E4M3 = 2 } jfa_dtype;
+typedef enum { JFA_BIAS_NONE = 0, JFA_BIAS_RELPOS = 1, JFA_BIAS_DENSE = 2 } jfa_bias_kind;
+
+typedef struct {
+  int32_t batch;            /* B >= 1 samples */
+  int32_t heads;            /* H >= 1 */
+  int32_t head_dim;         /* d: 64 or 128 */
+  int64_t total_q;          /* rows of Q / O (equals q_offsets[B]; checked on the device) */
+  int64_t total_kv;         /* rows of K / V (equals kv_offsets[B]; checked on the device) */
+  int32_t mode;             /* jfa_mode */
+  int32_t dtype;            /* jfa_dtype: storage type of Q, K, V (and O, dO, dQ, dK, dV
+                               for F32/BF16).  MXFP8 is forward only: O is bf16. */
+  int32_t causal;           /* 0 or 1; visible iff j <= i + (kv_len - q_len) */
+  float qk_scale;           /* 0 selects 1/sqrt(d) */
+  int32_t kv_len_normalize; /* -1 default (on for SiLU/GELU, off for softmax), 0, 1;
+                               must be 0 or -1 for softmax */
+  int32_t bias_kind;        /* jfa_bias_kind */
+  int32_t num_buckets;      /* RELPOS table width, 1..4096 (64 for the GEM workloads) */
+  int32_t split_slots;      /* forward tail balancing: 0 = auto (concurrent workgroups of the
+                               device), >0 = this many, <0 = never split a query tile */
+  int32_t bwd_fuse;         /* -1 default (on), 0 off: single-pass backward for samples with
+                               one query tile or one key tile */
+} jfa_problem;
+
+/*
+ * Bias layouts:
+ *  RELPOS: fp32 [H][num_buckets].  bias_h(b,i,j) = table[h][bucket(|i + (m-n) - j|)],
+ *          bucket(x) = x for x < 16, else min(num_buckets-1, 16 + 4(k-4) + ((x >> (k-2)) & 3))
+ *          with k = floor(log2 x).
+ *  DENSE:  storage dtype (fp32 for F32, bf16 otherwise); sample b's block [H][n][m] starts
+ *          at element H * sum_{b'<b} n_b' * m_b'.  bias_h(b,i,j) = block[h][i][j].
+ */
+
+/* Bytes of device workspace that jfa_forward (backward = 0) or jfa_backward (backward = 1)
+ * needs for this problem; 0 if the problem is invalid.  With split_slots = 0 this queries the
+ * current device. */
+size_t jfa_workspace_bytes(const jfa_problem* p, int backward);
+
+/* Forward pass.  q/k/v: [rows, H, d] of the storage dtype; for MXFP8 they are E4M3 codes
+ * (uint8) and q_scale/k_scale/v_scale are E8M0 codes [rows, H, d/32] (NULL otherwise).
+ * bias: NULL for JFA_BIAS_NONE.  o: [total_q, H, d] (bf16 for MXFP8).  lse: fp32 [H, total_q],
+ * required for softmax, ignored (may be NULL) for GDPA. */
+jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const void* v,
+                       const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                       const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                       void* o, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Backward pass (F32 and BF16).  o and lse are the forward's outputs (softmax; may be NULL
+ * for GDPA); dout like o.  Writes every row of dq [total_q, H, d], dk and dv [total_kv, H, d].
+ * Deterministic: repeated calls give bitwise-identical results. */
+jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Tile sizes the kernels use for this problem, in the order
+ * {bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse}: forward query/key tile rows, split slots
+ * (<= 0: no split), query-stationary backward tile rows, key-stationary backward tile rows,
+ * and whether single-pass backward classes are on.  Host only (queries the device only when
+ * split_slots = 0). */
+jfa_status jfa_tile_config(const jfa_problem* p, int32_t cfg_out[8]);
+
+/* Test hook: builds the tile lists of this problem into caller buffers (device).
+ * fwd, comb, bwd_q, bwd_kv: int32 [capacity][4]; fwd_slot: int32 [capacity];
+ * counts: int32 [8] = {forward, combine, q-stationary, kv-stationary records, split threshold,
+ * partial slots, status, 0}.  Records follow the order of jfa_tile_config's tiles:
+ * forward {b, t, kv_step_begin, kv_step_end} longest first (ties: b, t, kv_step_begin); combine
+ * {b, t, first_slot, chunks} in (b, t) order; q-stationary {b, t, 0, kv_steps};
+ * kv-stationary {b, u, q_step_begin, q_step_end}. */
+jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
+                              const int32_t* kv_offsets, int32_t* fwd, int32_t* fwd_slot,
+                              int32_t* comb, int32_t* bwd_q, int32_t* bwd_kv, int32_t* counts,
+                              int64_t capacity, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Offsets from lengths: offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] (device
+ * int32 arrays, B+1 and B entries).  status (device int32, may be NULL) receives 0, or
+ * JFA_ERR_DEVICE_DATA for a negative length or a total above INT32_MAX. */
+jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t* offsets,
+                                  int32_t* status, void* stream);
+
+/* MXFP8 (OCP Microscaling, E4M3 elements): for each row of x (bf16 [rows, d], d % 32 == 0)
+ * and each block of 32 consecutive elements, scale code s = floor(log2 amax) - 8 + 127
+ * (clamped to [0, 254]; 127 for an all-zero block) into scales [rows, d/32], and codes
+ * [rows, d] = E4M3 round-to-nearest-even of x * 2^(127 - s), saturating at +-448. */
+jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
+                              uint8_t* scales, void* stream);
+
+/* Waits for `stream` and returns the device status word of the last call that used this
+ * workspace (JFA_OK or JFA_ERR_DEVICE_DATA) in *status_out. */
+jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* status_out);
+
+/* Human-readable name of a status code (static storage). */
+const char* jfa_status_string(jfa_status s);
+
+/* Opt-in per-kernel timing (for benchmarks): while enabled, every kernel launch is bracketed
+ * by HIP events on its stream.  jfa_kernel_timing waits for those events and returns the
+ * summed milliseconds and launch count of kernels whose name starts with `name_prefix`
+ * ("" = all); reset clears the record.  Not for concurrent use from several threads. */
+void jfa_set_kernel_timing(int enable);
+jfa_status jfa_kernel_timing(const char* name_prefix, double* total_ms, int64_t* launches);
+void jfa_kernel_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JFA_H */

@@ -1,0 +1,459 @@
+// Host side of libjfa: argument checks, tile configuration, workspace layout, launches.
+// Entry points and their contracts are declared (with sources) in include/jfa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+// ------------------------------------------------------------ device facts
+int cu_count_of_current_device() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cache[dev] = cu;
+  return cu;
+}
+
+// ------------------------------------------------------------- validation
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+jfa_status check_problem(const jfa_problem* p) {
+  if (!p) return JFA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads < 1 || p->total_q < 0 || p->total_kv < 0) return JFA_ERR_INVALID_ARG;
+  if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX) return JFA_ERR_INVALID_ARG;
+  if (p->mode < JFA_MODE_SOFTMAX || p->mode > JFA_MODE_GELU) return JFA_ERR_INVALID_ARG;
+  if (p->dtype < JFA_F32 || p->dtype > JFA_MXFP8_E4M3) return JFA_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return JFA_ERR_INVALID_ARG;
+  if (p->bias_kind < JFA_BIAS_NONE || p->bias_kind > JFA_BIAS_DENSE) return JFA_ERR_INVALID_ARG;
+  if (p->bias_kind == JFA_BIAS_RELPOS && (p->num_buckets < 1 || p->num_buckets > 4096))
+    return JFA_ERR_INVALID_ARG;
+  if (p->kv_len_normalize < -1 || p->kv_len_normalize > 1) return JFA_ERR_INVALID_ARG;
+  if (p->mode == JFA_MODE_SOFTMAX && p->kv_len_normalize == 1) return JFA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->qk_scale)) return JFA_ERR_INVALID_ARG;
+  if (p->bwd_fuse < -1 || p->bwd_fuse > 1) return JFA_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+  if ((int64_t)p->heads * p->head_dim > (1 << 20)) return JFA_ERR_UNSUPPORTED;
+  return JFA_OK;
+}
+
+float qk_scale_of(const jfa_problem& p) {
+  return p.qk_scale != 0.f ? p.qk_scale : 1.0f / std::sqrt((float)p.head_dim);
+}
+int normalize_of(const jfa_problem& p) {
+  if (p.mode == JFA_MODE_SOFTMAX) return 0;
+  return p.kv_len_normalize == 0 ? 0 : 1;
+}
+
+// Tile sizes: query tiles of 64 rows when samples are short on average, else 128.
+jfa_status tile_cfg(const jfa_problem& p, TileCfg* t) {
+  if (p.dtype == JFA_F32) {
+    *t = TileCfg{F32_BM, F32_BN, -1, F32_BM, F32_BN, F32_BN, F32_BM, 0, 1, 1, 1};
+    return JFA_OK;
+  }
+  const bool short_q = p.total_q <= 64 * (int64_t)p.batch;
+  const bool short_kv = p.total_kv <= 64 * (int64_t)p.batch;
+  t->fwd_nw = short_q ? 2 : 4;
+  t->bm = 32 * t->fwd_nw;
+  t->bn = FWD_BN;
+  if (p.split_slots > 0) {
+    t->slots = p.split_slots;
+  } else if (p.split_slots < 0) {
+    t->slots = -1;
+  } else {
+    const int cu = cu_count_of_current_device();
+    if (cu <= 0) return JFA_ERR_LAUNCH;
+    t->slots = cu * (t->fwd_nw == 4 ? 2 : 4);
+  }
+  t->bq_nw = short_q ? 2 : 4;
+  t->bq_bm = 32 * t->bq_nw;
+  t->bq_bn = BQ_BN;
+  t->bk_nw = short_kv ? 2 : 4;
+  t->bk_bn = 32 * t->bk_nw;
+  t->bk_bm = BK_BM;
+  t->fuse = 0;   // single-pass backward classes: not enabled in this build
+  (void)p.bwd_fuse;
+  return JFA_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Layout layout_of(const jfa_problem& p, const TileCfg& tc, int backward) {
+  Layout L{};
+  const int64_t B = p.batch, H = p.heads, d = p.head_dim;
+  const int64_t tiles_f = p.total_q / tc.bm + B + 1;
+  L.cap_slots = tc.slots > 0 ? 2 * (int64_t)tc.slots / H + 2 : 0;
+  L.cap_f = tiles_f + L.cap_slots;
+  L.cap_c = tc.slots > 0 ? (int64_t)tc.slots / H + 2 : 1;
+  L.cap_q = p.total_q / tc.bq_bm + B + 1;
+  L.cap_k = p.total_kv / tc.bk_bn + B + 1;
+  L.cap_t = std::max({L.cap_f, L.cap_q, L.cap_k, tiles_f});
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.header = take(sizeof(WsHeader));
+  L.bias_off = take(8 * (B + 1));
+  L.s_tmp = take(4 * (B + 1));
+  L.t_tmp = take(4 * 4 * (L.cap_t + 1));
+  L.gen_recs = take(16 * L.cap_t);
+  L.gen_slot = take(4 * L.cap_t);
+  L.words_a = take(4 * L.cap_t);
+  L.words_b = take(4 * L.cap_t);
+  L.fwd = take(16 * L.cap_f);
+  L.fwd_slot = take(4 * L.cap_f);
+  L.comb = take(16 * L.cap_c);
+  L.bq = take(16 * L.cap_q);
+  L.bk = take(16 * L.cap_k);
+  if (!backward && L.cap_slots > 0) {
+    L.part_acc = take(4 * (size_t)L.cap_slots * H * tc.bm * d);
+    L.part_ml = take(4 * 2 * (size_t)L.cap_slots * H * tc.bm);
+  }
+  if (backward && p.mode == JFA_MODE_SOFTMAX) L.delta = take(4 * (size_t)H * std::max<int64_t>(p.total_q, 1));
+  L.total = off;
+  return L;
+}
+
+SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, char* ws,
+                     const int32_t* q_off, const int32_t* kv_off) {
+  SchedArgs a{};
+  a.q_off = q_off;
+  a.kv_off = kv_off;
+  a.B = p.batch;
+  a.H = p.heads;
+  a.causal = p.causal;
+  a.total_q = p.total_q;
+  a.total_kv = p.total_kv;
+  a.tc = tc;
+  a.want_bias_off = 1;
+  a.hdr = (WsHeader*)(ws + L.header);
+  a.bias_off = (int64_t*)(ws + L.bias_off);
+  a.s_tmp = (int32_t*)(ws + L.s_tmp);
+  a.t_tmp = (int32_t*)(ws + L.t_tmp);
+  a.gen_recs = (int4*)(ws + L.gen_recs);
+  a.gen_slot = (int32_t*)(ws + L.gen_slot);
+  a.words_a = (uint32_t*)(ws + L.words_a);
+  a.words_b = (uint32_t*)(ws + L.words_b);
+  a.fwd = (int4*)(ws + L.fwd);
+  a.fwd_slot = (int32_t*)(ws + L.fwd_slot);
+  a.comb = (int4*)(ws + L.comb);
+  a.bq = (int4*)(ws + L.bq);
+  a.bk = (int4*)(ws + L.bk);
+  a.cap_f = L.cap_f;
+  a.cap_c = L.cap_c;
+  a.cap_q = L.cap_q;
+  a.cap_k = L.cap_k;
+  a.cap_t = L.cap_t;
+  a.cap_slots = L.cap_slots;
+  a.counts_copy = nullptr;
+  return a;
+}
+
+jfa_status from_hip(hipError_t e) { return e == hipSuccess ? JFA_OK : JFA_ERR_LAUNCH; }
+
+// ------------------------------------------------------------------ timing
+struct TimingRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRec> g_timing;
+long g_timing_open = -1;   // index of the record waiting for its stop event
+
+}  // namespace
+
+void timing_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on) return;
+  TimingRec r;
+  r.name = name;
+  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+  if (hipEventRecord(r.start, s) != hipSuccess) return;
+  g_timing.push_back(r);
+  g_timing_open = (long)g_timing.size() - 1;
+}
+
+void timing_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on || g_timing_open < 0) return;
+  (void)hipEventRecord(g_timing[g_timing_open].stop, s);
+  g_timing_open = -1;
+}
+
+int resident_grid(const void* kernel, int threads, size_t dyn_lds, int cu_count) {
+  static std::mutex mu;
+  static std::unordered_map<std::string, int> cache;
+  const std::string key = std::to_string((uintptr_t)kernel) + ":" + std::to_string(threads) + ":" +
+                          std::to_string(dyn_lds);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second * cu_count;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = per_cu;
+  return per_cu * cu_count;
+}
+
+}  // namespace jfa
+
+using namespace jfa;
+
+extern "C" {
+
+const char* jfa_status_string(jfa_status s) {
+  switch (s) {
+    case JFA_OK: return "JFA_OK";
+    case JFA_ERR_INVALID_ARG: return "JFA_ERR_INVALID_ARG";
+    case JFA_ERR_UNSUPPORTED: return "JFA_ERR_UNSUPPORTED";
+    case JFA_ERR_WORKSPACE: return "JFA_ERR_WORKSPACE";
+    case JFA_ERR_LAUNCH: return "JFA_ERR_LAUNCH";
+    case JFA_ERR_DEVICE_DATA: return "JFA_ERR_DEVICE_DATA";
+  }
+  return "JFA_UNKNOWN_STATUS";
+}
+
+jfa_status jfa_tile_config(const jfa_problem* p, int32_t cfg_out[8]) {
+  jfa_status st = check_problem(p);
+  if (st != JFA_OK) return st;
+  if (!cfg_out) return JFA_ERR_INVALID_ARG;
+  TileCfg tc;
+  st = tile_cfg(*p, &tc);
+  if (st != JFA_OK) return st;
+  const int32_t v[8] = {tc.bm, tc.bn, tc.slots, tc.bq_bm, tc.bq_bn, tc.bk_bn, tc.bk_bm, tc.fuse};
+  std::memcpy(cfg_out, v, sizeof(v));
+  return JFA_OK;
+}
+
+size_t jfa_workspace_bytes(const jfa_problem* p, int backward) {
+  if (check_problem(p) != JFA_OK) return 0;
+  TileCfg tc;
+  if (tile_cfg(*p, &tc) != JFA_OK) return 0;
+  return layout_of(*p, tc, backward ? 1 : 0).total;
+}
+
+jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const void* v,
+                       const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                       const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                       void* o, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  jfa_status st = check_problem(p);
+  if (st != JFA_OK) return st;
+  const bool fp8 = p->dtype == JFA_MXFP8_E4M3;
+  if (!q || !k || !v || !o || !q_offsets || !kv_offsets || !workspace) return JFA_ERR_INVALID_ARG;
+  if (fp8 && (!q_scale || !k_scale || !v_scale)) return JFA_ERR_INVALID_ARG;
+  if ((p->bias_kind != JFA_BIAS_NONE) != (bias != nullptr)) return JFA_ERR_INVALID_ARG;
+  if (p->mode == JFA_MODE_SOFTMAX && !lse) return JFA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 256) || !aligned(q_offsets, 4) || !aligned(kv_offsets, 4) ||
+      (lse && !aligned(lse, 4)) || (bias && !aligned(bias, 4)))
+    return JFA_ERR_INVALID_ARG;
+  TileCfg tc;
+  st = tile_cfg(*p, &tc);
+  if (st != JFA_OK) return st;
+  const Layout L = layout_of(*p, tc, 0);
+  if (workspace_bytes < L.total) return JFA_ERR_WORKSPACE;
+  const int cu = cu_count_of_current_device();
+  if (cu <= 0) return JFA_ERR_LAUNCH;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
+  hipError_t e = launch_schedule(a, s);
+  if (e != hipSuccess) return JFA_ERR_LAUNCH;
+
+  FwdParams fp{};
+  fp.q = q; fp.k = k; fp.v = v;
+  fp.q_sc = q_scale; fp.k_sc = k_scale; fp.v_sc = v_scale;
+  fp.q_off = q_offsets; fp.kv_off = kv_offsets;
+  fp.bias = bias;
+  fp.bias_off = (const int64_t*)(ws + L.bias_off);
+  fp.o = o; fp.lse = lse;
+  fp.hdr_ro = (const WsHeader*)(ws + L.header);
+  fp.hdr = (WsHeader*)(ws + L.header);
+  fp.recs = (const int4*)(ws + L.fwd);
+  fp.rec_slot = (const int32_t*)(ws + L.fwd_slot);
+  fp.comb = (const int4*)(ws + L.comb);
+  fp.part_acc = L.cap_slots > 0 ? (float*)(ws + L.part_acc) : nullptr;
+  fp.part_ml = L.cap_slots > 0 ? (float*)(ws + L.part_ml) : nullptr;
+  fp.H = p->heads;
+  fp.causal = p->causal;
+  fp.bias_kind = p->bias_kind;
+  fp.num_buckets = p->num_buckets;
+  fp.normalize = normalize_of(*p);
+  fp.scale = qk_scale_of(*p);
+  fp.total_q = p->total_q;
+  e = launch_forward(fp, tc, p->head_dim, p->mode, p->dtype, L.cap_f * p->heads,
+                     L.cap_c * p->heads, cu, s);
+  return from_hip(e);
+}
+
+jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  jfa_status st = check_problem(p);
+  if (st != JFA_OK) return st;
+  if (p->dtype == JFA_MXFP8_E4M3) return JFA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || !q_offsets || !kv_offsets || !workspace)
+    return JFA_ERR_INVALID_ARG;
+  if ((p->bias_kind != JFA_BIAS_NONE) != (bias != nullptr)) return JFA_ERR_INVALID_ARG;
+  if (p->mode == JFA_MODE_SOFTMAX && (!o || !lse)) return JFA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || (o && !aligned(o, 16)) ||
+      !aligned(workspace, 256) || !aligned(q_offsets, 4) || !aligned(kv_offsets, 4) ||
+      (lse && !aligned(lse, 4)) || (bias && !aligned(bias, 4)))
+    return JFA_ERR_INVALID_ARG;
+  TileCfg tc;
+  st = tile_cfg(*p, &tc);
+  if (st != JFA_OK) return st;
+  const Layout L = layout_of(*p, tc, 1);
+  if (workspace_bytes < L.total) return JFA_ERR_WORKSPACE;
+  const int cu = cu_count_of_current_device();
+  if (cu <= 0) return JFA_ERR_LAUNCH;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
+  hipError_t e = launch_schedule(a, s);
+  if (e != hipSuccess) return JFA_ERR_LAUNCH;
+
+  BwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse; bp.dout = dout;
+  bp.q_off = q_offsets; bp.kv_off = kv_offsets;
+  bp.bias = bias;
+  bp.bias_off = (const int64_t*)(ws + L.bias_off);
+  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.delta = p->mode == JFA_MODE_SOFTMAX ? (float*)(ws + L.delta) : nullptr;
+  bp.hdr = (WsHeader*)(ws + L.header);
+  bp.bq = (const int4*)(ws + L.bq);
+  bp.bk = (const int4*)(ws + L.bk);
+  bp.H = p->heads;
+  bp.causal = p->causal;
+  bp.bias_kind = p->bias_kind;
+  bp.num_buckets = p->num_buckets;
+  bp.normalize = normalize_of(*p);
+  bp.mode = p->mode;
+  bp.fuse = tc.fuse;
+  bp.bq_bm = tc.bq_bm;
+  bp.bk_bn = tc.bk_bn;
+  bp.scale = qk_scale_of(*p);
+  bp.total_q = p->total_q;
+  bp.total_kv = p->total_kv;
+  e = launch_backward(bp, tc, p->head_dim, p->dtype, L.cap_q * p->heads, L.cap_k * p->heads, cu, s);
+  return from_hip(e);
+}
+
+jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
+                              const int32_t* kv_offsets, int32_t* fwd, int32_t* fwd_slot,
+                              int32_t* comb, int32_t* bwd_q, int32_t* bwd_kv, int32_t* counts,
+                              int64_t capacity, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  jfa_status st = check_problem(p);
+  if (st != JFA_OK) return st;
+  if (!q_offsets || !kv_offsets || !fwd || !fwd_slot || !comb || !bwd_q || !bwd_kv || !counts ||
+      !workspace || capacity < 0)
+    return JFA_ERR_INVALID_ARG;
+  TileCfg tc;
+  st = tile_cfg(*p, &tc);
+  if (st != JFA_OK) return st;
+  const Layout L = layout_of(*p, tc, 0);
+  if (workspace_bytes < L.total) return JFA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
+  a.fwd = (int4*)fwd;
+  a.fwd_slot = fwd_slot;
+  a.comb = (int4*)comb;
+  a.bq = (int4*)bwd_q;
+  a.bk = (int4*)bwd_kv;
+  a.cap_f = std::min<int64_t>(capacity, L.cap_f);
+  a.cap_c = std::min<int64_t>(capacity, L.cap_c);
+  a.cap_q = std::min<int64_t>(capacity, L.cap_q);
+  a.cap_k = std::min<int64_t>(capacity, L.cap_k);
+  a.counts_copy = counts;
+  return from_hip(launch_schedule(a, (hipStream_t)stream));
+}
+
+jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t* offsets,
+                                  int32_t* status, void* stream) {
+  if (!lengths || !offsets || batch < 0) return JFA_ERR_INVALID_ARG;
+  if (!aligned(lengths, 4) || !aligned(offsets, 4) || (status && !aligned(status, 4)))
+    return JFA_ERR_INVALID_ARG;
+  return from_hip(launch_lengths_to_offsets(lengths, batch, offsets, status, (hipStream_t)stream));
+}
+
+jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
+                              uint8_t* scales, void* stream) {
+  if (!x_bf16 || !codes || !scales || rows < 0 || d <= 0 || d % 32 != 0) return JFA_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 8)) return JFA_ERR_INVALID_ARG;
+  return from_hip(launch_quantize_mxfp8(x_bf16, rows, d, codes, scales, (hipStream_t)stream));
+}
+
+jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* status_out) {
+  if (!workspace || !status_out) return JFA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return JFA_ERR_LAUNCH;
+  int32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return JFA_ERR_LAUNCH;
+  *status_out = v;
+  return JFA_OK;
+}
+
+void jfa_set_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = enable != 0;
+}
+
+jfa_status jfa_kernel_timing(const char* name_prefix, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return JFA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  const std::string pre = name_prefix ? name_prefix : "";
+  double tot = 0.0;
+  int64_t cnt = 0;
+  for (auto& r : g_timing) {
+    if (r.name.compare(0, pre.size(), pre) != 0) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return JFA_ERR_LAUNCH;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return JFA_ERR_LAUNCH;
+    tot += ms;
+    ++cnt;
+  }
+  *total_ms = tot;
+  *launches = cnt;
+  return JFA_OK;
+}
+
+void jfa_kernel_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& r : g_timing) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_timing.clear();
+  g_timing_open = -1;
+}
+
+}  // extern "C"

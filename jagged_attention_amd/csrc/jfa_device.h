@@ -1,0 +1,100 @@
+// Device helpers shared by the libjfa kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+enum Mode { MODE_SOFTMAX = 0, MODE_SILU = 1, MODE_GELU = 2 };
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);   // round to nearest even
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// 32x32x16 bf16 MFMA: C[m][n] += sum_k A[m][k] B[k][n].  Lane l supplies A row (l % 32) and
+// B column (l % 32), eight k values chosen by l / 32; C element i of lane l is
+// (row 8*(i/4) + 4*(l/32) + i%4, column l % 32).
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 E4M3 MFMA with E8M0 block scales.  Lane (r, g) = (l % 32, l / 32) supplies 32 codes
+// of row r: bytes 0..15 belong to k block 0 and bytes 16..31 to k block 1 of the instruction;
+// its scale byte is the scale of row r's k block g.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 cat_bf16x8(u32x2 lo, u32x2 hi) {
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Relative-position bucket: exact below 16, four buckets per doubling, clamped to nb - 1.
+__device__ __forceinline__ int relpos_bucket(int x, int nb) {
+  x = x < 0 ? -x : x;
+  int bkt = x;
+  if (x >= 16) {
+    const int k = 31 - __clz(x);
+    bkt = 16 + 4 * (k - 4) + ((x >> (k - 2)) & 3);
+  }
+  return bkt < nb - 1 ? bkt : nb - 1;
+}
+
+// GDPA activations (fp32).  SiLU x*sigmoid(x); GELU 0.5 x (1 + erf(x / sqrt 2)).
+template <int MODE>
+__device__ __forceinline__ float act_f(float x) {
+  if (MODE == MODE_SILU) return x * fast_rcp(1.0f + __expf(-x));
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+template <int MODE>
+__device__ __forceinline__ float act_grad_f(float x) {
+  if (MODE == MODE_SILU) {
+    const float sg = fast_rcp(1.0f + __expf(-x));
+    return sg * (1.0f + x * (1.0f - sg));
+  }
+  const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
+  return cdf + x * pdf;
+}
+
+// E4M3 code (sign, 4-bit exponent bias 7, 3-bit mantissa, subnormals) to float.
+__device__ __forceinline__ float e4m3_to_f(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, f = c & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (f << 20))
+                : (float)f * 0.001953125f;   // f * 2^-9
+  return (c & 128u) ? -mag : mag;
+}
+// 2^(s - 127) for an E8M0 scale code s (0..254).
+__device__ __forceinline__ float e8m0_to_f(uint32_t s) {
+  return s == 0 ? 5.877471754111438e-39f : __uint_as_float(s << 23);
+}
+
+// Workgroup-wide work ticket: thread 0 takes the next item, everyone gets it.
+__device__ __forceinline__ int64_t next_ticket(uint32_t* counter, int* slot) {
+  if (threadIdx.x == 0) *slot = (int)atomicAdd(counter, 1u);
+  __syncthreads();
+  const int64_t w = *slot;
+  __syncthreads();
+  return w;
+}
+
+}  // namespace jfa

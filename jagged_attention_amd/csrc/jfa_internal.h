@@ -1,0 +1,162 @@
+// Internal declarations shared by the libjfa HIP sources (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/jfa.h"
+
+namespace jfa {
+
+// ------------------------------------------------------------------ tiles
+// Forward (bf16 / MXFP8): one workgroup owns FWD_BM query rows (32 per wave) of one head and
+// walks the sample's keys FWD_BN at a time.
+constexpr int FWD_BN = 64;
+// fp32 path (SIMT): one thread per query (or key) row, 64 rows per workgroup.
+constexpr int F32_BM = 64;
+constexpr int F32_BN = 64;
+// Backward q-stationary pass: 32 query rows per wave, keys in steps of BQ_BN.
+constexpr int BQ_BN = 64;
+// Backward kv-stationary pass: 32 key rows per wave, queries in steps of BK_BM.
+constexpr int BK_BM = 64;
+
+// Upper bound of a record's cost (kv or q steps) that the list sort accepts.
+constexpr int MAX_COST = 4095;
+
+// ------------------------------------------------------------ workspace
+// Header at the start of every workspace (device memory, 256 bytes).
+struct WsHeader {
+  int32_t status;      // JFA_OK or JFA_ERR_DEVICE_DATA
+  int32_t counts[8];   // forward, combine, q-stationary, kv-stationary records, threshold, slots
+  uint32_t tickets[8]; // work counters for persistent kernels, zeroed by the scheduler
+  int32_t pad[64 - 17];
+};
+static_assert(sizeof(WsHeader) == 256, "header size");
+
+enum Ticket { TK_FWD = 0, TK_COMB = 1, TK_BQ = 2, TK_BK = 3, TK_DELTA = 4 };
+
+struct TileCfg {
+  int bm, bn;          // forward tile rows (query), kv step rows
+  int slots;           // split slots (<=0: no split)
+  int bq_bm, bq_bn;    // q-stationary backward
+  int bk_bn, bk_bm;    // kv-stationary backward
+  int fuse;            // single-pass backward classes
+  int fwd_nw, bq_nw, bk_nw;   // waves per workgroup of the three MFMA kernels
+};
+
+// Byte layout of the workspace for one problem.
+struct Layout {
+  size_t header, bias_off, s_tmp, t_tmp, gen_recs, gen_slot, words_a, words_b;
+  size_t fwd, fwd_slot, comb, bq, bk;
+  size_t part_acc, part_ml, delta;
+  size_t total;
+  int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
+};
+
+// ------------------------------------------------------- scheduler args
+struct SchedArgs {
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  int32_t B, H, causal;
+  int64_t total_q, total_kv;
+  TileCfg tc;
+  int want_bias_off;
+  WsHeader* hdr;
+  int64_t* bias_off;
+  int32_t* s_tmp;      // per-sample scratch [4][B+1]
+  int32_t* t_tmp;      // per-tile scratch [4][cap_t+1]
+  int4* gen_recs;      // records in generation order
+  int32_t* gen_slot;
+  uint32_t* words_a;   // sort buffers (global fallback)
+  uint32_t* words_b;
+  int4* fwd;
+  int32_t* fwd_slot;
+  int4* comb;
+  int4* bq;
+  int4* bk;
+  int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
+  int32_t* counts_copy; // optional: counts also written here (test hook)
+};
+
+// ----------------------------------------------------- kernel parameters
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* q_sc;
+  const uint8_t* k_sc;
+  const uint8_t* v_sc;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const void* bias;
+  const int64_t* bias_off;
+  void* o;
+  float* lse;
+  const WsHeader* hdr_ro;
+  WsHeader* hdr;
+  const int4* recs;
+  const int32_t* rec_slot;
+  const int4* comb;
+  float* part_acc;
+  float* part_ml;
+  int32_t H;
+  int32_t causal;
+  int32_t bias_kind;
+  int32_t num_buckets;
+  int32_t normalize;
+  float scale;        // qk scale
+  int64_t total_q;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const void* bias;
+  const int64_t* bias_off;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // [H][total_q] (softmax)
+  WsHeader* hdr;
+  const int4* bq;
+  const int4* bk;
+  int32_t H;
+  int32_t causal;
+  int32_t bias_kind;
+  int32_t num_buckets;
+  int32_t normalize;
+  int32_t mode;
+  int32_t fuse;
+  int32_t bq_bm;       // q-stationary tile rows (for the single-pass class test)
+  int32_t bk_bn;       // kv-stationary tile rows
+  float scale;
+  int64_t total_q;
+  int64_t total_kv;
+};
+
+// ---------------------------------------------------------- launchers
+// Each returns hipSuccess or the first launch error.  `grid_slots` sizes persistent grids.
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t s);
+hipError_t launch_lengths_to_offsets(const int32_t* len, int32_t B, int32_t* off, int32_t* status,
+                                     hipStream_t s);
+hipError_t launch_forward(const FwdParams& p, const TileCfg& tc, int head_dim, int mode, int dtype,
+                          int64_t max_items, int64_t max_comb_items, int cu_count, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, int dtype,
+                           int64_t max_q_items, int64_t max_k_items, int cu_count, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+
+// Kernel timing hooks (api.cpp): bracket a launch with events when timing is enabled.
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
+// Persistent-grid size: concurrent workgroups of `kernel` on the device (at least 1 per CU).
+int resident_grid(const void* kernel, int threads, size_t dyn_lds, int cu_count);
+
+}  // namespace jfa

@@ -1,0 +1,373 @@
+// Jagged tile scheduler and offsets.
+//
+// Source: "Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a Different Stack",
+// section "Bottleneck move 1": once padding is removed, short and long samples finish at
+// different times, which exposes tile scheduling and backward accumulation; FAQ "What is a
+// jagged tensor?": values plus offsets.  The pages give no schedule; this one is:
+//  - forward: one record per (sample, query tile) covering the kv steps that tile can see
+//    (causal bottom-right alignment); a tile with more than C kv steps, where
+//    C = max(8, ceil(H * total_cost / slots)), splits into ceil(steps / C) near-equal chunks
+//    whose partial results a combine pass merges in chunk order;
+//  - backward: a query-stationary list (dQ) and a key-stationary list (dK, dV); a sample with
+//    one query tile (or else one key tile) takes a single pass that owns all its gradients;
+//  - every list is ordered longest first, ties by (sample, tile, first step): a total order,
+//    so the lists are unique and bit-reproducible.
+// One workgroup of 1024 threads does all of it with block scans and a stable 4-bit LSD radix
+// sort on the inverted cost; no host round trip.
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+constexpr int ST = 1024;
+constexpr int SW = ST / 64;
+constexpr int LDS_SORT_MAX = 8192;
+
+__device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Exclusive scan of one value per thread over the workgroup; *total receives the sum.
+__device__ int64_t block_scan(int64_t v, int64_t* total, int64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int64_t w = lane < SW ? red[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < SW; o <<= 1) {
+      int64_t y = __shfl_up(w, o, 64);
+      if (lane >= o) w += y;
+    }
+    if (lane < SW) red[lane] = w;
+  }
+  __syncthreads();
+  const int64_t pre = wave > 0 ? red[wave - 1] : 0;
+  *total = red[SW - 1];
+  __syncthreads();
+  return pre + x - v;
+}
+
+// out[i] = sum_{k<i} f(k) for i in [0, L]; returns the total.
+template <typename OutT, class F>
+__device__ int64_t scan_to(OutT* out, int64_t L, F f, int64_t* red) {
+  int64_t carry = 0;
+  for (int64_t base = 0; base < L; base += ST) {
+    const int64_t i = base + threadIdx.x;
+    const int64_t v = i < L ? f(i) : 0;
+    int64_t tot;
+    const int64_t ex = block_scan(v, &tot, red);
+    if (i < L) out[i] = (OutT)(carry + ex);
+    carry += tot;
+  }
+  if (threadIdx.x == 0) out[L] = (OutT)carry;
+  __syncthreads();
+  return carry;
+}
+
+// Largest b with base[b] <= x, for base[0] = 0 <= x < base[B].
+__device__ int owner_of(const int32_t* base, int B, int64_t x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (base[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Stable ascending sort of words by bits [20, 32), three 4-bit passes; result ends in b.
+__device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t* red) {
+  const int tid = threadIdx.x;
+  const int ipt = (n + ST - 1) / ST;
+  const int lo = min(n, tid * ipt), hi = min(n, lo + ipt);
+  uint32_t* src = a;
+  uint32_t* dst = b;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = 20 + 4 * pass;
+    for (int d = 0; d < 16; ++d) T[d * ST + tid] = 0;
+    for (int i = lo; i < hi; ++i) T[((src[i] >> sh) & 15) * ST + tid] += 1;
+    __syncthreads();
+    int64_t s = 0;
+    for (int k = 0; k < 16; ++k) s += T[tid * 16 + k];
+    int64_t tot;
+    int64_t run = block_scan(s, &tot, red);
+    for (int k = 0; k < 16; ++k) {
+      const int32_t c = T[tid * 16 + k];
+      T[tid * 16 + k] = (int32_t)run;
+      run += c;
+    }
+    __syncthreads();
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t w = src[i];
+      const int d = (w >> sh) & 15;
+      const int32_t p = T[d * ST + tid];
+      T[d * ST + tid] = p + 1;
+      dst[p] = w;
+    }
+    __syncthreads();
+    uint32_t* t = src; src = dst; dst = t;
+  }
+  // three passes: a -> b -> a -> b
+}
+
+struct Shared {
+  uint32_t sa[LDS_SORT_MAX];
+  uint32_t sb[LDS_SORT_MAX];
+  int32_t T[16 * ST];
+  int64_t red[SW];
+  int32_t flag;
+  int64_t sumcost;
+};
+
+// Sorts gen_recs[0..n) by cost (desc, stable) into out / out_slot; costs[] in t_cost.
+__device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32_t* t_cost,
+                              int4* out, int32_t* out_slot) {
+  uint32_t* wa = n <= LDS_SORT_MAX ? sh.sa : a.words_a;
+  uint32_t* wb = n <= LDS_SORT_MAX ? sh.sb : a.words_b;
+  for (int i = threadIdx.x; i < n; i += ST)
+    wa[i] = ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i;
+  __syncthreads();
+  radix_sort(wa, wb, n, sh.T, sh.red);
+  for (int i = threadIdx.x; i < n; i += ST) {
+    const uint32_t idx = wb[i] & 0xFFFFFu;
+    out[i] = a.gen_recs[idx];
+    if (out_slot) out_slot[i] = a.gen_slot[idx];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  const TileCfg tc = a.tc;
+
+  // ---- validation of the offsets (and the sort's cost limit)
+  if (tid == 0) sh.flag = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int b = tid; b < B; b += ST) {
+    const int64_t n = (int64_t)a.q_off[b + 1] - a.q_off[b];
+    const int64_t m = (int64_t)a.kv_off[b + 1] - a.kv_off[b];
+    if (n < 0 || m < 0) bad = 1;
+    else if (cdiv(m, min(tc.bn, tc.bq_bn)) > MAX_COST || cdiv(n, tc.bk_bm) > MAX_COST) bad = 1;
+  }
+  if (tid == 0 && (a.q_off[0] != 0 || a.kv_off[0] != 0 || a.q_off[B] != a.total_q ||
+                   a.kv_off[B] != a.total_kv))
+    bad = 1;
+  if (bad) atomicOr(&sh.flag, 1);
+  __syncthreads();
+  if (sh.flag) {
+    if (tid == 0) {
+      a.hdr->status = JFA_ERR_DEVICE_DATA;
+      for (int i = 0; i < 8; ++i) a.hdr->counts[i] = 0;
+      for (int i = 0; i < 8; ++i) a.hdr->tickets[i] = 0;
+      if (a.counts_copy) {
+        for (int i = 0; i < 8; ++i) a.counts_copy[i] = 0;
+        a.counts_copy[6] = JFA_ERR_DEVICE_DATA;
+      }
+    }
+    return;
+  }
+
+  const int32_t* qo = a.q_off;
+  const int32_t* ko = a.kv_off;
+  auto qlen = [&](int b) -> int64_t { return (int64_t)qo[b + 1] - qo[b]; };
+  auto klen = [&](int b) -> int64_t { return (int64_t)ko[b + 1] - ko[b]; };
+
+  // ---- dense-bias offsets: running sum of q_len * kv_len
+  if (a.want_bias_off)
+    scan_to(a.bias_off, B, [&](int64_t b) { return qlen((int)b) * klen((int)b); }, sh.red);
+
+  int32_t* s_base = a.s_tmp;                 // per-sample tile base [B+1]
+  int32_t* t_cost = a.t_tmp;                 // per record cost (generation order)
+  int32_t* t_rb = a.t_tmp + (a.cap_t + 1);   // per tile record base
+  int32_t* t_sb = a.t_tmp + 2 * (a.cap_t + 1); // per tile slot base
+  int32_t* t_cb = a.t_tmp + 3 * (a.cap_t + 1); // per tile combine index
+  int overflow = 0;
+
+  // ================= forward list =================
+  const int64_t ntiles = scan_to(s_base, B, [&](int64_t b) { return cdiv(qlen((int)b), tc.bm); },
+                                 sh.red);
+  if (ntiles > a.cap_t) overflow = 1;
+  auto fwd_steps = [&](int64_t tau, int& b, int64_t& t) -> int64_t {
+    b = owner_of(s_base, B, tau);
+    t = tau - s_base[b];
+    const int64_t n = qlen(b), m = klen(b);
+    const int64_t r1 = min((t + 1) * tc.bm, n);
+    int64_t e = m;
+    if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
+    return cdiv(e, tc.bn);
+  };
+  int64_t C = 0;
+  int64_t nrec = 0, nslot = 0, ncomb = 0;
+  if (!overflow) {
+    // total cost -> split threshold
+    int64_t part = 0;
+    for (int64_t tau = tid; tau < ntiles; tau += ST) {
+      int b; int64_t t;
+      part += max((int64_t)1, fwd_steps(tau, b, t));
+    }
+    int64_t tot;
+    block_scan(part, &tot, sh.red);
+    if (tc.slots > 0) C = max((int64_t)8, cdiv((int64_t)a.H * tot, tc.slots));
+    auto nch_of = [&](int64_t tau) -> int64_t {
+      int b; int64_t t;
+      const int64_t s = fwd_steps(tau, b, t);
+      return (C > 0 && s > C) ? cdiv(s, C) : 1;
+    };
+    nrec = scan_to(t_rb, ntiles, nch_of, sh.red);
+    nslot = scan_to(t_sb, ntiles, [&](int64_t tau) { int64_t c = nch_of(tau); return c > 1 ? c : 0; },
+                    sh.red);
+    ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; }, sh.red);
+    if (nrec > a.cap_f || nrec > a.cap_t || ncomb > a.cap_c || nslot > a.cap_slots) overflow = 1;
+  }
+  if (!overflow) {
+    for (int64_t tau = tid; tau < ntiles; tau += ST) {
+      int b; int64_t t;
+      const int64_t s = fwd_steps(tau, b, t);
+      const int64_t nch = (C > 0 && s > C) ? cdiv(s, C) : 1;
+      const int64_t rb = t_rb[tau];
+      for (int64_t c = 0; c < nch; ++c) {
+        const int64_t kb = c * s / nch, ke = (c + 1) * s / nch;
+        a.gen_recs[rb + c] = make_int4(b, (int)t, (int)kb, (int)ke);
+        a.gen_slot[rb + c] = nch > 1 ? (int32_t)(t_sb[tau] + c) : -1;
+        t_cost[rb + c] = (int32_t)max((int64_t)1, ke - kb);
+      }
+      if (nch > 1) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], (int)nch);
+    }
+    __syncthreads();
+    sort_and_emit(a, sh, (int)nrec, t_cost, a.fwd, a.fwd_slot);
+  }
+
+  // ================= q-stationary backward list =================
+  auto one_q = [&](int b) { return tc.fuse && cdiv(qlen(b), tc.bq_bm) == 1; };
+  auto one_k = [&](int b) { return tc.fuse && !one_q(b) && cdiv(klen(b), tc.bk_bn) == 1; };
+  int64_t nq = 0, nk = 0;
+  if (!overflow) {
+    nq = scan_to(s_base, B, [&](int64_t b) { return one_k((int)b) ? 0 : cdiv(qlen((int)b), tc.bq_bm); },
+                 sh.red);
+    if (nq > a.cap_q || nq > a.cap_t) overflow = 1;
+  }
+  if (!overflow) {
+    for (int64_t tau = tid; tau < nq; tau += ST) {
+      const int b = owner_of(s_base, B, tau);
+      const int64_t t = tau - s_base[b];
+      const int64_t n = qlen(b), m = klen(b);
+      int64_t steps;
+      if (one_q(b)) {
+        steps = cdiv(m, tc.bq_bn);
+      } else {
+        const int64_t r1 = min((t + 1) * tc.bq_bm, n);
+        int64_t e = m;
+        if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
+        steps = cdiv(e, tc.bq_bn);
+      }
+      a.gen_recs[tau] = make_int4(b, (int)t, 0, (int)steps);
+      a.gen_slot[tau] = -1;
+      t_cost[tau] = (int32_t)max((int64_t)1, steps);
+    }
+    __syncthreads();
+    sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr);
+  }
+
+  // ================= kv-stationary backward list =================
+  if (!overflow) {
+    nk = scan_to(s_base, B, [&](int64_t b) { return one_q((int)b) ? 0 : cdiv(klen((int)b), tc.bk_bn); },
+                 sh.red);
+    if (nk > a.cap_k || nk > a.cap_t) overflow = 1;
+  }
+  if (!overflow) {
+    for (int64_t tau = tid; tau < nk; tau += ST) {
+      const int b = owner_of(s_base, B, tau);
+      const int64_t u = tau - s_base[b];
+      const int64_t n = qlen(b), m = klen(b);
+      const int64_t nqs = cdiv(n, tc.bk_bm);
+      int64_t first = 0;
+      if (a.causal && !one_k(b)) {
+        const int64_t i0 = max((int64_t)0, u * tc.bk_bn - (m - n));
+        first = i0 >= n ? nqs : i0 / tc.bk_bm;
+      }
+      a.gen_recs[tau] = make_int4(b, (int)u, (int)first, (int)nqs);
+      a.gen_slot[tau] = -1;
+      t_cost[tau] = (int32_t)max((int64_t)1, nqs - first);
+    }
+    __syncthreads();
+    sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr);
+  }
+
+  if (tid == 0) {
+    const int st = overflow ? JFA_ERR_DEVICE_DATA : JFA_OK;
+    a.hdr->status = st;
+    const int32_t cnt[8] = {overflow ? 0 : (int32_t)nrec, overflow ? 0 : (int32_t)ncomb,
+                            overflow ? 0 : (int32_t)nq, overflow ? 0 : (int32_t)nk, (int32_t)C,
+                            overflow ? 0 : (int32_t)nslot, st, 0};
+    for (int i = 0; i < 8; ++i) a.hdr->counts[i] = cnt[i];
+    for (int i = 0; i < 8; ++i) a.hdr->tickets[i] = 0;
+    if (a.counts_copy)
+      for (int i = 0; i < 8; ++i) a.counts_copy[i] = cnt[i];
+  }
+}
+
+// offsets[b+1] = offsets[b] + lengths[b], in int64 with an int32 range check.
+__global__ __launch_bounds__(ST) void lengths_to_offsets_kernel(const int32_t* len, int32_t B,
+                                                                int32_t* off, int32_t* status) {
+  __shared__ int64_t red[SW];
+  __shared__ int32_t flag;
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int64_t carry = 0;
+  int bad = 0;
+  for (int64_t base = 0; base < B; base += ST) {
+    const int64_t i = base + threadIdx.x;
+    const int64_t v = i < B ? (int64_t)len[i] : 0;
+    if (v < 0) bad = 1;
+    int64_t tot;
+    const int64_t ex = block_scan(v, &tot, red);
+    if (i < B) {
+      const int64_t o = carry + ex;
+      if (o > INT32_MAX) bad = 1;
+      off[i] = (int32_t)o;
+    }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    if (carry > INT32_MAX) bad = 1;
+    off[B] = (int32_t)carry;
+  }
+  if (bad) atomicOr(&flag, 1);
+  __syncthreads();
+  if (threadIdx.x == 0 && status) *status = flag ? JFA_ERR_DEVICE_DATA : JFA_OK;
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  const size_t lds = sizeof(Shared);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)schedule_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  timing_begin("jfa_schedule", s);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(ST), lds, s, a);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_lengths_to_offsets(const int32_t* len, int32_t B, int32_t* off, int32_t* status,
+                                     hipStream_t s) {
+  timing_begin("jfa_offsets", s);
+  hipLaunchKernelGGL(lengths_to_offsets_kernel, dim3(1), dim3(ST), 0, s, len, B, off, status);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace jfa

