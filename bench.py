@@ -1,0 +1,337 @@
+"""Benchmark: jagged attention forward + backward on one MI355X.
+
+One step = the whole hot path over one synthetic batch: offsets from lengths, tile lists,
+forward (with split-KV combine), softmax preprocess, dK/dV and dQ passes.  The headline
+workload is causal jagged self-attention over user histories with a relative-position bias
+(B=64, lengths log-normal median 512 clipped to [16, 4096], H=4, d=128, bf16, seed 2).
+Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
+
+Useful FLOPs count only visible (query, key) pairs: 4*d per pair forward, 10*d backward.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "jagged attention fwd+bwd useful TFLOP/s and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(q_lens, kv_lens, causal):
+    n = q_lens.astype(np.int64)
+    m = kv_lens.astype(np.int64)
+    if not causal:
+        return n * m
+    # key j visible to query i iff j <= i + (m - n): sum over i of clamp(i + m - n + 1, 0, m)
+    out = np.zeros_like(n)
+    for b in range(len(n)):
+        i = np.arange(n[b])
+        out[b] = np.clip(i + m[b] - n[b] + 1, 0, m[b]).sum()
+    return out
+
+
+class Workload:
+    """Device buffers and preallocated outputs for one jfa_synth case."""
+
+    def __init__(self, case, with_backward=True):
+        import torch
+        import jagged_attention_amd as jfa
+        self.case = case
+        dev = torch.device("cuda:0")
+        self.q = case.q.to(dev)
+        self.k = case.k.to(dev)
+        self.v = case.v.to(dev)
+        self.bias = None if case.bias is None else case.bias.to(dev)
+        self.dout = case.dout.to(dev) if (with_backward and case.dout is not None) else None
+        self.q_lens = torch.as_tensor(case.q_lens, dtype=torch.int32, device=dev)
+        self.kv_lens = torch.as_tensor(case.kv_lens, dtype=torch.int32, device=dev)
+        self.qo = torch.empty(case.batch + 1, dtype=torch.int32, device=dev)
+        self.ko = torch.empty(case.batch + 1, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(2, dtype=torch.int32, device=dev)
+        self.fp8 = case.dtype == "mxfp8"
+        if self.fp8:
+            # the quantiser is part of the MXFP8 input path and runs inside every step
+            self.qc, self.qs = jfa.quantize_mxfp8(self.q)
+            self.kc, self.ks = jfa.quantize_mxfp8(self.k)
+            self.vc, self.vs = jfa.quantize_mxfp8(self.v)
+        self.problem = jfa.make_problem(case.batch, case.heads, case.head_dim, case.total_q,
+                                        case.total_kv, mode=case.mode,
+                                        dtype=case.dtype, causal=case.causal,
+                                        bias_kind=case.bias_kind, num_buckets=case.num_buckets)
+        odt = torch.float32 if case.dtype == "f32" else torch.bfloat16
+        self.o = torch.empty(self.q.shape, dtype=odt, device=dev)
+        self.lse = torch.empty((case.heads, case.total_q), dtype=torch.float32, device=dev) \
+            if case.mode == "softmax" else None
+        nf = jfa.jfa_workspace_bytes(self.problem, False)
+        self.ws_f = torch.empty(nf, dtype=torch.uint8, device=dev)
+        self.nf = nf
+        self.with_backward = self.dout is not None
+        if self.with_backward:
+            nb = jfa.jfa_workspace_bytes(self.problem, True)
+            self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.nb = nb
+            self.dq = torch.empty_like(self.q)
+            self.dk = torch.empty_like(self.k)
+            self.dv = torch.empty_like(self.v)
+        pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal) * case.heads
+        self.pairs = int(pairs.sum())
+        d = case.head_dim
+        self.fwd_flops = 4.0 * d * self.pairs
+        self.bwd_flops = 10.0 * d * self.pairs if self.with_backward else 0.0
+
+    def step(self):
+        import jagged_attention_amd as jfa
+        jfa.jfa_lengths_to_offsets(self.q_lens, self.case.batch, self.qo, self.status[0:1])
+        jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko, self.status[1:2])
+        if self.fp8:
+            d = self.case.head_dim
+            for x, c, sc in ((self.q, self.qc, self.qs), (self.k, self.kc, self.ks),
+                             (self.v, self.vc, self.vs)):
+                jfa.jfa_quantize_mxfp8(x, x.numel() // d, d, c, sc)
+            jfa.jfa_forward(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks, self.vs,
+                            self.qo, self.ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
+        else:
+            jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo,
+                            self.ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
+        if self.with_backward:
+            jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse, self.dout,
+                             self.qo, self.ko, self.bias, self.dq, self.dk, self.dv, self.ws_b,
+                             self.nb)
+
+    def algorithmic_bytes(self):
+        """HBM bytes the method must move per step (inputs once, outputs once)."""
+        c = self.case
+        el = 1 if c.dtype == "mxfp8" else (4 if c.dtype == "f32" else 2)
+        sc = (1.0 / 32) if c.dtype == "mxfp8" else 0.0
+        qb = c.total_q * c.heads * c.head_dim * (el + sc)
+        kb = c.total_kv * c.heads * c.head_dim * (el + sc)
+        ob = c.total_q * c.heads * c.head_dim * (4 if c.dtype == "f32" else 2)
+        lse = c.total_q * c.heads * 4 if c.mode == "softmax" else 0
+        bias = 0 if self.bias is None else self.bias.numel() * self.bias.element_size()
+        fwd = qb + 2 * kb + bias + ob + lse
+        bwd = 0
+        if self.with_backward:
+            bwd = qb + 2 * kb + bias + 2 * ob + lse + qb + 2 * kb   # read q,k,v,o,do,lse,bias; write dq,dk,dv
+        return fwd, bwd
+
+
+def time_steps(w, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        w.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        w.step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def kernel_times(w, steps):
+    """Average device time per launch of each library kernel (HIP events on its stream)."""
+    import torch
+    import jagged_attention_amd as jfa
+    jfa.jfa_kernel_timing_reset()
+    jfa.jfa_set_kernel_timing(True)
+    for _ in range(steps):
+        w.step()
+    torch.cuda.synchronize()
+    jfa.jfa_set_kernel_timing(False)
+    out = {}
+    for name in ("jfa_offsets", "jfa_schedule", "jfa_quant_mxfp8", "jfa_fwd_bf16", "jfa_fwd_mxfp8",
+                 "jfa_fwd_f32",
+                 "jfa_fwd_combine", "jfa_bwd_delta", "jfa_bwd_dkdv", "jfa_bwd_dq"):
+        ms, n = jfa.jfa_kernel_timing(name)
+        if n:
+            out[name] = dict(avg_ms=ms / n, launches=n)
+    jfa.jfa_kernel_timing_reset()
+    return out
+
+
+# algorithmic MFMA flops per visible pair (multiples of d) for each kernel
+KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_dkdv": 8,
+                         "jfa_bwd_dq": 6}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jagged_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM traffic of `kernel` per launch from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or rec.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, target_s=15.0):
+    """The oracle (fp64, all host threads) on a bounded sample of the headline workload."""
+    import oracle
+    oracle.build()
+    order = np.arange(case.batch)
+    pairs = visible_pairs(case.q_lens, case.kv_lens, True)
+    # calibrate on the shortest samples, then take samples (in order) up to the time target
+    qo = np.concatenate([[0], np.cumsum(case.q_lens)])
+
+    def sub(idx):
+        idx = np.asarray(idx)
+        ql = case.q_lens[idx]
+        rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in idx])
+        q, k, v, do = (t[rows] for t in (case.q, case.k, case.v, case.dout))
+        return ql, q, k, v, do
+
+    def run(idx):
+        ql, q, k, v, do = sub(idx)
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, ql, ql, causal=True, bias=case.bias, bias_kind="relpos")
+        oracle.backward(q, k, v, do, ql, ql, causal=True, bias=case.bias, bias_kind="relpos")
+        return time.perf_counter() - t0
+
+    small = order[np.argsort(pairs)][:8]
+    t_cal = run(small)
+    rate = (14.0 * 128 * 4 * pairs[small].sum()) / max(t_cal, 1e-6)      # useful flop/s
+    budget = rate * target_s
+    chosen, acc = [], 0.0
+    for b in order:
+        f = 14.0 * 128 * 4 * pairs[b]
+        if acc + f > budget and chosen:
+            continue
+        chosen.append(b)
+        acc += f
+    t = run(chosen)
+    flops = 14.0 * 128 * 4 * pairs[chosen].sum()
+    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=oracle.max_threads(), kind="oracle",
+                sample=f"{len(chosen)} of {case.batch} samples of the headline workload "
+                       f"({int(pairs[chosen].sum())} visible pairs per head, fwd+bwd fp64, "
+                       f"{t:.1f} s)")
+
+
+def bench_config(cfg, steps, warmup, seed=None):
+    from jfa_synth import make_case
+    case = make_case(cfg, seed)
+    w = Workload(case)
+    sec = time_steps(w, steps, warmup)
+    flops = w.fwd_flops + w.bwd_flops
+    peak = PEAK_FP8_TFLOPS if case.dtype == "mxfp8" else PEAK_BF16_TFLOPS
+    fb, bb = w.algorithmic_bytes()
+    intensity = flops / (fb + bb)
+    ceiling = min(peak, intensity * PEAK_HBM_GBS / 1000.0)
+    tf = flops / sec / 1e12
+    return w, dict(workload=case.name, seed=case.seed, ms_per_step=sec * 1e3, tflops=tf,
+                   frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
+                   frac_of_roofline=tf / ceiling, useful_gflop=flops / 1e9,
+                   passes="fwd" if not w.with_backward else "fwd+bwd")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the jagged attention path has no cross-GPU exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import jagged_attention_amd as jfa
+    jfa.load()
+
+    log(f"[bench] headline workload {args.config}: warmup {args.warmup}, steps {args.steps}")
+    w, head = bench_config(args.config, args.steps, args.warmup)
+    log(f"[bench] {head['workload']}: {head['ms_per_step']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s")
+    kt = kernel_times(w, max(3, args.steps // 2))
+    log(f"[bench] kernel times: {json.dumps(kt)}")
+    # dominant MFMA kernel of the step
+    cand = {k: v for k, v in kt.items() if k in KERNEL_FLOPS_PER_PAIR}
+    dom = max(cand, key=lambda k: cand[k]["avg_ms"] * cand[k]["launches"])
+    per_launch_flops = KERNEL_FLOPS_PER_PAIR[dom] * w.case.head_dim * w.pairs
+    achieved = per_launch_flops / (cand[dom]["avg_ms"] * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if "mxfp8" in dom else PEAK_BF16_TFLOPS
+    roof = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
+                unit="TFLOP/s", frac=round(achieved / peak, 4), traffic=traffic_for(dom),
+                flops_per_launch=per_launch_flops, avg_ms=cand[dom]["avg_ms"])
+
+    extra = {}
+    if not args.no_extra:
+        for cfg in (3, 4, 5):
+            if cfg == args.config:
+                continue
+            log(f"[bench] workload {cfg}")
+            wx, r = bench_config(cfg, max(3, args.steps // 2), 2)
+            r["kernels"] = kernel_times(wx, 3)
+            extra[f"workload_{cfg}"] = r
+            del wx
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline")
+        cpu = cpu_baseline(w.case)
+
+    case = w.case
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == "bf16" else case.dtype,
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "batch": case.batch, "heads": case.heads,
+                   "head_dim": case.head_dim, "total_tokens": case.total_q,
+                   "lengths": "log-normal median 512 clipped to [16, 4096]" if args.config == 2
+                   else "see jfa_synth", "mode": case.mode, "causal": case.causal,
+                   "bias": case.bias_kind, "seed": case.seed, "parallelism": "single GPU"},
+        "mfma_peak_frac": round(head["frac_of_mfma_peak"], 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kt,
+        "other_workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
