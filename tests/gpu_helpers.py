@@ -98,3 +98,29 @@ def compare_lse(got, want, mode, tol=1e-3):
     if fin.any():
         err = np.max(np.abs(g[fin] - want[fin]))
         assert err <= tol, f"LSE max-abs {err:.3g}"
+
+
+def sub_case(case, idx):
+    """The samples `idx` of a jfa_synth Case as a Case of their own (rows copied, bias sliced)."""
+    import copy
+    idx = [int(b) for b in idx]
+    ql = case.q_lens.astype(np.int64)
+    kl = case.kv_lens.astype(np.int64)
+    qo = np.concatenate([[0], np.cumsum(ql)])
+    ko = np.concatenate([[0], np.cumsum(kl)])
+    qr = torch.as_tensor(np.concatenate([np.arange(qo[b], qo[b + 1]) for b in idx] +
+                                        [np.zeros(0, np.int64)]))
+    kr = torch.as_tensor(np.concatenate([np.arange(ko[b], ko[b + 1]) for b in idx] +
+                                        [np.zeros(0, np.int64)]))
+    sub = copy.copy(case)
+    sub.q_lens = case.q_lens[idx].copy()
+    sub.kv_lens = case.kv_lens[idx].copy()
+    sub.q = case.q[qr]
+    sub.k = case.k[kr]
+    sub.v = case.v[kr]
+    sub.dout = None if case.dout is None else case.dout[qr]
+    if case.bias_kind == "dense":
+        H = case.heads
+        bo = np.concatenate([[0], np.cumsum(ql * kl)]) * H
+        sub.bias = torch.cat([case.bias[int(bo[b]):int(bo[b + 1])] for b in idx])
+    return sub
