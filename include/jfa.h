@@ -34,6 +34,10 @@
  *  - Streams: `stream` is a hipStream_t (NULL = default stream).  All work is
  *    enqueued asynchronously; nothing blocks the host except
  *    jfa_read_device_status and jfa_kernel_timing.
+ *  - Limits: one sample's rows are addressed with 32-bit byte offsets, so
+ *    (len + 256) * H * d * element_size (bf16 output size for MXFP8) must stay below 2^31
+ *    for every sample, and with a dense bias (q_len + 256) * (kv_len + 256) * 4 too; a sample
+ *    beyond these limits is reported like malformed offsets (JFA_ERR_DEVICE_DATA).
  *  - Errors: host-checkable mistakes return an error before anything is
  *    enqueued.  Malformed offsets found on the device set the status word in
  *    the workspace; the kernels of that call then write nothing, and
@@ -72,7 +76,7 @@ typedef struct {
   int32_t dtype;            /* jfa_dtype: storage type of Q, K, V (and O, dO, dQ, dK, dV
                                for F32/BF16).  MXFP8 is forward only: O is bf16. */
   int32_t causal;           /* 0 or 1; visible iff j <= i + (kv_len - q_len) */
-  float qk_scale;           /* 0 selects 1/sqrt(d) */
+  float qk_scale;           /* > 0, or 0 to select 1/sqrt(d); negative is invalid */
   int32_t kv_len_normalize; /* -1 default (on for SiLU/GELU, off for softmax), 0, 1;
                                must be 0 or -1 for softmax */
   int32_t bias_kind;        /* jfa_bias_kind */

@@ -45,7 +45,7 @@ jfa_status check_problem(const jfa_problem* p) {
     return JFA_ERR_INVALID_ARG;
   if (p->kv_len_normalize < -1 || p->kv_len_normalize > 1) return JFA_ERR_INVALID_ARG;
   if (p->mode == JFA_MODE_SOFTMAX && p->kv_len_normalize == 1) return JFA_ERR_INVALID_ARG;
-  if (!std::isfinite(p->qk_scale)) return JFA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->qk_scale) || p->qk_scale < 0.f) return JFA_ERR_INVALID_ARG;
   if (p->bwd_fuse < -1 || p->bwd_fuse > 1) return JFA_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
   if ((int64_t)p->heads * p->head_dim > (1 << 20)) return JFA_ERR_UNSUPPORTED;
@@ -143,6 +143,9 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.total_kv = p.total_kv;
   a.tc = tc;
   a.want_bias_off = 1;
+  a.hd_bytes = (int64_t)p.heads * p.head_dim * (p.dtype == JFA_F32 ? 4 : (p.dtype == JFA_BF16 ? 2 : 1));
+  if (p.dtype == JFA_MXFP8_E4M3) a.hd_bytes = (int64_t)p.heads * p.head_dim * 2;   // bf16 output rows
+  a.dense_bias = p.bias_kind == JFA_BIAS_DENSE;
   a.hdr = (WsHeader*)(ws + L.header);
   a.bias_off = (int64_t*)(ws + L.bias_off);
   a.s_tmp = (int32_t*)(ws + L.s_tmp);

@@ -8,16 +8,24 @@
 //
 // Design (gfx950):
 //  - A workgroup of NW waves owns BM = 32*NW query rows of one head of one sample and walks
-//    the keys in steps of 64.  K (row-major) and V (transposed) of a step are staged in LDS;
-//    the next step's global loads are issued before the current step's MFMAs.
-//  - Each wave computes S^T = K Q^T (32x32x16 bf16 MFMA, or the scaled 32x32x64 E4M3 MFMA with
-//    the MX block scales applied in hardware).  In the transposed accumulator a lane holds one
-//    query column, so the softmax row max/sum are in-lane reductions plus one exchange with
-//    the lane 32 away, and the probabilities P^T are already laid out as the B operand of
-//    O^T += V^T P^T: no LDS round trip for P.
+//    the keys 64 at a time.  Each step's K tile (row-major) and V tile (stored transposed,
+//    keys permuted so an MFMA operand is one 16-byte read) sit in one of two LDS stages: the
+//    next step's global loads are issued before this step's MFMAs and land in the other
+//    stage after them, so one barrier per step suffices.
+//  - Global loads go through per-(sample, head) buffer resources whose size ends at the
+//    sample's last row: rows past the end read as zeros with no branches.
+//  - Each wave computes S^T = K Q^T (32x32x16 bf16 MFMA, or the scaled 32x32x64 E4M3 MFMA
+//    with the MX block scales applied in hardware).  In the transposed accumulator a lane
+//    holds one query column, so the softmax row max/sum are in-lane reductions plus one
+//    exchange with the lane 32 away, and the probabilities P^T are already laid out as the B
+//    operand of O^T += V^T P^T: no LDS round trip for P.
+//  - The additive bias enters as the initial value of the S^T accumulator (bias / qk_scale),
+//    so it costs no VALU add: a relative-position bias from a per-step diagonal table in
+//    LDS, a dense bias from an LDS tile staged with coalesced loads.
 //  - Softmax keeps (max, sum) online in the log2 domain and rescales the accumulator only when
-//    the running max grows by more than 8 (2^8 headroom in fp32/bf16).  GDPA applies the
-//    activation elementwise and scales by 1/kv_len at the end.
+//    the running max grows by more than 8 (2^8 headroom in fp32); the row sum is kept in
+//    fp32 from the unrounded probabilities.  GDPA applies the activation
+//    elementwise and scales by 1/kv_len at the end.
 //  - Work items (tile record, head) come from the longest-first list; persistent workgroups
 //    take them with an atomic ticket.  Records that are chunks of a split tile write fp32
 //    partials (unnormalised accumulator, max, sum) that the combine kernel merges in chunk
@@ -29,54 +37,71 @@ namespace jfa {
 namespace {
 
 constexpr int BN = FWD_BN;
+enum BiasT { B_NONE = 0, B_RELPOS = 1, B_DENSE = 2 };
 
-// Dynamic LDS layout of the forward kernel.
-template <int D, int NW, bool FP8>
+constexpr int align16(int x) { return (x + 15) / 16 * 16; }
+
+// Dynamic LDS layout of one pipeline stage of the forward kernel (two stages are used).
+template <int D, int NW, int BIAS, bool FP8>
 struct FwdLds {
   static constexpr int BM = 32 * NW;
-  static constexpr int KS = FP8 ? (D + 16) : (D + 8);   // K row stride: bytes (fp8) or bf16
-  static constexpr int VS = BN + 4;                      // V^T row stride (bf16)
-  static constexpr int BS = BN + 4;                      // dense bias row stride (floats)
-  static constexpr int K_BYTES = BN * KS * (FP8 ? 1 : 2);
-  static constexpr int KSC_BYTES = FP8 ? BN * (D / 32) : 0;
-  static constexpr int V_OFF = (K_BYTES + KSC_BYTES + 15) / 16 * 16;
+  static constexpr int KRB = FP8 ? (D + 16) : 2 * (D + 8);   // K row stride in bytes
+  static constexpr int K_BYTES = BN * KRB;
+  static constexpr int KSC_BYTES = FP8 ? BN * 4 : 0;          // K scales: one dword per key
+  static constexpr int VS = BN + 8;                            // V^T row stride (bf16)
+  static constexpr int V_OFF = align16(K_BYTES + KSC_BYTES);
   static constexpr int V_BYTES = D * VS * 2;
-  static constexpr int BIAS_OFF = V_OFF + V_BYTES;
-  static constexpr int bias_bytes(int kind) {
-    return kind == JFA_BIAS_DENSE ? BM * BS * 4 : (kind == JFA_BIAS_RELPOS ? (BM + BN) * 4 : 0);
-  }
-  static constexpr int total(int kind) { return BIAS_OFF + bias_bytes(kind) + 16; }
+  static constexpr int RP = BM + BN + 4;                       // relpos copy length (floats)
+  static constexpr int BS = BN + 8;                            // dense bias row stride (bf16)
+  static constexpr int BIAS_BYTES =
+      BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);
+  static constexpr int B_OFF = V_OFF + V_BYTES;
+  static constexpr int STAGE = align16(B_OFF + BIAS_BYTES);
+  static constexpr int TOTAL = 2 * STAGE;
 };
 
-template <int D, int NW, int MODE, bool FP8>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
-  using L = FwdLds<D, NW, FP8>;
-  constexpr int BM = L::BM, NT = NW * 64, KS = L::KS, VS = L::VS, BS = L::BS;
+// Position of key k (0..63) inside its V^T row: within each group of 16 keys, key
+// 8a + 4g + b sits at 8g + 4a + b, so that the 8 keys an MFMA lane (g) contracts over in one
+// 32x32x16 step are contiguous.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
+}
+
+// Occupancy: two workgroups per CU.  With 4 waves per workgroup that is 2 waves per SIMD
+// (256 registers each); with 2 waves it is one wave per SIMD, which may use all 512.
+template <int D, int NW, int MODE, int BIAS, bool FP8>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2)))
+void fwd_kernel(FwdParams p) {
+  using L = FwdLds<D, NW, BIAS, FP8>;
+  constexpr int BM = L::BM, NT = NW * 64, VS = L::VS;
+  constexpr int ES = FP8 ? 1 : 2;                  // bytes per Q/K/V element
   extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char* k_lds = lds;
-  uint8_t* ksc_lds = lds + L::K_BYTES;
-  __bf16* vt_lds = reinterpret_cast<__bf16*>(lds + L::V_OFF);
-  float* bias_lds = reinterpret_cast<float*>(lds + L::BIAS_OFF);
   __shared__ int s_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int H = p.H;
-  const int64_t n_items = (int64_t)p.hdr_ro->counts[0] * H;
   if (p.hdr_ro->status != JFA_OK) return;
+  const int64_t n_items = (int64_t)p.hdr_ro->counts[0] * H;
+  // scores are handled as raw = q.k + bias/scale; x = raw * c_log is the (log2) logit
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
-  const float b_mul = MODE == MODE_SOFTMAX ? LOG2E : 1.0f;
+  const float inv_scale = 1.0f / p.scale;
+  const uint32_t row_bytes = (uint32_t)H * D * ES;           // stride between tokens
+  const uint32_t sc_row_bytes = (uint32_t)H * (D / 32);      // MXFP8 scales stride
 
-  // per-thread staging registers for one key step
-  constexpr int KROW_CH = FP8 ? D / 16 : D / 8;          // 16-byte chunks per K row
-  constexpr int KCH = (BN * KROW_CH + NT - 1) / NT;
-  constexpr int VBLK = (BN / 4) * (D / 8);               // 4 rows x 8 columns blocks of V
-  constexpr int VPT = (VBLK + NT - 1) / NT;
-  u32x4 kreg[KCH];
+  // staging assignments
+  constexpr int KCH = D * ES / 16;                          // 16-byte chunks per K row
+  constexpr int K_LOADS = BN * KCH / NT;                    // per thread
+  static_assert(BN * KCH % NT == 0, "K staging");
+  constexpr int VBLK = (BN / 4) * (D / 8);                  // 4 keys x 8 dims blocks of V
+  constexpr int V_LOADS = (VBLK + NT - 1) / NT;
+
+  u32x4 kreg[K_LOADS];
   uint32_t kscreg = 0;
-  u32x2 v8reg[FP8 ? VPT : 1][4];
-  u32x4 v16reg[FP8 ? 1 : VPT][4];
-  uint32_t vscreg[VPT][4];
+  u32x4 v16[FP8 ? 1 : V_LOADS][4];
+  u32x2 v8[FP8 ? V_LOADS : 1][4];
+  uint32_t vsc[FP8 ? V_LOADS : 1][4];
+  float rp_val = 0.f;                                        // relpos table entry of this thread
 
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_FWD], &s_ticket);
@@ -93,40 +118,52 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     const int qw0 = q0 + wave * 32;
     const int qil = wave * 32 + l32;        // tile-local query row of this lane
     const int qi = q0 + qil;                // sample-local query row
-    const bool wave_rows = qw0 < n;
     int wave_kend = m;
     if (p.causal) wave_kend = max(0, min(m, min(n, qw0 + 32) + delta));
+    const bool wave_rows = qw0 < n;
+
+    // per-(sample, head) buffer resources: rows past the sample's end read as zero
+    const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * ES : 0;
+    const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * ES : 0;
+    const rsrc_t rk = make_rsrc((const uint8_t*)p.k + ((int64_t)ko * H + h) * D * ES, kv_bytes);
+    const rsrc_t rv = make_rsrc((const uint8_t*)p.v + ((int64_t)ko * H + h) * D * ES, kv_bytes);
+    const rsrc_t rq = make_rsrc((const uint8_t*)p.q + ((int64_t)qo * H + h) * D * ES, q_bytes);
+    rsrc_t rks = rk, rvs = rv, rqs = rq;
+    if constexpr (FP8) {
+      const uint32_t kvs = m > 0 ? ((uint32_t)(m - 1) * H + 1) * (D / 32) : 0;
+      const uint32_t qs = n > 0 ? ((uint32_t)(n - 1) * H + 1) * (D / 32) : 0;
+      rks = make_rsrc(p.k_sc + ((int64_t)ko * H + h) * (D / 32), kvs);
+      rvs = make_rsrc(p.v_sc + ((int64_t)ko * H + h) * (D / 32), kvs);
+      rqs = make_rsrc(p.q_sc + ((int64_t)qo * H + h) * (D / 32), qs);
+    }
+    rsrc_t rb = rk;
+    if constexpr (BIAS == B_DENSE)
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+                     (uint32_t)n * (uint32_t)m * 2u);
 
     // ---- query fragment: B operand (column = query row, k = head dim)
     constexpr int QK = FP8 ? D / 64 : D / 16;
     i32x8 qf8[FP8 ? QK : 1];
     int qsc[FP8 ? QK : 1];
     bf16x8 qf[FP8 ? 1 : QK];
-    if constexpr (FP8) {
-      const uint8_t* qrow = (const uint8_t*)p.q + ((int64_t)(qo + qi) * H + h) * D;
-      const uint8_t* srow = p.q_sc + ((int64_t)(qo + qi) * H + h) * (D / 32);
+    {
+      const uint32_t qoff = (uint32_t)qi * row_bytes;
+      if constexpr (FP8) {
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) {
-        u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-        int sc = 127;
-        if (qi < n) {
-          lo = *(const u32x4*)(qrow + 64 * ks + 16 * g);
-          hi = *(const u32x4*)(qrow + 64 * ks + 32 + 16 * g);
-          sc = srow[2 * ks + g];
+        for (int ks = 0; ks < QK; ++ks) {
+          const u32x4 lo = ld16(rq, qoff + 64 * ks + 16 * g);
+          const u32x4 hi = ld16(rq, qoff + 64 * ks + 32 + 16 * g);
+          i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          qf8[ks] = v;
+          qsc[ks] = (int)ld1(rqs, (uint32_t)qi * sc_row_bytes + 2 * ks + g);
         }
-        i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        qf8[ks] = v;
-        qsc[ks] = sc;
-      }
-    } else {
-      const __bf16* qrow = (const __bf16*)p.q + ((int64_t)(qo + qi) * H + h) * D;
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) {
-        u32x4 v = {0, 0, 0, 0};
-        if (qi < n) v = *(const u32x4*)(qrow + 16 * ks + 8 * g);
-        qf[ks] = as_bf16x8(v);
+        for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(rq, qoff + 32 * ks + 16 * g));
       }
+      // the fragment is complete before the key loop: no wait on it inside the loop
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
 
     f32x16 acc[D / 32];
@@ -136,271 +173,316 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     float m_run = NEG_INF, l_run = 0.f;
 
-    const int64_t bias_base = p.bias_kind == JFA_BIAS_DENSE
-                                  ? (int64_t)H * p.bias_off[b] + (int64_t)h * n * m
-                                  : 0;
-
     // ---- staging: global -> registers for key step kt
     auto load_step = [&](int kt) {
       const int j0 = kt * BN;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int id = tid + i * NT;
-        const int r = id / KROW_CH, c = id % KROW_CH;
-        u32x4 v = {0, 0, 0, 0};
-        if (id < BN * KROW_CH && j0 + r < m) {
-          if constexpr (FP8)
-            v = *(const u32x4*)((const uint8_t*)p.k + ((int64_t)(ko + j0 + r) * H + h) * D + 16 * c);
-          else
-            v = *(const u32x4*)((const __bf16*)p.k + ((int64_t)(ko + j0 + r) * H + h) * D + 8 * c);
+      if constexpr (BIAS == B_RELPOS) {
+        // diagonal table: T[x] = bias(dist = q0 + delta - j0 + BM - 1 - x), issued first so
+        // that waiting for it never waits for the tile loads behind it
+        if (tid < BM + BN - 1) {
+          const int dist = q0 + delta - j0 + BM - 1 - tid;
+          const float* tab = (const float*)p.bias + (int64_t)h * p.num_buckets;
+          rp_val = tab[relpos_bucket(dist, p.num_buckets)];
         }
-        kreg[i] = v;
+      }
+#pragma unroll
+      for (int i = 0; i < K_LOADS; ++i) {
+        const int id = tid + i * NT;
+        const int r = id / KCH, c = id % KCH;
+        kreg[i] = ld16(rk, (uint32_t)(j0 + r) * row_bytes + 16 * c);
       }
       if constexpr (FP8) {
-        // K scales: one row (D/32 bytes, at most 4) per thread
-        kscreg = 0;
         if (tid < BN) {
-          const int r = tid;
-          if (j0 + r < m) {
-            const uint8_t* sp = p.k_sc + ((int64_t)(ko + j0 + r) * H + h) * (D / 32);
-            uint32_t wv = 0;
+          const uint32_t base = (uint32_t)(j0 + tid) * sc_row_bytes;
+          uint32_t wv = 0;
 #pragma unroll
-            for (int e = 0; e < D / 32; ++e) wv |= (uint32_t)sp[e] << (8 * e);
-            kscreg = wv;
-          }
+          for (int e = 0; e < D / 32; ++e) wv |= ld1(rks, base + e) << (8 * e);
+          kscreg = wv;
         }
       }
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
+      for (int i = 0; i < V_LOADS; ++i) {
         const int id = tid + i * NT;
-        const int rb = id % (BN / 4), cb = id / (BN / 4);
+        if (VBLK % NT != 0 && id >= VBLK) break;
+        const int rbk = id % (BN / 4), cb = id / (BN / 4);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int row = j0 + 4 * rb + rr;
-          const bool ok = id < VBLK && row < m;
+          const uint32_t row = (uint32_t)(j0 + 4 * rbk + rr);
           if constexpr (FP8) {
-            u32x2 v = {0, 0};
-            uint32_t sc = 127;
-            if (ok) {
-              v = *(const u32x2*)((const uint8_t*)p.v + ((int64_t)(ko + row) * H + h) * D + 8 * cb);
-              sc = p.v_sc[((int64_t)(ko + row) * H + h) * (D / 32) + (8 * cb) / 32];
-            }
-            v8reg[i][rr] = v;
-            vscreg[i][rr] = sc;
+            v8[i][rr] = ld8(rv, row * row_bytes + 8 * cb);
+            vsc[i][rr] = ld1(rvs, row * sc_row_bytes + (8 * cb) / 32);
           } else {
-            u32x4 v = {0, 0, 0, 0};
-            if (ok) v = *(const u32x4*)((const __bf16*)p.v + ((int64_t)(ko + row) * H + h) * D + 8 * cb);
-            v16reg[i][rr] = v;
+            v16[i][rr] = ld16(rv, row * row_bytes + 16 * cb);
           }
         }
       }
     };
 
-    // ---- staging: registers -> LDS (and the bias tile straight from global)
-    auto store_step = [&](int kt) {
-      const int j0 = kt * BN;
+    // ---- staging: registers -> LDS stage `st` (the dense bias goes global -> LDS here,
+    //      so no registers are held for it across the MFMAs)
+    auto store_step = [&](int st, int kt) {
+      unsigned char* base = lds + st * L::STAGE;
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
+      for (int i = 0; i < K_LOADS; ++i) {
         const int id = tid + i * NT;
-        const int r = id / KROW_CH, c = id % KROW_CH;
-        if (id < BN * KROW_CH) {
-          if constexpr (FP8) *(u32x4*)(k_lds + r * KS + 16 * c) = kreg[i];
-          else *(u32x4*)(k_lds + (r * KS + 8 * c) * 2) = kreg[i];
-        }
+        const int r = id / KCH, c = id % KCH;
+        *(u32x4*)(base + r * L::KRB + 16 * c) = kreg[i];
       }
       if constexpr (FP8) {
-        if (tid < BN) {
-#pragma unroll
-          for (int e = 0; e < D / 32; ++e) ksc_lds[tid * (D / 32) + e] = (kscreg >> (8 * e)) & 255u;
-        }
+        if (tid < BN) *(uint32_t*)(base + L::K_BYTES + 4 * tid) = kscreg;
       }
+      __bf16* vt = reinterpret_cast<__bf16*>(base + L::V_OFF);
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
+      for (int i = 0; i < V_LOADS; ++i) {
         const int id = tid + i * NT;
-        if (id >= VBLK) continue;
-        const int rb = id % (BN / 4), cb = id / (BN / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float f[4];
+        if (VBLK % NT != 0 && id >= VBLK) break;
+        const int rbk = id % (BN / 4), cb = id / (BN / 4);
+        const int pos = vt_pos(4 * rbk);
+        if constexpr (FP8) {
+          // dequantise 4 keys x 8 dims (E4M3 x 2^(s-127)) to bf16, then transpose
+          uint32_t w[4][4];   // [key][pair of dims] bf16x2
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            if constexpr (FP8) {
-              const uint32_t code = (v8reg[i][rr][e >> 2] >> (8 * (e & 3))) & 255u;
-              f[rr] = e4m3_to_f(code) * e8m0_to_f(vscreg[i][rr]);
-            } else {
-              const uint32_t word = v16reg[i][rr][e >> 1];
-              f[rr] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+            const float sc = e8m0_to_f(vsc[i][rr]);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t src = v8[i][rr][e2 >> 1];
+              typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+              const bf2 cv = (e2 & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, true)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, false);
+              w[rr][e2] = __builtin_bit_cast(uint32_t, cv);
             }
           }
-          u32x2 pk = {pack2bf(f[0], f[1]), pack2bf(f[2], f[3])};
-          *(u32x2*)(vt_lds + (8 * cb + e) * VS + 4 * rb) = pk;
-        }
-      }
-      if (p.bias_kind == JFA_BIAS_RELPOS) {
-        // bias by diagonal: entry x holds the bias of (query - key) = x - (BN - 1) in the tile
-        if (tid < BM + BN - 1) {
-          const int dist = tid - (BN - 1) + q0 + delta - j0;
-          const float* tab = (const float*)p.bias + (int64_t)h * p.num_buckets;
-          bias_lds[tid] = tab[relpos_bucket(dist, p.num_buckets)] * b_mul;
-        }
-      } else if (p.bias_kind == JFA_BIAS_DENSE) {
-        const __bf16* bp = (const __bf16*)p.bias + bias_base;
-        for (int e = tid; e < BM * BN; e += NT) {
-          const int r = e / BN, c = e % BN;
-          float v = 0.f;
-          if (q0 + r < n && j0 + c < m) v = (float)bp[(int64_t)(q0 + r) * m + j0 + c];
-          bias_lds[r * BS + c] = v * b_mul;
-        }
-      }
-    };
-
-    if (kb < ke) load_step(kb);
-    for (int kt = kb; kt < ke; ++kt) {
-      __syncthreads();
-      store_step(kt);
-      __syncthreads();
-      if (kt + 1 < ke) load_step(kt + 1);
-      const int j0 = kt * BN;
-      if (!wave_rows || j0 >= wave_kend) continue;
-
-      // ---- S^T = K Q^T for the 64 keys of this step (two 32-key blocks)
-      f32x16 sacc[2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
-        const int krow = blk * 32 + l32;
-        if constexpr (FP8) {
-#pragma unroll
-          for (int ks = 0; ks < QK; ++ks) {
-            const u32x4 lo = *(const u32x4*)(k_lds + krow * KS + 64 * ks + 16 * g);
-            const u32x4 hi = *(const u32x4*)(k_lds + krow * KS + 64 * ks + 32 + 16 * g);
-            i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            const int sa = ksc_lds[krow * (D / 32) + 2 * ks + g];
-            sacc[blk] = mfma_fp8(a, qf8[ks], sacc[blk], sa, qsc[ks]);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const u32x2 lo = {lo_halves(w[0][e2], w[1][e2]), lo_halves(w[2][e2], w[3][e2])};
+            const u32x2 hi = {hi_halves(w[0][e2], w[1][e2]), hi_halves(w[2][e2], w[3][e2])};
+            *(u32x2*)(vt + (8 * cb + 2 * e2) * VS + pos) = lo;
+            *(u32x2*)(vt + (8 * cb + 2 * e2 + 1) * VS + pos) = hi;
           }
         } else {
 #pragma unroll
-          for (int ks = 0; ks < QK; ++ks) {
-            const bf16x8 a = as_bf16x8(*(const u32x4*)(k_lds + (krow * KS + 16 * ks + 8 * g) * 2));
-            sacc[blk] = mfma_bf16(a, qf[ks], sacc[blk]);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const u32x2 lo = {lo_halves(v16[i][0][e2], v16[i][1][e2]),
+                              lo_halves(v16[i][2][e2], v16[i][3][e2])};
+            const u32x2 hi = {hi_halves(v16[i][0][e2], v16[i][1][e2]),
+                              hi_halves(v16[i][2][e2], v16[i][3][e2])};
+            *(u32x2*)(vt + (8 * cb + 2 * e2) * VS + pos) = lo;
+            *(u32x2*)(vt + (8 * cb + 2 * e2 + 1) * VS + pos) = hi;
           }
         }
       }
+      if constexpr (BIAS == B_RELPOS) {
+        float* rp = reinterpret_cast<float*>(base + L::B_OFF);
+        if (tid < BM + BN - 1) {
+          const float v = rp_val * inv_scale;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) rp[k * L::RP + tid + k] = v;
+        }
+      } else if constexpr (BIAS == B_DENSE) {
+        // [BM][BN] block, two adjacent columns per thread, coalesced along rows
+        __bf16* bt = reinterpret_cast<__bf16*>(base + L::B_OFF);
+        const int j0 = kt * BN;
+        constexpr int NB = BM * BN / NT / 2, CH = 4;
+#pragma unroll
+        for (int i0 = 0; i0 < NB; i0 += CH) {
+          uint32_t dv[CH];
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            const int e = 2 * (tid + (i0 + i) * NT);
+            const int r = e / BN, c = e % BN;
+            const int qq = q0 + r, jj = j0 + c;
+            const bool ok = qq < n;
+            const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
+            const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
+            const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
+            dv[i] = lo | (hi << 16);
+          }
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            const int e = 2 * (tid + (i0 + i) * NT);
+            const int r = e / BN, c = e % BN;
+            *(uint32_t*)(bt + r * L::BS + c) = dv[i];
+          }
+        }
+      }
+    };
 
-      // ---- scores: scale, bias, mask (element (blk, i) is key blk*32 + 8(i/4) + 4g + i%4)
-      const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta);
-      float x[2][16];
+    const int nsteps = ke - kb;
+    if (nsteps > 0) {
+      load_step(kb);
+      store_step(0, kb);
+    }
+    __syncthreads();
+    // one key step on LDS stage it&1 (the loop is peeled so that its loads and stores are
+    // unconditional: no load can be pending across the back edge)
+    auto compute_step = [&](int it) {
+      const int kt = kb + it;
+      const int j0 = kt * BN;
+      const unsigned char* sb = lds + (it & 1) * L::STAGE;
+      if (wave_rows && j0 < wave_kend) {
+        // ---- accumulator init = bias / scale (element (blk, i): key blk*32 + 8(i/4) + 4g + i%4)
+        f32x16 sacc[2];
+        if constexpr (BIAS == B_RELPOS) {
+          const float* rp = reinterpret_cast<const float*>(sb + L::B_OFF);
+          const int k = (1 + qil) & 3;                  // copy whose 4-runs are 16-byte aligned
+          const float* src = rp + k * L::RP + k + BM - 1 - qil + 4 * g;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[blk][i] = sacc[blk][i] * c_log;
-        if (p.bias_kind == JFA_BIAS_RELPOS) {
-          const float* br = bias_lds + (qil + BN - 1 - 4 * g) - blk * 32;
+            for (int qd = 0; qd < 4; ++qd) {
+              const f32x4 bv = *(const f32x4*)(src + blk * 32 + 8 * qd);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[blk][i] += br[-(8 * (i >> 2) + (i & 3))];
-        } else if (p.bias_kind == JFA_BIAS_DENSE) {
+              for (int e = 0; e < 4; ++e) sacc[blk][4 * qd + e] = bv[e];
+            }
+        } else if constexpr (BIAS == B_DENSE) {
+          const __bf16* bt = reinterpret_cast<const __bf16*>(sb + L::B_OFF) + qil * L::BS + 4 * g;
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x4 bv = *(const f32x4*)(bias_lds + qil * BS + blk * 32 + 8 * jq + 4 * g);
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[blk][4 * jq + e] += bv[e];
-          }
-        }
-      }
-      bool valid[2][16];
+            for (int qd = 0; qd < 4; ++qd) {
+              const u32x2 bv = *(const u32x2*)(bt + blk * 32 + 8 * qd);
+              sacc[blk][4 * qd + 0] = __uint_as_float(bv[0] << 16) * inv_scale;
+              sacc[blk][4 * qd + 1] = __uint_as_float(bv[0] & 0xffff0000u) * inv_scale;
+              sacc[blk][4 * qd + 2] = __uint_as_float(bv[1] << 16) * inv_scale;
+              sacc[blk][4 * qd + 3] = __uint_as_float(bv[1] & 0xffff0000u) * inv_scale;
+            }
+        } else {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + blk * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          valid[blk][i] = !need_mask || (j < m && (!p.causal || j <= qi + delta));
+            for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
         }
 
-      float pr[2][16];
-      if constexpr (MODE == MODE_SOFTMAX) {
-        float mt = NEG_INF;
+        // ---- S^T += K Q^T for the 64 keys of this step (two 32-key blocks)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk) {
+          const int krow = blk * 32 + l32;
+          if constexpr (FP8) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (!valid[blk][i]) x[blk][i] = NEG_INF;
-            mt = fmaxf(mt, x[blk][i]);
+            for (int ks = 0; ks < QK; ++ks) {
+              const unsigned char* kr = sb + krow * L::KRB + 64 * ks + 16 * g;
+              const u32x4 lo = *(const u32x4*)kr;
+              const u32x4 hi = *(const u32x4*)(kr + 32);
+              i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+              const uint32_t sw = *(const uint32_t*)(sb + L::K_BYTES + 4 * krow);
+              const int sa = (int)((sw >> (8 * (2 * ks + g))) & 255u);
+              sacc[blk] = mfma_fp8(a, qf8[ks], sacc[blk], sa, qsc[ks]);
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < QK; ++ks) {
+              const bf16x8 a = as_bf16x8(*(const u32x4*)(sb + krow * L::KRB + 32 * ks + 16 * g));
+              sacc[blk] = mfma_bf16(a, qf[ks], sacc[blk]);
+            }
           }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m_run, mt);
-        const bool need = mn > m_run + 8.0f;
-        if (__any(need)) {
-          const float m_new = need ? mn : m_run;
-          const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
         }
-        const float mu = m_run == NEG_INF ? 0.f : m_run;
-        float ls = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pr[blk][i] = fast_exp2(x[blk][i] - mu);
-            ls += pr[blk][i];
-          }
-        l_run += ls;
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) pr[blk][i] = valid[blk][i] ? act_f<MODE>(x[blk][i]) : 0.f;
-      }
 
-      // ---- O^T += V^T P^T: P^T chunk c covers keys 16c + 8(e/4) + 4g + e%4
-      bf16x8 pb[4];
+        // ---- mask (only tiles that cross the sample end or the causal diagonal): element
+        //      (blk, i) is visible iff its key offset blk*32 + 8(i/4) + i%4 < lim
+        const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta);
+        if (need_mask) {
+          const int kend = p.causal ? min(m, qi + delta + 1) : m;
+          const int lim = kend - j0 - 4 * g;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 pk;
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          pk[e2] = pack2bf(pr[c >> 1][8 * (c & 1) + 2 * e2], pr[c >> 1][8 * (c & 1) + 2 * e2 + 1]);
-        pb[c] = as_bf16x8(pk);
-      }
+            for (int i = 0; i < 16; ++i)
+              if (blk * 32 + 8 * (i >> 2) + (i & 3) >= lim) sacc[blk][i] = NEG_INF;
+        }
+
+        // ---- probabilities P^T (bf16 pairs, in MFMA B-operand order)
+        uint32_t pk[2][8];
+        if constexpr (MODE == MODE_SOFTMAX) {
+          float mt = NEG_INF;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const __bf16* vrow = vt_lds + (db * 32 + l32) * VS + 4 * g;
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mt = vmax(mt, vmax(sacc[blk][i], sacc[blk][i + 1]));
+          mt = vmax(mt, __shfl_xor(mt, 32));
+          const float mx = mt * c_log;
+          if (__any(mx > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_new == NEG_INF ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+          }
+          const float mu = m_run == NEG_INF ? 0.f : m_run;
+          float ls[4];
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+              const float p0 = fast_exp2(fmaf(sacc[blk][i], c_log, -mu));
+              const float p1 = fast_exp2(fmaf(sacc[blk][i + 1], c_log, -mu));
+              pk[blk][i >> 1] = pack2bf(p0, p1);
+              const int q = (i >> 1) & 3;
+              if (blk == 0 && i < 8) ls[q] = p0 + p1;
+              else ls[q] += p0 + p1;
+            }
+          l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+              // masked scores are -inf: act(-inf) is NaN for SiLU/GELU, so select zero
+              const float x0 = sacc[blk][i], x1 = sacc[blk][i + 1];
+              const float a0 = x0 == NEG_INF ? 0.f : act_f<MODE>(x0 * c_log);
+              const float a1 = x1 == NEG_INF ? 0.f : act_f<MODE>(x1 * c_log);
+              pk[blk][i >> 1] = pack2bf(a0, a1);
+            }
+        }
+
+        // ---- O^T += V^T P^T: chunk c covers keys 16c + 8(e/4) + 4g + e%4
+        const __bf16* vt = reinterpret_cast<const __bf16*>(sb + L::V_OFF);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const u32x2 lo = *(const u32x2*)(vrow + 16 * c);
-          const u32x2 hi = *(const u32x2*)(vrow + 16 * c + 8);
-          acc[db] = mfma_bf16(cat_bf16x8(lo, hi), pb[c], acc[db]);
+          const u32x4 pw = {pk[c >> 1][4 * (c & 1)], pk[c >> 1][4 * (c & 1) + 1],
+                            pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
+          const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = as_bf16x8(*(const u32x4*)(vt + (db * 32 + l32) * VS + 16 * c + 8 * g));
+            acc[db] = mfma_bf16(a, pb, acc[db]);
+          }
         }
       }
+    };
+    for (int it = 0; it + 1 < nsteps; ++it) {
+      load_step(kb + it + 1);
+      compute_step(it);
+      store_step((it + 1) & 1, kb + it + 1);
+      __syncthreads();
     }
+    if (nsteps > 0) compute_step(nsteps - 1);
 
     // ---- epilogue
     float l_tot = l_run;
     if constexpr (MODE == MODE_SOFTMAX) l_tot = l_run + __shfl_xor(l_run, 32);
     if (slot < 0) {
-      if (qi < n) {
-        float mul;
-        if constexpr (MODE == MODE_SOFTMAX) mul = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        else mul = (p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
-        __bf16* orow = (__bf16*)p.o + ((int64_t)(qo + qi) * H + h) * D;
+      float mul;
+      if constexpr (MODE == MODE_SOFTMAX) mul = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      else mul = (p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
+      const uint32_t o_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
+      const rsrc_t ro = make_rsrc((__bf16*)p.o + ((int64_t)qo * H + h) * D, o_bytes);
+      const uint32_t ooff = (uint32_t)qi * H * D * 2;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            u32x2 pk = {pack2bf(acc[db][4 * jq] * mul, acc[db][4 * jq + 1] * mul),
-                        pack2bf(acc[db][4 * jq + 2] * mul, acc[db][4 * jq + 3] * mul)};
-            *(u32x2*)(orow + db * 32 + 8 * jq + 4 * g) = pk;
-          }
-        if (MODE == MODE_SOFTMAX && g == 0 && p.lse)
-          p.lse[(int64_t)h * p.total_q + qo + qi] =
-              l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : NEG_INF;
-      }
+        for (int jq = 0; jq < 4; ++jq) {
+          u32x2 v = {pack2bf(acc[db][4 * jq] * mul, acc[db][4 * jq + 1] * mul),
+                     pack2bf(acc[db][4 * jq + 2] * mul, acc[db][4 * jq + 3] * mul)};
+          st8(v, ro, ooff + 2 * (db * 32 + 8 * jq + 4 * g));
+        }
+      if (MODE == MODE_SOFTMAX && g == 0 && p.lse && qi < n)
+        p.lse[(int64_t)h * p.total_q + qo + qi] =
+            l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : NEG_INF;
     } else {
       const int64_t pbase = ((int64_t)slot * H + h) * BM + qil;
       float* prow = p.part_acc + pbase * D;
@@ -468,16 +550,16 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, int MODE, bool FP8>
-hipError_t run_fwd(const FwdParams& p, int bias_kind, int64_t max_items, int64_t max_comb,
-                   int cu_count, hipStream_t s) {
-  using L = FwdLds<D, NW, FP8>;
-  const size_t lds = L::total(bias_kind);
-  auto kern = fwd_kernel<D, NW, MODE, FP8>;
+template <int D, int NW, int MODE, int BIAS, bool FP8>
+hipError_t run_fwd(const FwdParams& p, int64_t max_items, int64_t max_comb, int cu_count,
+                   hipStream_t s) {
+  using L = FwdLds<D, NW, BIAS, FP8>;
+  const size_t lds = L::TOTAL;
+  auto kern = fwd_kernel<D, NW, MODE, BIAS, FP8>;
   static int attr_done = 0;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       L::total(JFA_BIAS_DENSE));
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done = 1;
   }
@@ -495,13 +577,22 @@ hipError_t run_fwd(const FwdParams& p, int bias_kind, int64_t max_items, int64_t
   return hipGetLastError();
 }
 
+template <int D, int NW, int MODE, bool FP8>
+hipError_t run_fwd_bias(const FwdParams& p, int64_t mi, int64_t mc, int cu, hipStream_t s) {
+  switch (p.bias_kind) {
+    case JFA_BIAS_RELPOS: return run_fwd<D, NW, MODE, B_RELPOS, FP8>(p, mi, mc, cu, s);
+    case JFA_BIAS_DENSE: return run_fwd<D, NW, MODE, B_DENSE, FP8>(p, mi, mc, cu, s);
+    default: return run_fwd<D, NW, MODE, B_NONE, FP8>(p, mi, mc, cu, s);
+  }
+}
+
 template <int D, int NW, bool FP8>
-hipError_t run_fwd_mode(const FwdParams& p, int mode, int bias_kind, int64_t mi, int64_t mc,
-                        int cu, hipStream_t s) {
+hipError_t run_fwd_mode(const FwdParams& p, int mode, int64_t mi, int64_t mc, int cu,
+                        hipStream_t s) {
   switch (mode) {
-    case MODE_SOFTMAX: return run_fwd<D, NW, MODE_SOFTMAX, FP8>(p, bias_kind, mi, mc, cu, s);
-    case MODE_SILU: return run_fwd<D, NW, MODE_SILU, FP8>(p, bias_kind, mi, mc, cu, s);
-    default: return run_fwd<D, NW, MODE_GELU, FP8>(p, bias_kind, mi, mc, cu, s);
+    case MODE_SOFTMAX: return run_fwd_bias<D, NW, MODE_SOFTMAX, FP8>(p, mi, mc, cu, s);
+    case MODE_SILU: return run_fwd_bias<D, NW, MODE_SILU, FP8>(p, mi, mc, cu, s);
+    default: return run_fwd_bias<D, NW, MODE_GELU, FP8>(p, mi, mc, cu, s);
   }
 }
 
@@ -516,10 +607,10 @@ hipError_t launch_forward(const FwdParams& p, const TileCfg& tc, int head_dim, i
   const bool fp8 = dtype == JFA_MXFP8_E4M3;
   const int nw = tc.fwd_nw;
   const int64_t mc = tc.slots > 0 ? max_comb_items : 0;
-#define JFA_FWD_CASE(D_, NW_)                                                              \
-  if (head_dim == D_ && nw == NW_)                                                          \
-    return fp8 ? run_fwd_mode<D_, NW_, true>(p, mode, p.bias_kind, max_items, mc, cu_count, s) \
-               : run_fwd_mode<D_, NW_, false>(p, mode, p.bias_kind, max_items, mc, cu_count, s);
+#define JFA_FWD_CASE(D_, NW_)                                                          \
+  if (head_dim == D_ && nw == NW_)                                                      \
+    return fp8 ? run_fwd_mode<D_, NW_, true>(p, mode, max_items, mc, cu_count, s)       \
+               : run_fwd_mode<D_, NW_, false>(p, mode, max_items, mc, cu_count, s);
   JFA_FWD_CASE(128, 4)
   JFA_FWD_CASE(128, 2)
   JFA_FWD_CASE(64, 4)

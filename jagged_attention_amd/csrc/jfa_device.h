@@ -22,8 +22,16 @@ __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint
 __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);   // round to nearest even
 }
+// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// max without the NaN-quieting canonicalisation of fmaxf (operands here are never NaN)
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -86,6 +94,54 @@ __device__ __forceinline__ float e4m3_to_f(uint32_t c) {
 // 2^(s - 127) for an E8M0 scale code s (0..254).
 __device__ __forceinline__ float e8m0_to_f(uint32_t s) {
   return s == 0 ? 5.877471754111438e-39f : __uint_as_float(s << 23);
+}
+
+// ------------------------------------------------------------------ buffer access
+// A buffer resource covers [base, base + bytes): loads at or past `bytes` return zeros and
+// stores there are dropped, so ragged rows need no branches.  Offsets are 32-bit bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld1(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void st16(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void st4(uint32_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+// Byte permute: result byte k is byte sel_k of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// Low halves of two words (lo16(a) | lo16(b) << 16) and high halves (hi16(a) | hi16(b) << 16).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
+
+// Sum of the two bf16 halves of `w` added to `acc` (fp32).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
 }
 
 // Workgroup-wide work ticket: thread 0 takes the next item, everyone gets it.

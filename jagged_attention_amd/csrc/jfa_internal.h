@@ -61,6 +61,8 @@ struct SchedArgs {
   int64_t total_q, total_kv;
   TileCfg tc;
   int want_bias_off;
+  int64_t hd_bytes;    // bytes of one (row, all heads) vector: H * d * element size
+  int32_t dense_bias;  // dense bias present (its per-sample block must fit 32-bit offsets)
   WsHeader* hdr;
   int64_t* bias_off;
   int32_t* s_tmp;      // per-sample scratch [4][B+1]

@@ -156,6 +156,9 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     const int64_t m = (int64_t)a.kv_off[b + 1] - a.kv_off[b];
     if (n < 0 || m < 0) bad = 1;
     else if (cdiv(m, min(tc.bn, tc.bq_bn)) > MAX_COST || cdiv(n, tc.bk_bm) > MAX_COST) bad = 1;
+    // kernels address one sample's rows (plus one tile of overhang) with 32-bit byte offsets
+    else if ((n + 256) * a.hd_bytes > INT32_MAX || (m + 256) * a.hd_bytes > INT32_MAX) bad = 1;
+    else if (a.dense_bias && (n + 256) * (m + 256) * 4 > INT32_MAX) bad = 1;
   }
   if (tid == 0 && (a.q_off[0] != 0 || a.kv_off[0] != 0 || a.q_off[B] != a.total_q ||
                    a.kv_off[B] != a.total_kv))

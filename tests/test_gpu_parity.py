@@ -230,3 +230,35 @@ def test_mxfp8_forward_parity():
     say(f"[mxfp8] rel-L2 {rl:.3g}")
     assert rl <= 5e-2
     compare_lse(lse, lse_ref, "softmax", tol=1e-2)
+
+
+def test_mxfp8_forward_block_scales_differ():
+    """Every 32-element block along d gets its own power-of-two magnitude, so each row's
+    E8M0 scales differ block to block: a scale applied to the wrong block shows up."""
+    import jagged_attention_amd as jfa
+    ql = [200, 1, 77, 130]
+    case = custom_case(ql, ql, 2, 128, dtype="mxfp8", causal=True, seed=41, with_dout=False)
+    rng = np.random.default_rng(42)
+    dc = device_case(case)
+    scaled = []
+    for name in ("q", "k", "v"):
+        x = dc[name]
+        e = rng.integers(-4, 5, size=(x.shape[0], x.shape[1], x.shape[2] // 32))
+        f = torch.from_numpy(np.exp2(e).astype(np.float32)).repeat_interleave(32, dim=2)
+        scaled.append((x.float().cpu() * f).to(torch.bfloat16).cuda())
+    qs8 = [jfa.quantize_mxfp8(x) for x in scaled]
+    o, lse = jfa.forward(qs8[0][0], qs8[1][0], qs8[2][0], dc["qo"], dc["ko"], causal=True,
+                         q_scale=qs8[0][1], k_scale=qs8[1][1], v_scale=qs8[2][1])
+    torch.cuda.synchronize()
+    deq = [oracle.mxfp8_dequantize(c.cpu().numpy(), s.cpu().numpy()) for c, s in qs8]
+    for (c, s), x in zip(qs8, scaled):
+        # the per-block scales really differ within rows
+        sv = s.cpu().numpy().astype(np.int64)
+        assert (sv.max(axis=2) - sv.min(axis=2)).max() >= 4
+    o_ref, lse_ref = oracle.forward(deq[0], deq[1], deq[2], case.q_lens, case.kv_lens,
+                                    causal=True)
+    from tests.helpers import rel_l2
+    rl = rel_l2(o.float().cpu().numpy(), o_ref)
+    say(f"[mxfp8 block scales] rel-L2 {rl:.3g}")
+    assert rl <= 5e-2
+    compare_lse(lse, lse_ref, "softmax", tol=2e-2)
