@@ -83,7 +83,9 @@ jfa_status tile_cfg(const jfa_problem& p, TileCfg* t) {
   t->bq_nw = short_q ? 2 : 4;
   t->bq_bm = 32 * t->bq_nw;
   t->bq_bn = BQ_BN;
-  t->bk_nw = short_kv ? 2 : 4;
+  // key-stationary tiles: 128 keys, or 64 for short keys and for a dense bias at d = 128
+  // (its key-major bias tile would not fit two LDS stages next to the Q / dO tiles)
+  t->bk_nw = (short_kv || (p.bias_kind == JFA_BIAS_DENSE && p.head_dim == 128)) ? 2 : 4;
   t->bk_bn = 32 * t->bk_nw;
   t->bk_bm = BK_BM;
   t->fuse = 0;   // single-pass backward classes: not enabled in this build

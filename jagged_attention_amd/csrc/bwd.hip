@@ -1,25 +1,40 @@
-// Jagged attention backward on MFMA (bf16): softmax preprocess, query-stationary dQ pass and
-// key-stationary dK/dV pass.
+// Jagged attention backward on MFMA (bf16): softmax preprocess, key-stationary dK/dV pass and
+// query-stationary dQ pass.
 //
 // Source: "Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a Different Stack",
 // section "Bottleneck move 1": GDPA (SiLU/GELU in place of softmax) forward and backward;
 // removing padding exposes backward accumulation.  The gradients are those of <O, dO>:
-//   softmax: dP = dO V^T, dS = P (dP - D), D_i = dO_i . O_i
+//   softmax: dP = dO V^T, dS = P (dP - D), D_i = dO_i . O_i, dV = P^T dO
 //   GDPA:    dP = w dO V^T, dS = act'(S) dP, dV = w act(S)^T dO    (w = 1/kv_len or 1)
-//   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO (softmax).
+//   dQ = scale dS K, dK = scale dS^T Q.
 //
-// Determinism without float atomics: the query-stationary kernel owns dQ rows and sums over
-// key steps in order in registers; the key-stationary kernel owns dK/dV rows and sums over
-// query steps in order.  Each recomputes S (and P) from the forward's log-sum-exp.
+// Determinism without float atomics: the key-stationary kernel owns dK/dV rows and sums over
+// query steps in order in registers; the query-stationary kernel owns dQ rows and sums over
+// key steps in order.  Each recomputes S (and P) from the forward's log-sum-exp.
 //
-// Layout trick shared with the forward: the query-stationary kernel works on S^T (lane = one
-// query), the key-stationary kernel on S (lane = one key); in both the lane's accumulator row
-// is exactly the B operand of the next MFMA, so P and dS never go through LDS.
+// Layout (gfx950), shared with the forward:
+//  - the key-stationary kernel works on S = Q K^T with a lane owning one key column; the
+//    query-stationary kernel on S^T = K Q^T with a lane owning one query column.  In both the
+//    lane's accumulator column is exactly the B operand of the gradient MFMAs, so P and dS
+//    never go through LDS;
+//  - every tile is staged global -> registers -> LDS one step ahead (two LDS stages, one
+//    barrier per step); operands contracted over the step's rows (Q^T, dO^T, K^T) are written
+//    transposed with v_perm on bf16 pairs, rows permuted so each MFMA operand is one 16-byte
+//    read;
+//  - loads and stores go through per-(sample, head) buffer resources: rows past a sample's
+//    end read as zero and are never written, with no branches;
+//  - the additive bias initialises the S accumulator (bias / scale).
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
 namespace jfa {
 namespace {
+
+enum BiasT { B_NONE = 0, B_RELPOS = 1, B_DENSE = 2 };
+constexpr int STEP = 64;   // rows per step of either kernel's inner loop
+constexpr int TS = STEP + 8;   // stride (bf16) of a transposed tile row
+
+constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 
 // ------------------------------------------------------------------ preprocess
 // delta[h][i] = sum_c dO[i,h,c] * O[i,h,c]; LPR lanes read one (row, head) 16 bytes at a time.
@@ -57,265 +72,116 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
   }
 }
 
-// Copies a [rows x D] bf16 block of one head into LDS, row-major (stride RS) and transposed
-// (stride TS): each thread moves 4 rows x 8 columns.
-template <int D, int ROWS, int NT, int RS, int TS>
-__device__ __forceinline__ void stage_rows_and_transpose(const __bf16* base, int64_t row_stride,
-                                                         int r0, int rmax, __bf16* row_lds,
-                                                         __bf16* t_lds) {
-  constexpr int BLK = (ROWS / 4) * (D / 8);
-  for (int id = threadIdx.x; id < BLK; id += NT) {
-    const int rb = id % (ROWS / 4), cb = id / (ROWS / 4);
-    u32x4 v[4];
+// --------------------------------------------------------------- tile staging
+// A STEP x D bf16 tile is moved as blocks of 4 rows x 8 dims (one 16-byte load per row).
+// Block id -> (row block rb, dim block cb): within each 16 ids, 4 row blocks x 4 dim blocks,
+// so that a quarter wave's row-major writes cover all banks.
+__device__ __forceinline__ void blk_of(int id, int& rb, int& cb) {
+  rb = ((id >> 2) & 3) | (((id >> 4) & 3) << 2);
+  cb = (id & 3) | ((id >> 6) << 2);
+}
+
+template <int D, int NT>
+struct Tile {
+  static constexpr int NBLK = (STEP / 4) * (D / 8);
+  static constexpr int NB = (NBLK + NT - 1) / NT;
+  u32x4 v[NB][4];
+
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t row_bytes, int r0) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 4 * rb + rr;
-      v[rr] = u32x4{0, 0, 0, 0};
-      if (r0 + r < rmax) v[rr] = *(const u32x4*)(base + (int64_t)(r0 + r) * row_stride + 8 * cb);
-      if (row_lds) *(u32x4*)(row_lds + r * RS + 8 * cb) = v[rr];
+    for (int i = 0; i < NB; ++i) {
+      const int id = threadIdx.x + i * NT;
+      if (NBLK % NT != 0 && id >= NBLK) break;
+      int rb, cb;
+      blk_of(id, rb, cb);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        v[i][rr] = ld16(r, (uint32_t)(r0 + 4 * rb + rr) * row_bytes + 16 * cb);
     }
+  }
+  // rows: [STEP][D + 8] row-major (may be null); tr: [D][TS] transposed, rows permuted
+  __device__ __forceinline__ void store(__bf16* rows, __bf16* tr) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t h[4];
+    for (int i = 0; i < NB; ++i) {
+      const int id = threadIdx.x + i * NT;
+      if (NBLK % NT != 0 && id >= NBLK) break;
+      int rb, cb;
+      blk_of(id, rb, cb);
+      if (rows) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t word = v[rr][e >> 1];
-        h[rr] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        for (int rr = 0; rr < 4; ++rr) *(u32x4*)(rows + (4 * rb + rr) * (D + 8) + 8 * cb) = v[i][rr];
       }
-      u32x2 pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *(u32x2*)(t_lds + (8 * cb + e) * TS + 4 * rb) = pk;
+      if (tr) {
+        const int pos = vt_pos(4 * rb);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const u32x2 lo = {lo_halves(v[i][0][e2], v[i][1][e2]), lo_halves(v[i][2][e2], v[i][3][e2])};
+          const u32x2 hi = {hi_halves(v[i][0][e2], v[i][1][e2]), hi_halves(v[i][2][e2], v[i][3][e2])};
+          *(u32x2*)(tr + (8 * cb + 2 * e2) * TS + pos) = lo;
+          *(u32x2*)(tr + (8 * cb + 2 * e2 + 1) * TS + pos) = hi;
+        }
+      }
     }
   }
-}
-
-// Row-major copy of a [rows x D] bf16 block into LDS with row stride RS.
-template <int D, int ROWS, int NT, int RS>
-__device__ __forceinline__ void stage_rows(const __bf16* base, int64_t row_stride, int r0, int rmax,
-                                           __bf16* row_lds) {
-  constexpr int CH = ROWS * (D / 8);
-  for (int id = threadIdx.x; id < CH; id += NT) {
-    const int r = id / (D / 8), c = id % (D / 8);
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + r < rmax) v = *(const u32x4*)(base + (int64_t)(r0 + r) * row_stride + 8 * c);
-    *(u32x4*)(row_lds + r * RS + 8 * c) = v;
-  }
-}
-
-// B-operand fragment of one row (column of the transposed operand): k = 16 ks + 8 g + 0..7.
-template <int D>
-__device__ __forceinline__ void load_frag(const __bf16* row, bool ok, int g, bf16x8* f) {
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 v = {0, 0, 0, 0};
-    if (ok) v = *(const u32x4*)(row + 16 * ks + 8 * g);
-    f[ks] = as_bf16x8(v);
-  }
-}
-
-__device__ __forceinline__ bf16x8 pack_chunk(const float (&v)[2][16], int c) {
-  u32x4 pk;
-#pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2)
-    pk[e2] = pack2bf(v[c >> 1][8 * (c & 1) + 2 * e2], v[c >> 1][8 * (c & 1) + 2 * e2 + 1]);
-  return as_bf16x8(pk);
-}
-
-// --------------------------------------------------------- query-stationary dQ
-template <int D, int NW>
-struct BqLds {
-  static constexpr int BM = 32 * NW, BN = BQ_BN;
-  static constexpr int KS = D + 8, TS = BN + 4, BS = BN + 4;
-  static constexpr int K_OFF = 0;
-  static constexpr int KT_OFF = K_OFF + BN * KS * 2;
-  static constexpr int V_OFF = KT_OFF + D * TS * 2;
-  static constexpr int BIAS_OFF = V_OFF + BN * KS * 2;
-  static constexpr int bias_bytes(int kind) {
-    return kind == JFA_BIAS_DENSE ? BM * BS * 4 : (kind == JFA_BIAS_RELPOS ? (BM + BN) * 4 : 0);
-  }
-  static constexpr int total(int kind) { return BIAS_OFF + bias_bytes(kind) + 16; }
 };
 
-template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(BwdParams p) {
-  using L = BqLds<D, NW>;
-  constexpr int BM = L::BM, BN = L::BN, NT = NW * 64, KS = L::KS, TS = L::TS, BS = L::BS;
-  extern __shared__ __align__(16) unsigned char lds[];
-  __bf16* k_lds = reinterpret_cast<__bf16*>(lds + L::K_OFF);
-  __bf16* kt_lds = reinterpret_cast<__bf16*>(lds + L::KT_OFF);
-  __bf16* v_lds = reinterpret_cast<__bf16*>(lds + L::V_OFF);
-  float* bias_lds = reinterpret_cast<float*>(lds + L::BIAS_OFF);
-  __shared__ int s_ticket;
-
-  if (p.hdr->status != JFA_OK) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int H = p.H;
-  const int64_t n_items = (int64_t)p.hdr->counts[2] * H;
-  const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
-  const float b_mul = MODE == MODE_SOFTMAX ? LOG2E : 1.0f;
-
-  for (;;) {
-    const int64_t w = next_ticket(&p.hdr->tickets[TK_BQ], &s_ticket);
-    if (w >= n_items) break;
-    const int4 rec = p.bq[w / H];
-    const int h = (int)(w % H);
-    const int b = rec.x, t = rec.y, steps = rec.w;
-    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
-    const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
-    const int delta = m - n;
-    const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
-    const int q0 = t * BM, qw0 = q0 + wave * 32;
-    const int qil = wave * 32 + l32, qi = q0 + qil;
-    const bool wave_rows = qw0 < n;
-    int wave_kend = m;
-    if (p.causal) wave_kend = max(0, min(m, min(n, qw0 + 32) + delta));
-    const int64_t rowq = (int64_t)(qo + qi) * H + h;
-
-    bf16x8 qf[D / 16], dof[D / 16];
-    load_frag<D>((const __bf16*)p.q + rowq * D, qi < n, g, qf);
-    load_frag<D>((const __bf16*)p.dout + rowq * D, qi < n, g, dof);
-    float lse2 = 0.f, dlt = 0.f;
-    if (MODE == MODE_SOFTMAX && qi < n) {
-      lse2 = p.lse[(int64_t)h * p.total_q + qo + qi] * LOG2E;
-      dlt = p.delta[(int64_t)h * p.total_q + qo + qi];
-    }
-    f32x16 acc[D / 32];
+// Row-major-only staging of a STEP x D tile: 16-byte chunks, consecutive lanes along a row.
+template <int D, int NT>
+struct RowTile {
+  static constexpr int KCH = D / 8;
+  static constexpr int NL = STEP * KCH / NT;
+  static_assert(STEP * KCH % NT == 0, "row tile staging");
+  u32x4 v[NL];
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t row_bytes, int r0) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-    const int64_t bias_base =
-        p.bias_kind == JFA_BIAS_DENSE ? (int64_t)H * p.bias_off[b] + (int64_t)h * n * m : 0;
-    const __bf16* kbase = (const __bf16*)p.k + ((int64_t)ko * H + h) * D;
-    const __bf16* vbase = (const __bf16*)p.v + ((int64_t)ko * H + h) * D;
-
-    for (int kt = 0; kt < steps; ++kt) {
-      const int j0 = kt * BN;
-      __syncthreads();
-      stage_rows_and_transpose<D, BN, NT, KS, TS>(kbase, (int64_t)H * D, j0, m, k_lds, kt_lds);
-      stage_rows<D, BN, NT, KS>(vbase, (int64_t)H * D, j0, m, v_lds);
-      if (p.bias_kind == JFA_BIAS_RELPOS) {
-        if (tid < BM + BN - 1) {
-          const int dist = tid - (BN - 1) + q0 + delta - j0;
-          bias_lds[tid] = ((const float*)p.bias)[(int64_t)h * p.num_buckets +
-                                                relpos_bucket(dist, p.num_buckets)] * b_mul;
-        }
-      } else if (p.bias_kind == JFA_BIAS_DENSE) {
-        const __bf16* bp = (const __bf16*)p.bias + bias_base;
-        for (int e = tid; e < BM * BN; e += NT) {
-          const int r = e / BN, c = e % BN;
-          float v = 0.f;
-          if (q0 + r < n && j0 + c < m) v = (float)bp[(int64_t)(q0 + r) * m + j0 + c];
-          bias_lds[r * BS + c] = v * b_mul;
-        }
-      }
-      __syncthreads();
-      if (!wave_rows || j0 >= wave_kend) continue;
-
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { sacc[blk][i] = 0.f; pacc[blk][i] = 0.f; }
-        const int krow = blk * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(k_lds + krow * KS + 16 * ks + 8 * g));
-          sacc[blk] = mfma_bf16(ka, qf[ks], sacc[blk]);
-          const bf16x8 va = as_bf16x8(*(const u32x4*)(v_lds + krow * KS + 16 * ks + 8 * g));
-          pacc[blk] = mfma_bf16(va, dof[ks], pacc[blk]);
-        }
-      }
-      const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta);
-      float ds[2][16];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = sacc[blk][i] * c_log;
-        if (p.bias_kind == JFA_BIAS_RELPOS) {
-          const float* br = bias_lds + (qil + BN - 1 - 4 * g) - blk * 32;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] += br[-(8 * (i >> 2) + (i & 3))];
-        } else if (p.bias_kind == JFA_BIAS_DENSE) {
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x4 bv = *(const f32x4*)(bias_lds + qil * BS + blk * 32 + 8 * jq + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * jq + e] += bv[e];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + blk * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool valid = !need_mask || (j < m && (!p.causal || j <= qi + delta));
-          float d;
-          if constexpr (MODE == MODE_SOFTMAX) {
-            const float pr = valid ? fast_exp2(x[i] - lse2) : 0.f;
-            d = pr * (pacc[blk][i] - dlt);
-          } else {
-            d = valid ? act_grad_f<MODE>(x[i]) * pacc[blk][i] * wn : 0.f;
-          }
-          ds[blk][i] = d;
-        }
-      }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 db_op = pack_chunk(ds, c);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const __bf16* krow = kt_lds + (db * 32 + l32) * TS + 16 * c + 4 * g;
-          const u32x2 lo = *(const u32x2*)krow;
-          const u32x2 hi = *(const u32x2*)(krow + 8);
-          acc[db] = mfma_bf16(cat_bf16x8(lo, hi), db_op, acc[db]);
-        }
-      }
-    }
-    if (qi < n) {
-      __bf16* out = (__bf16*)p.dq + rowq * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          u32x2 pk = {pack2bf(acc[db][4 * jq] * p.scale, acc[db][4 * jq + 1] * p.scale),
-                      pack2bf(acc[db][4 * jq + 2] * p.scale, acc[db][4 * jq + 3] * p.scale)};
-          *(u32x2*)(out + db * 32 + 8 * jq + 4 * g) = pk;
-        }
+    for (int i = 0; i < NL; ++i) {
+      const int id = threadIdx.x + i * NT;
+      v[i] = ld16(r, (uint32_t)(r0 + id / KCH) * row_bytes + 16 * (id % KCH));
     }
   }
-}
-
-// ------------------------------------------------------- key-stationary dK, dV
-template <int D, int NW>
-struct BkLds {
-  static constexpr int BNK = 32 * NW, BM = BK_BM;
-  static constexpr int QS = D + 8, TS = BM + 4, BS = BM + 4;
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = Q_OFF + BM * QS * 2;
-  static constexpr int QT_OFF = DO_OFF + BM * QS * 2;
-  static constexpr int DOT_OFF = QT_OFF + D * TS * 2;
-  static constexpr int LSE_OFF = DOT_OFF + D * TS * 2;
-  static constexpr int DLT_OFF = LSE_OFF + BM * 4;
-  static constexpr int BIAS_OFF = DLT_OFF + BM * 4;
-  static constexpr int bias_bytes(int kind) {
-    return kind == JFA_BIAS_DENSE ? BNK * BS * 4 : (kind == JFA_BIAS_RELPOS ? (BM + BNK) * 4 : 0);
+  __device__ __forceinline__ void store(__bf16* rows) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int id = threadIdx.x + i * NT;
+      *(u32x4*)(rows + (id / KCH) * (D + 8) + 8 * (id % KCH)) = v[i];
+    }
   }
-  static constexpr int total(int kind) { return BIAS_OFF + bias_bytes(kind) + 16; }
 };
 
-template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_kv_kernel(BwdParams p) {
-  using L = BkLds<D, NW>;
-  constexpr int BNK = L::BNK, BM = L::BM, NT = NW * 64, QS = L::QS, TS = L::TS, BS = L::BS;
+// Four copies of a diagonal bias table, copy k shifted by k floats, so that any run of 4
+// consecutive entries is one aligned 16-byte read from the copy k = (4 - start % 4) % 4.
+template <int RP>
+__device__ __forceinline__ void store_diag(float* rp, int idx, float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rp[k * RP + idx + k] = v;
+}
+
+// ================================================= key-stationary dK, dV
+template <int D, int NW, int BIAS>
+struct KvLds {
+  static constexpr int BNK = 32 * NW;
+  static constexpr int RS = D + 8;
+  static constexpr int QR = 0;                            // Q rows [STEP][RS]
+  static constexpr int DR = QR + STEP * RS * 2;           // dO rows
+  static constexpr int QT = DR + STEP * RS * 2;           // Q^T [D][TS]
+  static constexpr int DT = QT + D * TS * 2;              // dO^T
+  static constexpr int LS = DT + D * TS * 2;              // lse * log2 e [STEP]
+  static constexpr int DL = LS + STEP * 4;                // delta [STEP]
+  static constexpr int BO = DL + STEP * 4;
+  static constexpr int RP = STEP + BNK + 4;
+  static constexpr int BS = STEP + 8;                     // dense tile [BNK][BS] bf16 (key-major)
+  static constexpr int BIAS_BYTES =
+      BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BNK * BS * 2 : 0);
+  static constexpr int STAGE = align16(BO + BIAS_BYTES);
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_kv_kernel(BwdParams p) {
+  using L = KvLds<D, NW, BIAS>;
+  constexpr int BNK = L::BNK, NT = NW * 64, RS = L::RS;
   extern __shared__ __align__(16) unsigned char lds[];
-  __bf16* q_lds = reinterpret_cast<__bf16*>(lds + L::Q_OFF);
-  __bf16* do_lds = reinterpret_cast<__bf16*>(lds + L::DO_OFF);
-  __bf16* qt_lds = reinterpret_cast<__bf16*>(lds + L::QT_OFF);
-  __bf16* dot_lds = reinterpret_cast<__bf16*>(lds + L::DOT_OFF);
-  float* lse_lds = reinterpret_cast<float*>(lds + L::LSE_OFF);
-  float* dlt_lds = reinterpret_cast<float*>(lds + L::DLT_OFF);
-  float* bias_lds = reinterpret_cast<float*>(lds + L::BIAS_OFF);
   __shared__ int s_ticket;
 
   if (p.hdr->status != JFA_OK) return;
@@ -324,7 +190,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kv_kernel(BwdParams p) {
   const int H = p.H;
   const int64_t n_items = (int64_t)p.hdr->counts[3] * H;
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
-  const float b_mul = MODE == MODE_SOFTMAX ? LOG2E : 1.0f;
+  const float inv_scale = 1.0f / p.scale;
+  const uint32_t row_bytes = (uint32_t)H * D * 2;
+
+  Tile<D, NT> tq, tdo;
+  float lsv = 0.f, dlv = 0.f;       // lse / delta entry staged by threads < STEP
+  float rpv = 0.f;                  // relpos table entry
 
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_BK], &s_ticket);
@@ -338,190 +209,511 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kv_kernel(BwdParams p) {
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int j0 = u * BNK, jw0 = j0 + wave * 32;
     const int kvl = wave * 32 + l32, j = j0 + kvl;
-    const int64_t rowk = (int64_t)(ko + j) * H + h;
 
+    const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
+    const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
+    const rsrc_t rk = make_rsrc((const __bf16*)p.k + ((int64_t)ko * H + h) * D, kv_bytes);
+    const rsrc_t rv = make_rsrc((const __bf16*)p.v + ((int64_t)ko * H + h) * D, kv_bytes);
+    const rsrc_t rq = make_rsrc((const __bf16*)p.q + ((int64_t)qo * H + h) * D, q_bytes);
+    const rsrc_t rdo = make_rsrc((const __bf16*)p.dout + ((int64_t)qo * H + h) * D, q_bytes);
+    rsrc_t rls = rq, rdl = rq, rb = rq;
+    if constexpr (MODE == MODE_SOFTMAX) {
+      rls = make_rsrc(p.lse + (int64_t)h * p.total_q + qo, (uint32_t)n * 4u);
+      rdl = make_rsrc(p.delta + (int64_t)h * p.total_q + qo, (uint32_t)n * 4u);
+    }
+    if constexpr (BIAS == B_DENSE)
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+                     (uint32_t)n * (uint32_t)m * 2u);
+
+    // this lane's key as the B operand (column = key, k = head dim)
     bf16x8 kf[D / 16], vf[D / 16];
-    load_frag<D>((const __bf16*)p.k + rowk * D, j < m, g, kf);
-    load_frag<D>((const __bf16*)p.v + rowk * D, j < m, g, vf);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = as_bf16x8(ld16(rk, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
+      vf[ks] = as_bf16x8(ld16(rv, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): fragments complete before the loop
+
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
-    const int64_t bias_base =
-        p.bias_kind == JFA_BIAS_DENSE ? (int64_t)H * p.bias_off[b] + (int64_t)h * n * m : 0;
-    const __bf16* qbase = (const __bf16*)p.q + ((int64_t)qo * H + h) * D;
-    const __bf16* dobase = (const __bf16*)p.dout + ((int64_t)qo * H + h) * D;
 
-    for (int qs = qs_first; qs < qs_end; ++qs) {
-      const int q0 = qs * BM;
-      __syncthreads();
-      stage_rows_and_transpose<D, BM, NT, QS, TS>(qbase, (int64_t)H * D, q0, n, q_lds, qt_lds);
-      stage_rows_and_transpose<D, BM, NT, QS, TS>(dobase, (int64_t)H * D, q0, n, do_lds, dot_lds);
-      if (tid < BM) {
-        float l2 = 0.f, dl = 0.f;
-        if (MODE == MODE_SOFTMAX && q0 + tid < n) {
-          l2 = p.lse[(int64_t)h * p.total_q + qo + q0 + tid] * LOG2E;
-          dl = p.delta[(int64_t)h * p.total_q + qo + q0 + tid];
-        }
-        lse_lds[tid] = l2;
-        dlt_lds[tid] = dl;
-      }
-      if (p.bias_kind == JFA_BIAS_RELPOS) {
-        // entry x: bias of (query - key) = x - (BNK - 1) within the tile
-        if (tid < BM + BNK - 1) {
-          const int dist = tid - (BNK - 1) + q0 + delta - j0;
-          bias_lds[tid] = ((const float*)p.bias)[(int64_t)h * p.num_buckets +
-                                                relpos_bucket(dist, p.num_buckets)] * b_mul;
-        }
-      } else if (p.bias_kind == JFA_BIAS_DENSE) {
-        // stored transposed: [key][query]
-        const __bf16* bp = (const __bf16*)p.bias + bias_base;
-        for (int e = tid; e < BM * BNK; e += NT) {
-          const int r = e / BNK, c = e % BNK;
-          float v = 0.f;
-          if (q0 + r < n && j0 + c < m) v = (float)bp[(int64_t)(q0 + r) * m + j0 + c];
-          bias_lds[c * BS + r] = v * b_mul;
+    auto load_step = [&](int qs) {
+      const int q0 = qs * STEP;
+      if constexpr (BIAS == B_RELPOS) {
+        // T[x] = bias(dist = q0 + delta - j0 + x - (BNK - 1)), x = query - key + BNK - 1
+        if (tid < STEP + BNK - 1) {
+          const int dist = q0 + delta - j0 + tid - (BNK - 1);
+          rpv = ((const float*)p.bias)[(int64_t)h * p.num_buckets +
+                                       relpos_bucket(dist, p.num_buckets)];
         }
       }
-      __syncthreads();
-      if (jw0 >= m || (p.causal && q0 + BM - 1 + delta < jw0)) continue;
+      if constexpr (MODE == MODE_SOFTMAX) {
+        if (tid < STEP) {
+          lsv = __uint_as_float(ld4(rls, (uint32_t)(q0 + tid) * 4u));
+          dlv = __uint_as_float(ld4(rdl, (uint32_t)(q0 + tid) * 4u));
+        }
+      }
+      tq.load(rq, row_bytes, q0);
+      tdo.load(rdo, row_bytes, q0);
+    };
+    auto store_step = [&](int st, int qs) {
+      unsigned char* base = lds + st * L::STAGE;
+      const int q0 = qs * STEP;
+      tq.store(reinterpret_cast<__bf16*>(base + L::QR), reinterpret_cast<__bf16*>(base + L::QT));
+      tdo.store(reinterpret_cast<__bf16*>(base + L::DR), reinterpret_cast<__bf16*>(base + L::DT));
+      if constexpr (MODE == MODE_SOFTMAX) {
+        if (tid < STEP) {
+          reinterpret_cast<float*>(base + L::LS)[tid] = lsv * LOG2E;
+          reinterpret_cast<float*>(base + L::DL)[tid] = dlv;
+        }
+      }
+      if constexpr (BIAS == B_RELPOS) {
+        if (tid < STEP + BNK - 1)
+          store_diag<L::RP>(reinterpret_cast<float*>(base + L::BO), tid, rpv * inv_scale);
+      } else if constexpr (BIAS == B_DENSE) {
+        // key-major tile [BNK][BS]: two query rows per thread and key, coalesced along keys
+        __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
+        constexpr int NPAIR = BNK * STEP / 2 / NT;
+#pragma unroll 4
+        for (int i = 0; i < NPAIR; ++i) {
+          const int e = tid + i * NT;
+          const int jj = e % BNK, qq = 2 * (e / BNK);
+          const int qa = q0 + qq, ja = j0 + jj;
+          const bool okj = ja < m;
+          const uint32_t off = ((uint32_t)qa * (uint32_t)m + (uint32_t)ja) * 2u;
+          const uint32_t lo = (okj && qa < n) ? ld2(rb, off) : 0u;
+          const uint32_t hi = (okj && qa + 1 < n) ? ld2(rb, off + 2u * (uint32_t)m) : 0u;
+          *(uint32_t*)(bt + jj * L::BS + qq) = lo | (hi << 16);
+        }
+      }
+    };
 
+    auto compute_step = [&](int it, int qs) {
+      const int q0 = qs * STEP;
+      const unsigned char* sb = lds + (it & 1) * L::STAGE;
+      if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0)) return;
+      const __bf16* qr = reinterpret_cast<const __bf16*>(sb + L::QR);
+      const __bf16* dr = reinterpret_cast<const __bf16*>(sb + L::DR);
+      // element (blk, i): query q0 + blk*32 + 8(i/4) + 4g + i%4 of this step, key j
       f32x16 sacc[2], pacc[2];
+      if constexpr (BIAS == B_RELPOS) {
+        const float* rp = reinterpret_cast<const float*>(sb + L::BO);
+        const int k = (1 + kvl) & 3;
+        const float* src = rp + k * L::RP + k + 4 * g - kvl + BNK - 1;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 bv = *(const f32x4*)(src + blk * 32 + 8 * qd);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[blk][4 * qd + e] = bv[e];
+          }
+      } else if constexpr (BIAS == B_DENSE) {
+        const __bf16* bt = reinterpret_cast<const __bf16*>(sb + L::BO) + kvl * L::BS + 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const u32x2 bv = *(const u32x2*)(bt + blk * 32 + 8 * qd);
+            sacc[blk][4 * qd + 0] = __uint_as_float(bv[0] << 16) * inv_scale;
+            sacc[blk][4 * qd + 1] = __uint_as_float(bv[0] & 0xffff0000u) * inv_scale;
+            sacc[blk][4 * qd + 2] = __uint_as_float(bv[1] << 16) * inv_scale;
+            sacc[blk][4 * qd + 3] = __uint_as_float(bv[1] & 0xffff0000u) * inv_scale;
+          }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+      }
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { sacc[blk][i] = 0.f; pacc[blk][i] = 0.f; }
+        for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
         const int qrow = blk * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 qa = as_bf16x8(*(const u32x4*)(q_lds + qrow * QS + 16 * ks + 8 * g));
+          const bf16x8 qa = as_bf16x8(*(const u32x4*)(qr + qrow * RS + 16 * ks + 8 * g));
           sacc[blk] = mfma_bf16(qa, kf[ks], sacc[blk]);
-          const bf16x8 da = as_bf16x8(*(const u32x4*)(do_lds + qrow * QS + 16 * ks + 8 * g));
+          const bf16x8 da = as_bf16x8(*(const u32x4*)(dr + qrow * RS + 16 * ks + 8 * g));
           pacc[blk] = mfma_bf16(da, vf[ks], pacc[blk]);
         }
       }
-      // element (blk, i): query q0 + blk*32 + 8(i/4) + 4g + i%4, key j
-      const bool need_mask = (q0 + BM > n) || (jw0 + 32 > m) ||
+      // visibility: query offset o = blk*32 + 8(i/4) + i%4 (+4g) is visible iff qlo <= o < qhi
+      const bool need_mask = (q0 + STEP > n) || (jw0 + 32 > m) ||
                              (p.causal && q0 + delta < jw0 + 31);
-      float pv[2][16], ds[2][16];
+      const int qhi = j < m ? n - q0 - 4 * g : -1;
+      const int qlo = p.causal ? j - delta - q0 - 4 * g : -1;
+      uint32_t pp[2][8], dd[2][8];
+      const float* lsl = reinterpret_cast<const float*>(sb + L::LS);
+      const float* dll = reinterpret_cast<const float*>(sb + L::DL);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        float x[16];
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = sacc[blk][i] * c_log;
-        if (p.bias_kind == JFA_BIAS_RELPOS) {
-          const float* br = bias_lds + (blk * 32 + 4 * g + BNK - 1) - kvl;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] += br[8 * (i >> 2) + (i & 3)];
-        } else if (p.bias_kind == JFA_BIAS_DENSE) {
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x4 bv = *(const f32x4*)(bias_lds + kvl * BS + blk * 32 + 8 * jq + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * jq + e] += bv[e];
-          }
-        }
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int ql = blk * 32 + 8 * jq + 4 * g;
+        for (int qd = 0; qd < 4; ++qd) {
           f32x4 l2 = {0.f, 0.f, 0.f, 0.f}, dl = {0.f, 0.f, 0.f, 0.f};
           if constexpr (MODE == MODE_SOFTMAX) {
-            l2 = *(const f32x4*)(lse_lds + ql);
-            dl = *(const f32x4*)(dlt_lds + ql);
+            l2 = *(const f32x4*)(lsl + blk * 32 + 8 * qd + 4 * g);
+            dl = *(const f32x4*)(dll + blk * 32 + 8 * qd + 4 * g);
           }
+          float pv[4], dsv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 4 * jq + e;
-            const int qi = q0 + ql + e;
-            const bool valid = !need_mask || (qi < n && j < m && (!p.causal || j <= qi + delta));
+            const int i = 4 * qd + e;
+            const int o = blk * 32 + 8 * qd + e;
+            const bool valid = !need_mask || (o >= qlo && o < qhi);
+            const float x = sacc[blk][i] * c_log;
             if constexpr (MODE == MODE_SOFTMAX) {
-              const float pr = valid ? fast_exp2(x[i] - l2[e]) : 0.f;
-              pv[blk][i] = pr;
-              ds[blk][i] = pr * (pacc[blk][i] - dl[e]);
+              const float pr = valid ? fast_exp2(x - l2[e]) : 0.f;
+              pv[e] = pr;
+              dsv[e] = pr * (pacc[blk][i] - dl[e]);
             } else {
-              pv[blk][i] = valid ? act_f<MODE>(x[i]) * wn : 0.f;
-              ds[blk][i] = valid ? act_grad_f<MODE>(x[i]) * pacc[blk][i] * wn : 0.f;
+              pv[e] = valid ? act_f<MODE>(x) * wn : 0.f;
+              dsv[e] = valid ? act_grad_f<MODE>(x) * pacc[blk][i] * wn : 0.f;
             }
           }
+          pp[blk][2 * qd] = pack2bf(pv[0], pv[1]);
+          pp[blk][2 * qd + 1] = pack2bf(pv[2], pv[3]);
+          dd[blk][2 * qd] = pack2bf(dsv[0], dsv[1]);
+          dd[blk][2 * qd + 1] = pack2bf(dsv[2], dsv[3]);
         }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (chunk c covers queries 16c + 8(e/4) + 4g + e%4)
+      // dV^T += dO^T P, dK^T += Q^T dS; chunk c covers queries 16c + 8(e/4) + 4g + e%4
+      const __bf16* qt = reinterpret_cast<const __bf16*>(sb + L::QT);
+      const __bf16* dt = reinterpret_cast<const __bf16*>(sb + L::DT);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 pop = pack_chunk(pv, c);
-        const bf16x8 dsop = pack_chunk(ds, c);
+        const u32x4 pw = {pp[c >> 1][4 * (c & 1)], pp[c >> 1][4 * (c & 1) + 1],
+                          pp[c >> 1][4 * (c & 1) + 2], pp[c >> 1][4 * (c & 1) + 3]};
+        const u32x4 dw = {dd[c >> 1][4 * (c & 1)], dd[c >> 1][4 * (c & 1) + 1],
+                          dd[c >> 1][4 * (c & 1) + 2], dd[c >> 1][4 * (c & 1) + 3]};
+        const bf16x8 pb = as_bf16x8(pw), db8 = as_bf16x8(dw);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const __bf16* drow = dot_lds + (db * 32 + l32) * TS + 16 * c + 4 * g;
-          dv[db] = mfma_bf16(cat_bf16x8(*(const u32x2*)drow, *(const u32x2*)(drow + 8)), pop, dv[db]);
-          const __bf16* qrow = qt_lds + (db * 32 + l32) * TS + 16 * c + 4 * g;
-          dk[db] = mfma_bf16(cat_bf16x8(*(const u32x2*)qrow, *(const u32x2*)(qrow + 8)), dsop, dk[db]);
+          const bf16x8 da = as_bf16x8(*(const u32x4*)(dt + (db * 32 + l32) * TS + 16 * c + 8 * g));
+          dv[db] = mfma_bf16(da, pb, dv[db]);
+          const bf16x8 qa = as_bf16x8(*(const u32x4*)(qt + (db * 32 + l32) * TS + 16 * c + 8 * g));
+          dk[db] = mfma_bf16(qa, db8, dk[db]);
         }
       }
+    };
+
+    const int nsteps = qs_end - qs_first;
+    if (nsteps > 0) {
+      load_step(qs_first);
+      store_step(0, qs_first);
     }
-    if (j < m) {
-      __bf16* okr = (__bf16*)p.dk + rowk * D;
-      __bf16* ovr = (__bf16*)p.dv + rowk * D;
+    __syncthreads();
+    for (int it = 0; it + 1 < nsteps; ++it) {
+      load_step(qs_first + it + 1);
+      compute_step(it, qs_first + it);
+      store_step((it + 1) & 1, qs_first + it + 1);
+      __syncthreads();
+    }
+    if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1);
+
+    // epilogue: this lane's key row of dK (x scale) and dV; keys past the sample are dropped
+    const rsrc_t rdk = make_rsrc((__bf16*)p.dk + ((int64_t)ko * H + h) * D, kv_bytes);
+    const rsrc_t rdv = make_rsrc((__bf16*)p.dv + ((int64_t)ko * H + h) * D, kv_bytes);
+    const uint32_t orow = (uint32_t)j * row_bytes;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          u32x2 pk = {pack2bf(dk[db][4 * jq] * p.scale, dk[db][4 * jq + 1] * p.scale),
-                      pack2bf(dk[db][4 * jq + 2] * p.scale, dk[db][4 * jq + 3] * p.scale)};
-          *(u32x2*)(okr + db * 32 + 8 * jq + 4 * g) = pk;
-          u32x2 pv2 = {pack2bf(dv[db][4 * jq], dv[db][4 * jq + 1]),
-                       pack2bf(dv[db][4 * jq + 2], dv[db][4 * jq + 3])};
-          *(u32x2*)(ovr + db * 32 + 8 * jq + 4 * g) = pv2;
+      for (int jq = 0; jq < 4; ++jq) {
+        const u32x2 k2 = {pack2bf(dk[db][4 * jq] * p.scale, dk[db][4 * jq + 1] * p.scale),
+                          pack2bf(dk[db][4 * jq + 2] * p.scale, dk[db][4 * jq + 3] * p.scale)};
+        const u32x2 v2 = {pack2bf(dv[db][4 * jq], dv[db][4 * jq + 1]),
+                          pack2bf(dv[db][4 * jq + 2], dv[db][4 * jq + 3])};
+        const uint32_t off = orow + 2 * (db * 32 + 8 * jq + 4 * g);
+        st8(k2, rdk, off);
+        st8(v2, rdv, off);
+      }
+  }
+}
+
+// ================================================= query-stationary dQ
+template <int D, int NW, int BIAS>
+struct QLds {
+  static constexpr int BM = 32 * NW;
+  static constexpr int RS = D + 8;
+  static constexpr int KR = 0;                            // K rows [STEP][RS]
+  static constexpr int VR = KR + STEP * RS * 2;           // V rows
+  static constexpr int KT = VR + STEP * RS * 2;           // K^T [D][TS]
+  static constexpr int BO = KT + D * TS * 2;
+  static constexpr int RP = BM + STEP + 4;
+  static constexpr int BS = STEP + 8;                     // dense tile [BM][BS] bf16 (query-major)
+  static constexpr int BIAS_BYTES =
+      BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);
+  static constexpr int STAGE = align16(BO + BIAS_BYTES);
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_q_kernel(BwdParams p) {
+  using L = QLds<D, NW, BIAS>;
+  constexpr int BM = L::BM, NT = NW * 64, RS = L::RS;
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int s_ticket;
+
+  if (p.hdr->status != JFA_OK) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int H = p.H;
+  const int64_t n_items = (int64_t)p.hdr->counts[2] * H;
+  const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
+  const float inv_scale = 1.0f / p.scale;
+  const uint32_t row_bytes = (uint32_t)H * D * 2;
+
+  Tile<D, NT> tk;
+  RowTile<D, NT> tv;
+  float rpv = 0.f;
+
+  for (;;) {
+    const int64_t w = next_ticket(&p.hdr->tickets[TK_BQ], &s_ticket);
+    if (w >= n_items) break;
+    const int4 rec = p.bq[w / H];
+    const int h = (int)(w % H);
+    const int b = rec.x, t = rec.y, steps = rec.w;
+    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
+    const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
+    const int delta = m - n;
+    const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
+    const int q0 = t * BM, qw0 = q0 + wave * 32;
+    const int qil = wave * 32 + l32, qi = q0 + qil;
+    int wave_kend = m;
+    if (p.causal) wave_kend = max(0, min(m, min(n, qw0 + 32) + delta));
+    const bool wave_rows = qw0 < n;
+
+    const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
+    const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
+    const rsrc_t rk = make_rsrc((const __bf16*)p.k + ((int64_t)ko * H + h) * D, kv_bytes);
+    const rsrc_t rv = make_rsrc((const __bf16*)p.v + ((int64_t)ko * H + h) * D, kv_bytes);
+    const rsrc_t rq = make_rsrc((const __bf16*)p.q + ((int64_t)qo * H + h) * D, q_bytes);
+    const rsrc_t rdo = make_rsrc((const __bf16*)p.dout + ((int64_t)qo * H + h) * D, q_bytes);
+    rsrc_t rb = rq;
+    if constexpr (BIAS == B_DENSE)
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+                     (uint32_t)n * (uint32_t)m * 2u);
+
+    bf16x8 qf[D / 16], dof[D / 16];
+    const uint32_t qoff = (uint32_t)qi * row_bytes;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = as_bf16x8(ld16(rq, qoff + 32 * ks + 16 * g));
+      dof[ks] = as_bf16x8(ld16(rdo, qoff + 32 * ks + 16 * g));
+    }
+    float lse2 = 0.f, dlt = 0.f;
+    if constexpr (MODE == MODE_SOFTMAX) {
+      if (qi < n) {
+        lse2 = p.lse[(int64_t)h * p.total_q + qo + qi] * LOG2E;
+        dlt = p.delta[(int64_t)h * p.total_q + qo + qi];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+    auto load_step = [&](int kt) {
+      const int j0 = kt * STEP;
+      if constexpr (BIAS == B_RELPOS) {
+        if (tid < BM + STEP - 1) {
+          const int dist = q0 + delta - j0 + BM - 1 - tid;
+          rpv = ((const float*)p.bias)[(int64_t)h * p.num_buckets +
+                                       relpos_bucket(dist, p.num_buckets)];
         }
+      }
+      tk.load(rk, row_bytes, j0);
+      tv.load(rv, row_bytes, j0);
+    };
+    auto store_step = [&](int st, int kt) {
+      unsigned char* base = lds + st * L::STAGE;
+      const int j0 = kt * STEP;
+      tk.store(reinterpret_cast<__bf16*>(base + L::KR), reinterpret_cast<__bf16*>(base + L::KT));
+      tv.store(reinterpret_cast<__bf16*>(base + L::VR));
+      if constexpr (BIAS == B_RELPOS) {
+        if (tid < BM + STEP - 1)
+          store_diag<L::RP>(reinterpret_cast<float*>(base + L::BO), tid, rpv * inv_scale);
+      } else if constexpr (BIAS == B_DENSE) {
+        __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
+        constexpr int NB = BM * STEP / NT / 2;
+#pragma unroll 4
+        for (int i = 0; i < NB; ++i) {
+          const int e = 2 * (tid + i * NT);
+          const int r = e / STEP, c = e % STEP;
+          const int qq = q0 + r, jj = j0 + c;
+          const bool ok = qq < n;
+          const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
+          const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
+          const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
+          *(uint32_t*)(bt + r * L::BS + c) = lo | (hi << 16);
+        }
+      }
+    };
+
+    auto compute_step = [&](int it) {
+      const int j0 = it * STEP;
+      const unsigned char* sb = lds + (it & 1) * L::STAGE;
+      if (!wave_rows || j0 >= wave_kend) return;
+      const __bf16* kr = reinterpret_cast<const __bf16*>(sb + L::KR);
+      const __bf16* vr = reinterpret_cast<const __bf16*>(sb + L::VR);
+      // element (blk, i): key j0 + blk*32 + 8(i/4) + 4g + i%4, query qi
+      f32x16 sacc[2], pacc[2];
+      if constexpr (BIAS == B_RELPOS) {
+        const float* rp = reinterpret_cast<const float*>(sb + L::BO);
+        const int k = (1 + qil) & 3;
+        const float* src = rp + k * L::RP + k + BM - 1 - qil + 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 bv = *(const f32x4*)(src + blk * 32 + 8 * qd);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[blk][4 * qd + e] = bv[e];
+          }
+      } else if constexpr (BIAS == B_DENSE) {
+        const __bf16* bt = reinterpret_cast<const __bf16*>(sb + L::BO) + qil * L::BS + 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const u32x2 bv = *(const u32x2*)(bt + blk * 32 + 8 * qd);
+            sacc[blk][4 * qd + 0] = __uint_as_float(bv[0] << 16) * inv_scale;
+            sacc[blk][4 * qd + 1] = __uint_as_float(bv[0] & 0xffff0000u) * inv_scale;
+            sacc[blk][4 * qd + 2] = __uint_as_float(bv[1] << 16) * inv_scale;
+            sacc[blk][4 * qd + 3] = __uint_as_float(bv[1] & 0xffff0000u) * inv_scale;
+          }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
+        const int krow = blk * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 ka = as_bf16x8(*(const u32x4*)(kr + krow * RS + 16 * ks + 8 * g));
+          sacc[blk] = mfma_bf16(ka, qf[ks], sacc[blk]);
+          const bf16x8 va = as_bf16x8(*(const u32x4*)(vr + krow * RS + 16 * ks + 8 * g));
+          pacc[blk] = mfma_bf16(va, dof[ks], pacc[blk]);
+        }
+      }
+      const bool need_mask = (j0 + STEP > m) || (p.causal && j0 + STEP - 1 > qw0 + delta) ||
+                             (qw0 + 32 > n);
+      const int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
+      const int lim = kend - j0 - 4 * g;
+      uint32_t dd[2][8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float d2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int ii = i + e;
+            const bool valid = !need_mask || (blk * 32 + 8 * (ii >> 2) + (ii & 3) < lim);
+            const float x = sacc[blk][ii] * c_log;
+            if constexpr (MODE == MODE_SOFTMAX) {
+              const float pr = valid ? fast_exp2(x - lse2) : 0.f;
+              d2[e] = pr * (pacc[blk][ii] - dlt);
+            } else {
+              d2[e] = valid ? act_grad_f<MODE>(x) * pacc[blk][ii] * wn : 0.f;
+            }
+          }
+          dd[blk][i >> 1] = pack2bf(d2[0], d2[1]);
+        }
+      // dQ^T += K^T dS^T; chunk c covers keys 16c + 8(e/4) + 4g + e%4
+      const __bf16* kt = reinterpret_cast<const __bf16*>(sb + L::KT);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 dw = {dd[c >> 1][4 * (c & 1)], dd[c >> 1][4 * (c & 1) + 1],
+                          dd[c >> 1][4 * (c & 1) + 2], dd[c >> 1][4 * (c & 1) + 3]};
+        const bf16x8 db8 = as_bf16x8(dw);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 ka = as_bf16x8(*(const u32x4*)(kt + (db * 32 + l32) * TS + 16 * c + 8 * g));
+          acc[db] = mfma_bf16(ka, db8, acc[db]);
+        }
+      }
+    };
+
+    if (steps > 0) {
+      load_step(0);
+      store_step(0, 0);
     }
+    __syncthreads();
+    for (int it = 0; it + 1 < steps; ++it) {
+      load_step(it + 1);
+      compute_step(it);
+      store_step((it + 1) & 1, it + 1);
+      __syncthreads();
+    }
+    if (steps > 0) compute_step(steps - 1);
+
+    const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const u32x2 q2 = {pack2bf(acc[db][4 * jq] * p.scale, acc[db][4 * jq + 1] * p.scale),
+                          pack2bf(acc[db][4 * jq + 2] * p.scale, acc[db][4 * jq + 3] * p.scale)};
+        st8(q2, rdq, qoff + 2 * (db * 32 + 8 * jq + 4 * g));
+      }
   }
 }
 
-template <int D, int NW, int MODE>
-hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  using L = BqLds<D, NW>;
-  auto kern = bwd_q_kernel<D, NW, MODE>;
-  static int attr = 0;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       L::total(JFA_BIAS_DENSE));
+template <class K>
+hipError_t launch_persistent(K kern, size_t lds, int threads, int64_t max_items, int cu,
+                             const BwdParams& p, const char* tname, hipStream_t s, int* attr) {
+  if (!*attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr = 1;
+    *attr = 1;
   }
-  const size_t lds = L::total(p.bias_kind);
-  int grid = resident_grid((const void*)kern, NW * 64, lds, cu);
+  int grid = resident_grid((const void*)kern, threads, lds, cu);
   if ((int64_t)grid > max_items) grid = (int)max(max_items, (int64_t)1);
-  timing_begin("jfa_bwd_dq", s);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, s, p);
+  timing_begin(tname, s);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, p);
   timing_end(s);
   return hipGetLastError();
 }
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, int BIAS>
 hipError_t run_bk(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  using L = BkLds<D, NW>;
-  auto kern = bwd_kv_kernel<D, NW, MODE>;
   static int attr = 0;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       L::total(JFA_BIAS_DENSE));
-    if (e != hipSuccess) return e;
-    attr = 1;
-  }
-  const size_t lds = L::total(p.bias_kind);
-  int grid = resident_grid((const void*)kern, NW * 64, lds, cu);
-  if ((int64_t)grid > max_items) grid = (int)max(max_items, (int64_t)1);
-  timing_begin("jfa_bwd_dkdv", s);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, s, p);
-  timing_end(s);
-  return hipGetLastError();
+  return launch_persistent(bwd_kv_kernel<D, NW, MODE, BIAS>, KvLds<D, NW, BIAS>::TOTAL, NW * 64,
+                           max_items, cu, p, "jfa_bwd_dkdv", s, &attr);
+}
+template <int D, int NW, int MODE, int BIAS>
+hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
+  static int attr = 0;
+  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
+                           max_items, cu, p, "jfa_bwd_dq", s, &attr);
+}
+
+template <int D, int MODE, int BIAS>
+hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
+                        hipStream_t s) {
+  hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS>(p, mk, cu, s)
+                               : run_bk<D, 2, MODE, BIAS>(p, mk, cu, s);
+  if (e != hipSuccess) return e;
+  return tc.bq_nw == 4 ? run_bq<D, 4, MODE, BIAS>(p, mq, cu, s) : run_bq<D, 2, MODE, BIAS>(p, mq, cu, s);
 }
 
 template <int D, int MODE>
 hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                    hipStream_t s) {
-  hipError_t e = hipSuccess;
   if (MODE == MODE_SOFTMAX) {
     constexpr int RPB = 256 / (D / 8);
     const int64_t pairs = p.total_q * p.H;
@@ -531,13 +723,15 @@ hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk
                          dim3(256), 0, s, (const __bf16*)p.o, (const __bf16*)p.dout, p.delta,
                          p.total_q, p.H);
       timing_end(s);
-      e = hipGetLastError();
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  e = tc.bk_nw == 4 ? run_bk<D, 4, MODE>(p, mk, cu, s) : run_bk<D, 2, MODE>(p, mk, cu, s);
-  if (e != hipSuccess) return e;
-  return tc.bq_nw == 4 ? run_bq<D, 4, MODE>(p, mq, cu, s) : run_bq<D, 2, MODE>(p, mq, cu, s);
+  switch (p.bias_kind) {
+    case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS>(p, tc, mq, mk, cu, s);
+    case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE>(p, tc, mq, mk, cu, s);
+    default: return run_bwd_bias<D, MODE, B_NONE>(p, tc, mq, mk, cu, s);
+  }
 }
 
 }  // namespace

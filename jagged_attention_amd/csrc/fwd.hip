@@ -60,13 +60,6 @@ struct FwdLds {
   static constexpr int TOTAL = 2 * STAGE;
 };
 
-// Position of key k (0..63) inside its V^T row: within each group of 16 keys, key
-// 8a + 4g + b sits at 8g + 4a + b, so that the 8 keys an MFMA lane (g) contracts over in one
-// 32x32x16 step are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
-
 // Occupancy: two workgroups per CU.  With 4 waves per workgroup that is 2 waves per SIMD
 // (256 registers each); with 2 waves it is one wave per SIMD, which may use all 512.
 template <int D, int NW, int MODE, int BIAS, bool FP8>

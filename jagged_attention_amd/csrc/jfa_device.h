@@ -96,6 +96,14 @@ __device__ __forceinline__ float e8m0_to_f(uint32_t s) {
   return s == 0 ? 5.877471754111438e-39f : __uint_as_float(s << 23);
 }
 
+// Position of row k (0..63) of a tile stored transposed for the contraction of a 32x32x16
+// MFMA whose other operand comes from a 32x32 accumulator: within each group of 16, row
+// 8a + 4g + b sits at 8g + 4a + b, so the 8 contraction indices of MFMA lane half g (the
+// accumulator rows 8a + 4g + b that lane half holds) are one contiguous 16-byte read.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
+}
+
 // ------------------------------------------------------------------ buffer access
 // A buffer resource covers [base, base + bytes): loads at or past `bytes` return zeros and
 // stores there are dropped, so ragged rows need no branches.  Offsets are 32-bit bytes.
