@@ -145,6 +145,7 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.total_kv = p.total_kv;
   a.tc = tc;
   a.want_bias_off = 1;
+  a.lists = 7;
   a.hd_bytes = (int64_t)p.heads * p.head_dim * (p.dtype == JFA_F32 ? 4 : (p.dtype == JFA_BF16 ? 2 : 1));
   if (p.dtype == JFA_MXFP8_E4M3) a.hd_bytes = (int64_t)p.heads * p.head_dim * 2;   // bf16 output rows
   a.dense_bias = p.bias_kind == JFA_BIAS_DENSE;
@@ -286,6 +287,7 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   char* ws = (char*)workspace;
 
   SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
+  a.lists = 1;
   hipError_t e = launch_schedule(a, s);
   if (e != hipSuccess) return JFA_ERR_LAUNCH;
 
@@ -343,6 +345,7 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   char* ws = (char*)workspace;
 
   SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
+  a.lists = 6;
   hipError_t e = launch_schedule(a, s);
   if (e != hipSuccess) return JFA_ERR_LAUNCH;
 

@@ -30,6 +30,8 @@
 //    take them with an atomic ticket.  Records that are chunks of a split tile write fp32
 //    partials (unnormalised accumulator, max, sum) that the combine kernel merges in chunk
 //    order.
+#include <algorithm>
+
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -494,52 +496,55 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-// Merges the chunks of every split tile in chunk order (deterministic).
+// Merges the chunks of every split tile in chunk order (deterministic).  A work unit is RPU
+// rows of one (split tile, head); each thread owns 4 dims of one row, finds the row's running
+// max over the chunks and sums the chunks' accumulators with weights e^(m_c - M) / sum_c
+// e^(m_c - M) l_c (softmax) or 1/kv_len (GDPA); all of a thread's loads are independent.
 template <int D, int BM, int MODE>
 __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
+  constexpr int RPU = 1024 / D;            // rows per unit: 256 threads x 4 dims
+  constexpr int UPT = BM / RPU;            // units per (tile, head)
   const int H = p.H;
   if (p.hdr_ro->status != JFA_OK) return;
-  const int64_t n_items = (int64_t)p.hdr_ro->counts[1] * H;
-  const int64_t w = blockIdx.x;
-  if (w >= n_items) return;
-  const int4 rec = p.comb[w / H];
-  const int h = (int)(w % H);
-  const int b = rec.x, t = rec.y, slot0 = rec.z, nch = rec.w;
-  const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
-  const int m = p.kv_off[b + 1] - p.kv_off[b];
-  const int q0 = t * BM;
-  for (int e = threadIdx.x; e < BM * (D / 4); e += 256) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
+  const int64_t n_units = (int64_t)p.hdr_ro->counts[1] * H * UPT;
+  const int r_in = threadIdx.x / (D / 4), c4 = threadIdx.x % (D / 4);
+  for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int64_t w = u / UPT;
+    const int r = (int)(u % UPT) * RPU + r_in;
+    const int4 rec = p.comb[w / H];
+    const int h = (int)(w % H);
+    const int b = rec.x, t = rec.y, slot0 = rec.z, nch = rec.w;
+    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
+    const int m = p.kv_off[b + 1] - p.kv_off[b];
+    const int q0 = t * BM;
     if (q0 + r >= n) continue;
+    auto pb = [&](int c) { return ((int64_t)(slot0 + c) * H + h) * BM + r; };
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float lse = NEG_INF;
     if constexpr (MODE == MODE_SOFTMAX) {
       float M = NEG_INF;
-      for (int c = 0; c < nch; ++c)
-        M = fmaxf(M, p.part_ml[2 * (((int64_t)(slot0 + c) * H + h) * BM + r)]);
-      if (M != NEG_INF) {
-        float Lsum = 0.f;
-        for (int c = 0; c < nch; ++c) {
-          const int64_t pb = ((int64_t)(slot0 + c) * H + h) * BM + r;
-          const float wgt = fast_exp2(p.part_ml[2 * pb] - M);
-          Lsum += wgt * p.part_ml[2 * pb + 1];
-          const f32x4 a = *(const f32x4*)(p.part_acc + pb * D + 4 * c4);
-          o += wgt * a;
-        }
-        o *= 1.0f / Lsum;
-        lse = (M + __log2f(Lsum)) * LN2;
-      }
-    } else {
+#pragma unroll 4
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, p.part_ml[2 * pb(c)]);
+      float Lsum = 0.f;
+#pragma unroll 4
       for (int c = 0; c < nch; ++c) {
-        const int64_t pb = ((int64_t)(slot0 + c) * H + h) * BM + r;
-        o += *(const f32x4*)(p.part_acc + pb * D + 4 * c4);
+        const float2 ml = *(const float2*)(p.part_ml + 2 * pb(c));
+        const f32x4 a = *(const f32x4*)(p.part_acc + pb(c) * D + 4 * c4);
+        const float wgt = M == NEG_INF ? 0.f : fast_exp2(ml.x - M);
+        Lsum += wgt * ml.y;
+        o += wgt * a;
       }
+      o *= Lsum > 0.f ? 1.0f / Lsum : 0.f;
+      if (c4 == 0 && p.lse)
+        p.lse[(int64_t)h * p.total_q + qo + q0 + r] =
+            (M != NEG_INF && Lsum > 0.f) ? (M + __log2f(Lsum)) * LN2 : NEG_INF;
+    } else {
+#pragma unroll 4
+      for (int c = 0; c < nch; ++c) o += *(const f32x4*)(p.part_acc + pb(c) * D + 4 * c4);
       o *= (p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     }
     __bf16* orow = (__bf16*)p.o + ((int64_t)(qo + q0 + r) * H + h) * D;
-    u32x2 pk = {pack2bf(o[0], o[1]), pack2bf(o[2], o[3])};
+    const u32x2 pk = {pack2bf(o[0], o[1]), pack2bf(o[2], o[3])};
     *(u32x2*)(orow + 4 * c4) = pk;
-    if (MODE == MODE_SOFTMAX && c4 == 0 && p.lse) p.lse[(int64_t)h * p.total_q + qo + q0 + r] = lse;
   }
 }
 
@@ -563,9 +568,11 @@ hipError_t run_fwd(const FwdParams& p, int64_t max_items, int64_t max_comb, int 
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_comb <= 0) return e;
+  // combine units: (split tile, head, group of 1024/D rows); the count is on the device
+  const int64_t units = max_comb * (32 * NW) / (1024 / D);
+  const unsigned cgrid = (unsigned)std::min<int64_t>(std::max<int64_t>(units, 1), 2048);
   timing_begin("jfa_fwd_combine", s);
-  hipLaunchKernelGGL((combine_kernel<D, 32 * NW, MODE>), dim3((unsigned)max_comb), dim3(256), 0,
-                     s, p);
+  hipLaunchKernelGGL((combine_kernel<D, 32 * NW, MODE>), dim3(cgrid), dim3(256), 0, s, p);
   timing_end(s);
   return hipGetLastError();
 }

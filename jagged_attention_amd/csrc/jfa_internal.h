@@ -61,6 +61,7 @@ struct SchedArgs {
   int64_t total_q, total_kv;
   TileCfg tc;
   int want_bias_off;
+  int lists;           // bit 0: forward + combine, bit 1: q-stationary, bit 2: kv-stationary
   int64_t hd_bytes;    // bytes of one (row, all heads) vector: H * d * element size
   int32_t dense_bias;  // dense bias present (its per-sample block must fit 32-bit offsets)
   WsHeader* hdr;

@@ -12,8 +12,9 @@
 //    one query tile (or else one key tile) takes a single pass that owns all its gradients;
 //  - every list is ordered longest first, ties by (sample, tile, first step): a total order,
 //    so the lists are unique and bit-reproducible.
-// One workgroup of 1024 threads does all of it with block scans and a stable 4-bit LSD radix
-// sort on the inverted cost; no host round trip.
+// One workgroup of 1024 threads does all of it with block scans and a sort on the inverted
+// cost (bitonic in LDS, or a stable radix sort in global memory for long lists); no host
+// round trip.
 #include "jfa_internal.h"
 
 namespace jfa {
@@ -116,24 +117,54 @@ __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t*
 
 struct Shared {
   uint32_t sa[LDS_SORT_MAX];
-  uint32_t sb[LDS_SORT_MAX];
   int32_t T[16 * ST];
   int64_t red[SW];
   int32_t flag;
   int64_t sumcost;
 };
 
-// Sorts gen_recs[0..n) by cost (desc, stable) into out / out_slot; costs[] in t_cost.
+// Ascending bitonic sort of N (a power of two, at most LDS_SORT_MAX) keys in LDS; keys are unique, so the result is the unique sorted order.
+__device__ void bitonic_sort(uint32_t* s, int N) {
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < N / 2; i += ST) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo + j;
+        const bool up = (lo & k) == 0;
+        const uint32_t x = s[lo], y = s[hi];
+        if ((x > y) == up) {
+          s[lo] = y;
+          s[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Sorts gen_recs[0..n) by cost (desc, ties by generation index) into out / out_slot; the keys
+// (inverted cost << 20 | index) are unique, so the order is total.  Lists that fit in LDS use a
+// bitonic sort there; longer ones a stable radix sort in global memory.
 __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32_t* t_cost,
                               int4* out, int32_t* out_slot) {
-  uint32_t* wa = n <= LDS_SORT_MAX ? sh.sa : a.words_a;
-  uint32_t* wb = n <= LDS_SORT_MAX ? sh.sb : a.words_b;
-  for (int i = threadIdx.x; i < n; i += ST)
-    wa[i] = ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i;
-  __syncthreads();
-  radix_sort(wa, wb, n, sh.T, sh.red);
+  const uint32_t* sorted;
+  if (n <= LDS_SORT_MAX) {
+    int N = 1;
+    while (N < n) N <<= 1;
+    for (int i = threadIdx.x; i < N; i += ST)
+      sh.sa[i] = i < n ? ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort(sh.sa, N);
+    sorted = sh.sa;
+  } else {
+    for (int i = threadIdx.x; i < n; i += ST)
+      a.words_a[i] = ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i;
+    __syncthreads();
+    radix_sort(a.words_a, a.words_b, n, sh.T, sh.red);
+    sorted = a.words_b;
+  }
   for (int i = threadIdx.x; i < n; i += ST) {
-    const uint32_t idx = wb[i] & 0xFFFFFu;
+    const uint32_t idx = sorted[i] & 0xFFFFFu;
     out[i] = a.gen_recs[idx];
     if (out_slot) out_slot[i] = a.gen_slot[idx];
   }
@@ -187,7 +218,9 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (a.want_bias_off)
     scan_to(a.bias_off, B, [&](int64_t b) { return qlen((int)b) * klen((int)b); }, sh.red);
 
-  int32_t* s_base = a.s_tmp;                 // per-sample tile base [B+1]
+  // per-sample tile base [B+1]: in LDS (the sort's counter space, idle during generation)
+  // whenever it fits, since every tile looks its sample up there by binary search
+  int32_t* s_base = (B + 1 <= 16 * ST) ? sh.T : a.s_tmp;
   int32_t* t_cost = a.t_tmp;                 // per record cost (generation order)
   int32_t* t_rb = a.t_tmp + (a.cap_t + 1);   // per tile record base
   int32_t* t_sb = a.t_tmp + 2 * (a.cap_t + 1); // per tile slot base
@@ -195,8 +228,9 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   int overflow = 0;
 
   // ================= forward list =================
-  const int64_t ntiles = scan_to(s_base, B, [&](int64_t b) { return cdiv(qlen((int)b), tc.bm); },
-                                 sh.red);
+  const bool want_f = a.lists & 1, want_q = a.lists & 2, want_k = a.lists & 4;
+  const int64_t ntiles =
+      want_f ? scan_to(s_base, B, [&](int64_t b) { return cdiv(qlen((int)b), tc.bm); }, sh.red) : 0;
   if (ntiles > a.cap_t) overflow = 1;
   auto fwd_steps = [&](int64_t tau, int& b, int64_t& t) -> int64_t {
     b = owner_of(s_base, B, tau);
@@ -209,7 +243,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   };
   int64_t C = 0;
   int64_t nrec = 0, nslot = 0, ncomb = 0;
-  if (!overflow) {
+  if (want_f && !overflow) {
     // total cost -> split threshold
     int64_t part = 0;
     for (int64_t tau = tid; tau < ntiles; tau += ST) {
@@ -230,7 +264,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; }, sh.red);
     if (nrec > a.cap_f || nrec > a.cap_t || ncomb > a.cap_c || nslot > a.cap_slots) overflow = 1;
   }
-  if (!overflow) {
+  if (want_f && !overflow) {
     for (int64_t tau = tid; tau < ntiles; tau += ST) {
       int b; int64_t t;
       const int64_t s = fwd_steps(tau, b, t);
@@ -252,12 +286,12 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   auto one_q = [&](int b) { return tc.fuse && cdiv(qlen(b), tc.bq_bm) == 1; };
   auto one_k = [&](int b) { return tc.fuse && !one_q(b) && cdiv(klen(b), tc.bk_bn) == 1; };
   int64_t nq = 0, nk = 0;
-  if (!overflow) {
+  if (want_q && !overflow) {
     nq = scan_to(s_base, B, [&](int64_t b) { return one_k((int)b) ? 0 : cdiv(qlen((int)b), tc.bq_bm); },
                  sh.red);
     if (nq > a.cap_q || nq > a.cap_t) overflow = 1;
   }
-  if (!overflow) {
+  if (want_q && !overflow) {
     for (int64_t tau = tid; tau < nq; tau += ST) {
       const int b = owner_of(s_base, B, tau);
       const int64_t t = tau - s_base[b];
@@ -280,12 +314,12 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   }
 
   // ================= kv-stationary backward list =================
-  if (!overflow) {
+  if (want_k && !overflow) {
     nk = scan_to(s_base, B, [&](int64_t b) { return one_q((int)b) ? 0 : cdiv(klen((int)b), tc.bk_bn); },
                  sh.red);
     if (nk > a.cap_k || nk > a.cap_t) overflow = 1;
   }
-  if (!overflow) {
+  if (want_k && !overflow) {
     for (int64_t tau = tid; tau < nk; tau += ST) {
       const int b = owner_of(s_base, B, tau);
       const int64_t u = tau - s_base[b];
