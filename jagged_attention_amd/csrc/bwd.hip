@@ -99,6 +99,29 @@ struct Tile {
         v[i][rr] = ld16(r, (uint32_t)(r0 + 4 * rb + rr) * row_bytes + 16 * cb);
     }
   }
+  // One sixth of block I's stores: PART 0, 1 write rows 2*PART, 2*PART+1 row-major; PART 2..5
+  // write dims 8cb + 2(PART-2) and + 1 transposed (so the stores can be spread out).
+  static constexpr int PARTS = 6 * NB;
+  template <int P>
+  __device__ __forceinline__ void store_part(__bf16* rows, __bf16* tr) const {
+    constexpr int i = P / 6, part = P % 6;
+    const int id = threadIdx.x + i * NT;
+    if (NBLK % NT != 0 && id >= NBLK) return;
+    int rb, cb;
+    blk_of(id, rb, cb);
+    if constexpr (part < 2) {
+#pragma unroll
+      for (int rr = 2 * part; rr < 2 * part + 2; ++rr)
+        *(u32x4*)(rows + (4 * rb + rr) * (D + 8) + 8 * cb) = v[i][rr];
+    } else {
+      constexpr int e2 = part - 2;
+      const int pos = vt_pos(4 * rb);
+      const u32x2 lo = {lo_halves(v[i][0][e2], v[i][1][e2]), lo_halves(v[i][2][e2], v[i][3][e2])};
+      const u32x2 hi = {hi_halves(v[i][0][e2], v[i][1][e2]), hi_halves(v[i][2][e2], v[i][3][e2])};
+      *(u32x2*)(tr + (8 * cb + 2 * e2) * TS + pos) = lo;
+      *(u32x2*)(tr + (8 * cb + 2 * e2 + 1) * TS + pos) = hi;
+    }
+  }
   // rows: [STEP][D + 8] row-major (may be null); tr: [D][TS] transposed, rows permuted
   __device__ __forceinline__ void store(__bf16* rows, __bf16* tr) const {
 #pragma unroll
@@ -156,6 +179,42 @@ __device__ __forceinline__ void store_diag(float* rp, int idx, float v) {
   for (int k = 0; k < 4; ++k) rp[k * RP + idx + k] = v;
 }
 
+// Scheduling pattern for a region holding the MFMAs (and their LDS operand reads) of one
+// phase and the VALU work of another: a few reads ahead, then MFMA / read / VALU groups.
+#ifndef JFA_SCHED_VARIANT
+#define JFA_SCHED_VARIANT 1
+#endif
+template <int NM>
+__device__ __forceinline__ void kv_interleave(int id) {
+#if JFA_SCHED_VARIANT == 1
+  (void)id;
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+#elif JFA_SCHED_VARIANT == 2
+  (void)id;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+#elif JFA_SCHED_VARIANT == 4
+  (void)id;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+#else
+  (void)id;
+#endif
+}
+
 // ================================================= key-stationary dK, dV
 template <int D, int NW, int BIAS>
 struct KvLds {
@@ -165,10 +224,10 @@ struct KvLds {
   static constexpr int DR = QR + STEP * RS * 2;           // dO rows
   static constexpr int QT = DR + STEP * RS * 2;           // Q^T [D][TS]
   static constexpr int DT = QT + D * TS * 2;              // dO^T
-  static constexpr int LS = DT + D * TS * 2;              // lse * log2 e [STEP]
+  static constexpr int LS = DT + D * TS * 2;              // lse / scale [STEP]
   static constexpr int DL = LS + STEP * 4;                // delta [STEP]
   static constexpr int BO = DL + STEP * 4;
-  static constexpr int RP = STEP + BNK + 4;
+  static constexpr int RP = diag_stride(STEP + BNK + 4);
   static constexpr int BS = STEP + 8;                     // dense tile [BNK][BS] bf16 (key-major)
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BNK * BS * 2 : 0);
@@ -259,14 +318,27 @@ void bwd_kv_kernel(BwdParams p) {
       tq.load(rq, row_bytes, q0);
       tdo.load(rdo, row_bytes, q0);
     };
-    auto store_step = [&](int st, int qs) {
+    // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
+    constexpr int TP = Tile<D, NT>::PARTS;
+    auto store_tile_piece = [&](auto pc, int st) {
+      constexpr int P = decltype(pc)::value;
+      unsigned char* base = lds + st * L::STAGE;
+      if constexpr (P < TP)
+        tq.template store_part<P>(reinterpret_cast<__bf16*>(base + L::QR),
+                                  reinterpret_cast<__bf16*>(base + L::QT));
+      else
+        tdo.template store_part<P - TP>(reinterpret_cast<__bf16*>(base + L::DR),
+                                        reinterpret_cast<__bf16*>(base + L::DT));
+    };
+    auto store_step = [&](int st, int qs, bool tiles) {
       unsigned char* base = lds + st * L::STAGE;
       const int q0 = qs * STEP;
-      tq.store(reinterpret_cast<__bf16*>(base + L::QR), reinterpret_cast<__bf16*>(base + L::QT));
-      tdo.store(reinterpret_cast<__bf16*>(base + L::DR), reinterpret_cast<__bf16*>(base + L::DT));
+      if (tiles) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, st); });
       if constexpr (MODE == MODE_SOFTMAX) {
         if (tid < STEP) {
-          reinterpret_cast<float*>(base + L::LS)[tid] = lsv * LOG2E;
+          // rows without a visible key have lse = -inf; all their pairs are masked to -inf,
+          // so any finite value keeps exp2(-inf - lse) = 0
+          reinterpret_cast<float*>(base + L::LS)[tid] = lsv == NEG_INF ? 0.f : lsv * inv_scale;
           reinterpret_cast<float*>(base + L::DL)[tid] = dlv;
         }
       }
@@ -291,12 +363,28 @@ void bwd_kv_kernel(BwdParams p) {
       }
     };
 
-    auto compute_step = [&](int it, int qs) {
+    // One query step, software-pipelined by hand.  The step is a stream of 64 MFMAs:
+    //   A(h), h = 0, 1: S_h = Q_h K^T and dP_h = dO_h V^T    (queries 32h .. 32h+31)
+    //   C(h):           dV^T += dO_h^T P_h, dK^T += Q_h^T dS_h
+    // in the order A(0) A(1) C(0) C(1).  Every MFMA's LDS operand is read PF MFMAs ahead, and the
+    // VALU work B(h) that turns S_h, dP_h into P_h, dS_h is spread one element per MFMA over the
+    // next phase (B(0) under A(1), B(1) under C(0)), so the matrix cores stay busy in this
+    // one-wave-per-SIMD kernel.  sched_barrier pins that order against the compiler's scheduler.
+    // `nst` >= 0: the LDS stage that the prefetched next tiles go to; their stores are spread
+    // over the last phase C(1), whose MFMAs need no VALU work.
+    auto compute_step = [&](int it, int qs, int nst) {
       const int q0 = qs * STEP;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
-      if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0)) return;
+      if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0)) {
+        if (nst >= 0) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, nst); });
+        return;
+      }
       const __bf16* qr = reinterpret_cast<const __bf16*>(sb + L::QR);
       const __bf16* dr = reinterpret_cast<const __bf16*>(sb + L::DR);
+      const __bf16* qt = reinterpret_cast<const __bf16*>(sb + L::QT);
+      const __bf16* dt = reinterpret_cast<const __bf16*>(sb + L::DT);
+      const float* lsl = reinterpret_cast<const float*>(sb + L::LS);
+      const float* dll = reinterpret_cast<const float*>(sb + L::DL);
       // element (blk, i): query q0 + blk*32 + 8(i/4) + 4g + i%4 of this step, key j
       f32x16 sacc[2], pacc[2];
       if constexpr (BIAS == B_RELPOS) {
@@ -329,90 +417,139 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
       }
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
-        const int qrow = blk * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 qa = as_bf16x8(*(const u32x4*)(qr + qrow * RS + 16 * ks + 8 * g));
-          sacc[blk] = mfma_bf16(qa, kf[ks], sacc[blk]);
-          const bf16x8 da = as_bf16x8(*(const u32x4*)(dr + qrow * RS + 16 * ks + 8 * g));
-          pacc[blk] = mfma_bf16(da, vf[ks], pacc[blk]);
-        }
-      }
-      // visibility: query offset o = blk*32 + 8(i/4) + i%4 (+4g) is visible iff qlo <= o < qhi
+      // pairs that are not visible start at -inf, so P = 0 and dS = 0 with no per-element test
+      // later: query offset o = blk*32 + 8(i/4) + i%4 (+4g) is visible iff qlo <= o < qhi
       const bool need_mask = (q0 + STEP > n) || (jw0 + 32 > m) ||
                              (p.causal && q0 + delta < jw0 + 31);
-      const int qhi = j < m ? n - q0 - 4 * g : -1;
-      const int qlo = p.causal ? j - delta - q0 - 4 * g : -1;
-      uint32_t pp[2][8], dd[2][8];
-      const float* lsl = reinterpret_cast<const float*>(sb + L::LS);
-      const float* dll = reinterpret_cast<const float*>(sb + L::DL);
+      if (need_mask) {
+        const int qhi = j < m ? n - q0 - 4 * g : -1;
+        const int qlo = p.causal ? j - delta - q0 - 4 * g : -1;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          f32x4 l2 = {0.f, 0.f, 0.f, 0.f}, dl = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (MODE == MODE_SOFTMAX) {
-            l2 = *(const f32x4*)(lsl + blk * 32 + 8 * qd + 4 * g);
-            dl = *(const f32x4*)(dll + blk * 32 + 8 * qd + 4 * g);
+          for (int i = 0; i < 16; ++i) {
+            const int o = blk * 32 + 8 * (i >> 2) + (i & 3);
+            if (o < qlo || o >= qhi) sacc[blk][i] = NEG_INF;
           }
-          float pv[4], dsv[4];
+      }
+      // softmax: S starts at bias/scale - lse/scale and dP at -delta, so that the VALU work per
+      // pair is P = exp2(S c), dS = P dP (masked pairs stay at -inf)
+      if constexpr (MODE == MODE_SOFTMAX) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * qd + e;
-            const int o = blk * 32 + 8 * qd + e;
-            const bool valid = !need_mask || (o >= qlo && o < qhi);
-            const float x = sacc[blk][i] * c_log;
-            if constexpr (MODE == MODE_SOFTMAX) {
-              const float pr = valid ? fast_exp2(x - l2[e]) : 0.f;
-              pv[e] = pr;
-              dsv[e] = pr * (pacc[blk][i] - dl[e]);
-            } else {
-              pv[e] = valid ? act_f<MODE>(x) * wn : 0.f;
-              dsv[e] = valid ? act_grad_f<MODE>(x) * pacc[blk][i] * wn : 0.f;
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 l = *(const f32x4*)(lsl + blk * 32 + 8 * qd + 4 * g);
+            const f32x4 dl = *(const f32x4*)(dll + blk * 32 + 8 * qd + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sacc[blk][4 * qd + e] -= l[e];
+              pacc[blk][4 * qd + e] = -dl[e];
             }
           }
-          pp[blk][2 * qd] = pack2bf(pv[0], pv[1]);
-          pp[blk][2 * qd + 1] = pack2bf(pv[2], pv[3]);
-          dd[blk][2 * qd] = pack2bf(dsv[0], dsv[1]);
-          dd[blk][2 * qd + 1] = pack2bf(dsv[2], dsv[3]);
-        }
-      // dV^T += dO^T P, dK^T += Q^T dS; chunk c covers queries 16c + 8(e/4) + 4g + e%4
-      const __bf16* qt = reinterpret_cast<const __bf16*>(sb + L::QT);
-      const __bf16* dt = reinterpret_cast<const __bf16*>(sb + L::DT);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 pw = {pp[c >> 1][4 * (c & 1)], pp[c >> 1][4 * (c & 1) + 1],
-                          pp[c >> 1][4 * (c & 1) + 2], pp[c >> 1][4 * (c & 1) + 3]};
-        const u32x4 dw = {dd[c >> 1][4 * (c & 1)], dd[c >> 1][4 * (c & 1) + 1],
-                          dd[c >> 1][4 * (c & 1) + 2], dd[c >> 1][4 * (c & 1) + 3]};
-        const bf16x8 pb = as_bf16x8(pw), db8 = as_bf16x8(dw);
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 da = as_bf16x8(*(const u32x4*)(dt + (db * 32 + l32) * TS + 16 * c + 8 * g));
-          dv[db] = mfma_bf16(da, pb, dv[db]);
-          const bf16x8 qa = as_bf16x8(*(const u32x4*)(qt + (db * 32 + l32) * TS + 16 * c + 8 * g));
-          dk[db] = mfma_bf16(qa, db8, dk[db]);
-        }
+          for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
       }
+
+      constexpr int NA = D / 8;          // MFMAs per phase: 16 at d = 128, 8 at d = 64
+      constexpr int NS = 4 * NA;         // MFMAs per step
+      constexpr int PF = 6;              // operand read distance (MFMAs)
+      constexpr int RING = 8;
+      // operand of stream MFMA s
+      auto opnd = [&](int s) -> u32x4 {
+        if (s < 2 * NA) {
+          const int h = s / NA, jj = s % NA, ks = jj >> 1;
+          const __bf16* base = (jj & 1) ? dr : qr;
+          return *(const u32x4*)(base + (h * 32 + l32) * RS + 16 * ks + 8 * g);
+        }
+        const int h = (s - 2 * NA) / NA, jj = (s - 2 * NA) % NA;
+        const int cc = jj / (NA / 2), db = (jj % (NA / 2)) >> 1;
+        const __bf16* base = (jj & 1) ? qt : dt;
+        return *(const u32x4*)(base + (db * 32 + l32) * TS + 16 * (2 * h + cc) + 8 * g);
+      };
+      uint32_t pp[2][8], dd[2][8];
+      // B(h) element i (query offset blk*32 + 8(i/4) + i%4 with blk = h)
+      float pv_t = 0.f, ds_t = 0.f;
+      auto valu_b = [&](int h, int i) {
+        float pv, dsv;
+        if constexpr (MODE == MODE_SOFTMAX) {
+          pv = fast_exp2(sacc[h][i] * c_log);
+          dsv = pv * pacc[h][i];
+        } else {
+          const bool vis = sacc[h][i] != NEG_INF;
+          const float x = sacc[h][i] * c_log;
+          pv = vis ? act_f<MODE>(x) * wn : 0.f;
+          dsv = vis ? act_grad_f<MODE>(x) * pacc[h][i] * wn : 0.f;
+        }
+        if (i & 1) {
+          pp[h][i >> 1] = pack2bf(pv_t, pv);
+          dd[h][i >> 1] = pack2bf(ds_t, dsv);
+        } else {
+          pv_t = pv;
+          ds_t = dsv;
+        }
+      };
+      auto mfma_s = [&](int s, u32x4 o) {
+        const bf16x8 a = as_bf16x8(o);
+        if (s < 2 * NA) {
+          const int h = s / NA, jj = s % NA, ks = jj >> 1;
+          if (jj & 1) pacc[h] = mfma_bf16(a, vf[ks], pacc[h]);
+          else sacc[h] = mfma_bf16(a, kf[ks], sacc[h]);
+          return;
+        }
+        const int h = (s - 2 * NA) / NA, jj = (s - 2 * NA) % NA;
+        const int cc = jj / (NA / 2), db = (jj % (NA / 2)) >> 1;
+        if (jj & 1) {
+          const u32x4 w = {dd[h][4 * cc], dd[h][4 * cc + 1], dd[h][4 * cc + 2], dd[h][4 * cc + 3]};
+          dk[db] = mfma_bf16(a, as_bf16x8(w), dk[db]);
+        } else {
+          const u32x4 w = {pp[h][4 * cc], pp[h][4 * cc + 1], pp[h][4 * cc + 2], pp[h][4 * cc + 3]};
+          dv[db] = mfma_bf16(a, as_bf16x8(w), dv[db]);
+        }
+      };
+      u32x4 ring[RING];
+      static_for<0, PF>([&](auto s) { ring[s] = opnd(s); });
+      static_for<0, NS>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (s + PF < NS) ring[(s + PF) % RING] = opnd(s + PF);
+        mfma_s(s, ring[s % RING]);
+        // B(0) under A(1), B(1) under C(0): one element per MFMA (16 elements per half)
+        constexpr int EPM = 16 / NA;     // elements per MFMA (1 at d = 128, 2 at d = 64)
+        if constexpr (s >= NA && s < 2 * NA) {
+          static_for<0, EPM>([&](auto e) { valu_b(0, (s - NA) * EPM + e); });
+        }
+        if constexpr (s >= 2 * NA && s < 3 * NA) {
+          static_for<0, EPM>([&](auto e) { valu_b(1, (s - 2 * NA) * EPM + e); });
+        }
+        // next tiles' stores: piece k of 2 * TP goes with MFMA 3 NA + k NA / (2 TP)
+        if constexpr (s >= 3 * NA) {
+          if (nst >= 0) {
+            static_for<0, 2 * TP>([&](auto pc) {
+              constexpr int P = decltype(pc)::value;
+              if constexpr (3 * NA + P * NA / (2 * TP) == s) store_tile_piece(pc, nst);
+            });
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     const int nsteps = qs_end - qs_first;
     if (nsteps > 0) {
       load_step(qs_first);
-      store_step(0, qs_first);
+      store_step(0, qs_first, true);
     }
     __syncthreads();
     for (int it = 0; it + 1 < nsteps; ++it) {
       load_step(qs_first + it + 1);
-      compute_step(it, qs_first + it);
-      store_step((it + 1) & 1, qs_first + it + 1);
+      compute_step(it, qs_first + it, -1);
+      store_step((it + 1) & 1, qs_first + it + 1, true);
       __syncthreads();
     }
-    if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1);
+    if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1, -1);
 
     // epilogue: this lane's key row of dK (x scale) and dV; keys past the sample are dropped
     const rsrc_t rdk = make_rsrc((__bf16*)p.dk + ((int64_t)ko * H + h) * D, kv_bytes);
@@ -442,7 +579,7 @@ struct QLds {
   static constexpr int VR = KR + STEP * RS * 2;           // V rows
   static constexpr int KT = VR + STEP * RS * 2;           // K^T [D][TS]
   static constexpr int BO = KT + D * TS * 2;
-  static constexpr int RP = BM + STEP + 4;
+  static constexpr int RP = diag_stride(BM + STEP + 4);
   static constexpr int BS = STEP + 8;                     // dense tile [BM][BS] bf16 (query-major)
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);

@@ -53,7 +53,7 @@ struct FwdLds {
   static constexpr int VS = BN + 8;                            // V^T row stride (bf16)
   static constexpr int V_OFF = align16(K_BYTES + KSC_BYTES);
   static constexpr int V_BYTES = D * VS * 2;
-  static constexpr int RP = BM + BN + 4;                       // relpos copy length (floats)
+  static constexpr int RP = diag_stride(BM + BN + 4);          // relpos copy length (floats)
   static constexpr int BS = BN + 8;                            // dense bias row stride (bf16)
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);

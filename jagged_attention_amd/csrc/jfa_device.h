@@ -5,6 +5,17 @@
 
 namespace jfa {
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E), every index a constant
+// expression (fully unrolled however large the body).
+template <int I> struct ic { static constexpr int value = I; constexpr operator int() const { return I; } };
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -103,6 +114,11 @@ __device__ __forceinline__ float e8m0_to_f(uint32_t s) {
 __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
 }
+
+// Length (floats) of one copy of a four-copy diagonal bias table: at least `len`, and 16 mod 64,
+// so that the 16 lanes reading 16 consecutive diagonals from rotating copies hit 16 distinct
+// 16-byte bank groups.
+constexpr int diag_stride(int len) { return (len - 16 + 63) / 64 * 64 + 16; }
 
 // ------------------------------------------------------------------ buffer access
 // A buffer resource covers [base, base + bytes): loads at or past `bytes` return zeros and
