@@ -68,7 +68,9 @@ jfa_status tile_cfg(const jfa_problem& p, TileCfg* t) {
   }
   const bool short_q = p.total_q <= 64 * (int64_t)p.batch;
   const bool short_kv = p.total_kv <= 64 * (int64_t)p.batch;
-  t->fwd_nw = short_q ? 2 : 4;
+  // 64-row query tiles for short queries, and for a dense bias at d = 128 (the 128-row kernel
+  // would spill registers holding the prefetched bias block)
+  t->fwd_nw = (short_q || (p.bias_kind == JFA_BIAS_DENSE && p.head_dim == 128)) ? 2 : 4;
   t->bm = 32 * t->fwd_nw;
   t->bn = FWD_BN;
   if (p.split_slots > 0) {

@@ -255,6 +255,11 @@ void bwd_kv_kernel(BwdParams p) {
   Tile<D, NT> tq, tdo;
   float lsv = 0.f, dlv = 0.f;       // lse / delta entry staged by threads < STEP
   float rpv = 0.f;                  // relpos table entry
+  // Dense bias pairs (two queries, one key) per thread and step; the first NPRE are prefetched
+  // into registers with the Q/dO tiles, the rest (where registers run short) load while staging.
+  constexpr int NDB = BIAS == B_DENSE ? BNK * STEP / 2 / NT : 1;
+  constexpr int NPRE = D == 128 ? 0 : NDB;
+  uint32_t dbr[NPRE > 0 ? NPRE : 1];
 
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_BK], &s_ticket);
@@ -299,6 +304,15 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
 
+    auto dense_pair = [&](int i, int q0) -> uint32_t {
+      const int e = tid + i * NT;
+      const int qa = q0 + 2 * (e / BNK), ja = j0 + e % BNK;
+      const bool okj = ja < m;
+      const uint32_t off = ((uint32_t)qa * (uint32_t)m + (uint32_t)ja) * 2u;
+      const uint32_t lo = (okj && qa < n) ? ld2(rb, off) : 0u;
+      const uint32_t hi = (okj && qa + 1 < n) ? ld2(rb, off + 2u * (uint32_t)m) : 0u;
+      return lo | (hi << 16);
+    };
     auto load_step = [&](int qs) {
       const int q0 = qs * STEP;
       if constexpr (BIAS == B_RELPOS) {
@@ -317,6 +331,10 @@ void bwd_kv_kernel(BwdParams p) {
       }
       tq.load(rq, row_bytes, q0);
       tdo.load(rdo, row_bytes, q0);
+      if constexpr (BIAS == B_DENSE) {
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_pair(i, q0);
+      }
     };
     // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
     constexpr int TP = Tile<D, NT>::PARTS;
@@ -348,17 +366,11 @@ void bwd_kv_kernel(BwdParams p) {
       } else if constexpr (BIAS == B_DENSE) {
         // key-major tile [BNK][BS]: two query rows per thread and key, coalesced along keys
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
-        constexpr int NPAIR = BNK * STEP / 2 / NT;
-#pragma unroll 4
-        for (int i = 0; i < NPAIR; ++i) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
           const int e = tid + i * NT;
-          const int jj = e % BNK, qq = 2 * (e / BNK);
-          const int qa = q0 + qq, ja = j0 + jj;
-          const bool okj = ja < m;
-          const uint32_t off = ((uint32_t)qa * (uint32_t)m + (uint32_t)ja) * 2u;
-          const uint32_t lo = (okj && qa < n) ? ld2(rb, off) : 0u;
-          const uint32_t hi = (okj && qa + 1 < n) ? ld2(rb, off + 2u * (uint32_t)m) : 0u;
-          *(uint32_t*)(bt + jj * L::BS + qq) = lo | (hi << 16);
+          *(uint32_t*)(bt + (e % BNK) * L::BS + 2 * (e / BNK)) =
+              i < NPRE ? dbr[i] : dense_pair(i, qs * STEP);
         }
       }
     };
@@ -480,9 +492,10 @@ void bwd_kv_kernel(BwdParams p) {
           dsv = pv * pacc[h][i];
         } else {
           const bool vis = sacc[h][i] != NEG_INF;
-          const float x = sacc[h][i] * c_log;
-          pv = vis ? act_f<MODE>(x) * wn : 0.f;
-          dsv = vis ? act_grad_f<MODE>(x) * pacc[h][i] * wn : 0.f;
+          float a, da;
+          act_pair<MODE>(sacc[h][i] * c_log, a, da);
+          pv = vis ? a * wn : 0.f;
+          dsv = vis ? da * pacc[h][i] * wn : 0.f;
         }
         if (i & 1) {
           pp[h][i >> 1] = pack2bf(pv_t, pv);
@@ -607,6 +620,8 @@ void bwd_q_kernel(BwdParams p) {
   Tile<D, NT> tk;
   RowTile<D, NT> tv;
   float rpv = 0.f;
+  constexpr int NDB = BIAS == B_DENSE ? BM * STEP / NT / 2 : 1;
+  uint32_t dbr[NDB];                // dense bias pairs (one query, two keys) of the next step
 
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_BQ], &s_ticket);
@@ -668,6 +683,19 @@ void bwd_q_kernel(BwdParams p) {
       }
       tk.load(rk, row_bytes, j0);
       tv.load(rv, row_bytes, j0);
+      if constexpr (BIAS == B_DENSE) {
+        // [BM][STEP] block, two adjacent keys per pair, coalesced along rows
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
+          const int e = 2 * (tid + i * NT);
+          const int qq = q0 + e / STEP, jj = j0 + e % STEP;
+          const bool ok = qq < n;
+          const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
+          const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
+          const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
+          dbr[i] = lo | (hi << 16);
+        }
+      }
     };
     auto store_step = [&](int st, int kt) {
       unsigned char* base = lds + st * L::STAGE;
@@ -679,17 +707,10 @@ void bwd_q_kernel(BwdParams p) {
           store_diag<L::RP>(reinterpret_cast<float*>(base + L::BO), tid, rpv * inv_scale);
       } else if constexpr (BIAS == B_DENSE) {
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
-        constexpr int NB = BM * STEP / NT / 2;
-#pragma unroll 4
-        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
           const int e = 2 * (tid + i * NT);
-          const int r = e / STEP, c = e % STEP;
-          const int qq = q0 + r, jj = j0 + c;
-          const bool ok = qq < n;
-          const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
-          const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
-          const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
-          *(uint32_t*)(bt + r * L::BS + c) = lo | (hi << 16);
+          *(uint32_t*)(bt + (e / STEP) * L::BS + e % STEP) = dbr[i];
         }
       }
     };
@@ -764,7 +785,9 @@ void bwd_q_kernel(BwdParams p) {
               const float pr = valid ? fast_exp2(x - lse2) : 0.f;
               d2[e] = pr * (pacc[blk][ii] - dlt);
             } else {
-              d2[e] = valid ? act_grad_f<MODE>(x) * pacc[blk][ii] * wn : 0.f;
+              float a, da;
+              act_pair<MODE>(x, a, da);
+              d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
             }
           }
           dd[blk][i >> 1] = pack2bf(d2[0], d2[1]);

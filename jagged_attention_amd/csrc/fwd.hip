@@ -97,6 +97,11 @@ void fwd_kernel(FwdParams p) {
   u32x2 v8[FP8 ? V_LOADS : 1][4];
   uint32_t vsc[FP8 ? V_LOADS : 1][4];
   float rp_val = 0.f;                                        // relpos table entry of this thread
+  // Dense bias: NDB pairs per thread and step; the first NPRE are prefetched into registers
+  // with the K/V tiles (the rest, where registers run short, load while staging).
+  constexpr int NDB = BIAS == B_DENSE ? BM * BN / NT / 2 : 1;
+  constexpr int NPRE = (D == 128 && NW == 4) ? 0 : NDB;
+  uint32_t dbr[NPRE > 0 ? NPRE : 1];
 
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_FWD], &s_ticket);
@@ -169,8 +174,22 @@ void fwd_kernel(FwdParams p) {
     float m_run = NEG_INF, l_run = 0.f;
 
     // ---- staging: global -> registers for key step kt
+    // [BM][BN] block of the dense bias, two adjacent keys per pair, coalesced along rows
+    auto dense_pair = [&](int i, int j0) -> uint32_t {
+      const int e = 2 * (tid + i * NT);
+      const int qq = q0 + e / BN, jj = j0 + e % BN;
+      const bool ok = qq < n;
+      const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
+      const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
+      const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
+      return lo | (hi << 16);
+    };
     auto load_step = [&](int kt) {
       const int j0 = kt * BN;
+      if constexpr (BIAS == B_DENSE) {
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_pair(i, j0);
+      }
       if constexpr (BIAS == B_RELPOS) {
         // diagonal table: T[x] = bias(dist = q0 + delta - j0 + BM - 1 - x), issued first so
         // that waiting for it never waits for the tile loads behind it
@@ -213,8 +232,7 @@ void fwd_kernel(FwdParams p) {
       }
     };
 
-    // ---- staging: registers -> LDS stage `st` (the dense bias goes global -> LDS here,
-    //      so no registers are held for it across the MFMAs)
+    // ---- staging: registers -> LDS stage `st`
     auto store_step = [&](int st, int kt) {
       unsigned char* base = lds + st * L::STAGE;
 #pragma unroll
@@ -275,30 +293,11 @@ void fwd_kernel(FwdParams p) {
           for (int k = 0; k < 4; ++k) rp[k * L::RP + tid + k] = v;
         }
       } else if constexpr (BIAS == B_DENSE) {
-        // [BM][BN] block, two adjacent columns per thread, coalesced along rows
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::B_OFF);
-        const int j0 = kt * BN;
-        constexpr int NB = BM * BN / NT / 2, CH = 4;
 #pragma unroll
-        for (int i0 = 0; i0 < NB; i0 += CH) {
-          uint32_t dv[CH];
-#pragma unroll
-          for (int i = 0; i < CH; ++i) {
-            const int e = 2 * (tid + (i0 + i) * NT);
-            const int r = e / BN, c = e % BN;
-            const int qq = q0 + r, jj = j0 + c;
-            const bool ok = qq < n;
-            const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
-            const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
-            const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
-            dv[i] = lo | (hi << 16);
-          }
-#pragma unroll
-          for (int i = 0; i < CH; ++i) {
-            const int e = 2 * (tid + (i0 + i) * NT);
-            const int r = e / BN, c = e % BN;
-            *(uint32_t*)(bt + r * L::BS + c) = dv[i];
-          }
+        for (int i = 0; i < NDB; ++i) {
+          const int e = 2 * (tid + i * NT);
+          *(uint32_t*)(bt + (e / BN) * L::BS + e % BN) = i < NPRE ? dbr[i] : dense_pair(i, kt * BN);
         }
       }
     };
@@ -428,8 +427,8 @@ void fwd_kernel(FwdParams p) {
             for (int i = 0; i < 16; i += 2) {
               // masked scores are -inf: act(-inf) is NaN for SiLU/GELU, so select zero
               const float x0 = sacc[blk][i], x1 = sacc[blk][i + 1];
-              const float a0 = x0 == NEG_INF ? 0.f : act_f<MODE>(x0 * c_log);
-              const float a1 = x1 == NEG_INF ? 0.f : act_f<MODE>(x1 * c_log);
+              const float a0 = x0 == NEG_INF ? 0.f : act_fast<MODE>(x0 * c_log);
+              const float a1 = x1 == NEG_INF ? 0.f : act_fast<MODE>(x1 * c_log);
               pk[blk][i >> 1] = pack2bf(a0, a1);
             }
         }

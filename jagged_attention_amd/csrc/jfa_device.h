@@ -95,6 +95,44 @@ __device__ __forceinline__ float act_grad_f(float x) {
   return cdf + x * pdf;
 }
 
+// Branch-free activations for the bf16 / MXFP8 kernels (errors far below bf16 rounding).
+// GELU: Phi(x) from the erfc approximation of Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error of erf| <= 1.5e-7): with z = |x|/sqrt 2, t = 1/(1 + p z),
+// erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2).  exp(-z^2) = exp(-x^2/2) is
+// also the Gaussian density factor of the derivative, so value and derivative share one exp
+// and one reciprocal.  Returns Phi(x) and writes exp(-x^2/2) to e.
+__device__ __forceinline__ float gelu_cdf(float x, float& e) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = fast_rcp(fmaf(0.3275911f, z, 1.0f));
+  e = fast_exp2(-z * z * 1.4426950408889634f);
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float half_erfc = 0.5f * t * poly * e;            // (1 - erf(z)) / 2
+  return x >= 0.f ? 1.0f - half_erfc : half_erfc;
+}
+template <int MODE>
+__device__ __forceinline__ float act_fast(float x) {
+  if (MODE == MODE_SILU) return x * fast_rcp(1.0f + fast_exp2(-x * 1.4426950408889634f));
+  float e;
+  return x * gelu_cdf(x, e);
+}
+// Activation and its derivative at x.
+template <int MODE>
+__device__ __forceinline__ void act_pair(float x, float& a, float& da) {
+  if (MODE == MODE_SILU) {
+    const float sg = fast_rcp(1.0f + fast_exp2(-x * 1.4426950408889634f));
+    a = x * sg;
+    da = sg * (1.0f + x * (1.0f - sg));
+  } else {
+    float e;
+    const float cdf = gelu_cdf(x, e);
+    a = x * cdf;
+    da = fmaf(x * 0.39894228040143268f, e, cdf);
+  }
+}
+
 // E4M3 code (sign, 4-bit exponent bias 7, 3-bit mantissa, subnormals) to float.
 __device__ __forceinline__ float e4m3_to_f(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, f = c & 7u;
@@ -124,8 +162,15 @@ constexpr int diag_stride(int len) { return (len - 16 + 63) / 64 * 64 + 16; }
 // A buffer resource covers [base, base + bytes): loads at or past `bytes` return zeros and
 // stores there are dropped, so ragged rows need no branches.  Offsets are 32-bit bytes.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Every resource here describes one (sample, head) slice, so base and size are uniform over the
+// workgroup; readfirstlane states that to the compiler, which otherwise may keep a resource
+// it cannot prove uniform in vector registers and wrap each load in a waterfall loop.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
                                            0x00020000);
 }
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
