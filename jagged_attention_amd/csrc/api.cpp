@@ -121,11 +121,10 @@ Layout layout_of(const jfa_problem& p, const TileCfg& tc, int backward) {
   L.gen_slot = take(4 * L.cap_t);
   L.words_a = take(4 * L.cap_t);
   L.words_b = take(4 * L.cap_t);
-  L.fwd = take(16 * L.cap_f);
-  L.fwd_slot = take(4 * L.cap_f);
+  L.fwd = take(sizeof(ItemRec) * L.cap_f);
   L.comb = take(16 * L.cap_c);
-  L.bq = take(16 * L.cap_q);
-  L.bk = take(16 * L.cap_k);
+  L.bq = take(sizeof(ItemRec) * L.cap_q);
+  L.bk = take(sizeof(ItemRec) * L.cap_k);
   if (!backward && L.cap_slots > 0) {
     L.part_acc = take(4 * (size_t)L.cap_slots * H * tc.bm * d);
     L.part_ml = take(4 * 2 * (size_t)L.cap_slots * H * tc.bm);
@@ -159,11 +158,14 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.gen_slot = (int32_t*)(ws + L.gen_slot);
   a.words_a = (uint32_t*)(ws + L.words_a);
   a.words_b = (uint32_t*)(ws + L.words_b);
-  a.fwd = (int4*)(ws + L.fwd);
-  a.fwd_slot = (int32_t*)(ws + L.fwd_slot);
+  a.fwd = nullptr;
+  a.fwd_slot = nullptr;
   a.comb = (int4*)(ws + L.comb);
-  a.bq = (int4*)(ws + L.bq);
-  a.bk = (int4*)(ws + L.bk);
+  a.bq = nullptr;
+  a.bk = nullptr;
+  a.fwd_items = (ItemRec*)(ws + L.fwd);
+  a.bq_items = (ItemRec*)(ws + L.bq);
+  a.bk_items = (ItemRec*)(ws + L.bk);
   a.cap_f = L.cap_f;
   a.cap_c = L.cap_c;
   a.cap_q = L.cap_q;
@@ -302,8 +304,7 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   fp.o = o; fp.lse = lse;
   fp.hdr_ro = (const WsHeader*)(ws + L.header);
   fp.hdr = (WsHeader*)(ws + L.header);
-  fp.recs = (const int4*)(ws + L.fwd);
-  fp.rec_slot = (const int32_t*)(ws + L.fwd_slot);
+  fp.items = (const ItemRec*)(ws + L.fwd);
   fp.comb = (const int4*)(ws + L.comb);
   fp.part_acc = L.cap_slots > 0 ? (float*)(ws + L.part_acc) : nullptr;
   fp.part_ml = L.cap_slots > 0 ? (float*)(ws + L.part_ml) : nullptr;
@@ -359,8 +360,8 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.delta = p->mode == JFA_MODE_SOFTMAX ? (float*)(ws + L.delta) : nullptr;
   bp.hdr = (WsHeader*)(ws + L.header);
-  bp.bq = (const int4*)(ws + L.bq);
-  bp.bk = (const int4*)(ws + L.bk);
+  bp.bq = (const ItemRec*)(ws + L.bq);
+  bp.bk = (const ItemRec*)(ws + L.bk);
   bp.H = p->heads;
   bp.causal = p->causal;
   bp.bias_kind = p->bias_kind;
@@ -399,6 +400,7 @@ jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
   a.comb = (int4*)comb;
   a.bq = (int4*)bwd_q;
   a.bk = (int4*)bwd_kv;
+  a.fwd_items = a.bq_items = a.bk_items = nullptr;
   a.cap_f = std::min<int64_t>(capacity, L.cap_f);
   a.cap_c = std::min<int64_t>(capacity, L.cap_c);
   a.cap_q = std::min<int64_t>(capacity, L.cap_q);

@@ -241,7 +241,7 @@ void bwd_kv_kernel(BwdParams p) {
   using L = KvLds<D, NW, BIAS>;
   constexpr int BNK = L::BNK, NT = NW * 64, RS = L::RS;
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int s_ticket;
+  __shared__ int s_desc[2][IF_WORDS];
 
   if (p.hdr->status != JFA_OK) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -255,20 +255,27 @@ void bwd_kv_kernel(BwdParams p) {
   Tile<D, NT> tq, tdo;
   float lsv = 0.f, dlv = 0.f;       // lse / delta entry staged by threads < STEP
   float rpv = 0.f;                  // relpos table entry
-  // Dense bias pairs (two queries, one key) per thread and step; the first NPRE are prefetched
-  // into registers with the Q/dO tiles, the rest (where registers run short) load while staging.
-  constexpr int NDB = BIAS == B_DENSE ? BNK * STEP / 2 / NT : 1;
+  // Dense bias: NDB units per thread and step, each two 16-byte chunks (8 keys of queries q and
+  // q + 1) that are stored transposed as (q, q + 1) pairs per key; prefetched into registers
+  // with the Q / dO tiles unless registers run short (then loaded while staging).
+  constexpr int KCHK = BNK / 8;
+  constexpr int NDB = BIAS == B_DENSE ? (STEP / 2) * KCHK / NT : 1;
   constexpr int NPRE = D == 128 ? 0 : NDB;
-  uint32_t dbr[NPRE > 0 ? NPRE : 1];
+  u32x4 dbr[NPRE > 0 ? NPRE : 1][2];
 
-  for (;;) {
-    const int64_t w = next_ticket(&p.hdr->tickets[TK_BK], &s_ticket);
+  ItemPipe pipe{&p.hdr->tickets[TK_BK], p.bk, n_items, H};
+  if (wave == 0) pipe.start(s_desc[0], lane);
+  __syncthreads();
+  for (int buf = 0;; buf ^= 1) {
+    const int* dsc = s_desc[buf];
+    const int w = item_field(dsc, IF_W);
     if (w >= n_items) break;
-    const int4 rec = p.bk[w / H];
-    const int h = (int)(w % H);
-    const int b = rec.x, u = rec.y, qs_first = rec.z, qs_end = rec.w;
-    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
-    const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
+    const int h = w % H;
+    const int u = item_field(dsc, IF_X), qs_first = item_field(dsc, IF_Y);
+    const int qs_end = item_field(dsc, IF_Z);
+    const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
+    const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
+    const int64_t boff = item_boff(dsc);
     const int delta = m - n;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int j0 = u * BNK, jw0 = j0 + wave * 32;
@@ -286,7 +293,7 @@ void bwd_kv_kernel(BwdParams p) {
       rdl = make_rsrc(p.delta + (int64_t)h * p.total_q + qo, (uint32_t)n * 4u);
     }
     if constexpr (BIAS == B_DENSE)
-      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * boff + (int64_t)h * n * m,
                      (uint32_t)n * (uint32_t)m * 2u);
 
     // this lane's key as the B operand (column = key, k = head dim)
@@ -296,7 +303,6 @@ void bwd_kv_kernel(BwdParams p) {
       kf[ks] = as_bf16x8(ld16(rk, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
       vf[ks] = as_bf16x8(ld16(rv, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): fragments complete before the loop
 
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -304,14 +310,12 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
 
-    auto dense_pair = [&](int i, int q0) -> uint32_t {
-      const int e = tid + i * NT;
-      const int qa = q0 + 2 * (e / BNK), ja = j0 + e % BNK;
-      const bool okj = ja < m;
-      const uint32_t off = ((uint32_t)qa * (uint32_t)m + (uint32_t)ja) * 2u;
-      const uint32_t lo = (okj && qa < n) ? ld2(rb, off) : 0u;
-      const uint32_t hi = (okj && qa + 1 < n) ? ld2(rb, off + 2u * (uint32_t)m) : 0u;
-      return lo | (hi << 16);
+    auto dense_chunk = [&](int i, int q0, int half) -> u32x4 {
+      const int id = tid + i * NT;
+      const int qa = q0 + 2 * (id / KCHK) + half, k0 = j0 + 8 * (id % KCHK);
+      const int valid = qa < n ? min(8, m - k0) : 0;
+      return bias_chunk(rb, ((uint32_t)qa * (uint32_t)m + (uint32_t)k0) * 2u, valid,
+                        (uint32_t)n * (uint32_t)m * 2u);
     };
     auto load_step = [&](int qs) {
       const int q0 = qs * STEP;
@@ -333,7 +337,10 @@ void bwd_kv_kernel(BwdParams p) {
       tdo.load(rdo, row_bytes, q0);
       if constexpr (BIAS == B_DENSE) {
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_pair(i, q0);
+        for (int i = 0; i < NPRE; ++i) {
+          dbr[i][0] = dense_chunk(i, q0, 0);
+          dbr[i][1] = dense_chunk(i, q0, 1);
+        }
       }
     };
     // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
@@ -368,9 +375,15 @@ void bwd_kv_kernel(BwdParams p) {
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
-          const int e = tid + i * NT;
-          *(uint32_t*)(bt + (e % BNK) * L::BS + 2 * (e / BNK)) =
-              i < NPRE ? dbr[i] : dense_pair(i, qs * STEP);
+          const int id = tid + i * NT;
+          const u32x4 a = i < NPRE ? dbr[i][0] : dense_chunk(i, qs * STEP, 0);
+          const u32x4 c = i < NPRE ? dbr[i][1] : dense_chunk(i, qs * STEP, 1);
+          __bf16* dst = bt + 8 * (id % KCHK) * L::BS + 2 * (id / KCHK);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            *(uint32_t*)(dst + (2 * w) * L::BS) = lo_halves(a[w], c[w]);
+            *(uint32_t*)(dst + (2 * w + 1) * L::BS) = hi_halves(a[w], c[w]);
+          }
         }
       }
     };
@@ -555,14 +568,21 @@ void bwd_kv_kernel(BwdParams p) {
       load_step(qs_first);
       store_step(0, qs_first, true);
     }
+    // the key fragments (loaded with the first tiles) are complete before the query loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
+    const int claim_it = max(0, nsteps - CLAIM_AHEAD);
     for (int it = 0; it + 1 < nsteps; ++it) {
+      if (it == claim_it && wave == 0) pipe.fetch(lane);
       load_step(qs_first + it + 1);
       compute_step(it, qs_first + it, -1);
       store_step((it + 1) & 1, qs_first + it + 1, true);
       __syncthreads();
     }
+    if (claim_it >= nsteps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1, -1);
+    // publish the next descriptor before the epilogue's stores (see the forward kernel)
+    if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     // epilogue: this lane's key row of dK (x scale) and dV; keys past the sample are dropped
     const rsrc_t rdk = make_rsrc((__bf16*)p.dk + ((int64_t)ko * H + h) * D, kv_bytes);
@@ -580,6 +600,7 @@ void bwd_kv_kernel(BwdParams p) {
         st8(k2, rdk, off);
         st8(v2, rdv, off);
       }
+    __syncthreads();
   }
 }
 
@@ -606,7 +627,7 @@ void bwd_q_kernel(BwdParams p) {
   using L = QLds<D, NW, BIAS>;
   constexpr int BM = L::BM, NT = NW * 64, RS = L::RS;
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int s_ticket;
+  __shared__ int s_desc[2][IF_WORDS];
 
   if (p.hdr->status != JFA_OK) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -620,17 +641,21 @@ void bwd_q_kernel(BwdParams p) {
   Tile<D, NT> tk;
   RowTile<D, NT> tv;
   float rpv = 0.f;
-  constexpr int NDB = BIAS == B_DENSE ? BM * STEP / NT / 2 : 1;
-  uint32_t dbr[NDB];                // dense bias pairs (one query, two keys) of the next step
+  constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
+  u32x4 dbr[NDB];                   // dense bias chunks (8 keys of one query) of the next step
 
-  for (;;) {
-    const int64_t w = next_ticket(&p.hdr->tickets[TK_BQ], &s_ticket);
+  ItemPipe pipe{&p.hdr->tickets[TK_BQ], p.bq, n_items, H};
+  if (wave == 0) pipe.start(s_desc[0], lane);
+  __syncthreads();
+  for (int buf = 0;; buf ^= 1) {
+    const int* dsc = s_desc[buf];
+    const int w = item_field(dsc, IF_W);
     if (w >= n_items) break;
-    const int4 rec = p.bq[w / H];
-    const int h = (int)(w % H);
-    const int b = rec.x, t = rec.y, steps = rec.w;
-    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
-    const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
+    const int h = w % H;
+    const int t = item_field(dsc, IF_X), steps = item_field(dsc, IF_Z);
+    const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
+    const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
+    const int64_t boff = item_boff(dsc);
     const int delta = m - n;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int q0 = t * BM, qw0 = q0 + wave * 32;
@@ -647,7 +672,7 @@ void bwd_q_kernel(BwdParams p) {
     const rsrc_t rdo = make_rsrc((const __bf16*)p.dout + ((int64_t)qo * H + h) * D, q_bytes);
     rsrc_t rb = rq;
     if constexpr (BIAS == B_DENSE)
-      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * boff + (int64_t)h * n * m,
                      (uint32_t)n * (uint32_t)m * 2u);
 
     bf16x8 qf[D / 16], dof[D / 16];
@@ -664,7 +689,6 @@ void bwd_q_kernel(BwdParams p) {
         dlt = p.delta[(int64_t)h * p.total_q + qo + qi];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -684,16 +708,14 @@ void bwd_q_kernel(BwdParams p) {
       tk.load(rk, row_bytes, j0);
       tv.load(rv, row_bytes, j0);
       if constexpr (BIAS == B_DENSE) {
-        // [BM][STEP] block, two adjacent keys per pair, coalesced along rows
+        // [BM][STEP] block as chunks of 8 keys, consecutive lanes along a row
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
-          const int e = 2 * (tid + i * NT);
-          const int qq = q0 + e / STEP, jj = j0 + e % STEP;
-          const bool ok = qq < n;
-          const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
-          const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
-          const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
-          dbr[i] = lo | (hi << 16);
+          const int id = tid + i * NT;
+          const int qq = q0 + id / (STEP / 8), k0 = j0 + 8 * (id % (STEP / 8));
+          const int valid = qq < n ? min(8, m - k0) : 0;
+          dbr[i] = bias_chunk(rb, ((uint32_t)qq * (uint32_t)m + (uint32_t)k0) * 2u, valid,
+                        (uint32_t)n * (uint32_t)m * 2u);
         }
       }
     };
@@ -709,8 +731,8 @@ void bwd_q_kernel(BwdParams p) {
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
-          const int e = 2 * (tid + i * NT);
-          *(uint32_t*)(bt + (e / STEP) * L::BS + e % STEP) = dbr[i];
+          const int id = tid + i * NT;
+          *(u32x4*)(bt + (id / (STEP / 8)) * L::BS + 8 * (id % (STEP / 8))) = dbr[i];
         }
       }
     };
@@ -811,14 +833,21 @@ void bwd_q_kernel(BwdParams p) {
       load_step(0);
       store_step(0, 0);
     }
+    // the query fragments (loaded with the first tiles) are complete before the key loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
+    const int claim_it = max(0, steps - CLAIM_AHEAD);
     for (int it = 0; it + 1 < steps; ++it) {
+      if (it == claim_it && wave == 0) pipe.fetch(lane);
       load_step(it + 1);
       compute_step(it);
       store_step((it + 1) & 1, it + 1);
       __syncthreads();
     }
+    if (claim_it >= steps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (steps > 0) compute_step(steps - 1);
+    // publish the next descriptor before the epilogue's stores (see the forward kernel)
+    if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
 #pragma unroll
@@ -829,6 +858,7 @@ void bwd_q_kernel(BwdParams p) {
                           pack2bf(acc[db][4 * jq + 2] * p.scale, acc[db][4 * jq + 3] * p.scale)};
         st8(q2, rdq, qoff + 2 * (db * 32 + 8 * jq + 4 * g));
       }
+    __syncthreads();
   }
 }
 

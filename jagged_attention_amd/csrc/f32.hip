@@ -35,7 +35,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_FWD], &s_ticket);
     if (w >= n_items) break;
-    const int4 rec = p.recs[w / H];
+    const ItemRec& it = p.items[w / H];
+    const int4 rec = make_int4(it.b, it.x, it.y, it.z);
     const int h = (int)(w % H);
     const int b = rec.x, t = rec.y, kb = rec.z, ke = rec.w;
     const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
@@ -132,7 +133,8 @@ __global__ __launch_bounds__(NT) void bwd_q_f32_kernel(BwdParams p) {
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_BQ], &s_ticket);
     if (w >= n_items) break;
-    const int4 rec = p.bq[w / H];
+    const ItemRec& it = p.bq[w / H];
+    const int4 rec = make_int4(it.b, it.x, it.y, it.z);
     const int h = (int)(w % H);
     const int b = rec.x, t = rec.y, steps = rec.w;
     const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(NT) void bwd_kv_f32_kernel(BwdParams p) {
   for (;;) {
     const int64_t w = next_ticket(&p.hdr->tickets[TK_BK], &s_ticket);
     if (w >= n_items) break;
-    const int4 rec = p.bk[w / H];
+    const ItemRec& it = p.bk[w / H];
+    const int4 rec = make_int4(it.b, it.x, it.y, it.z);
     const int h = (int)(w % H);
     const int b = rec.x, u = rec.y, qs0 = rec.z, qs1 = rec.w;
     const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;

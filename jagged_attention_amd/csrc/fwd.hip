@@ -71,7 +71,7 @@ void fwd_kernel(FwdParams p) {
   constexpr int BM = L::BM, NT = NW * 64, VS = L::VS;
   constexpr int ES = FP8 ? 1 : 2;                  // bytes per Q/K/V element
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int s_ticket;
+  __shared__ int s_desc[2][IF_WORDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -97,22 +97,24 @@ void fwd_kernel(FwdParams p) {
   u32x2 v8[FP8 ? V_LOADS : 1][4];
   uint32_t vsc[FP8 ? V_LOADS : 1][4];
   float rp_val = 0.f;                                        // relpos table entry of this thread
-  // Dense bias: NDB pairs per thread and step; the first NPRE are prefetched into registers
-  // with the K/V tiles (the rest, where registers run short, load while staging).
-  constexpr int NDB = BIAS == B_DENSE ? BM * BN / NT / 2 : 1;
+  // Dense bias: NDB 16-byte chunks (8 keys of one query row) per thread and step, prefetched
+  // into registers with the K/V tiles unless registers run short (then loaded while staging).
+  constexpr int NDB = BIAS == B_DENSE ? BM * (BN / 8) / NT : 1;
   constexpr int NPRE = (D == 128 && NW == 4) ? 0 : NDB;
-  uint32_t dbr[NPRE > 0 ? NPRE : 1];
+  u32x4 dbr[NPRE > 0 ? NPRE : 1];
 
-  for (;;) {
-    const int64_t w = next_ticket(&p.hdr->tickets[TK_FWD], &s_ticket);
+  ItemPipe pipe{&p.hdr->tickets[TK_FWD], p.items, n_items, H};
+  if (wave == 0) pipe.start(s_desc[0], lane);
+  __syncthreads();
+  for (int buf = 0;; buf ^= 1) {
+    const int* dsc = s_desc[buf];
+    const int w = item_field(dsc, IF_W);
     if (w >= n_items) break;
-    const int ri = (int)(w / H);
-    const int h = (int)(w % H);
-    const int4 rec = p.recs[ri];
-    const int slot = p.rec_slot[ri];
-    const int b = rec.x, t = rec.y, kb = rec.z, ke = rec.w;
-    const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
-    const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
+    const int h = w % H;
+    const int t = item_field(dsc, IF_X), kb = item_field(dsc, IF_Y), ke = item_field(dsc, IF_Z);
+    const int slot = item_field(dsc, IF_SLOT);
+    const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
+    const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
     const int delta = m - n;
     const int q0 = t * BM;
     const int qw0 = q0 + wave * 32;
@@ -138,7 +140,7 @@ void fwd_kernel(FwdParams p) {
     }
     rsrc_t rb = rk;
     if constexpr (BIAS == B_DENSE)
-      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * p.bias_off[b] + (int64_t)h * n * m,
+      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * item_boff(dsc) + (int64_t)h * n * m,
                      (uint32_t)n * (uint32_t)m * 2u);
 
     // ---- query fragment: B operand (column = query row, k = head dim)
@@ -162,8 +164,6 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(rq, qoff + 32 * ks + 16 * g));
       }
-      // the fragment is complete before the key loop: no wait on it inside the loop
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
 
     f32x16 acc[D / 32];
@@ -174,21 +174,19 @@ void fwd_kernel(FwdParams p) {
     float m_run = NEG_INF, l_run = 0.f;
 
     // ---- staging: global -> registers for key step kt
-    // [BM][BN] block of the dense bias, two adjacent keys per pair, coalesced along rows
-    auto dense_pair = [&](int i, int j0) -> uint32_t {
-      const int e = 2 * (tid + i * NT);
-      const int qq = q0 + e / BN, jj = j0 + e % BN;
-      const bool ok = qq < n;
-      const uint32_t off = ((uint32_t)qq * (uint32_t)m + (uint32_t)jj) * 2u;
-      const uint32_t lo = (ok && jj < m) ? ld2(rb, off) : 0u;
-      const uint32_t hi = (ok && jj + 1 < m) ? ld2(rb, off + 2) : 0u;
-      return lo | (hi << 16);
+    // [BM][BN] block of the dense bias as chunks of 8 keys, consecutive lanes along a row
+    auto dense_chunk = [&](int i, int j0) -> u32x4 {
+      const int id = tid + i * NT;
+      const int qq = q0 + id / (BN / 8), k0 = j0 + 8 * (id % (BN / 8));
+      const int valid = qq < n ? min(8, m - k0) : 0;
+      return bias_chunk(rb, ((uint32_t)qq * (uint32_t)m + (uint32_t)k0) * 2u, valid,
+                        (uint32_t)n * (uint32_t)m * 2u);
     };
     auto load_step = [&](int kt) {
       const int j0 = kt * BN;
       if constexpr (BIAS == B_DENSE) {
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_pair(i, j0);
+        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_chunk(i, j0);
       }
       if constexpr (BIAS == B_RELPOS) {
         // diagonal table: T[x] = bias(dist = q0 + delta - j0 + BM - 1 - x), issued first so
@@ -296,8 +294,9 @@ void fwd_kernel(FwdParams p) {
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::B_OFF);
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
-          const int e = 2 * (tid + i * NT);
-          *(uint32_t*)(bt + (e / BN) * L::BS + e % BN) = i < NPRE ? dbr[i] : dense_pair(i, kt * BN);
+          const int id = tid + i * NT;
+          *(u32x4*)(bt + (id / (BN / 8)) * L::BS + 8 * (id % (BN / 8))) =
+              i < NPRE ? dbr[i] : dense_chunk(i, kt * BN);
         }
       }
     };
@@ -307,6 +306,8 @@ void fwd_kernel(FwdParams p) {
       load_step(kb);
       store_step(0, kb);
     }
+    // the query fragment (loaded with the first tiles) is complete before the key loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     // one key step on LDS stage it&1 (the loop is peeled so that its loads and stores are
     // unconditional: no load can be pending across the back edge)
@@ -448,13 +449,19 @@ void fwd_kernel(FwdParams p) {
         }
       }
     };
+    const int claim_it = max(0, nsteps - CLAIM_AHEAD);
     for (int it = 0; it + 1 < nsteps; ++it) {
+      if (it == claim_it && wave == 0) pipe.fetch(lane);
       load_step(kb + it + 1);
       compute_step(it);
       store_step((it + 1) & 1, kb + it + 1);
       __syncthreads();
     }
+    if (claim_it >= nsteps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (nsteps > 0) compute_step(nsteps - 1);
+    // publish the next descriptor before the epilogue's stores: waiting for the claimed ticket
+    // after them would also wait for the stores to complete
+    if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     // ---- epilogue
     float l_tot = l_run;
@@ -492,6 +499,7 @@ void fwd_kernel(FwdParams p) {
         p.part_ml[2 * pbase + 1] = l_tot;
       }
     }
+    __syncthreads();
   }
 }
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "jfa_internal.h"
+
 namespace jfa {
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E), every index a constant
@@ -206,6 +208,42 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
 
+// Eight consecutive bf16 of a dense-bias row from byte offset `off` (2-byte aligned) of a buffer
+// of `size` bytes, elements at or past `valid` (0..8) set to zero.  Dword-aligned loads of the
+// five dwords that cover the chunk, shifted by one element when `off` is not dword-aligned:
+// sub-dword loads of the same bytes cost several times more.  The range check drops a dword
+// that only partly lies in the buffer, so a final element in such a dword is loaded alone.
+__device__ __forceinline__ u32x4 bias_chunk(rsrc_t r, uint32_t off, int valid, uint32_t size) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (valid > 0) {
+    const uint32_t base = off & ~3u;
+    const u32x4 x = ld16(r, base);
+    const uint32_t y = ld4(r, base + 16);
+    if (off & 2u) {
+      v[0] = __builtin_amdgcn_alignbyte(x[1], x[0], 2);
+      v[1] = __builtin_amdgcn_alignbyte(x[2], x[1], 2);
+      v[2] = __builtin_amdgcn_alignbyte(x[3], x[2], 2);
+      v[3] = __builtin_amdgcn_alignbyte(y, x[3], 2);
+    } else {
+      v = x;
+    }
+    const uint32_t last = off + 2u * (uint32_t)(valid - 1);
+    if ((size & 2u) && last + 2u == size) {
+      const int e = valid - 1;
+      const uint32_t sh = 16u * (uint32_t)(e & 1);
+      v[e >> 1] = (v[e >> 1] & ~(0xFFFFu << sh)) | (ld2(r, last) << sh);
+    }
+  }
+  if (valid < 8) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t keep = 2 * w + 1 < valid ? 0xFFFFFFFFu : (2 * w < valid ? 0xFFFFu : 0u);
+      v[w] &= keep;
+    }
+  }
+  return v;
+}
+
 // Sum of the two bf16 halves of `w` added to `acc` (fp32).
 __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -214,6 +252,57 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
 }
 
 // Workgroup-wide work ticket: thread 0 takes the next item, everyone gets it.
+// Work-item pipeline of a persistent workgroup.  Wave 0 claims tickets one item ahead and, while
+// the workgroup works on the current item, loads the next item's 64-byte work record (one dword
+// per lane) and claims the ticket after it; starting an item then costs no memory round trip.
+// Descriptors - the record's 16 dwords and the ticket - reach the other waves through two LDS
+// buffers, published at the end of each item before the barrier that separates items.
+enum ItemField {
+  IF_B = 0, IF_X = 1, IF_Y = 2, IF_Z = 3, IF_SLOT = 4, IF_QO = 5, IF_N = 6, IF_KO = 7, IF_M = 8,
+  IF_BOFF = 10, IF_W = 16, IF_WORDS = 17
+};
+// Steps before an item's end at which its workgroup claims the next ticket: a device-scope
+// atomic takes several microseconds to return, about as long as a few steps of work, while
+// claiming much earlier would let workgroups hold work that idle ones could take.
+constexpr int CLAIM_AHEAD = 4;
+
+struct ItemPipe {
+  uint32_t* ctr;
+  const ItemRec* items;
+  int64_t n_items;
+  int H;
+  int tk = 0;                // ticket of the next item (wave 0, uniform)
+  int v = 0;                 // lane L < IF_WORDS: dword L of the next item's descriptor
+  uint32_t t = 0;            // lane 0: the ticket claimed after tk
+
+  // Items 0 .. gridDim.x - 1 go to the workgroups in order; later tickets come from the counter
+  // (offset by the grid), so that the launch does not start with every workgroup contending
+  // for one atomic.
+  __device__ __forceinline__ void fetch(int lane) {
+    if (lane == IF_W) v = tk;
+    else if (lane < IF_W && tk < n_items) v = reinterpret_cast<const int*>(items + tk / H)[lane];
+    if (lane == 0) t = atomicAdd(ctr, 1u) + gridDim.x;
+  }
+  __device__ __forceinline__ void publish(int* dst, int lane) {
+    if (lane < IF_WORDS) dst[lane] = v;
+    tk = __builtin_amdgcn_readfirstlane(t);
+  }
+  // first descriptor into dst (wave 0; the caller then synchronises the workgroup)
+  __device__ __forceinline__ void start(int* dst, int lane) {
+    tk = blockIdx.x;
+    fetch(lane);
+    publish(dst, lane);
+  }
+};
+
+// Item fields read back from LDS, made wave-uniform.
+__device__ __forceinline__ int item_field(const int* d, int f) {
+  return __builtin_amdgcn_readfirstlane(d[f]);
+}
+__device__ __forceinline__ int64_t item_boff(const int* d) {
+  return ((int64_t)item_field(d, IF_BOFF + 1) << 32) | (uint32_t)item_field(d, IF_BOFF);
+}
+
 __device__ __forceinline__ int64_t next_ticket(uint32_t* counter, int* slot) {
   if (threadIdx.x == 0) *slot = (int)atomicAdd(counter, 1u);
   __syncthreads();

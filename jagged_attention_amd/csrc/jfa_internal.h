@@ -47,11 +47,23 @@ struct TileCfg {
 // Byte layout of the workspace for one problem.
 struct Layout {
   size_t header, bias_off, s_tmp, t_tmp, gen_recs, gen_slot, words_a, words_b;
-  size_t fwd, fwd_slot, comb, bq, bk;
+  size_t fwd, comb, bq, bk;
   size_t part_acc, part_ml, delta;
   size_t total;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
 };
+
+// Work record of the persistent kernels (64 bytes): a list record together with everything a
+// kernel needs to start the item, so that one load describes it.
+struct ItemRec {
+  int32_t b, x, y, z;      // the list record: sample, tile, range (see jfa_build_schedule)
+  int32_t slot;            // forward split slot (-1: not split)
+  int32_t qo, n, ko, m;    // the sample's first q / kv row and its lengths
+  int32_t pad0;
+  int64_t boff;            // element offset of the sample's dense-bias block over all heads
+  int32_t pad1[4];
+};
+static_assert(sizeof(ItemRec) == 64, "item record size");
 
 // ------------------------------------------------------- scheduler args
 struct SchedArgs {
@@ -72,11 +84,14 @@ struct SchedArgs {
   int32_t* gen_slot;
   uint32_t* words_a;   // sort buffers (global fallback)
   uint32_t* words_b;
-  int4* fwd;
+  int4* fwd;            // list records (test hook; may be null)
   int32_t* fwd_slot;
   int4* comb;
   int4* bq;
   int4* bk;
+  ItemRec* fwd_items;   // the same lists as kernel work records (may be null)
+  ItemRec* bq_items;
+  ItemRec* bk_items;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
   int32_t* counts_copy; // optional: counts also written here (test hook)
 };
@@ -97,8 +112,7 @@ struct FwdParams {
   float* lse;
   const WsHeader* hdr_ro;
   WsHeader* hdr;
-  const int4* recs;
-  const int32_t* rec_slot;
+  const ItemRec* items;
   const int4* comb;
   float* part_acc;
   float* part_ml;
@@ -127,8 +141,8 @@ struct BwdParams {
   void* dv;
   float* delta;        // [H][total_q] (softmax)
   WsHeader* hdr;
-  const int4* bq;
-  const int4* bk;
+  const ItemRec* bq;
+  const ItemRec* bk;
   int32_t H;
   int32_t causal;
   int32_t bias_kind;

@@ -142,11 +142,12 @@ __device__ void bitonic_sort(uint32_t* s, int N) {
   }
 }
 
-// Sorts gen_recs[0..n) by cost (desc, ties by generation index) into out / out_slot; the keys
-// (inverted cost << 20 | index) are unique, so the order is total.  Lists that fit in LDS use a
-// bitonic sort there; longer ones a stable radix sort in global memory.
+// Sorts gen_recs[0..n) by cost (desc, ties by generation index) into out / out_slot and the work
+// records `items` (each output may be null); the keys (inverted cost << 20 | index) are unique,
+// so the order is total.  Lists that fit in LDS use a bitonic sort there; longer ones a stable
+// radix sort in global memory.
 __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32_t* t_cost,
-                              int4* out, int32_t* out_slot) {
+                              int4* out, int32_t* out_slot, ItemRec* items) {
   const uint32_t* sorted;
   if (n <= LDS_SORT_MAX) {
     int N = 1;
@@ -165,8 +166,21 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
   }
   for (int i = threadIdx.x; i < n; i += ST) {
     const uint32_t idx = sorted[i] & 0xFFFFFu;
-    out[i] = a.gen_recs[idx];
-    if (out_slot) out_slot[i] = a.gen_slot[idx];
+    const int4 r = a.gen_recs[idx];
+    const int slot = out_slot || items ? a.gen_slot[idx] : -1;
+    if (out) out[i] = r;
+    if (out_slot) out_slot[i] = slot;
+    if (items) {
+      ItemRec it{};
+      it.b = r.x; it.x = r.y; it.y = r.z; it.z = r.w;
+      it.slot = slot;
+      it.qo = a.q_off[r.x];
+      it.n = a.q_off[r.x + 1] - it.qo;
+      it.ko = a.kv_off[r.x];
+      it.m = a.kv_off[r.x + 1] - it.ko;
+      it.boff = a.want_bias_off ? a.bias_off[r.x] : 0;
+      items[i] = it;
+    }
   }
   __syncthreads();
 }
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       if (nch > 1) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], (int)nch);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nrec, t_cost, a.fwd, a.fwd_slot);
+    sort_and_emit(a, sh, (int)nrec, t_cost, a.fwd, a.fwd_slot, a.fwd_items);
   }
 
   // ================= q-stationary backward list =================
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       t_cost[tau] = (int32_t)max((int64_t)1, steps);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr);
+    sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr, a.bq_items);
   }
 
   // ================= kv-stationary backward list =================
@@ -335,7 +349,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       t_cost[tau] = (int32_t)max((int64_t)1, nqs - first);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr);
+    sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr, a.bk_items);
   }
 
   if (tid == 0) {
