@@ -169,16 +169,6 @@ KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_dkdv": 
                          "jfa_bwd_dq": 6}
 
 
-def source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "jagged_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_for(kernel):
     """HBM traffic of `kernel` per launch from the committed counter summary, if current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -188,6 +178,7 @@ def traffic_for(kernel):
         rec = json.load(open(path))
     except Exception:
         return None
+    from jagged_attention_amd.traffic import source_hash
     ent = rec.get("kernels", {}).get(kernel)
     if not ent or rec.get("source_hash") != source_hash():
         return None
@@ -261,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -273,6 +266,15 @@ def main():
     import jagged_attention_amd as jfa
     jfa.load()
 
+    if args.copy_mib > 0:
+        # a plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it calibrates them
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy: {args.copy_mib} MiB x 3")
     log(f"[bench] headline workload {args.config}: warmup {args.warmup}, steps {args.steps}")
     w, head = bench_config(args.config, args.steps, args.warmup)
     log(f"[bench] {head['workload']}: {head['ms_per_step']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s")

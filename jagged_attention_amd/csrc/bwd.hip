@@ -231,7 +231,9 @@ struct KvLds {
   static constexpr int BS = STEP + 8;                     // dense tile [BNK][BS] bf16 (key-major)
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BNK * BS * 2 : 0);
-  static constexpr int STAGE = align16(BO + BIAS_BYTES);
+  // a stage also holds the epilogue's dK and dV rows (two staging areas per wave)
+  static constexpr int STAGE = align16(BO + BIAS_BYTES) > 2 * NW * out_stage_bytes<D>()
+                                   ? align16(BO + BIAS_BYTES) : 2 * NW * out_stage_bytes<D>();
   static constexpr int TOTAL = 2 * STAGE;
 };
 
@@ -587,19 +589,12 @@ void bwd_kv_kernel(BwdParams p) {
     // epilogue: this lane's key row of dK (x scale) and dV; keys past the sample are dropped
     const rsrc_t rdk = make_rsrc((__bf16*)p.dk + ((int64_t)ko * H + h) * D, kv_bytes);
     const rsrc_t rdv = make_rsrc((__bf16*)p.dv + ((int64_t)ko * H + h) * D, kv_bytes);
-    const uint32_t orow = (uint32_t)j * row_bytes;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const u32x2 k2 = {pack2bf(dk[db][4 * jq] * p.scale, dk[db][4 * jq + 1] * p.scale),
-                          pack2bf(dk[db][4 * jq + 2] * p.scale, dk[db][4 * jq + 3] * p.scale)};
-        const u32x2 v2 = {pack2bf(dv[db][4 * jq], dv[db][4 * jq + 1]),
-                          pack2bf(dv[db][4 * jq + 2], dv[db][4 * jq + 3])};
-        const uint32_t off = orow + 2 * (db * 32 + 8 * jq + 4 * g);
-        st8(k2, rdk, off);
-        st8(v2, rdv, off);
-      }
+    // through the stage that the last query step left free (rows of this wave only)
+    unsigned char* ost = lds + (nsteps & 1) * L::STAGE + wave * 2 * out_stage_bytes<D>();
+    store_rows_via_lds<D>(dk, p.scale, reinterpret_cast<__bf16*>(ost), rdk,
+                          (uint32_t)jw0 * row_bytes, row_bytes, lane);
+    store_rows_via_lds<D>(dv, 1.0f, reinterpret_cast<__bf16*>(ost + out_stage_bytes<D>()), rdv,
+                          (uint32_t)jw0 * row_bytes, row_bytes, lane);
     __syncthreads();
   }
 }
@@ -617,7 +612,9 @@ struct QLds {
   static constexpr int BS = STEP + 8;                     // dense tile [BM][BS] bf16 (query-major)
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);
-  static constexpr int STAGE = align16(BO + BIAS_BYTES);
+  // a stage also holds the epilogue's dQ rows (one staging area per wave)
+  static constexpr int STAGE = align16(BO + BIAS_BYTES) > NW * out_stage_bytes<D>()
+                                   ? align16(BO + BIAS_BYTES) : NW * out_stage_bytes<D>();
   static constexpr int TOTAL = 2 * STAGE;
 };
 
@@ -850,14 +847,10 @@ void bwd_q_kernel(BwdParams p) {
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const u32x2 q2 = {pack2bf(acc[db][4 * jq] * p.scale, acc[db][4 * jq + 1] * p.scale),
-                          pack2bf(acc[db][4 * jq + 2] * p.scale, acc[db][4 * jq + 3] * p.scale)};
-        st8(q2, rdq, qoff + 2 * (db * 32 + 8 * jq + 4 * g));
-      }
+    // through the stage that the last key step left free (rows of this wave only)
+    __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
+                                            wave * out_stage_bytes<D>());
+    store_rows_via_lds<D>(acc, p.scale, ost, rdq, (uint32_t)qw0 * row_bytes, row_bytes, lane);
     __syncthreads();
   }
 }

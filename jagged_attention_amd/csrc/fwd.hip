@@ -58,7 +58,9 @@ struct FwdLds {
   static constexpr int BIAS_BYTES =
       BIAS == B_RELPOS ? 4 * RP * 4 : (BIAS == B_DENSE ? BM * BS * 2 : 0);
   static constexpr int B_OFF = V_OFF + V_BYTES;
-  static constexpr int STAGE = align16(B_OFF + BIAS_BYTES);
+  // a stage also holds the epilogue's output rows (one staging area per wave)
+  static constexpr int STAGE = align16(B_OFF + BIAS_BYTES) > NW * out_stage_bytes<D>()
+                                   ? align16(B_OFF + BIAS_BYTES) : NW * out_stage_bytes<D>();
   static constexpr int TOTAL = 2 * STAGE;
 };
 
@@ -472,15 +474,11 @@ void fwd_kernel(FwdParams p) {
       else mul = (p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
       const uint32_t o_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
       const rsrc_t ro = make_rsrc((__bf16*)p.o + ((int64_t)qo * H + h) * D, o_bytes);
-      const uint32_t ooff = (uint32_t)qi * H * D * 2;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          u32x2 v = {pack2bf(acc[db][4 * jq] * mul, acc[db][4 * jq + 1] * mul),
-                     pack2bf(acc[db][4 * jq + 2] * mul, acc[db][4 * jq + 3] * mul)};
-          st8(v, ro, ooff + 2 * (db * 32 + 8 * jq + 4 * g));
-        }
+      // through the stage that the last key step left free (rows of this wave only)
+      __bf16* ost = reinterpret_cast<__bf16*>(lds + (nsteps & 1) * L::STAGE +
+                                              wave * out_stage_bytes<D>());
+      store_rows_via_lds<D>(acc, mul, ost, ro, (uint32_t)qw0 * H * D * 2, (uint32_t)H * D * 2,
+                            lane);
       if (MODE == MODE_SOFTMAX && g == 0 && p.lse && qi < n)
         p.lse[(int64_t)h * p.total_q + qo + qi] =
             l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : NEG_INF;

@@ -200,6 +200,41 @@ __device__ __forceinline__ void st4(uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// Row stride (bf16) of a wave's output staging area: 32 rows of D, padded against bank conflicts.
+template <int D>
+constexpr int out_stage_stride() { return D + 8; }
+template <int D>
+constexpr int out_stage_bytes() { return 32 * out_stage_stride<D>() * 2; }
+
+// Writes one wave's 32 output rows of D bf16 through LDS, so that the global stores are whole
+// 16-byte chunks with consecutive lanes along a row.  acc holds the transposed MFMA layout: lane
+// (r, g) = (lane % 32, lane / 32) has row r's elements 32 db + 8 jq + 4 g + 0..3, multiplied by
+// `mul` on the way.  `stage` is the wave's own LDS area (out_stage_bytes), read back only by this
+// wave; row i goes to byte offset row0 + i * row_bytes of `r` (rows past its range are dropped).
+template <int D>
+__device__ __forceinline__ void store_rows_via_lds(const f32x16* acc, float mul, __bf16* stage,
+                                                   rsrc_t r, uint32_t row0, uint32_t row_bytes,
+                                                   int lane) {
+  constexpr int OS = out_stage_stride<D>();
+  const int rr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const u32x2 v = {pack2bf(acc[db][4 * jq] * mul, acc[db][4 * jq + 1] * mul),
+                       pack2bf(acc[db][4 * jq + 2] * mul, acc[db][4 * jq + 3] * mul)};
+      *(u32x2*)(stage + rr * OS + db * 32 + 8 * jq + 4 * g) = v;
+    }
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+#pragma unroll
+  for (int k = 0; k < 32 * CPR / 64; ++k) {
+    const int c = k * 64 + lane;
+    const int row = c / CPR, col = c % CPR;
+    const u32x4 v = *(const u32x4*)(stage + row * OS + 8 * col);
+    st16(v, r, row0 + (uint32_t)row * row_bytes + 16u * (uint32_t)col);
+  }
+}
+
 // Byte permute: result byte k is byte sel_k of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
