@@ -125,6 +125,7 @@ Layout layout_of(const jfa_problem& p, const TileCfg& tc, int backward) {
   L.comb = take(16 * L.cap_c);
   L.bq = take(sizeof(ItemRec) * L.cap_q);
   L.bk = take(sizeof(ItemRec) * L.cap_k);
+  L.xtk = take(XTK_BYTES);
   if (!backward && L.cap_slots > 0) {
     L.part_acc = take(4 * (size_t)L.cap_slots * H * tc.bm * d);
     L.part_ml = take(4 * 2 * (size_t)L.cap_slots * H * tc.bm);
@@ -163,6 +164,7 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.comb = (int4*)(ws + L.comb);
   a.bq = nullptr;
   a.bk = nullptr;
+  a.xtk = (uint32_t*)(ws + L.xtk);
   a.fwd_items = (ItemRec*)(ws + L.fwd);
   a.bq_items = (ItemRec*)(ws + L.bq);
   a.bk_items = (ItemRec*)(ws + L.bk);
@@ -305,6 +307,7 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   fp.hdr_ro = (const WsHeader*)(ws + L.header);
   fp.hdr = (WsHeader*)(ws + L.header);
   fp.items = (const ItemRec*)(ws + L.fwd);
+  fp.xtk = (uint32_t*)(ws + L.xtk) + TK_FWD * XTK_XCDS * XTK_STRIDE;
   fp.comb = (const int4*)(ws + L.comb);
   fp.part_acc = L.cap_slots > 0 ? (float*)(ws + L.part_acc) : nullptr;
   fp.part_ml = L.cap_slots > 0 ? (float*)(ws + L.part_ml) : nullptr;
@@ -362,6 +365,8 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   bp.hdr = (WsHeader*)(ws + L.header);
   bp.bq = (const ItemRec*)(ws + L.bq);
   bp.bk = (const ItemRec*)(ws + L.bk);
+  bp.xtk_q = (uint32_t*)(ws + L.xtk) + TK_BQ * XTK_XCDS * XTK_STRIDE;
+  bp.xtk_k = (uint32_t*)(ws + L.xtk) + TK_BK * XTK_XCDS * XTK_STRIDE;
   bp.H = p->heads;
   bp.causal = p->causal;
   bp.bias_kind = p->bias_kind;

@@ -265,7 +265,7 @@ void bwd_kv_kernel(BwdParams p) {
   constexpr int NPRE = D == 128 ? 0 : NDB;
   u32x4 dbr[NPRE > 0 ? NPRE : 1][2];
 
-  ItemPipe pipe{&p.hdr->tickets[TK_BK], p.bk, n_items, H};
+  ItemPipe pipe{p.xtk_k, p.bk, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -573,16 +573,21 @@ void bwd_kv_kernel(BwdParams p) {
     // the key fragments (loaded with the first tiles) are complete before the query loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    const int claim_it = max(0, nsteps - CLAIM_AHEAD);
+    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
+    const bool short_item = nsteps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
+    const int claim_it = short_item ? -1 : nsteps - CLAIM_AHEAD;
+    const int resolve_it = short_item ? -1 : nsteps - 2;
     for (int it = 0; it + 1 < nsteps; ++it) {
-      if (it == claim_it && wave == 0) pipe.fetch(lane);
+      if (it == claim_it && wave == 0) pipe.claim(lane);
+      if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(qs_first + it + 1);
       compute_step(it, qs_first + it, -1);
       store_step((it + 1) & 1, qs_first + it + 1, true);
       __syncthreads();
     }
-    if (claim_it >= nsteps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1, -1);
+    if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
@@ -641,7 +646,7 @@ void bwd_q_kernel(BwdParams p) {
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
   u32x4 dbr[NDB];                   // dense bias chunks (8 keys of one query) of the next step
 
-  ItemPipe pipe{&p.hdr->tickets[TK_BQ], p.bq, n_items, H};
+  ItemPipe pipe{p.xtk_q, p.bq, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -833,16 +838,21 @@ void bwd_q_kernel(BwdParams p) {
     // the query fragments (loaded with the first tiles) are complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    const int claim_it = max(0, steps - CLAIM_AHEAD);
+    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
+    const bool short_item = steps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
+    const int claim_it = short_item ? -1 : steps - CLAIM_AHEAD;
+    const int resolve_it = short_item ? -1 : steps - 2;
     for (int it = 0; it + 1 < steps; ++it) {
-      if (it == claim_it && wave == 0) pipe.fetch(lane);
+      if (it == claim_it && wave == 0) pipe.claim(lane);
+      if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(it + 1);
       compute_step(it);
       store_step((it + 1) & 1, it + 1);
       __syncthreads();
     }
-    if (claim_it >= steps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (steps > 0) compute_step(steps - 1);
+    if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 

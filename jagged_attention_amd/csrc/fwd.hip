@@ -105,7 +105,7 @@ void fwd_kernel(FwdParams p) {
   constexpr int NPRE = (D == 128 && NW == 4) ? 0 : NDB;
   u32x4 dbr[NPRE > 0 ? NPRE : 1];
 
-  ItemPipe pipe{&p.hdr->tickets[TK_FWD], p.items, n_items, H};
+  ItemPipe pipe{p.xtk, p.items, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -311,6 +311,9 @@ void fwd_kernel(FwdParams p) {
     // the query fragment (loaded with the first tiles) is complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
+    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
+    const bool short_item = nsteps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
     // one key step on LDS stage it&1 (the loop is peeled so that its loads and stores are
     // unconditional: no load can be pending across the back edge)
     auto compute_step = [&](int it) {
@@ -451,17 +454,19 @@ void fwd_kernel(FwdParams p) {
         }
       }
     };
-    const int claim_it = max(0, nsteps - CLAIM_AHEAD);
+    const int claim_it = short_item ? -1 : nsteps - CLAIM_AHEAD;
+    const int resolve_it = short_item ? -1 : nsteps - 2;
     for (int it = 0; it + 1 < nsteps; ++it) {
-      if (it == claim_it && wave == 0) pipe.fetch(lane);
+      if (it == claim_it && wave == 0) pipe.claim(lane);
+      if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(kb + it + 1);
       compute_step(it);
       store_step((it + 1) & 1, kb + it + 1);
       __syncthreads();
     }
-    if (claim_it >= nsteps - 1 && wave == 0) pipe.fetch(lane);   // not claimed in the loop
     if (nsteps > 0) compute_step(nsteps - 1);
-    // publish the next descriptor before the epilogue's stores: waiting for the claimed ticket
+    if (short_item && wave == 0) pipe.resolve(lane);
+    // publish the next descriptor before the epilogue's stores: waiting for its record load
     // after them would also wait for the stores to complete
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 

@@ -287,45 +287,88 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
 }
 
 // Workgroup-wide work ticket: thread 0 takes the next item, everyone gets it.
-// Work-item pipeline of a persistent workgroup.  Wave 0 claims tickets one item ahead and, while
-// the workgroup works on the current item, loads the next item's 64-byte work record (one dword
-// per lane) and claims the ticket after it; starting an item then costs no memory round trip.
-// Descriptors - the record's 16 dwords and the ticket - reach the other waves through two LDS
-// buffers, published at the end of each item before the barrier that separates items.
+// Work-item pipeline of a persistent workgroup.  Wave 0 claims the next item while the workgroup
+// works on the current one, in three steps spread over the item so that none of them waits:
+// claim (an atomic ticket, which takes microseconds to return), resolve (turn the ticket into an
+// item and load its 64-byte work record, one dword per lane) and publish (write the record and
+// the item index to an LDS buffer before the barrier that ends the item).  A workgroup only ever
+// holds its current item and the next one.
+//
+// Items w = record * H + head are striped over the eight XCDs: XCD x owns w = 8k + x, k = 0, 1, ...
+// in list order.  Workgroup g runs on XCD g % 8 and starts on item g; later items of its XCD come
+// from that XCD's ticket counter.  When H divides 8 (or 8 divides H) an XCD sees only one head of
+// a sample, on at most 8 / H XCDs, so the sample's K/V tiles are reused from that XCD's L2.  A
+// workgroup whose XCD has run out takes tickets from the XCD with the most items left.
 enum ItemField {
   IF_B = 0, IF_X = 1, IF_Y = 2, IF_Z = 3, IF_SLOT = 4, IF_QO = 5, IF_N = 6, IF_KO = 7, IF_M = 8,
   IF_BOFF = 10, IF_W = 16, IF_WORDS = 17
 };
-// Steps before an item's end at which its workgroup claims the next ticket: a device-scope
-// atomic takes several microseconds to return, about as long as a few steps of work, while
-// claiming much earlier would let workgroups hold work that idle ones could take.
+// An item of more steps claims the next one this many steps before its end; shorter items claim
+// it before their first tile loads.
 constexpr int CLAIM_AHEAD = 4;
+constexpr int XCDS = 8;
+constexpr int XCD_TICKET_STRIDE = 32;   // dwords between per-XCD counters (own cache lines)
+static_assert(XCDS == XTK_XCDS && XCD_TICKET_STRIDE == XTK_STRIDE, "workspace counter layout");
 
 struct ItemPipe {
-  uint32_t* ctr;
+  uint32_t* ctr;             // XCDS counters, XCD_TICKET_STRIDE dwords apart, zeroed per call
   const ItemRec* items;
-  int64_t n_items;
+  int n_items;
   int H;
-  int tk = 0;                // ticket of the next item (wave 0, uniform)
+  int cx = 0;                // XCD list being drawn from (wave 0, uniform)
   int v = 0;                 // lane L < IF_WORDS: dword L of the next item's descriptor
-  uint32_t t = 0;            // lane 0: the ticket claimed after tk
+  uint32_t t = 0;            // lane 0: the claimed ticket of list cx
 
-  // Items 0 .. gridDim.x - 1 go to the workgroups in order; later tickets come from the counter
-  // (offset by the grid), so that the launch does not start with every workgroup contending
-  // for one atomic.
-  __device__ __forceinline__ void fetch(int lane) {
-    if (lane == IF_W) v = tk;
-    else if (lane < IF_W && tk < n_items) v = reinterpret_cast<const int*>(items + tk / H)[lane];
-    if (lane == 0) t = atomicAdd(ctr, 1u) + gridDim.x;
+  __device__ __forceinline__ int len(int x) const {
+    return n_items > x ? (n_items - x + XCDS - 1) / XCDS : 0;
+  }
+  // workgroups that start on XCD x's list (they take its first entries without a ticket)
+  __device__ __forceinline__ int homed(int x) const {
+    return ((int)gridDim.x - x + XCDS - 1) / XCDS;
+  }
+  __device__ __forceinline__ void load_record(int w, int lane) {
+    if (lane == IF_W) v = w;
+    else if (lane < IF_W && w < n_items) v = reinterpret_cast<const int*>(items + w / H)[lane];
+  }
+  __device__ __forceinline__ void claim(int lane) {
+    if (lane == 0) t = atomicAdd(ctr + XCD_TICKET_STRIDE * cx, 1u);
+  }
+  __device__ __forceinline__ void resolve(int lane) {
+    int k = (int)__builtin_amdgcn_readfirstlane(t) + homed(cx);
+    if (k >= len(cx)) {
+      // this list is exhausted: take from the list with the most entries left.  A failed claim
+      // exhausts one more list for good, so at most XCDS attempts precede success or the end.
+      k = -1;
+      for (int attempt = 0; attempt <= XCDS && k < 0; ++attempt) {
+        int rem = 0;
+        if (lane < XCDS) {
+          const uint32_t c = __hip_atomic_load(ctr + XCD_TICKET_STRIDE * lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          rem = len(lane) - ((int)c + homed(lane));
+        }
+        int best = -1, best_rem = 0;
+#pragma unroll
+        for (int x = 0; x < XCDS; ++x) {
+          const int r = __builtin_amdgcn_readlane(rem, x);
+          if (r > best_rem) { best_rem = r; best = x; }
+        }
+        if (best < 0) break;
+        cx = best;
+        uint32_t tt = 0;
+        if (lane == 0) tt = atomicAdd(ctr + XCD_TICKET_STRIDE * cx, 1u);
+        const int kk = (int)__builtin_amdgcn_readfirstlane(tt) + homed(cx);
+        if (kk < len(cx)) k = kk;
+      }
+    }
+    load_record(k >= 0 ? XCDS * k + cx : n_items, lane);
   }
   __device__ __forceinline__ void publish(int* dst, int lane) {
     if (lane < IF_WORDS) dst[lane] = v;
-    tk = __builtin_amdgcn_readfirstlane(t);
   }
   // first descriptor into dst (wave 0; the caller then synchronises the workgroup)
   __device__ __forceinline__ void start(int* dst, int lane) {
-    tk = blockIdx.x;
-    fetch(lane);
+    cx = blockIdx.x % XCDS;
+    load_record(blockIdx.x, lane);
     publish(dst, lane);
   }
 };

@@ -34,6 +34,9 @@ struct WsHeader {
 static_assert(sizeof(WsHeader) == 256, "header size");
 
 enum Ticket { TK_FWD = 0, TK_COMB = 1, TK_BQ = 2, TK_BK = 3, TK_DELTA = 4 };
+// Per-XCD work counters: kind k, XCD x at dword (8 k + x) * 32 of the workspace's counter area.
+constexpr int XTK_KINDS = 8, XTK_XCDS = 8, XTK_STRIDE = 32;
+constexpr size_t XTK_BYTES = (size_t)XTK_KINDS * XTK_XCDS * XTK_STRIDE * 4;
 
 struct TileCfg {
   int bm, bn;          // forward tile rows (query), kv step rows
@@ -47,7 +50,7 @@ struct TileCfg {
 // Byte layout of the workspace for one problem.
 struct Layout {
   size_t header, bias_off, s_tmp, t_tmp, gen_recs, gen_slot, words_a, words_b;
-  size_t fwd, comb, bq, bk;
+  size_t fwd, comb, bq, bk, xtk;
   size_t part_acc, part_ml, delta;
   size_t total;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
@@ -94,6 +97,7 @@ struct SchedArgs {
   ItemRec* bk_items;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
   int32_t* counts_copy; // optional: counts also written here (test hook)
+  uint32_t* xtk;        // per-XCD work counters of the persistent kernels (zeroed here)
 };
 
 // ----------------------------------------------------- kernel parameters
@@ -113,6 +117,7 @@ struct FwdParams {
   const WsHeader* hdr_ro;
   WsHeader* hdr;
   const ItemRec* items;
+  uint32_t* xtk;       // per-XCD work counters of this kernel
   const int4* comb;
   float* part_acc;
   float* part_ml;
@@ -143,6 +148,8 @@ struct BwdParams {
   WsHeader* hdr;
   const ItemRec* bq;
   const ItemRec* bk;
+  uint32_t* xtk_q;     // per-XCD work counters of the query-stationary kernel
+  uint32_t* xtk_k;     // and of the key-stationary kernel
   int32_t H;
   int32_t causal;
   int32_t bias_kind;

@@ -363,6 +363,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     if (a.counts_copy)
       for (int i = 0; i < 8; ++i) a.counts_copy[i] = cnt[i];
   }
+  if (a.xtk && tid < XTK_KINDS * XTK_XCDS) a.xtk[tid * XTK_STRIDE] = 0;
 }
 
 // offsets[b+1] = offsets[b] + lengths[b], in int64 with an int32 range check.
