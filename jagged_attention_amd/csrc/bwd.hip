@@ -222,9 +222,8 @@ struct KvLds {
   static constexpr int RS = D + 8;
   static constexpr int QR = 0;                            // Q rows [STEP][RS]
   static constexpr int DR = QR + STEP * RS * 2;           // dO rows
-  static constexpr int QT = DR + STEP * RS * 2;           // Q^T [D][TS]
-  static constexpr int DT = QT + D * TS * 2;              // dO^T
-  static constexpr int LS = DT + D * TS * 2;              // lse / scale [STEP]
+  // Q^T and dO^T operands are read from the row tiles with transposing LDS reads
+  static constexpr int LS = DR + STEP * RS * 2;           // lse / scale [STEP]
   static constexpr int DL = LS + STEP * 4;                // delta [STEP]
   static constexpr int BO = DL + STEP * 4;
   static constexpr int RP = diag_stride(STEP + BNK + 4);
@@ -250,6 +249,10 @@ void bwd_kv_kernel(BwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   const int H = p.H;
   const int64_t n_items = (int64_t)p.hdr->counts[3] * H;
+  // this lane's element of a transposing read: row 4(G/2) + (j/4), column 16(G%2) + 4(j%4) for
+  // 16-lane group G and lane j within it (plus the operand's base row and column)
+  const int tr_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * L::RS + 16 * ((lane >> 4) & 1) +
+                      4 * (lane & 3);
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
   const float inv_scale = 1.0f / p.scale;
   const uint32_t row_bytes = (uint32_t)H * D * 2;
@@ -350,12 +353,12 @@ void bwd_kv_kernel(BwdParams p) {
     auto store_tile_piece = [&](auto pc, int st) {
       constexpr int P = decltype(pc)::value;
       unsigned char* base = lds + st * L::STAGE;
-      if constexpr (P < TP)
-        tq.template store_part<P>(reinterpret_cast<__bf16*>(base + L::QR),
-                                  reinterpret_cast<__bf16*>(base + L::QT));
-      else
-        tdo.template store_part<P - TP>(reinterpret_cast<__bf16*>(base + L::DR),
-                                        reinterpret_cast<__bf16*>(base + L::DT));
+      if constexpr (P % 6 < 2) {   // row stores only: no transposed copies
+        if constexpr (P < TP)
+          tq.template store_part<P>(reinterpret_cast<__bf16*>(base + L::QR), nullptr);
+        else
+          tdo.template store_part<P - TP>(reinterpret_cast<__bf16*>(base + L::DR), nullptr);
+      }
     };
     auto store_step = [&](int st, int qs, bool tiles) {
       unsigned char* base = lds + st * L::STAGE;
@@ -408,8 +411,6 @@ void bwd_kv_kernel(BwdParams p) {
       }
       const __bf16* qr = reinterpret_cast<const __bf16*>(sb + L::QR);
       const __bf16* dr = reinterpret_cast<const __bf16*>(sb + L::DR);
-      const __bf16* qt = reinterpret_cast<const __bf16*>(sb + L::QT);
-      const __bf16* dt = reinterpret_cast<const __bf16*>(sb + L::DT);
       const float* lsl = reinterpret_cast<const float*>(sb + L::LS);
       const float* dll = reinterpret_cast<const float*>(sb + L::DL);
       // element (blk, i): query q0 + blk*32 + 8(i/4) + 4g + i%4 of this step, key j
@@ -492,10 +493,14 @@ void bwd_kv_kernel(BwdParams p) {
           const __bf16* base = (jj & 1) ? dr : qr;
           return *(const u32x4*)(base + (h * 32 + l32) * RS + 16 * ks + 8 * g);
         }
+        // dV^T += dO^T P_h, dK^T += Q^T dS_h: A operand rows = head dims db*32 + (lane % 32),
+        // k = 8g + j <-> query 32h + 16cc + 8(j/4) + 4g + j%4 of the step (the order in which
+        // P and dS leave the S accumulator), read as two column strips of 4 queries
         const int h = (s - 2 * NA) / NA, jj = (s - 2 * NA) % NA;
         const int cc = jj / (NA / 2), db = (jj % (NA / 2)) >> 1;
-        const __bf16* base = (jj & 1) ? qt : dt;
-        return *(const u32x4*)(base + (db * 32 + l32) * TS + 16 * (2 * h + cc) + 8 * g);
+        const __bf16* p = ((jj & 1) ? qr : dr) + tr_lane + (32 * h + 16 * cc) * RS + db * 32;
+        const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * RS);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
       };
       uint32_t pp[2][8], dd[2][8];
       // B(h) element i (query offset blk*32 + 8(i/4) + i%4 with blk = h)

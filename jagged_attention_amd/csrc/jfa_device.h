@@ -200,6 +200,18 @@ __device__ __forceinline__ void st4(uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// names 4 consecutive 16-bit elements A[j][0..3]; lane c receives A[4e + c/4][c % 4], e = 0..3.
+// With lane j = 4e + q pointing at row r0 + e, columns c0 + 4q .. c0 + 4q + 3 of a row-major
+// tile, lane c receives column c0 + c of rows r0 .. r0 + 3: a column strip, as an MFMA operand
+// whose contraction runs along the tile's rows needs.
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4* lp;
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Row stride (bf16) of a wave's output staging area: 32 rows of D, padded against bank conflicts.
 template <int D>
 constexpr int out_stage_stride() { return D + 8; }
