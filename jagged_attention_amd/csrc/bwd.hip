@@ -18,9 +18,8 @@
 //    lane's accumulator column is exactly the B operand of the gradient MFMAs, so P and dS
 //    never go through LDS;
 //  - every tile is staged global -> registers -> LDS one step ahead (two LDS stages, one
-//    barrier per step); operands contracted over the step's rows (Q^T, dO^T, K^T) are written
-//    transposed with v_perm on bf16 pairs, rows permuted so each MFMA operand is one 16-byte
-//    read;
+//    barrier per step), row-major; operands contracted over the step's rows (Q^T, dO^T, K^T)
+//    are read from the row tiles with transposing LDS reads (ds_read_b64_tr_b16);
 //  - loads and stores go through per-(sample, head) buffer resources: rows past a sample's
 //    end read as zero and are never written, with no branches;
 //  - the additive bias initialises the S accumulator (bias / scale).
@@ -616,8 +615,8 @@ struct QLds {
   static constexpr int RS = D + 8;
   static constexpr int KR = 0;                            // K rows [STEP][RS]
   static constexpr int VR = KR + STEP * RS * 2;           // V rows
-  static constexpr int KT = VR + STEP * RS * 2;           // K^T [D][TS]
-  static constexpr int BO = KT + D * TS * 2;
+  // the K^T operand is read from the K rows with transposing LDS reads
+  static constexpr int BO = VR + STEP * RS * 2;
   static constexpr int RP = diag_stride(BM + STEP + 4);
   static constexpr int BS = STEP + 8;                     // dense tile [BM][BS] bf16 (query-major)
   static constexpr int BIAS_BYTES =
@@ -641,6 +640,9 @@ void bwd_q_kernel(BwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   const int H = p.H;
   const int64_t n_items = (int64_t)p.hdr->counts[2] * H;
+  // this lane's element of a transposing read (see the key-stationary kernel)
+  const int tr_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * L::RS + 16 * ((lane >> 4) & 1) +
+                      4 * (lane & 3);
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
   const float inv_scale = 1.0f / p.scale;
   const uint32_t row_bytes = (uint32_t)H * D * 2;
@@ -729,7 +731,7 @@ void bwd_q_kernel(BwdParams p) {
     auto store_step = [&](int st, int kt) {
       unsigned char* base = lds + st * L::STAGE;
       const int j0 = kt * STEP;
-      tk.store(reinterpret_cast<__bf16*>(base + L::KR), reinterpret_cast<__bf16*>(base + L::KT));
+      tk.store(reinterpret_cast<__bf16*>(base + L::KR), nullptr);
       tv.store(reinterpret_cast<__bf16*>(base + L::VR));
       if constexpr (BIAS == B_RELPOS) {
         if (tid < BM + STEP - 1)
@@ -822,7 +824,7 @@ void bwd_q_kernel(BwdParams p) {
           dd[blk][i >> 1] = pack2bf(d2[0], d2[1]);
         }
       // dQ^T += K^T dS^T; chunk c covers keys 16c + 8(e/4) + 4g + e%4
-      const __bf16* kt = reinterpret_cast<const __bf16*>(sb + L::KT);
+
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 dw = {dd[c >> 1][4 * (c & 1)], dd[c >> 1][4 * (c & 1) + 1],
@@ -830,7 +832,11 @@ void bwd_q_kernel(BwdParams p) {
         const bf16x8 db8 = as_bf16x8(dw);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(kt + (db * 32 + l32) * TS + 16 * c + 8 * g));
+          // K^T rows = head dims, k = 8g + j <-> key 16c + 8(j/4) + 4g + j%4: two column
+          // strips of 4 keys of the K rows
+          const __bf16* pk = kr + tr_lane + 16 * c * RS + db * 32;
+          const u32x2 lo = lds_read_tr16(pk), hi = lds_read_tr16(pk + 8 * RS);
+          const bf16x8 ka = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
           acc[db] = mfma_bf16(ka, db8, acc[db]);
         }
       }

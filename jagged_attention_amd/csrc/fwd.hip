@@ -8,10 +8,10 @@
 //
 // Design (gfx950):
 //  - A workgroup of NW waves owns BM = 32*NW query rows of one head of one sample and walks
-//    the keys 64 at a time.  Each step's K tile (row-major) and V tile (stored transposed,
-//    keys permuted so an MFMA operand is one 16-byte read) sit in one of two LDS stages: the
-//    next step's global loads are issued before this step's MFMAs and land in the other
-//    stage after them, so one barrier per step suffices.
+//    the keys 64 at a time.  Each step's K and V tiles (row-major; the V^T operand of PV is
+//    read with transposing LDS reads) sit in one of two LDS stages: the next step's global
+//    loads are issued before this step's MFMAs and land in the other stage after them, so one
+//    barrier per step suffices.
 //  - Global loads go through per-(sample, head) buffer resources whose size ends at the
 //    sample's last row: rows past the end read as zeros with no branches.
 //  - Each wave computes S^T = K Q^T (32x32x16 bf16 MFMA, or the scaled 32x32x64 E4M3 MFMA
@@ -50,9 +50,9 @@ struct FwdLds {
   static constexpr int KRB = FP8 ? (D + 16) : 2 * (D + 8);   // K row stride in bytes
   static constexpr int K_BYTES = BN * KRB;
   static constexpr int KSC_BYTES = FP8 ? BN * 4 : 0;          // K scales: one dword per key
-  static constexpr int VS = BN + 8;                            // V^T row stride (bf16)
+  static constexpr int VS = D + 8;                             // V row stride (bf16)
   static constexpr int V_OFF = align16(K_BYTES + KSC_BYTES);
-  static constexpr int V_BYTES = D * VS * 2;
+  static constexpr int V_BYTES = BN * VS * 2;
   static constexpr int RP = diag_stride(BM + BN + 4);          // relpos copy length (floats)
   static constexpr int BS = BN + 8;                            // dense bias row stride (bf16)
   static constexpr int BIAS_BYTES =
@@ -91,6 +91,10 @@ void fwd_kernel(FwdParams p) {
   constexpr int K_LOADS = BN * KCH / NT;                    // per thread
   static_assert(BN * KCH % NT == 0, "K staging");
   constexpr int VBLK = (BN / 4) * (D / 8);                  // 4 keys x 8 dims blocks of V
+  // this lane's element of a transposing read: row 4(G/2) + (j/4), column 16(G%2) + 4(j%4) for
+  // 16-lane group G and lane j within it (plus the operand's base row and column)
+  const int tr_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) +
+                      4 * (lane & 3);
   constexpr int V_LOADS = (VBLK + NT - 1) / NT;
 
   u32x4 kreg[K_LOADS];
@@ -218,7 +222,7 @@ void fwd_kernel(FwdParams p) {
       for (int i = 0; i < V_LOADS; ++i) {
         const int id = tid + i * NT;
         if (VBLK % NT != 0 && id >= VBLK) break;
-        const int rbk = id % (BN / 4), cb = id / (BN / 4);
+        const int cb = id % (D / 8), rbk = id / (D / 8);   // lanes along a row
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const uint32_t row = (uint32_t)(j0 + 4 * rbk + rr);
@@ -244,44 +248,31 @@ void fwd_kernel(FwdParams p) {
       if constexpr (FP8) {
         if (tid < BN) *(uint32_t*)(base + L::K_BYTES + 4 * tid) = kscreg;
       }
-      __bf16* vt = reinterpret_cast<__bf16*>(base + L::V_OFF);
+      // V rows [BN][VS]; the PV operand V^T is read from them with transposing reads
+      __bf16* vr = reinterpret_cast<__bf16*>(base + L::V_OFF);
 #pragma unroll
       for (int i = 0; i < V_LOADS; ++i) {
         const int id = tid + i * NT;
         if (VBLK % NT != 0 && id >= VBLK) break;
-        const int rbk = id % (BN / 4), cb = id / (BN / 4);
-        const int pos = vt_pos(4 * rbk);
-        if constexpr (FP8) {
-          // dequantise 4 keys x 8 dims (E4M3 x 2^(s-127)) to bf16, then transpose
-          uint32_t w[4][4];   // [key][pair of dims] bf16x2
+        const int cb = id % (D / 8), rbk = id / (D / 8);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
+        for (int rr = 0; rr < 4; ++rr) {
+          __bf16* dst = vr + (4 * rbk + rr) * VS + 8 * cb;
+          if constexpr (FP8) {
+            // dequantise 8 dims (E4M3 x 2^(s-127)) of one key to bf16
             const float sc = e8m0_to_f(vsc[i][rr]);
+            u32x4 w;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
               const uint32_t src = v8[i][rr][e2 >> 1];
               typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
               const bf2 cv = (e2 & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, true)
                                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, false);
-              w[rr][e2] = __builtin_bit_cast(uint32_t, cv);
+              w[e2] = __builtin_bit_cast(uint32_t, cv);
             }
-          }
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const u32x2 lo = {lo_halves(w[0][e2], w[1][e2]), lo_halves(w[2][e2], w[3][e2])};
-            const u32x2 hi = {hi_halves(w[0][e2], w[1][e2]), hi_halves(w[2][e2], w[3][e2])};
-            *(u32x2*)(vt + (8 * cb + 2 * e2) * VS + pos) = lo;
-            *(u32x2*)(vt + (8 * cb + 2 * e2 + 1) * VS + pos) = hi;
-          }
-        } else {
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const u32x2 lo = {lo_halves(v16[i][0][e2], v16[i][1][e2]),
-                              lo_halves(v16[i][2][e2], v16[i][3][e2])};
-            const u32x2 hi = {hi_halves(v16[i][0][e2], v16[i][1][e2]),
-                              hi_halves(v16[i][2][e2], v16[i][3][e2])};
-            *(u32x2*)(vt + (8 * cb + 2 * e2) * VS + pos) = lo;
-            *(u32x2*)(vt + (8 * cb + 2 * e2 + 1) * VS + pos) = hi;
+            *(u32x4*)dst = w;
+          } else {
+            *(u32x4*)dst = v16[i][rr];
           }
         }
       }
@@ -440,7 +431,7 @@ void fwd_kernel(FwdParams p) {
         }
 
         // ---- O^T += V^T P^T: chunk c covers keys 16c + 8(e/4) + 4g + e%4
-        const __bf16* vt = reinterpret_cast<const __bf16*>(sb + L::V_OFF);
+        const __bf16* vr = reinterpret_cast<const __bf16*>(sb + L::V_OFF);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const u32x4 pw = {pk[c >> 1][4 * (c & 1)], pk[c >> 1][4 * (c & 1) + 1],
@@ -448,7 +439,11 @@ void fwd_kernel(FwdParams p) {
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = as_bf16x8(*(const u32x4*)(vt + (db * 32 + l32) * VS + 16 * c + 8 * g));
+            // V^T rows = head dims, k = 8g + j <-> key 16c + 8(j/4) + 4g + j%4: two column
+            // strips of 4 keys of the V rows
+            const __bf16* pv = vr + tr_lane + 16 * c * VS + db * 32;
+            const u32x2 lo = lds_read_tr16(pv), hi = lds_read_tr16(pv + 8 * VS);
+            const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             acc[db] = mfma_bf16(a, pb, acc[db]);
           }
         }
