@@ -12,9 +12,8 @@
 //    one query tile (or else one key tile) takes a single pass that owns all its gradients;
 //  - every list is ordered longest first, ties by (sample, tile, first step): a total order,
 //    so the lists are unique and bit-reproducible.
-// One workgroup of 1024 threads does all of it with block scans and a sort on the inverted
-// cost (bitonic in LDS, or a stable radix sort in global memory for long lists); no host
-// round trip.
+// One workgroup of 1024 threads does all of it with block scans and a sort on the inverted cost
+// (bitonic or radix in LDS, radix in global memory for long lists); no host round trip.
 #include "jfa_internal.h"
 
 namespace jfa {
@@ -23,6 +22,7 @@ namespace {
 constexpr int ST = 1024;
 constexpr int SW = ST / 64;
 constexpr int LDS_SORT_MAX = 8192;
+constexpr int BITONIC_MAX = 1024;
 
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -80,6 +80,24 @@ __device__ int owner_of(const int32_t* base, int B, int64_t x) {
   return lo;
 }
 
+// Ascending bitonic sort of N (a power of two, at most LDS_SORT_MAX) unique keys in LDS.
+__device__ void bitonic_sort(uint32_t* s, int N) {
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < N / 2; i += ST) {
+        const int lo = 2 * j * (i / j) + (i % j), hi = lo + j;
+        const bool up = (lo & k) == 0;
+        const uint32_t x = s[lo], y = s[hi];
+        if ((x > y) == up) {
+          s[lo] = y;
+          s[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // Stable ascending sort of words by bits [20, 32), three 4-bit passes; result ends in b.
 __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t* red) {
   const int tid = threadIdx.x;
@@ -115,41 +133,29 @@ __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t*
   // three passes: a -> b -> a -> b
 }
 
+// Sample offsets are copied to LDS when B is at most this (every tile looks its sample up).
+constexpr int LDS_OFF_MAX = 4095;
+
 struct Shared {
   uint32_t sa[LDS_SORT_MAX];
   int32_t T[16 * ST];
+  int32_t qo[LDS_OFF_MAX + 1];
+  int32_t ko[LDS_OFF_MAX + 1];
   int64_t red[SW];
   int32_t flag;
   int64_t sumcost;
 };
 
-// Ascending bitonic sort of N (a power of two, at most LDS_SORT_MAX) keys in LDS; keys are unique, so the result is the unique sorted order.
-__device__ void bitonic_sort(uint32_t* s, int N) {
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < N / 2; i += ST) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const bool up = (lo & k) == 0;
-        const uint32_t x = s[lo], y = s[hi];
-        if ((x > y) == up) {
-          s[lo] = y;
-          s[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // Sorts gen_recs[0..n) by cost (desc, ties by generation index) into out / out_slot and the work
 // records `items` (each output may be null); the keys (inverted cost << 20 | index) are unique,
-// so the order is total.  Lists that fit in LDS use a bitonic sort there; longer ones a stable
-// radix sort in global memory.
+// so the order is total.  Short lists use a bitonic sort in LDS; longer ones, whose keys arrive
+// in generation order, a stable 3-pass radix sort on the cost bits alone (in LDS up to 4096
+// entries, else in global memory).
 __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32_t* t_cost,
-                              int4* out, int32_t* out_slot, ItemRec* items) {
+                              int4* out, int32_t* out_slot, ItemRec* items, const int32_t* qo,
+                              const int32_t* ko) {
   const uint32_t* sorted;
-  if (n <= LDS_SORT_MAX) {
+  if (n <= BITONIC_MAX) {
     int N = 1;
     while (N < n) N <<= 1;
     for (int i = threadIdx.x; i < N; i += ST)
@@ -157,6 +163,12 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
     __syncthreads();
     bitonic_sort(sh.sa, N);
     sorted = sh.sa;
+  } else if (n <= LDS_SORT_MAX / 2) {
+    for (int i = threadIdx.x; i < n; i += ST)
+      sh.sa[i] = ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i;
+    __syncthreads();
+    radix_sort(sh.sa, sh.sa + LDS_SORT_MAX / 2, n, sh.T, sh.red);
+    sorted = sh.sa + LDS_SORT_MAX / 2;
   } else {
     for (int i = threadIdx.x; i < n; i += ST)
       a.words_a[i] = ((uint32_t)(MAX_COST - t_cost[i]) << 20) | (uint32_t)i;
@@ -164,22 +176,44 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
     radix_sort(a.words_a, a.words_b, n, sh.T, sh.red);
     sorted = a.words_b;
   }
-  for (int i = threadIdx.x; i < n; i += ST) {
-    const uint32_t idx = sorted[i] & 0xFFFFFu;
-    const int4 r = a.gen_recs[idx];
-    const int slot = out_slot || items ? a.gen_slot[idx] : -1;
-    if (out) out[i] = r;
-    if (out_slot) out_slot[i] = slot;
-    if (items) {
-      ItemRec it{};
-      it.b = r.x; it.x = r.y; it.y = r.z; it.z = r.w;
-      it.slot = slot;
-      it.qo = a.q_off[r.x];
-      it.n = a.q_off[r.x + 1] - it.qo;
-      it.ko = a.kv_off[r.x];
-      it.m = a.kv_off[r.x + 1] - it.ko;
-      it.boff = a.want_bias_off ? a.bias_off[r.x] : 0;
-      items[i] = it;
+  // U records per thread at a time, all their loads issued before any use: the records are
+  // gathered from global memory, and one at a time each would wait a full memory round trip
+  constexpr int U = 4;
+  for (int base = 0; base < n; base += ST * U) {
+    int4 r[U];
+    int slot[U];
+    int64_t boff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * ST + threadIdx.x;
+      if (i < n) {
+        const uint32_t idx = sorted[i] & 0xFFFFFu;
+        r[u] = a.gen_recs[idx];
+        slot[u] = out_slot || items ? a.gen_slot[idx] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * ST + threadIdx.x;
+      boff[u] = (i < n && items && a.want_bias_off) ? a.bias_off[r[u].x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * ST + threadIdx.x;
+      if (i >= n) continue;
+      if (out) out[i] = r[u];
+      if (out_slot) out_slot[i] = slot[u];
+      if (items) {
+        ItemRec it{};
+        it.b = r[u].x; it.x = r[u].y; it.y = r[u].z; it.z = r[u].w;
+        it.slot = slot[u];
+        it.qo = qo[r[u].x];
+        it.n = qo[r[u].x + 1] - it.qo;
+        it.ko = ko[r[u].x];
+        it.m = ko[r[u].x + 1] - it.ko;
+        it.boff = boff[u];
+        items[i] = it;
+      }
     }
   }
   __syncthreads();
@@ -223,8 +257,18 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     return;
   }
 
+  // sample offsets: from LDS when they fit (every tile and record looks its sample up)
   const int32_t* qo = a.q_off;
   const int32_t* ko = a.kv_off;
+  if (B <= LDS_OFF_MAX) {
+    for (int b = tid; b <= B; b += ST) {
+      sh.qo[b] = a.q_off[b];
+      sh.ko[b] = a.kv_off[b];
+    }
+    __syncthreads();
+    qo = sh.qo;
+    ko = sh.ko;
+  }
   auto qlen = [&](int b) -> int64_t { return (int64_t)qo[b + 1] - qo[b]; };
   auto klen = [&](int b) -> int64_t { return (int64_t)ko[b + 1] - ko[b]; };
 
@@ -293,7 +337,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       if (nch > 1) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], (int)nch);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nrec, t_cost, a.fwd, a.fwd_slot, a.fwd_items);
+    sort_and_emit(a, sh, (int)nrec, t_cost, a.fwd, a.fwd_slot, a.fwd_items, qo, ko);
   }
 
   // ================= q-stationary backward list =================
@@ -324,7 +368,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       t_cost[tau] = (int32_t)max((int64_t)1, steps);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr, a.bq_items);
+    sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr, a.bq_items, qo, ko);
   }
 
   // ================= kv-stationary backward list =================
@@ -349,7 +393,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       t_cost[tau] = (int32_t)max((int64_t)1, nqs - first);
     }
     __syncthreads();
-    sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr, a.bk_items);
+    sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr, a.bk_items, qo, ko);
   }
 
   if (tid == 0) {
