@@ -83,8 +83,8 @@ typedef struct {
   int32_t num_buckets;      /* RELPOS table width, 1..4096 (64 for the GEM workloads) */
   int32_t split_slots;      /* forward tail balancing: 0 = auto (concurrent workgroups of the
                                device), >0 = this many, <0 = never split a query tile */
-  int32_t bwd_fuse;         /* -1 default (on), 0 off: single-pass backward for samples with
-                               one query tile or one key tile */
+  int32_t bwd_fuse;         /* -1 default (on where built), 0 off: single-pass backward for
+                               samples with one key tile (d = 64) */
 } jfa_problem;
 
 /*
@@ -123,7 +123,8 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
 /* Tile sizes the kernels use for this problem, in the order
  * {bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse}: forward query/key tile rows, split slots
  * (<= 0: no split), query-stationary backward tile rows, key-stationary backward tile rows,
- * and whether single-pass backward classes are on.  Host only (queries the device only when
+ * and the single-pass backward classes that are on (bit 0: samples with one query tile, bit 1:
+ * samples with one key tile).  Host only (queries the device only when
  * split_slots = 0). */
 jfa_status jfa_tile_config(const jfa_problem* p, int32_t cfg_out[8]);
 

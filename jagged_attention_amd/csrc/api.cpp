@@ -90,8 +90,10 @@ jfa_status tile_cfg(const jfa_problem& p, TileCfg* t) {
   t->bk_nw = (short_kv || (p.bias_kind == JFA_BIAS_DENSE && p.head_dim == 128)) ? 2 : 4;
   t->bk_bn = 32 * t->bk_nw;
   t->bk_bm = BK_BM;
-  t->fuse = 0;   // single-pass backward classes: not enabled in this build
-  (void)p.bwd_fuse;
+  // single-pass backward classes (bit 1: a sample with one key tile runs only the
+  // key-stationary pass, which then also writes dQ; built at d = 64.  Bit 0, a sample with one
+  // query tile, is not built)
+  t->fuse = (p.bwd_fuse != 0 && p.head_dim == 64) ? 2 : 0;
   return JFA_OK;
 }
 

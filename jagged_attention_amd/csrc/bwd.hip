@@ -232,7 +232,13 @@ struct KvLds {
   // a stage also holds the epilogue's dK and dV rows (two staging areas per wave)
   static constexpr int STAGE = align16(BO + BIAS_BYTES) > 2 * NW * out_stage_bytes<D>()
                                    ? align16(BO + BIAS_BYTES) : 2 * NW * out_stage_bytes<D>();
-  static constexpr int TOTAL = 2 * STAGE;
+  // single pass for a sample with one key tile (built at d = 64): the item's K rows and each
+  // step's dS, from which the workgroup also computes the step's dQ
+  static constexpr bool K1 = D == 64;
+  static constexpr int QS = STEP + 8;                     // dS tile [BNK keys][QS] (bf16)
+  static constexpr int K1_KR = 2 * STAGE;
+  static constexpr int K1_DS = K1_KR + BNK * RS * 2;
+  static constexpr int TOTAL = 2 * STAGE + (K1 ? BNK * RS * 2 + BNK * QS * 2 : 0);
 };
 
 template <int D, int NW, int MODE, int BIAS>
@@ -283,6 +289,9 @@ void bwd_kv_kernel(BwdParams p) {
     const int delta = m - n;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int j0 = u * BNK, jw0 = j0 + wave * 32;
+    // single-pass class (the scheduler's test): one key tile and not one query tile
+    const bool one_k = L::K1 && (p.fuse & 2) && !((p.fuse & 1) && n > 0 && n <= p.bq_bm) &&
+                       m > 0 && m <= BNK;
     const int kvl = wave * 32 + l32, j = j0 + kvl;
 
     const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
@@ -406,6 +415,12 @@ void bwd_kv_kernel(BwdParams p) {
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
       if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0)) {
         if (nst >= 0) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, nst); });
+        if (L::K1 && one_k) {     // these keys contribute nothing to this step's dQ
+          uint32_t* ds = reinterpret_cast<uint32_t*>(
+              reinterpret_cast<__bf16*>(lds + L::K1_DS) + kvl * L::QS);
+#pragma unroll
+          for (int i = 0; i < STEP / 2 / 2; ++i) ds[2 * i + g] = 0u;
+        }
         return;
       }
       const __bf16* qr = reinterpret_cast<const __bf16*>(sb + L::QR);
@@ -567,6 +582,58 @@ void bwd_kv_kernel(BwdParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+      if (L::K1 && one_k) {
+        // dS [key][query] of this step: element pair p of half h holds queries q, q + 1 with
+        // q = 32h + 8(p/2) + 4g + 2(p%2)
+        __bf16* ds = reinterpret_cast<__bf16*>(lds + L::K1_DS) + kvl * L::QS;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int pi = 0; pi < 8; ++pi)
+            *(uint32_t*)(ds + 32 * h + 8 * (pi >> 1) + 4 * g + 2 * (pi & 1)) = dd[h][pi];
+      }
+    };
+
+    // dQ of a query step of a one-key-tile sample: dQ^T = scale K^T dS^T over the item's keys,
+    // both operands read with transposing LDS reads in natural key order (k = 8g + j <-> key
+    // 16 kc + 8g + j).  Wave w computes output blocks b = w, w + NW, ... of (query half b % 2,
+    // head-dim block b / 2) and stores its rows directly.
+    auto dq_step = [&](int qs) {
+      if constexpr (L::K1) {
+        constexpr int NBLK = 2 * (D / 32), BPW = NBLK / NW;
+        static_assert(NBLK % NW == 0, "dQ blocks per wave");
+        const __bf16* kr1 = reinterpret_cast<const __bf16*>(lds + L::K1_KR);
+        const __bf16* ds1 = reinterpret_cast<const __bf16*>(lds + L::K1_DS);
+        const int tr_k = (8 * (lane >> 5) + ((lane & 15) >> 2)) * RS + 16 * ((lane >> 4) & 1) +
+                         4 * (lane & 3);
+        const int tr_d = (8 * (lane >> 5) + ((lane & 15) >> 2)) * L::QS +
+                         16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
+#pragma unroll
+        for (int bi = 0; bi < BPW; ++bi) {
+          const int b = wave + bi * NW, half = b & 1, db = b >> 1;
+          f32x16 qa;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) qa[i] = 0.f;
+#pragma unroll
+          for (int kc = 0; kc < BNK / 16; ++kc) {
+            const __bf16* pa = kr1 + tr_k + 16 * kc * RS + db * 32;
+            const __bf16* pb = ds1 + tr_d + 16 * kc * L::QS + 32 * half;
+            const u32x2 a0 = lds_read_tr16(pa), a1 = lds_read_tr16(pa + 4 * RS);
+            const u32x2 b0 = lds_read_tr16(pb), b1 = lds_read_tr16(pb + 4 * L::QS);
+            qa = mfma_bf16(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}),
+                           as_bf16x8(u32x4{b0[0], b0[1], b1[0], b1[1]}), qa);
+          }
+          // lane (query 32 half + l32, g) holds head dims db*32 + 8 jq + 4g + 0..3
+          const uint32_t row = (uint32_t)(qs * STEP + 32 * half + l32) * row_bytes;
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const u32x2 v = {pack2bf(qa[4 * jq] * p.scale, qa[4 * jq + 1] * p.scale),
+                             pack2bf(qa[4 * jq + 2] * p.scale, qa[4 * jq + 3] * p.scale)};
+            st8(v, rdq, row + 2u * (uint32_t)(db * 32 + 8 * jq + 4 * g));
+          }
+        }
+      }
     };
 
     const int nsteps = qs_end - qs_first;
@@ -576,6 +643,12 @@ void bwd_kv_kernel(BwdParams p) {
     }
     // the key fragments (loaded with the first tiles) are complete before the query loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (L::K1 && one_k) {
+      // the item's K rows for the dQ steps: lane (key, g) holds head dims 16 ks + 8g + 0..7
+      __bf16* kr1 = reinterpret_cast<__bf16*>(lds + L::K1_KR) + kvl * RS;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) *(bf16x8*)(kr1 + 16 * ks + 8 * g) = kf[ks];
+    }
     __syncthreads();
     // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
     const bool short_item = nsteps <= CLAIM_AHEAD;
@@ -587,10 +660,18 @@ void bwd_kv_kernel(BwdParams p) {
       if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(qs_first + it + 1);
       compute_step(it, qs_first + it, -1);
+      if (one_k) {
+        __syncthreads();
+        dq_step(qs_first + it);
+      }
       store_step((it + 1) & 1, qs_first + it + 1, true);
       __syncthreads();
     }
     if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1, -1);
+    if (one_k && nsteps > 0) {
+      __syncthreads();
+      dq_step(qs_end - 1);
+    }
     if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);

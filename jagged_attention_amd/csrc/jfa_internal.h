@@ -43,7 +43,7 @@ struct TileCfg {
   int slots;           // split slots (<=0: no split)
   int bq_bm, bq_bn;    // q-stationary backward
   int bk_bn, bk_bm;    // kv-stationary backward
-  int fuse;            // single-pass backward classes
+  int fuse;            // single-pass backward classes: bit 0 one query tile, bit 1 one key tile
   int fwd_nw, bq_nw, bk_nw;   // waves per workgroup of the three MFMA kernels
 };
 

@@ -341,8 +341,8 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   }
 
   // ================= q-stationary backward list =================
-  auto one_q = [&](int b) { return tc.fuse && cdiv(qlen(b), tc.bq_bm) == 1; };
-  auto one_k = [&](int b) { return tc.fuse && !one_q(b) && cdiv(klen(b), tc.bk_bn) == 1; };
+  auto one_q = [&](int b) { return (tc.fuse & 1) && cdiv(qlen(b), tc.bq_bm) == 1; };
+  auto one_k = [&](int b) { return (tc.fuse & 2) && !one_q(b) && cdiv(klen(b), tc.bk_bn) == 1; };
   int64_t nq = 0, nk = 0;
   if (want_q && !overflow) {
     nq = scan_to(s_base, B, [&](int64_t b) { return one_k((int)b) ? 0 : cdiv(qlen((int)b), tc.bq_bm); },

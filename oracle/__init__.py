@@ -185,8 +185,11 @@ def case_backward(case, **kw):
 # ------------------------------------------------------------- tile lists
 
 def schedule(q_offsets, kv_offsets, heads: int, causal: bool, *, bm: int, bn: int, slots: int,
-             bq_bm: int, bq_bn: int, bk_bn: int, bk_bm: int, fuse: bool = True) -> dict:
-    """Forward / combine / backward tile lists (see ``ora_schedule`` in the C source)."""
+             bq_bm: int, bq_bn: int, bk_bn: int, bk_bm: int, fuse: int = 3) -> dict:
+    """Forward / combine / backward tile lists (see ``ora_schedule`` in the C source).
+
+    fuse: single-pass backward classes, bit 0 for samples with one query tile, bit 1 for
+    samples with one key tile (True means both)."""
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
     ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
     B = qo.shape[0] - 1
@@ -200,7 +203,8 @@ def schedule(q_offsets, kv_offsets, heads: int, causal: bool, *, bm: int, bn: in
     bq = np.zeros((cap, 4), np.int32)
     bk = np.zeros((cap, 4), np.int32)
     counts = np.zeros(5, np.int64)
-    sp = _SchedParams(bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, int(bool(fuse)))
+    fuse = 3 if fuse is True else int(fuse)
+    sp = _SchedParams(bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse)
     rc = lib().ora_schedule(_ptr(qo), _ptr(ko), B, heads, int(bool(causal)), ctypes.byref(sp),
                             _ptr(fwd), _ptr(fslot), _ptr(comb), _ptr(bq), _ptr(bk), cap,
                             _ptr(counts))

@@ -302,7 +302,8 @@ typedef struct {
   int32_t slots;         /* >0: split long forward tiles for this many concurrent workers; <=0: never */
   int32_t bq_bm, bq_bn;  /* query-stationary backward: query rows per tile, key rows per step */
   int32_t bk_bn, bk_bm;  /* key-stationary backward: key rows per tile, query rows per step */
-  int32_t fuse;          /* 1: samples with one query tile (or one key tile) take a single backward pass */
+  int32_t fuse;          /* single backward pass: bit 0 for samples with one query tile, bit 1 for
+                            samples with one key tile (and not one query tile) */
 } ora_sched_params;
 
 typedef struct { int32_t b, t, lo, hi; } ora_rec;
@@ -421,8 +422,8 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
     const int64_t n = qo[b + 1] - qo[b], m = ko[b + 1] - ko[b];
     const int64_t nqt = ceil_div64(n, sp->bq_bm);    /* query tiles of the q-stationary pass */
     const int64_t nkt = ceil_div64(m, sp->bk_bn);    /* key tiles of the kv-stationary pass */
-    const int one_q = sp->fuse && nqt == 1;
-    const int one_k = sp->fuse && !one_q && nkt == 1;
+    const int one_q = (sp->fuse & 1) && nqt == 1;
+    const int one_k = (sp->fuse & 2) && !one_q && nkt == 1;
     if (!one_k) {            /* q-stationary pass: every query tile */
       for (int64_t t = 0; t < nqt; ++t) {
         int64_t r1 = (t + 1) * sp->bq_bm < n ? (t + 1) * sp->bq_bm : n;

@@ -65,7 +65,7 @@ def test_schedule_bitexact(dtype, bi, slots):
     got = jfa.build_schedule(p, qo, ko)
     want = oracle.schedule(oracle.offsets(ql), oracle.offsets(kl), H, causal, bm=tc["bm"],
                            bn=tc["bn"], slots=tc["slots"], bq_bm=tc["bq_bm"], bq_bn=tc["bq_bn"],
-                           bk_bn=tc["bk_bn"], bk_bm=tc["bk_bm"], fuse=bool(tc["fuse"]))
+                           bk_bn=tc["bk_bn"], bk_bm=tc["bk_bm"], fuse=int(tc["fuse"]))
     assert got["status"] == 0
     assert np.array_equal(got["fwd"].numpy(), want["fwd"])
     assert np.array_equal(got["fwd_slot"].numpy(), want["fwd_slot"])
@@ -88,7 +88,7 @@ def test_schedule_large_list_global_sort():
                              torch.as_tensor(off.astype(np.int32)).cuda())
     want = oracle.schedule(off, off, 2, True, bm=tc["bm"], bn=tc["bn"], slots=tc["slots"],
                            bq_bm=tc["bq_bm"], bq_bn=tc["bq_bn"], bk_bn=tc["bk_bn"],
-                           bk_bm=tc["bk_bm"], fuse=bool(tc["fuse"]))
+                           bk_bm=tc["bk_bm"], fuse=int(tc["fuse"]))
     assert len(want["fwd"]) > 8192
     assert np.array_equal(got["fwd"].numpy(), want["fwd"])
     assert np.array_equal(got["bwd_kv"].numpy(), want["bwd_kv"])
