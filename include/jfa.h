@@ -84,7 +84,8 @@ typedef struct {
   int32_t split_slots;      /* forward tail balancing: 0 = auto (concurrent workgroups of the
                                device), >0 = this many, <0 = never split a query tile */
   int32_t bwd_fuse;         /* -1 default (on where built), 0 off: single-pass backward for
-                               samples with one key tile (d = 64) */
+                               samples with one query tile (64-row query tiles) or one key
+                               tile (d = 64) */
 } jfa_problem;
 
 /*

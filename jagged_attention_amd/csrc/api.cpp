@@ -90,10 +90,11 @@ jfa_status tile_cfg(const jfa_problem& p, TileCfg* t) {
   t->bk_nw = (short_kv || (p.bias_kind == JFA_BIAS_DENSE && p.head_dim == 128)) ? 2 : 4;
   t->bk_bn = 32 * t->bk_nw;
   t->bk_bm = BK_BM;
-  // single-pass backward classes (bit 1: a sample with one key tile runs only the
-  // key-stationary pass, which then also writes dQ; built at d = 64.  Bit 0, a sample with one
-  // query tile, is not built)
-  t->fuse = (p.bwd_fuse != 0 && p.head_dim == 64) ? 2 : 0;
+  // single-pass backward classes: bit 0, a sample with one query tile runs only the
+  // query-stationary pass, which then also writes dK and dV (built for 64-row query tiles);
+  // bit 1, a sample with one key tile runs only the key-stationary pass, which then also writes
+  // dQ (built at d = 64)
+  t->fuse = p.bwd_fuse == 0 ? 0 : ((t->bq_nw == 2 ? 1 : 0) | (p.head_dim == 64 ? 2 : 0));
   return JFA_OK;
 }
 

@@ -705,7 +705,16 @@ struct QLds {
   // a stage also holds the epilogue's dQ rows (one staging area per wave)
   static constexpr int STAGE = align16(BO + BIAS_BYTES) > NW * out_stage_bytes<D>()
                                    ? align16(BO + BIAS_BYTES) : NW * out_stage_bytes<D>();
-  static constexpr int TOTAL = 2 * STAGE;
+  // single pass for a sample with one query tile (built for 64-row tiles): the item's Q and dO
+  // rows and each step's P and dS [query][key], from which wave w computes the step's dV, dK
+  // rows of keys 32w .. 32w + 31
+  static constexpr bool Q1 = NW == 2;
+  static constexpr int PS = STEP + 8;                     // P / dS tile row stride (bf16)
+  static constexpr int Q1_QR = 2 * STAGE;
+  static constexpr int Q1_DR = Q1_QR + BM * RS * 2;
+  static constexpr int Q1_P = Q1_DR + BM * RS * 2;
+  static constexpr int Q1_DS = Q1_P + BM * PS * 2;
+  static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 : 0);
 };
 
 template <int D, int NW, int MODE, int BIAS>
@@ -746,6 +755,8 @@ void bwd_q_kernel(BwdParams p) {
     const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
     const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
     const int64_t boff = item_boff(dsc);
+    // single-pass class (the scheduler's test): the sample's queries fit one tile
+    const bool one_q = L::Q1 && (p.fuse & 1) && n > 0 && n <= BM;
     const int delta = m - n;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int q0 = t * BM, qw0 = q0 + wave * 32;
@@ -830,7 +841,20 @@ void bwd_q_kernel(BwdParams p) {
     auto compute_step = [&](int it) {
       const int j0 = it * STEP;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
-      if (!wave_rows || j0 >= wave_kend) return;
+      if (!wave_rows || j0 >= wave_kend) {
+        if (L::Q1 && one_q) {     // this wave's queries contribute nothing to this step's dK, dV
+          uint32_t* pq = reinterpret_cast<uint32_t*>(
+              reinterpret_cast<__bf16*>(lds + L::Q1_P) + qil * L::PS);
+          uint32_t* dq = reinterpret_cast<uint32_t*>(
+              reinterpret_cast<__bf16*>(lds + L::Q1_DS) + qil * L::PS);
+#pragma unroll
+          for (int i = 0; i < STEP / 2 / 2; ++i) {
+            pq[2 * i + g] = 0u;
+            dq[2 * i + g] = 0u;
+          }
+        }
+        return;
+      }
       const __bf16* kr = reinterpret_cast<const __bf16*>(sb + L::KR);
       const __bf16* vr = reinterpret_cast<const __bf16*>(sb + L::VR);
       // element (blk, i): key j0 + blk*32 + 8(i/4) + 4g + i%4, query qi
@@ -882,12 +906,12 @@ void bwd_q_kernel(BwdParams p) {
                              (qw0 + 32 > n);
       const int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
       const int lim = kend - j0 - 4 * g;
-      uint32_t dd[2][8];
+      uint32_t dd[2][8], pq2[2][8];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          float d2[2];
+          float d2[2], p2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int ii = i + e;
@@ -896,13 +920,16 @@ void bwd_q_kernel(BwdParams p) {
             if constexpr (MODE == MODE_SOFTMAX) {
               const float pr = valid ? fast_exp2(x - lse2) : 0.f;
               d2[e] = pr * (pacc[blk][ii] - dlt);
+              p2[e] = pr;
             } else {
               float a, da;
               act_pair<MODE>(x, a, da);
               d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
+              p2[e] = valid ? a * wn : 0.f;
             }
           }
           dd[blk][i >> 1] = pack2bf(d2[0], d2[1]);
+          pq2[blk][i >> 1] = pack2bf(p2[0], p2[1]);
         }
       // dQ^T += K^T dS^T; chunk c covers keys 16c + 8(e/4) + 4g + e%4
 
@@ -921,6 +948,64 @@ void bwd_q_kernel(BwdParams p) {
           acc[db] = mfma_bf16(ka, db8, acc[db]);
         }
       }
+      if (L::Q1 && one_q) {
+        // P and dS [query][key] of this step: pair p of block blk holds keys k, k + 1 with
+        // k = 32 blk + 8(p/2) + 4g + 2(p%2)
+        __bf16* pr = reinterpret_cast<__bf16*>(lds + L::Q1_P) + qil * L::PS;
+        __bf16* dr = reinterpret_cast<__bf16*>(lds + L::Q1_DS) + qil * L::PS;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int pi = 0; pi < 8; ++pi) {
+            const int k = 32 * blk + 8 * (pi >> 1) + 4 * g + 2 * (pi & 1);
+            *(uint32_t*)(pr + k) = pq2[blk][pi];
+            *(uint32_t*)(dr + k) = dd[blk][pi];
+          }
+      }
+    };
+
+    // dK, dV of a key step of a one-query-tile sample: dV^T = dO^T P and dK^T = scale Q^T dS
+    // over the tile's queries, operands read with transposing LDS reads in natural query order
+    // (k = 8g + j <-> query 16 kc + 8g + j).  Wave w owns keys 32w .. 32w + 31 of the step and
+    // writes their rows through its staging area in the step's (now idle) LDS stage.
+    auto dkdv_step = [&](int kt) {
+      if constexpr (L::Q1) {
+        const __bf16* qr1 = reinterpret_cast<const __bf16*>(lds + L::Q1_QR);
+        const __bf16* dr1 = reinterpret_cast<const __bf16*>(lds + L::Q1_DR);
+        const __bf16* pt = reinterpret_cast<const __bf16*>(lds + L::Q1_P);
+        const __bf16* st = reinterpret_cast<const __bf16*>(lds + L::Q1_DS);
+        const int trq = (8 * (lane >> 5) + ((lane & 15) >> 2)) * RS + 16 * ((lane >> 4) & 1) +
+                        4 * (lane & 3);
+        const int trp = (8 * (lane >> 5) + ((lane & 15) >> 2)) * L::PS +
+                        16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        __bf16* ost = reinterpret_cast<__bf16*>(lds + (kt & 1) * L::STAGE +
+                                                wave * out_stage_bytes<D>());
+        const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
+        const uint32_t row0 = (uint32_t)(kt * STEP + 32 * wave) * row_bytes;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {       // 0: dV = P^T dO, 1: dK = s dS^T Q
+          const __bf16* xa = which ? qr1 : dr1;
+          const __bf16* xb = which ? st : pt;
+          f32x16 o[D / 32];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < BM / 16; ++kc) {
+              const __bf16* pa = xa + trq + 16 * kc * RS + db * 32;
+              const __bf16* pb = xb + trp + 16 * kc * L::PS + 32 * wave;
+              const u32x2 a0 = lds_read_tr16(pa), a1 = lds_read_tr16(pa + 4 * RS);
+              const u32x2 b0 = lds_read_tr16(pb), b1 = lds_read_tr16(pb + 4 * L::PS);
+              o[db] = mfma_bf16(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}),
+                                as_bf16x8(u32x4{b0[0], b0[1], b1[0], b1[1]}), o[db]);
+            }
+          }
+          const rsrc_t r = make_rsrc((__bf16*)(which ? p.dk : p.dv) + ((int64_t)ko * H + h) * D,
+                                     kv_bytes);
+          store_rows_via_lds<D>(o, which ? p.scale : 1.0f, ost, r, row0, row_bytes, lane);
+        }
+      }
     };
 
     if (steps > 0) {
@@ -929,6 +1014,17 @@ void bwd_q_kernel(BwdParams p) {
     }
     // the query fragments (loaded with the first tiles) are complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (L::Q1 && one_q) {
+      // the tile's Q and dO rows for the dK / dV steps: lane (query, g) holds head dims
+      // 16 ks + 8g + 0..7
+      __bf16* q1 = reinterpret_cast<__bf16*>(lds + L::Q1_QR) + qil * RS;
+      __bf16* d1 = reinterpret_cast<__bf16*>(lds + L::Q1_DR) + qil * RS;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        *(bf16x8*)(q1 + 16 * ks + 8 * g) = qf[ks];
+        *(bf16x8*)(d1 + 16 * ks + 8 * g) = dof[ks];
+      }
+    }
     __syncthreads();
     // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
     const bool short_item = steps <= CLAIM_AHEAD;
@@ -940,10 +1036,18 @@ void bwd_q_kernel(BwdParams p) {
       if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(it + 1);
       compute_step(it);
+      if (one_q) {
+        __syncthreads();
+        dkdv_step(it);
+      }
       store_step((it + 1) & 1, it + 1);
       __syncthreads();
     }
     if (steps > 0) compute_step(steps - 1);
+    if (one_q && steps > 0) {
+      __syncthreads();
+      dkdv_step(steps - 1);
+    }
     if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
