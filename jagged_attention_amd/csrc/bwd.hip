@@ -890,64 +890,93 @@ void bwd_q_kernel(BwdParams p) {
           for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
       }
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
-        const int krow = blk * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(kr + krow * RS + 16 * ks + 8 * g));
-          sacc[blk] = mfma_bf16(ka, qf[ks], sacc[blk]);
-          const bf16x8 va = as_bf16x8(*(const u32x4*)(vr + krow * RS + 16 * ks + 8 * g));
-          pacc[blk] = mfma_bf16(va, dof[ks], pacc[blk]);
-        }
-      }
       const bool need_mask = (j0 + STEP > m) || (p.causal && j0 + STEP - 1 > qw0 + delta) ||
                              (qw0 + 32 > n);
       const int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
       const int lim = kend - j0 - 4 * g;
       uint32_t dd[2][8], pq2[2][8];
+      // B(blk) pair pi: dS and P of elements 2 pi, 2 pi + 1 of block blk
+      auto valu_b = [&](int blk, int pi) {
+        float d2[2], p2[2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          float d2[2], p2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int ii = i + e;
-            const bool valid = !need_mask || (blk * 32 + 8 * (ii >> 2) + (ii & 3) < lim);
-            const float x = sacc[blk][ii] * c_log;
-            if constexpr (MODE == MODE_SOFTMAX) {
-              const float pr = valid ? fast_exp2(x - lse2) : 0.f;
-              d2[e] = pr * (pacc[blk][ii] - dlt);
-              p2[e] = pr;
-            } else {
-              float a, da;
-              act_pair<MODE>(x, a, da);
-              d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
-              p2[e] = valid ? a * wn : 0.f;
-            }
+        for (int e = 0; e < 2; ++e) {
+          const int ii = 2 * pi + e;
+          const bool valid = !need_mask || (blk * 32 + 8 * (ii >> 2) + (ii & 3) < lim);
+          const float x = sacc[blk][ii] * c_log;
+          if constexpr (MODE == MODE_SOFTMAX) {
+            const float pr = valid ? fast_exp2(x - lse2) : 0.f;
+            d2[e] = pr * (pacc[blk][ii] - dlt);
+            p2[e] = pr;
+          } else {
+            float a, da;
+            act_pair<MODE>(x, a, da);
+            d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
+            p2[e] = valid ? a * wn : 0.f;
           }
-          dd[blk][i >> 1] = pack2bf(d2[0], d2[1]);
-          pq2[blk][i >> 1] = pack2bf(p2[0], p2[1]);
         }
-      // dQ^T += K^T dS^T; chunk c covers keys 16c + 8(e/4) + 4g + e%4
+        dd[blk][pi] = pack2bf(d2[0], d2[1]);
+        pq2[blk][pi] = pack2bf(p2[0], p2[1]);
+      };
 
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      // One key step, software-pipelined by hand, as a stream of MFMAs:
+      //   A(blk), blk = 0, 1: S^T and dP^T of keys 32 blk .. 32 blk + 31   (NA MFMAs each)
+      //   C: dQ^T += K^T dS^T, key chunk c = 0..3 (chunks 0, 1 use block 0, chunks 2, 3 block 1)
+      // in the order A(0) A(1) C.  Each MFMA's LDS operand is read PF MFMAs ahead; the VALU work
+      // B(0) (dS, P of block 0) runs under A(1) and B(1) under the first half of C, so the matrix
+      // cores keep busy in this one-wave-per-SIMD kernel.
+      constexpr int NA = D / 8;          // 16 at d = 128, 8 at d = 64
+      constexpr int NCB = D / 32;        // dQ MFMAs per key chunk
+      constexpr int NS = 2 * NA + 4 * NCB;
+      constexpr int PF = 6;
+      constexpr int RING = 8;
+      auto opnd = [&](int st) -> u32x4 {
+        if (st < 2 * NA) {
+          const int blk = st / NA, jj = st % NA, ks = jj >> 1;
+          const __bf16* base = (jj & 1) ? vr : kr;
+          return *(const u32x4*)(base + (blk * 32 + l32) * RS + 16 * ks + 8 * g);
+        }
+        // K^T rows = head dims, k = 8g + j <-> key 16c + 8(j/4) + 4g + j%4: two column strips
+        // of 4 keys of the K rows
+        const int c = (st - 2 * NA) / NCB, db = (st - 2 * NA) % NCB;
+        const __bf16* pk = kr + tr_lane + 16 * c * RS + db * 32;
+        const u32x2 lo = lds_read_tr16(pk), hi = lds_read_tr16(pk + 8 * RS);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      auto mfma_s = [&](int st, u32x4 o) {
+        const bf16x8 a = as_bf16x8(o);
+        if (st < 2 * NA) {
+          const int blk = st / NA, jj = st % NA, ks = jj >> 1;
+          if (jj & 1) pacc[blk] = mfma_bf16(a, dof[ks], pacc[blk]);
+          else sacc[blk] = mfma_bf16(a, qf[ks], sacc[blk]);
+          return;
+        }
+        // chunk c covers keys 16c + 8(e/4) + 4g + e%4: elements 8(c%2) .. 8(c%2) + 7 of block c/2
+        const int c = (st - 2 * NA) / NCB, db = (st - 2 * NA) % NCB;
         const u32x4 dw = {dd[c >> 1][4 * (c & 1)], dd[c >> 1][4 * (c & 1) + 1],
                           dd[c >> 1][4 * (c & 1) + 2], dd[c >> 1][4 * (c & 1) + 3]};
-        const bf16x8 db8 = as_bf16x8(dw);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          // K^T rows = head dims, k = 8g + j <-> key 16c + 8(j/4) + 4g + j%4: two column
-          // strips of 4 keys of the K rows
-          const __bf16* pk = kr + tr_lane + 16 * c * RS + db * 32;
-          const u32x2 lo = lds_read_tr16(pk), hi = lds_read_tr16(pk + 8 * RS);
-          const bf16x8 ka = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          acc[db] = mfma_bf16(ka, db8, acc[db]);
+        acc[db] = mfma_bf16(a, as_bf16x8(dw), acc[db]);
+      };
+      u32x4 ring[RING];
+      static_for<0, PF>([&](auto sc) { ring[decltype(sc)::value] = opnd(decltype(sc)::value); });
+      static_for<0, NS>([&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        if constexpr (st + PF < NS) ring[(st + PF) % RING] = opnd(st + PF);
+        mfma_s(st, ring[st % RING]);
+        if constexpr (st >= NA && st < 2 * NA) {          // B(0) under A(1)
+          static_for<(st - NA) * 8 / NA, (st - NA + 1) * 8 / NA>([&](auto pc) {
+            valu_b(0, decltype(pc)::value);
+          });
         }
-      }
+        if constexpr (st >= 2 * NA && st < 2 * NA + 2 * NCB) {   // B(1) under C(0)
+          static_for<(st - 2 * NA) * 8 / (2 * NCB), (st - 2 * NA + 1) * 8 / (2 * NCB)>([&](auto pc) {
+            valu_b(1, decltype(pc)::value);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
       if (L::Q1 && one_q) {
         // P and dS [query][key] of this step: pair p of block blk holds keys k, k + 1 with
         // k = 32 blk + 8(p/2) + 4g + 2(p%2)
