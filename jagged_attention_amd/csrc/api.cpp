@@ -297,6 +297,7 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
 
   SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
   a.lists = 1;
+  a.parallel = 1;
   hipError_t e = launch_schedule(a, s);
   if (e != hipSuccess) return JFA_ERR_LAUNCH;
 
@@ -355,6 +356,16 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
 
   SchedArgs a = sched_args(*p, tc, L, ws, q_offsets, kv_offsets);
   a.lists = 6;
+  a.parallel = 1;
+  if (p->mode == JFA_MODE_SOFTMAX && p->total_q > 0) {
+    // D = rowsum(dO * O) runs on the workgroups the two list builders leave idle
+    a.d_o = o;
+    a.d_dout = dout;
+    a.d_delta = (float*)(ws + L.delta);
+    a.d_head_dim = p->head_dim;
+    a.d_esize = p->dtype == JFA_F32 ? 4 : 2;
+    a.delta_blocks = std::max(1, cu - 2);
+  }
   hipError_t e = launch_schedule(a, s);
   if (e != hipSuccess) return JFA_ERR_LAUNCH;
 
@@ -436,8 +447,11 @@ jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* 
   if (!workspace || !status_out) return JFA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (hipStreamSynchronize(s) != hipSuccess) return JFA_ERR_LAUNCH;
-  int32_t v = 0;
-  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return JFA_ERR_LAUNCH;
+  WsHeader h;
+  if (hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return JFA_ERR_LAUNCH;
+  // the offsets check, then the per-list capacity checks
+  int32_t v = h.status;
+  for (int i = 0; i < 3 && v == JFA_OK; ++i) v = h.list_status[i];
   *status_out = v;
   return JFA_OK;
 }

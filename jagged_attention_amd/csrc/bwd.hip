@@ -35,42 +35,6 @@ constexpr int TS = STEP + 8;   // stride (bf16) of a transposed tile row
 
 constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 
-// ------------------------------------------------------------------ preprocess
-// delta[h][i] = sum_c dO[i,h,c] * O[i,h,c]; LPR lanes read one (row, head) 16 bytes at a time.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
-                                                    const T* __restrict__ dout, float* delta,
-                                                    int64_t total_q, int H) {
-  constexpr int EPL = 16 / sizeof(T);            // elements per 16-byte load
-  constexpr int LPR = D / EPL;                   // lanes per (row, head)
-  constexpr int RPB = 256 / LPR;                 // (row, head) pairs per block
-  const int sub = threadIdx.x % LPR;
-  const int64_t rh = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const bool ok = rh < total_q * H;
-  float s = 0.f;
-  if (ok) {
-    const u32x4 a = *(const u32x4*)(o + rh * D + sub * EPL);
-    const u32x4 c = *(const u32x4*)(dout + rh * D + sub * EPL);
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
-        s += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(c[e] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s += __uint_as_float(a[e]) * __uint_as_float(c[e]);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (ok && sub == 0) {
-    const int64_t i = rh / H;
-    const int h = (int)(rh % H);
-    delta[(int64_t)h * total_q + i] = s;
-  }
-}
-
 // --------------------------------------------------------------- tile staging
 // A STEP x D bf16 tile is moved as blocks of 4 rows x 8 dims (one 16-byte load per row).
 // Block id -> (row block rb, dim block cb): within each 16 ids, 4 row blocks x 4 dim blocks,
@@ -1132,19 +1096,7 @@ hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64
 template <int D, int MODE>
 hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                    hipStream_t s) {
-  if (MODE == MODE_SOFTMAX) {
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t pairs = p.total_q * p.H;
-    if (pairs > 0) {
-      timing_begin("jfa_bwd_delta", s);
-      hipLaunchKernelGGL((delta_kernel<__bf16, D>), dim3((unsigned)((pairs + RPB - 1) / RPB)),
-                         dim3(256), 0, s, (const __bf16*)p.o, (const __bf16*)p.dout, p.delta,
-                         p.total_q, p.H);
-      timing_end(s);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
+  // D (softmax) was computed by the scheduler launch
   switch (p.bias_kind) {
     case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS>(p, tc, mq, mk, cu, s);
     case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE>(p, tc, mq, mk, cu, s);

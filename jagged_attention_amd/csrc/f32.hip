@@ -111,16 +111,6 @@ __device__ __forceinline__ float bias_at_b(const BwdParams& p, int64_t bias_base
   return 0.f;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void delta_f32_kernel(const float* o, const float* dout,
-                                                        float* delta, int64_t total_q, int H) {
-  const int64_t rh = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (rh >= total_q * H) return;
-  float s = 0.f;
-  for (int c = 0; c < D; ++c) s = fmaf(o[rh * D + c], dout[rh * D + c], s);
-  delta[(int64_t)(rh % H) * total_q + rh / H] = s;
-}
-
 // dQ: one thread per query row, keys in steps of 64.
 template <int D, int MODE>
 __global__ __launch_bounds__(NT) void bwd_q_f32_kernel(BwdParams p) {
@@ -292,15 +282,7 @@ hipError_t run_fwd32(const FwdParams& p, int64_t max_items, int cu, hipStream_t 
 
 template <int D, int MODE>
 hipError_t run_bwd32(const BwdParams& p, int64_t mq, int64_t mk, int cu, hipStream_t s) {
-  if (MODE == MODE_SOFTMAX && p.total_q * p.H > 0) {
-    timing_begin("jfa_bwd_delta_f32", s);
-    hipLaunchKernelGGL((delta_f32_kernel<D>), dim3((unsigned)((p.total_q * p.H + 255) / 256)),
-                       dim3(256), 0, s, (const float*)p.o, (const float*)p.dout, p.delta,
-                       p.total_q, p.H);
-    timing_end(s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // D (softmax) was computed by the scheduler launch
   {
     auto kern = bwd_kv_f32_kernel<D, MODE>;
     int grid = resident_grid((const void*)kern, NT, 0, cu);

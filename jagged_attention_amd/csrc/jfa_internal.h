@@ -29,7 +29,9 @@ struct WsHeader {
   int32_t status;      // JFA_OK or JFA_ERR_DEVICE_DATA
   int32_t counts[8];   // forward, combine, q-stationary, kv-stationary records, threshold, slots
   uint32_t tickets[8]; // work counters for persistent kernels, zeroed by the scheduler
-  int32_t pad[64 - 17];
+  int32_t list_status[4]; // per list (forward, q-stationary, kv-stationary): JFA_OK, or
+                          // JFA_ERR_DEVICE_DATA when the list did not fit its capacity
+  int32_t pad[64 - 21];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -98,6 +100,15 @@ struct SchedArgs {
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
   int32_t* counts_copy; // optional: counts also written here (test hook)
   uint32_t* xtk;        // per-XCD work counters of the persistent kernels (zeroed here)
+  int32_t parallel;     // 1: one workgroup per requested list; 0: one workgroup builds them all
+  // softmax backward preprocess D = rowsum(dO * O), run by the workgroups after the list
+  // builders (delta_blocks of them; 0 = none)
+  const void* d_o;
+  const void* d_dout;
+  float* d_delta;       // [H][total_q]
+  int32_t delta_blocks;
+  int32_t d_head_dim;
+  int32_t d_esize;      // bytes per element of O / dO (2 bf16, 4 fp32)
 };
 
 // ----------------------------------------------------- kernel parameters

@@ -19,6 +19,8 @@
 namespace jfa {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int ST = 1024;
 constexpr int SW = ST / 64;
 constexpr int LDS_SORT_MAX = 8192;
@@ -133,6 +135,46 @@ __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t*
   // three passes: a -> b -> a -> b
 }
 
+// Stable counting sort of n <= ST records by cost descending (ties in index order), for costs
+// in [1, kmax] with kmax * SW <= 16 * ST: the rank of record i is the number of records of
+// higher cost, plus those of equal cost in earlier waves, plus those of equal cost on lower
+// lanes of its own wave (found by matching the key bits with ballots).  A handful of barriers,
+// where a bitonic sort of the same list needs one per merge phase.  out[rank] = i.
+__device__ void count_sort(const int32_t* t_cost, int n, int kmax, uint32_t* out, int32_t* T,
+                           int64_t* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nent = kmax * SW;                 // counters [key][wave], key = kmax - cost
+  for (int i = tid; i < nent; i += ST) T[i] = 0;
+  const bool act = tid < n;
+  const int key = act ? kmax - t_cost[tid] : 0;
+  uint64_t same = __ballot(act);
+  for (int bit = 0; (1 << bit) < kmax; ++bit) {
+    const uint64_t bal = __ballot(act && ((key >> bit) & 1));
+    same &= ((key >> bit) & 1) ? bal : ~bal;
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int r = __popcll(same & below);
+  const int cnt = __popcll(same);
+  __syncthreads();
+  if (act && r == cnt - 1) T[key * SW + wave] = cnt;
+  __syncthreads();
+  // exclusive scan of the counters in (key, wave) order: EPT contiguous entries per thread
+  const int ept = (nent + ST - 1) / ST;
+  const int lo = min(nent, tid * ept), hi = min(nent, lo + ept);
+  int64_t part = 0;
+  for (int i = lo; i < hi; ++i) part += T[i];
+  int64_t tot;
+  int64_t run = block_scan(part, &tot, red);
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = T[i];
+    T[i] = (int32_t)run;
+    run += c;
+  }
+  __syncthreads();
+  if (act) out[T[key * SW + wave] + r] = (uint32_t)tid;
+  __syncthreads();
+}
+
 // Sample offsets are copied to LDS when B is at most this (every tile looks its sample up).
 constexpr int LDS_OFF_MAX = 4095;
 
@@ -155,7 +197,20 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
                               int4* out, int32_t* out_slot, ItemRec* items, const int32_t* qo,
                               const int32_t* ko) {
   const uint32_t* sorted;
-  if (n <= BITONIC_MAX) {
+  int kmax = 0;
+  if (n <= ST) {
+    int c = threadIdx.x < n ? t_cost[threadIdx.x] : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
+    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = c;
+    __syncthreads();
+    for (int w = 0; w < SW; ++w) kmax = max(kmax, (int)sh.red[w]);
+    __syncthreads();
+  }
+  if (n <= ST && kmax * SW <= 16 * ST) {
+    count_sort(t_cost, n, max(kmax, 1), sh.sa, sh.T, sh.red);
+    sorted = sh.sa;
+  } else if (n <= BITONIC_MAX) {
     int N = 1;
     while (N < n) N <<= 1;
     for (int i = threadIdx.x; i < N; i += ST)
@@ -219,12 +274,90 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
   __syncthreads();
 }
 
+// D[h][i] = sum_c dO[i,h,c] * O[i,h,c] for every (query row, head): the softmax backward's
+// preprocess, run by the workgroups of the scheduler launch that build no list, so that it
+// overlaps the single-workgroup list building.  Each (row, head) vector is LPR consecutive
+// lanes with one 16-byte load each of O and dO; lanes combine with xor shuffles.
+template <int ES, int D>
+__device__ void delta_rows(const SchedArgs& a, int block, int nblocks) {
+  constexpr int EPL = 16 / ES;                    // elements per 16-byte load
+  constexpr int LPR = D / EPL;                    // lanes per (row, head) vector
+  constexpr int U = 4;                            // vectors in flight per thread
+  const int64_t nchunks = a.total_q * a.H * LPR;
+  const int64_t stride = (int64_t)nblocks * ST;
+  const uint8_t* o = (const uint8_t*)a.d_o;
+  const uint8_t* g = (const uint8_t*)a.d_dout;
+  for (int64_t base = (int64_t)block * ST + threadIdx.x; base < nchunks; base += U * stride) {
+    u32x4 x[U], y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * stride;
+      if (c < nchunks) {
+        x[u] = *(const u32x4*)(o + c * 16);
+        y[u] = *(const u32x4*)(g + c * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * stride;
+      float acc = 0.f;
+      if (c < nchunks) {
+        if constexpr (ES == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(x[u][e] << 16), __uint_as_float(y[u][e] << 16), acc);
+            acc = fmaf(__uint_as_float(x[u][e] & 0xffff0000u),
+                       __uint_as_float(y[u][e] & 0xffff0000u), acc);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = fmaf(__uint_as_float(x[u][e]), __uint_as_float(y[u][e]), acc);
+        }
+      }
+      // the LPR lanes of a vector are aligned and share c / LPR, so the whole group is either
+      // in range or out of it
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (c < nchunks && (threadIdx.x % LPR) == 0) {   // c and the lane agree mod LPR
+        const int64_t rh = c / LPR;
+        a.d_delta[(rh % a.H) * a.total_q + rh / a.H] = acc;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
   const int tid = threadIdx.x;
   const int B = a.B;
   const TileCfg tc = a.tc;
+
+  // roles: with a.parallel, workgroup r builds the r-th requested list; otherwise workgroup 0
+  // builds them all.  Workgroups past the list builders compute D.
+  const int nroles = a.parallel ? __popc(a.lists & 7) : 1;
+  if ((int)blockIdx.x >= nroles) {
+    const int blk = blockIdx.x - nroles, nblk = gridDim.x - nroles;
+    if (a.d_esize == 2) {
+      if (a.d_head_dim == 128) delta_rows<2, 128>(a, blk, nblk);
+      else delta_rows<2, 64>(a, blk, nblk);
+    } else {
+      if (a.d_head_dim == 128) delta_rows<4, 128>(a, blk, nblk);
+      else delta_rows<4, 64>(a, blk, nblk);
+    }
+    return;
+  }
+  const int role = blockIdx.x;
+  int my_lists = a.lists & 7;
+  if (a.parallel) {
+    int k = role;
+    for (int bit = 0; bit < 3; ++bit)
+      if ((a.lists >> bit) & 1) {
+        if (k == 0) { my_lists = 1 << bit; break; }
+        --k;
+      }
+  }
 
   // ---- validation of the offsets (and the sort's cost limit)
   if (tid == 0) sh.flag = 0;
@@ -245,10 +378,12 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (bad) atomicOr(&sh.flag, 1);
   __syncthreads();
   if (sh.flag) {
+    // every role finds the same failure and writes the same values
     if (tid == 0) {
       a.hdr->status = JFA_ERR_DEVICE_DATA;
       for (int i = 0; i < 8; ++i) a.hdr->counts[i] = 0;
       for (int i = 0; i < 8; ++i) a.hdr->tickets[i] = 0;
+      for (int i = 0; i < 4; ++i) a.hdr->list_status[i] = JFA_OK;
       if (a.counts_copy) {
         for (int i = 0; i < 8; ++i) a.counts_copy[i] = 0;
         a.counts_copy[6] = JFA_ERR_DEVICE_DATA;
@@ -286,7 +421,7 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   int overflow = 0;
 
   // ================= forward list =================
-  const bool want_f = a.lists & 1, want_q = a.lists & 2, want_k = a.lists & 4;
+  const bool want_f = my_lists & 1, want_q = my_lists & 2, want_k = my_lists & 4;
   const int64_t ntiles =
       want_f ? scan_to(s_base, B, [&](int64_t b) { return cdiv(qlen((int)b), tc.bm); }, sh.red) : 0;
   if (ntiles > a.cap_t) overflow = 1;
@@ -398,16 +533,45 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
 
   if (tid == 0) {
     const int st = overflow ? JFA_ERR_DEVICE_DATA : JFA_OK;
-    a.hdr->status = st;
     const int32_t cnt[8] = {overflow ? 0 : (int32_t)nrec, overflow ? 0 : (int32_t)ncomb,
                             overflow ? 0 : (int32_t)nq, overflow ? 0 : (int32_t)nk, (int32_t)C,
                             overflow ? 0 : (int32_t)nslot, st, 0};
-    for (int i = 0; i < 8; ++i) a.hdr->counts[i] = cnt[i];
-    for (int i = 0; i < 8; ++i) a.hdr->tickets[i] = 0;
-    if (a.counts_copy)
-      for (int i = 0; i < 8; ++i) a.counts_copy[i] = cnt[i];
+    if (!a.parallel) {
+      a.hdr->status = st;
+      for (int i = 0; i < 8; ++i) a.hdr->counts[i] = cnt[i];
+      for (int i = 0; i < 4; ++i) a.hdr->list_status[i] = JFA_OK;
+      if (a.counts_copy)
+        for (int i = 0; i < 8; ++i) a.counts_copy[i] = cnt[i];
+    } else {
+      // the offsets are valid (every role checked them alike); a list that overflowed its
+      // capacity is left empty and flagged in its own status word
+      a.hdr->status = JFA_OK;
+      const int li = want_f ? 0 : (want_q ? 1 : 2);
+      a.hdr->list_status[li] = st;
+      if (want_f) {
+        a.hdr->counts[0] = cnt[0];
+        a.hdr->counts[1] = cnt[1];
+        a.hdr->counts[4] = cnt[4];
+        a.hdr->counts[5] = cnt[5];
+      }
+      if (want_q) a.hdr->counts[2] = cnt[2];
+      if (want_k) a.hdr->counts[3] = cnt[3];
+      if (role == 0) {
+        // words of the lists nobody builds in this call
+        if (!(a.lists & 1)) {
+          a.hdr->counts[0] = a.hdr->counts[1] = a.hdr->counts[4] = a.hdr->counts[5] = 0;
+          a.hdr->list_status[0] = JFA_OK;
+        }
+        if (!(a.lists & 2)) { a.hdr->counts[2] = 0; a.hdr->list_status[1] = JFA_OK; }
+        if (!(a.lists & 4)) { a.hdr->counts[3] = 0; a.hdr->list_status[2] = JFA_OK; }
+        a.hdr->list_status[3] = JFA_OK;
+        a.hdr->counts[6] = a.hdr->counts[7] = 0;
+      }
+    }
+    if (role == 0)
+      for (int i = 0; i < 8; ++i) a.hdr->tickets[i] = 0;
   }
-  if (a.xtk && tid < XTK_KINDS * XTK_XCDS) a.xtk[tid * XTK_STRIDE] = 0;
+  if (role == 0 && a.xtk && tid < XTK_KINDS * XTK_XCDS) a.xtk[tid * XTK_STRIDE] = 0;
 }
 
 // offsets[b+1] = offsets[b] + lengths[b], in int64 with an int32 range check.
@@ -452,8 +616,10 @@ hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  const int roles = a.parallel ? __builtin_popcount(a.lists & 7) : 1;
   timing_begin("jfa_schedule", s);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(ST), lds, s, a);
+  hipLaunchKernelGGL(schedule_kernel, dim3(roles + max(0, (int)a.delta_blocks)), dim3(ST), lds, s,
+                     a);
   timing_end(s);
   return hipGetLastError();
 }
