@@ -180,7 +180,7 @@ def traffic_for(kernel):
         return None
     from jagged_attention_amd.traffic import source_hash
     ent = rec.get("kernels", {}).get(kernel)
-    if not ent or rec.get("source_hash") != source_hash():
+    if not ent or ent.get("source_hash") != source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 

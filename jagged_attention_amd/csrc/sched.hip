@@ -135,30 +135,44 @@ __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t*
   // three passes: a -> b -> a -> b
 }
 
-// Stable counting sort of n <= ST records by cost descending (ties in index order), for costs
-// in [1, kmax] with kmax * SW <= 16 * ST: the rank of record i is the number of records of
-// higher cost, plus those of equal cost in earlier waves, plus those of equal cost on lower
-// lanes of its own wave (found by matching the key bits with ballots).  A handful of barriers,
-// where a bitonic sort of the same list needs one per merge phase.  out[rank] = i.
+// Stable counting sort of n <= CS_MAX records by cost descending (ties in index order), for
+// costs in [1, kmax] with kmax * ceil(n / 64) <= 16 * ST.  Records are taken in chunks of 64
+// (record i is lane i % 64 of chunk i / 64; a wave handles chunks wave, wave + SW, ...).  The
+// rank of record i is the number of records of higher cost, plus those of equal cost in
+// earlier chunks, plus those of equal cost on lower lanes of its own chunk (found by matching
+// the key bits with ballots).  A handful of barriers, where a bitonic sort of the same list
+// needs one per merge phase.  out[rank] = i.
+constexpr int CS_MAX = 4096;
 __device__ void count_sort(const int32_t* t_cost, int n, int kmax, uint32_t* out, int32_t* T,
                            int64_t* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nent = kmax * SW;                 // counters [key][wave], key = kmax - cost
+  constexpr int R = CS_MAX / ST;              // records per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nchunk = (n + 63) / 64;
+  const int nent = kmax * nchunk;             // counters [key][chunk], key = kmax - cost
   for (int i = tid; i < nent; i += ST) T[i] = 0;
-  const bool act = tid < n;
-  const int key = act ? kmax - t_cost[tid] : 0;
-  uint64_t same = __ballot(act);
-  for (int bit = 0; (1 << bit) < kmax; ++bit) {
-    const uint64_t bal = __ballot(act && ((key >> bit) & 1));
-    same &= ((key >> bit) & 1) ? bal : ~bal;
-  }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const int r = __popcll(same & below);
-  const int cnt = __popcll(same);
+  int key[R], r[R], cnt[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    const bool act = i < n;
+    key[k] = act ? kmax - t_cost[i] : 0;
+    uint64_t same = __ballot(act);
+    for (int bit = 0; (1 << bit) < kmax; ++bit) {
+      const uint64_t bal = __ballot(act && ((key[k] >> bit) & 1));
+      same &= ((key[k] >> bit) & 1) ? bal : ~bal;
+    }
+    r[k] = __popcll(same & below);
+    cnt[k] = act ? __popcll(same) : 0;
+  }
   __syncthreads();
-  if (act && r == cnt - 1) T[key * SW + wave] = cnt;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    if (i < n && r[k] == cnt[k] - 1) T[key[k] * nchunk + (i >> 6)] = cnt[k];
+  }
   __syncthreads();
-  // exclusive scan of the counters in (key, wave) order: EPT contiguous entries per thread
+  // exclusive scan of the counters in (key, chunk) order: EPT contiguous entries per thread
   const int ept = (nent + ST - 1) / ST;
   const int lo = min(nent, tid * ept), hi = min(nent, lo + ept);
   int64_t part = 0;
@@ -171,7 +185,11 @@ __device__ void count_sort(const int32_t* t_cost, int n, int kmax, uint32_t* out
     run += c;
   }
   __syncthreads();
-  if (act) out[T[key * SW + wave] + r] = (uint32_t)tid;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    if (i < n) out[T[key[k] * nchunk + (i >> 6)] + r[k]] = (uint32_t)i;
+  }
   __syncthreads();
 }
 
@@ -198,8 +216,9 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
                               const int32_t* ko) {
   const uint32_t* sorted;
   int kmax = 0;
-  if (n <= ST) {
-    int c = threadIdx.x < n ? t_cost[threadIdx.x] : 0;
+  if (n <= CS_MAX) {
+    int c = 0;
+    for (int i = threadIdx.x; i < n; i += ST) c = max(c, t_cost[i]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
     if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = c;
@@ -207,7 +226,7 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
     for (int w = 0; w < SW; ++w) kmax = max(kmax, (int)sh.red[w]);
     __syncthreads();
   }
-  if (n <= ST && kmax * SW <= 16 * ST) {
+  if (n <= CS_MAX && (int64_t)max(kmax, 1) * ((n + 63) / 64) <= 16 * ST) {
     count_sort(t_cost, n, max(kmax, 1), sh.sa, sh.T, sh.red);
     sorted = sh.sa;
   } else if (n <= BITONIC_MAX) {

@@ -25,11 +25,29 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources (jagged_attention_amd/csrc): counters describe one version."""
+# timing name -> the source file that defines the kernel
+KERNEL_SOURCE = {"jfa_bwd_dkdv": "bwd.hip", "jfa_bwd_dq": "bwd.hip", "jfa_fwd_bf16": "fwd.hip",
+                 "jfa_fwd_mxfp8": "fwd.hip", "jfa_fwd_combine": "fwd.hip",
+                 "jfa_schedule": "sched.hip", "jfa_offsets": "sched.hip",
+                 "jfa_quant_mxfp8": "quant.hip", "jfa_fwd_f32": "f32.hip",
+                 "jfa_bwd_dq_f32": "f32.hip", "jfa_bwd_dkdv_f32": "f32.hip"}
+# what every kernel's code and launch configuration also depend on
+SHARED_SOURCES = ("jfa_device.h", "jfa_internal.h", "api.cpp")
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources a kernel is built and launched from (its own file plus the shared
+    headers and the launcher), or of every source when `kernel` is None: counters describe one
+    version of that code."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for f in sorted(os.listdir(csrc)):
+    if kernel is None:
+        files = sorted(os.listdir(csrc))
+    else:
+        files = sorted({KERNEL_SOURCE.get(kernel, "")} - {""} | set(SHARED_SOURCES))
+        if kernel not in KERNEL_SOURCE:
+            files = sorted(os.listdir(csrc))
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -98,7 +116,8 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
         fb = (sum(fv) / len(fv)) * 1024.0 * kf if fv else 0.0
         wb = (sum(wv) / len(wv)) * 1024.0 * kw if wv else 0.0
         kernels[name] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
-                             bytes_per_launch=round(fb + wb), dispatches=len(fv))
+                             bytes_per_launch=round(fb + wb), dispatches=len(fv),
+                             source_hash=source_hash(name))
     calib = dict(copy_bytes=copy_bytes, fetch_kib=cf, write_kib=cw, fetch_factor=round(kf, 4),
                  write_factor=round(kw, 4))
     return kernels, calib
@@ -123,7 +142,7 @@ def main():
              f"Calibration: a {a.copy_mib} MiB device copy in the same run read FETCH_SIZE "
              f"{calib['fetch_kib']:.0f} KiB and WRITE_SIZE {calib['write_kib']:.0f} KiB; factors "
              f"{calib['fetch_factor']} and {calib['write_factor']} convert the counters to bytes.",
-             f"Kernel sources: {rec['source_hash']}.", "",
+             f"Kernel sources (all files): {rec['source_hash']}; per kernel in traffic.json.", "",
              "| kernel | fetch MB | write MB | total MB / launch | dispatches |",
              "|---|---|---|---|---|"]
     for n, e in kernels.items():

@@ -40,3 +40,11 @@ def test_summary_scales_by_the_copy(tmp_path):
     assert e["write_bytes"] == 100 * 1024 * 4
     assert e["bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"]
     assert calib["fetch_factor"] == 2.0 and calib["write_factor"] == 4.0
+
+
+def test_per_kernel_source_hash():
+    # a kernel's counters stay valid across edits to other kernels' files
+    a = traffic.source_hash("jfa_bwd_dkdv")
+    assert a == traffic.source_hash("jfa_bwd_dq")          # same source file
+    assert a != traffic.source_hash("jfa_fwd_bf16")
+    assert traffic.source_hash() not in (a, traffic.source_hash("jfa_fwd_bf16"))
