@@ -44,7 +44,7 @@ class _Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_double),
                 ("normalize", ctypes.c_int32), ("bias_kind", ctypes.c_int32),
-                ("num_buckets", ctypes.c_int32)]
+                ("num_buckets", ctypes.c_int32), ("block", ctypes.c_int32)]
 
 
 class _SchedParams(ctypes.Structure):
@@ -64,6 +64,8 @@ def lib():
         P = ctypes.c_void_p
         _lib.ora_offsets.argtypes = [P, ctypes.c_int32, P]
         _lib.ora_bias_offsets.argtypes = [P, P, ctypes.c_int32, P]
+        _lib.ora_block_offsets.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64]
+        _lib.ora_block_offsets.restype = ctypes.c_int64
         _lib.ora_relpos_bucket.argtypes = [ctypes.c_int64, ctypes.c_int32]
         _lib.ora_relpos_bucket.restype = ctypes.c_int
         _lib.ora_forward.argtypes = [P] * 10
@@ -118,24 +120,51 @@ def bias_offsets(q_lens, kv_lens) -> np.ndarray:
     return out
 
 
+def block_batch_bound(batch: int, total_rows: int, block: int) -> int:
+    """Refined batch size that always holds the blocks: sum_b ceil(n_b / W) <= B + T // W."""
+    return int(batch) + int(total_rows) // int(block)
+
+
+def block_offsets(offsets_, block: int, out_batch: Optional[int] = None) -> np.ndarray:
+    """BlockAttention's refined offsets (int64 [out_batch + 1]); see ``ora_block_offsets``."""
+    off = np.ascontiguousarray(offsets_, dtype=np.int64)
+    B = off.shape[0] - 1
+    if out_batch is None:
+        out_batch = block_batch_bound(B, int(off[-1]), block)
+    out = np.zeros(out_batch + 1, dtype=np.int64)
+    if lib().ora_block_offsets(_ptr(off), B, int(block), _ptr(out), int(out_batch)) < 0:
+        raise ValueError("blocks exceed out_batch, or block < 1")
+    return out
+
+
 def relpos_bucket(delta: int, num_buckets: int = 64) -> int:
     return int(lib().ora_relpos_bucket(int(delta), int(num_buckets)))
 
 
 # ------------------------------------------------------------ attention
 
-def _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets):
+def _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block=0):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if normalize is None:
         normalize = mode != "softmax"
     return _Problem(B, H, d, MODES[mode], int(bool(causal)), float(scale), int(bool(normalize)),
-                    BIAS[bias_kind], int(num_buckets))
+                    BIAS[bias_kind], int(num_buckets), int(block))
+
+
+def _check_block(block, q_lens, kv_lens, bias_kind):
+    if block:
+        # BlockAttention is self-attention over one sequence: blocks are the same rows on both
+        # sides; a dense bias is defined on the refined batch, not here
+        assert block > 0 and bias_kind != "dense"
+        assert np.array_equal(np.asarray(q_lens), np.asarray(kv_lens))
 
 
 def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-            bias_kind="none", num_buckets=64, scale=None, normalize=None):
-    """Returns (o [Tq,H,d] fp64, lse [H,Tq] fp64 or None for GDPA)."""
+            bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
+    """Returns (o [Tq,H,d] fp64, lse [H,Tq] fp64 or None for GDPA).  block > 0: BlockAttention
+    with blocks of that many rows."""
+    _check_block(block, q_lens, kv_lens, bias_kind)
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, H, d = q.shape
     qo, ko = offsets(q_lens), offsets(kv_lens)
@@ -145,7 +174,7 @@ def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None
     bias64 = _f64(bias) if bias is not None else None
     if bias_kind != "none":
         assert bias64 is not None
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
     o = np.zeros_like(q)
     lse = np.full((H, Tq), np.nan) if mode == "softmax" else None
     lib().ora_forward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
@@ -154,15 +183,16 @@ def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None
 
 
 def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-             bias_kind="none", num_buckets=64, scale=None, normalize=None):
+             bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
     """Returns (dq, dk, dv) in fp64: the gradients of <O, dout>."""
+    _check_block(block, q_lens, kv_lens, bias_kind)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     Tq, H, d = q.shape
     qo, ko = offsets(q_lens), offsets(kv_lens)
     B = qo.shape[0] - 1
     bo = bias_offsets(q_lens, kv_lens)
     bias64 = _f64(bias) if bias is not None else None
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     lib().ora_backward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                        _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))

@@ -43,6 +43,9 @@ typedef struct {
   int32_t normalize;   /* GDPA only: 1 divides the output by the sample's kv_len */
   int32_t bias_kind;   /* 0 none, 1 relative-position bucket table, 2 dense jagged */
   int32_t num_buckets; /* relative-position table width */
+  int32_t block;       /* BlockAttention: >0 splits every sample (q_len = kv_len) into
+                          consecutive blocks of this many rows that attend only within
+                          themselves; 0 = full attention over the sample */
 } ora_problem;
 
 /* ---------------------------------------------------------------- threads */
@@ -84,6 +87,24 @@ int ora_bias_offsets(const int32_t* qlen, const int32_t* kvlen, int32_t n, int64
     bo[b + 1] = bo[b] + (int64_t)qlen[b] * (int64_t)kvlen[b];
   }
   return 0;
+}
+
+/* Block boundaries of BlockAttention as offsets of a refined batch: every sample of length n
+ * contributes ceil(n / block) entries (its block starts, block rows apart), in sample order;
+ * the remaining entries up to out[out_batch] hold the total row count (empty blocks).
+ * Returns the number of blocks, or -1 when they exceed out_batch or block < 1. */
+int64_t ora_block_offsets(const int64_t* off, int32_t n, int32_t block, int64_t* out,
+                          int64_t out_batch) {
+  if (block < 1) return -1;
+  int64_t e = 0;
+  for (int32_t b = 0; b < n; ++b) {
+    for (int64_t start = off[b]; start < off[b + 1]; start += block) {
+      if (e >= out_batch) return -1;
+      out[e++] = start;
+    }
+  }
+  for (int64_t x = e; x <= out_batch; ++x) out[x] = off[n];
+  return e;
 }
 
 /* ------------------------------------------------------- relative position */
@@ -133,8 +154,25 @@ static double act_grad(int mode, double x) {
   return cdf + x * pdf;
 }
 
+/* BlockAttention ("Meta GEM Training Efficiency: ...", section "Bottleneck move 1": long
+ * sequences become independent fixed-size blocks; "Meta Enhances GEM Training Efficiency ...",
+ * "Exploring the Customized Kernel Library": windows in place of full attention): query i and
+ * key j interact only when they fall in the same block of p->block consecutive rows. */
 static int visible(const ora_problem* p, int64_t i, int64_t j, int64_t n, int64_t m) {
+  if (p->block > 0 && i / p->block != j / p->block) return 0;
   return !p->causal || j <= i + (m - n);
+}
+
+/* GDPA output weight of query i: 1 / (number of keys it attends over before masking), the
+ * sample's kv_len, or with BlockAttention the length of i's block. */
+static double gdpa_weight(const ora_problem* p, int64_t i, int64_t m) {
+  if (!p->normalize || m <= 0) return 1.0;
+  if (p->block > 0) {
+    const int64_t start = (i / p->block) * p->block;
+    const int64_t len = m - start < p->block ? m - start : p->block;
+    return 1.0 / (double)len;
+  }
+  return 1.0 / (double)m;
 }
 
 static double score(const ora_problem* p, const double* q, const double* k, const double* bias,
@@ -191,7 +229,7 @@ void ora_forward(const ora_problem* p, const int64_t* qo, const int64_t* ko,
         }
         if (lse) lse[h * Tq + qo[b] + i] = mx + log(l);
       } else {
-        const double w = (p->normalize && m > 0) ? 1.0 / (double)m : 1.0;
+        const double w = gdpa_weight(p, i, m);
         for (int64_t j = 0; j < m; ++j) {
           if (!visible(p, i, j, n, m)) continue;
           const double pij = act(p->mode, s[j]);
@@ -269,7 +307,7 @@ void ora_backward(const ora_problem* p, const int64_t* qo, const int64_t* ko,
           }
         }
       } else {
-        const double w = (p->normalize && m > 0) ? 1.0 / (double)m : 1.0;
+        const double w = gdpa_weight(p, i, m);
         for (int64_t j = 0; j < m; ++j) {
           if (!visible(p, i, j, n, m)) continue;
           const double* kj = k + ((ko[b] + j) * H + h) * d;

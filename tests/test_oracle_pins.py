@@ -438,3 +438,83 @@ def test_mxfp8_against_torch_cast_and_bounds(oracle_mod):
             sat = ~inr                                        # y in (448, 512) clips to 448
             rel = np.abs(deq[r, 32 * blk:32 * blk + 32][sat] - xb[sat]) / np.abs(xb[sat])
             assert np.all(rel < 1.0 / 8)
+
+
+# ------------------------------------------------------------ BlockAttention
+
+def _split_lengths(lens, w):
+    """Block lengths of each sample, written out by hand: full blocks of w, then the rest."""
+    out = []
+    for n in lens:
+        n = int(n)
+        out += [w] * (n // w) + ([n % w] if n % w else [])
+    return out
+
+
+def test_block_offsets_bruteforce(oracle_mod):
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        B = int(rng.integers(1, 9))
+        lens = rng.integers(0, 40, size=B)
+        w = int(rng.integers(1, 17))
+        off = np.concatenate([[0], np.cumsum(lens)])
+        got = oracle_mod.block_offsets(off, w)
+        blocks = _split_lengths(lens, w)
+        want = np.concatenate([[0], np.cumsum(blocks)])
+        nb = len(blocks)
+        assert nb <= B + int(off[-1]) // w              # the documented bound holds
+        assert got.shape[0] == B + int(off[-1]) // w + 1
+        assert np.array_equal(got[:nb + 1], want)
+        assert np.all(got[nb:] == off[-1])              # trailing empty blocks
+    with pytest.raises(ValueError):
+        oracle_mod.block_offsets([0, 10], 3, out_batch=3)   # needs 4 blocks
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal,bias_kind", [(False, "none"), (True, "relpos")])
+def test_block_attention_is_attention_per_block(oracle_mod, mode, causal, bias_kind):
+    """BlockAttention over samples = plain attention (torch SDPA / autograd) over every block
+    taken as a sample of its own."""
+    lens, w = [11, 0, 4, 9], 4
+    case = custom_case(lens, lens, 2, 8, dtype="f32", mode=mode, causal=causal,
+                       bias_kind=bias_kind, num_buckets=64, seed=31, bias_std=0.5)
+    o, lse = oracle_mod.forward(case.q, case.k, case.v, lens, lens, mode=mode, causal=causal,
+                                bias=case.bias, bias_kind=bias_kind, block=w)
+    dq, dk, dv = oracle_mod.backward(case.q, case.k, case.v, case.dout, lens, lens, mode=mode,
+                                     causal=causal, bias=case.bias, bias_kind=bias_kind, block=w)
+    blocks = _split_lengths(lens, w)
+    ref = torch_reference(case.q, case.k, case.v, blocks, blocks, mode, causal, case.bias,
+                          bias_kind, oracle_mod.relpos_bucket, dout=case.dout)
+    assert max_abs(o, ref["o"]) < 1e-12
+    if mode == "softmax":
+        assert max_abs(lse, ref["lse"]) < 1e-12
+    for got, want in ((dq, ref["dq"]), (dk, ref["dk"]), (dv, ref["dv"])):
+        assert max_abs(got, want) < 1e-11
+    # blocks do change the result (the test would pass vacuously otherwise)
+    o_full, _ = oracle_mod.forward(case.q, case.k, case.v, lens, lens, mode=mode, causal=causal,
+                                   bias=case.bias, bias_kind=bias_kind)
+    assert max_abs(o, o_full) > 1e-3
+
+
+def test_block_attention_special_cases(oracle_mod):
+    lens = [7, 3, 12]
+    case = custom_case(lens, lens, 2, 8, dtype="f32", mode="softmax", causal=False, seed=32)
+    # a block as long as the longest sample is full attention, bit for bit
+    o_w, lse_w = oracle_mod.forward(case.q, case.k, case.v, lens, lens, block=12)
+    o_f, lse_f = oracle_mod.forward(case.q, case.k, case.v, lens, lens)
+    assert np.array_equal(o_w, o_f) and np.array_equal(lse_w, lse_f)
+    # one-row blocks: every query sees only its own key, so O = V, and the softmax weight is
+    # constant 1, so dQ = dK = 0 and dV = dO
+    o1, _ = oracle_mod.forward(case.q, case.k, case.v, lens, lens, block=1)
+    assert max_abs(o1, np.asarray(case.v, np.float64)) < 1e-15
+    dq, dk, dv = oracle_mod.backward(case.q, case.k, case.v, case.dout, lens, lens, block=1)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    assert max_abs(dv, np.asarray(case.dout, np.float64)) < 1e-15
+    # GDPA with one-row blocks: O_i = act(S_ii) V_i (the block has one key: weight 1)
+    g = custom_case(lens, lens, 1, 8, dtype="f32", mode="silu", seed=33)
+    og, _ = oracle_mod.forward(g.q, g.k, g.v, lens, lens, mode="silu", block=1)
+    q = np.asarray(g.q, np.float64)[:, 0]
+    k = np.asarray(g.k, np.float64)[:, 0]
+    s = (q * k).sum(-1) / math.sqrt(8)
+    a = s / (1 + np.exp(-s))
+    assert max_abs(og[:, 0], a[:, None] * np.asarray(g.v, np.float64)[:, 0]) < 1e-14
