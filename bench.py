@@ -27,6 +27,7 @@ METRIC = "jagged attention fwd+bwd useful TFLOP/s and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+BLOCK_ROWS = 256                 # BlockAttention block size of the extra workload
 
 
 def log(*a):
@@ -49,10 +50,11 @@ def visible_pairs(q_lens, kv_lens, causal):
 class Workload:
     """Device buffers and preallocated outputs for one jfa_synth case."""
 
-    def __init__(self, case, with_backward=True):
+    def __init__(self, case, with_backward=True, block=0):
         import torch
         import jagged_attention_amd as jfa
         self.case = case
+        self.block = block
         dev = torch.device("cuda:0")
         self.q = case.q.to(dev)
         self.k = case.k.to(dev)
@@ -70,7 +72,13 @@ class Workload:
             self.qc, self.qs = jfa.quantize_mxfp8(self.q)
             self.kc, self.ks = jfa.quantize_mxfp8(self.k)
             self.vc, self.vs = jfa.quantize_mxfp8(self.v)
-        self.problem = jfa.make_problem(case.batch, case.heads, case.head_dim, case.total_q,
+        batch = case.batch
+        if block:
+            # BlockAttention: the attention calls run on the refined batch of blocks
+            batch = case.batch + case.total_q // block
+            self.boff = torch.empty(batch + 1, dtype=torch.int32, device=dev)
+        self.batch = batch
+        self.problem = jfa.make_problem(batch, case.heads, case.head_dim, case.total_q,
                                         case.total_kv, mode=case.mode,
                                         dtype=case.dtype, causal=case.causal,
                                         bias_kind=case.bias_kind, num_buckets=case.num_buckets)
@@ -89,7 +97,12 @@ class Workload:
             self.dq = torch.empty_like(self.q)
             self.dk = torch.empty_like(self.k)
             self.dv = torch.empty_like(self.v)
-        pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal) * case.heads
+        if block:
+            bl = np.array([min(block, n - s) for n in case.q_lens for s in range(0, n, block)],
+                          dtype=np.int64)
+            pairs = visible_pairs(bl, bl, case.causal) * case.heads
+        else:
+            pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal) * case.heads
         self.pairs = int(pairs.sum())
         d = case.head_dim
         self.fwd_flops = 4.0 * d * self.pairs
@@ -98,6 +111,17 @@ class Workload:
     def step(self):
         import jagged_attention_amd as jfa
         jfa.jfa_lengths_to_offsets(self.q_lens, self.case.batch, self.qo, self.status[0:1])
+        if self.block:
+            # self-attention split into blocks: one offsets array, refined, on both sides
+            jfa.jfa_block_offsets(self.qo, self.case.batch, self.block, self.boff, self.batch,
+                                  self.status[1:2])
+            jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.boff,
+                            self.boff, self.bias, self.o, self.lse, self.ws_f, self.nf)
+            if self.with_backward:
+                jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse,
+                                 self.dout, self.boff, self.boff, self.bias, self.dq, self.dk,
+                                 self.dv, self.ws_b, self.nb)
+            return
         jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko, self.status[1:2])
         if self.fp8:
             d = self.case.head_dim
@@ -154,7 +178,8 @@ def kernel_times(w, steps):
     torch.cuda.synchronize()
     jfa.jfa_set_kernel_timing(False)
     out = {}
-    for name in ("jfa_offsets", "jfa_schedule", "jfa_quant_mxfp8", "jfa_fwd_bf16", "jfa_fwd_mxfp8",
+    for name in ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
+                 "jfa_fwd_bf16", "jfa_fwd_mxfp8",
                  "jfa_fwd_f32",
                  "jfa_fwd_combine", "jfa_bwd_delta", "jfa_bwd_dkdv", "jfa_bwd_dq"):
         ms, n = jfa.jfa_kernel_timing(name)
@@ -227,10 +252,10 @@ def cpu_baseline(case, target_s=15.0):
                        f"{t:.1f} s)")
 
 
-def bench_config(cfg, steps, warmup, seed=None):
+def bench_config(cfg, steps, warmup, seed=None, block=0):
     from jfa_synth import make_case
     case = make_case(cfg, seed)
-    w = Workload(case)
+    w = Workload(case, block=block)
     sec = time_steps(w, steps, warmup)
     flops = w.fwd_flops + w.bwd_flops
     peak = PEAK_FP8_TFLOPS if case.dtype == "mxfp8" else PEAK_BF16_TFLOPS
@@ -238,7 +263,8 @@ def bench_config(cfg, steps, warmup, seed=None):
     intensity = flops / (fb + bb)
     ceiling = min(peak, intensity * PEAK_HBM_GBS / 1000.0)
     tf = flops / sec / 1e12
-    return w, dict(workload=case.name, seed=case.seed, ms_per_step=sec * 1e3, tflops=tf,
+    name = case.name if not block else f"block{block}-" + case.name
+    return w, dict(workload=name, seed=case.seed, ms_per_step=sec * 1e3, tflops=tf,
                    frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
                    frac_of_roofline=tf / ceiling, useful_gflop=flops / 1e9,
                    passes="fwd" if not w.with_backward else "fwd+bwd")
@@ -301,6 +327,14 @@ def main():
             extra[f"workload_{cfg}"] = r
             del wx
             torch.cuda.empty_cache()
+        # BlockAttention: the headline batch with every sample split into blocks of 256 rows
+        log("[bench] block attention")
+        wx, r = bench_config(2, max(3, args.steps // 2), 2, block=BLOCK_ROWS)
+        r["kernels"] = kernel_times(wx, 3)
+        r["block_rows"] = BLOCK_ROWS
+        extra["block_attention"] = r
+        del wx
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

@@ -148,6 +148,26 @@ jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
 jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t* offsets,
                                   int32_t* status, void* stream);
 
+/* BlockAttention ("Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a Different
+ * Stack", section "Bottleneck move 1": eligible long-sequence attention becomes independent
+ * fixed-size blocks; "Meta Enhances GEM Training Efficiency with Advanced LLM-Scale
+ * Innovations", section "Exploring the Customized Kernel Library": windows in place of full
+ * attention).  Splits every sample of `offsets` (device int32 [batch+1], as for the attention
+ * calls) into ceil(len / block) consecutive blocks of `block` rows, the last one shorter, and
+ * writes them as the samples of a refined batch: block_offsets (device int32 [out_batch+1])
+ * receives the block starts in sample order, then the total row count in every remaining
+ * entry (empty samples).  out_batch = batch + total_rows / block always suffices.  Running
+ * jfa_forward / jfa_backward with batch = out_batch and block_offsets as both q and kv offsets
+ * is BlockAttention of a self-attention batch: every query attends to the keys of its own
+ * block (causal within the block when causal = 1; relative positions are block-local, equal
+ * to the sample-local distance; GDPA's 1/kv_len is 1/block length; a dense bias is laid out
+ * over the refined samples).  status (device int32, may be NULL) receives 0, or
+ * JFA_ERR_DEVICE_DATA for malformed offsets or more blocks than out_batch, in which case
+ * block_offsets is left untouched.  block < 1 or out_batch < 0 is JFA_ERR_INVALID_ARG. */
+jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t block,
+                             int32_t* block_offsets, int32_t out_batch, int32_t* status,
+                             void* stream);
+
 /* MXFP8 (OCP Microscaling, E4M3 elements): for each row of x (bf16 [rows, d], d % 32 == 0)
  * and each block of 32 consecutive elements, scale code s = floor(log2 amax) - 8 + 127
  * (clamped to [0, 254]; 127 for an all-zero block) into scales [rows, d/32], and codes

@@ -10,14 +10,16 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # noqa: F401
-                   jfa_backward, jfa_build_schedule, jfa_forward, jfa_kernel_timing,
+                   jfa_backward, jfa_block_offsets, jfa_build_schedule, jfa_forward,
+                   jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
                    jfa_read_device_status, jfa_set_kernel_timing, jfa_tile_config,
                    jfa_workspace_bytes, load, status_string)
 
 jfa_status_string = status_string
 
-__all__ = ["make_problem", "forward", "backward", "lengths_to_offsets", "quantize_mxfp8",
+__all__ = ["make_problem", "forward", "backward", "lengths_to_offsets", "block_offsets",
+           "quantize_mxfp8",
            "build_schedule", "JaggedAttention", "load"]
 
 
@@ -99,6 +101,19 @@ def lengths_to_offsets(lengths):
     status = torch.empty(1, dtype=torch.int32, device=lengths.device)
     jfa_lengths_to_offsets(lengths, lengths.shape[0], off, status)
     return off, status
+
+
+def block_offsets(offsets, block: int, total_rows: int):
+    """BlockAttention: device offsets int32 [B+1] -> (refined offsets int32 [B'+1], B',
+    status int32 [1]) with B' = B + total_rows // block (trailing samples empty).  Run the
+    attention calls with batch B' and the refined offsets on both sides."""
+    import torch
+    B = offsets.shape[0] - 1
+    out_batch = B + int(total_rows) // int(block)
+    out = torch.empty(out_batch + 1, dtype=torch.int32, device=offsets.device)
+    status = torch.empty(1, dtype=torch.int32, device=offsets.device)
+    jfa_block_offsets(offsets, B, block, out, out_batch, status)
+    return out, out_batch, status
 
 
 def quantize_mxfp8(x):

@@ -26,7 +26,8 @@ BIAS_KINDS = {"none": 0, "relpos": 1, "dense": 2}
 
 # every symbol include/jfa.h declares
 EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_tile_config",
-           "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_quantize_mxfp8",
+           "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
+           "jfa_quantize_mxfp8",
            "jfa_read_device_status", "jfa_status_string", "jfa_set_kernel_timing",
            "jfa_kernel_timing", "jfa_kernel_timing_reset")
 
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_build_schedule.restype = ctypes.c_int
     lib.jfa_lengths_to_offsets.argtypes = [P, I32, P, P, P]
     lib.jfa_lengths_to_offsets.restype = ctypes.c_int
+    lib.jfa_block_offsets.argtypes = [P, I32, I32, P, I32, P, P]
+    lib.jfa_block_offsets.restype = ctypes.c_int
     lib.jfa_quantize_mxfp8.argtypes = [P, I64, I32, P, P, P]
     lib.jfa_quantize_mxfp8.restype = ctypes.c_int
     lib.jfa_read_device_status.argtypes = [P, P, ctypes.POINTER(I32)]
@@ -157,6 +160,13 @@ def jfa_lengths_to_offsets(lengths, batch: int, offsets, status=None, stream=Non
     st = load().jfa_lengths_to_offsets(_ptr(lengths), int(batch), _ptr(offsets), _ptr(status),
                                        _stream(stream))
     _check("jfa_lengths_to_offsets", st)
+
+
+def jfa_block_offsets(offsets, batch: int, block: int, block_offsets, out_batch: int,
+                      status=None, stream=None) -> None:
+    st = load().jfa_block_offsets(_ptr(offsets), int(batch), int(block), _ptr(block_offsets),
+                                  int(out_batch), _ptr(status), _stream(stream))
+    _check("jfa_block_offsets", st)
 
 
 def jfa_quantize_mxfp8(x, rows: int, d: int, codes, scales, stream=None) -> None:

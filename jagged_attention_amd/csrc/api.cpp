@@ -436,6 +436,17 @@ jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t
   return from_hip(launch_lengths_to_offsets(lengths, batch, offsets, status, (hipStream_t)stream));
 }
 
+jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t block,
+                             int32_t* block_offsets, int32_t out_batch, int32_t* status,
+                             void* stream) {
+  if (!offsets || !block_offsets || batch < 0 || block < 1 || out_batch < 0)
+    return JFA_ERR_INVALID_ARG;
+  if (!aligned(offsets, 4) || !aligned(block_offsets, 4) || (status && !aligned(status, 4)))
+    return JFA_ERR_INVALID_ARG;
+  return from_hip(launch_block_offsets(offsets, batch, block, block_offsets, out_batch, status,
+                                       (hipStream_t)stream));
+}
+
 jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
                               uint8_t* scales, void* stream) {
   if (!x_bf16 || !codes || !scales || rows < 0 || d <= 0 || d % 32 != 0) return JFA_ERR_INVALID_ARG;

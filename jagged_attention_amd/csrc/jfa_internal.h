@@ -184,6 +184,8 @@ hipError_t launch_forward(const FwdParams& p, const TileCfg& tc, int head_dim, i
                           int64_t max_items, int64_t max_comb_items, int cu_count, hipStream_t s);
 hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, int dtype,
                            int64_t max_q_items, int64_t max_k_items, int cu_count, hipStream_t s);
+hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_t* out,
+                                int32_t out_batch, int32_t* status, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);
 

@@ -624,7 +624,62 @@ __global__ __launch_bounds__(ST) void lengths_to_offsets_kernel(const int32_t* l
   if (threadIdx.x == 0 && status) *status = flag ? JFA_ERR_DEVICE_DATA : JFA_OK;
 }
 
+// BlockAttention's refined offsets: sample b (rows [off[b], off[b+1])) becomes ceil(n_b / W)
+// samples, its consecutive blocks of W rows (the last one shorter), in sample order; entries
+// past the last block up to out[out_batch] hold the total row count (empty samples).  The
+// block count is found first, so nothing is written when it exceeds out_batch.
+__global__ __launch_bounds__(ST) void block_offsets_kernel(const int32_t* off, int32_t B,
+                                                           int32_t W, int32_t* out,
+                                                           int32_t out_batch, int32_t* status) {
+  __shared__ int64_t red[SW];
+  __shared__ int32_t flag;
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int bad = 0;
+  auto nblk = [&](int64_t b) -> int64_t {
+    const int64_t n = (int64_t)off[b + 1] - off[b];
+    if (n < 0) bad = 1;
+    return n > 0 ? (n + W - 1) / W : 0;
+  };
+  // pass 1: the total number of blocks
+  int64_t total = 0;
+  for (int64_t base = 0; base < B; base += ST) {
+    const int64_t b = base + threadIdx.x;
+    int64_t tot;
+    block_scan(b < B ? nblk(b) : 0, &tot, red);
+    total += tot;
+  }
+  if (threadIdx.x == 0 && off[0] != 0) bad = 1;
+  if (bad) atomicOr(&flag, 1);
+  __syncthreads();
+  const bool ok = flag == 0 && total <= out_batch;
+  if (ok) {
+    // pass 2: every sample writes its block starts at its exclusive block count
+    int64_t carry = 0;
+    for (int64_t base = 0; base < B; base += ST) {
+      const int64_t b = base + threadIdx.x;
+      const int64_t c = b < B ? nblk(b) : 0;
+      int64_t tot;
+      const int64_t e0 = carry + block_scan(c, &tot, red);
+      for (int64_t k = 0; k < c; ++k) out[e0 + k] = (int32_t)(off[b] + k * W);
+      carry += tot;
+    }
+    const int32_t end = off[B];
+    for (int64_t e = total + threadIdx.x; e <= out_batch; e += ST) out[e] = end;
+  }
+  if (threadIdx.x == 0 && status) *status = ok ? JFA_OK : JFA_ERR_DEVICE_DATA;
+}
+
 }  // namespace
+
+hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_t* out,
+                                int32_t out_batch, int32_t* status, hipStream_t s) {
+  timing_begin("jfa_block_offsets", s);
+  hipLaunchKernelGGL(block_offsets_kernel, dim3(1), dim3(ST), 0, s, off, B, W, out, out_batch,
+                     status);
+  timing_end(s);
+  return hipGetLastError();
+}
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
   static bool attr_set = false;
