@@ -63,6 +63,8 @@ class Workload:
         self.dout = case.dout.to(dev) if (with_backward and case.dout is not None) else None
         self.q_lens = torch.as_tensor(case.q_lens, dtype=torch.int32, device=dev)
         self.kv_lens = torch.as_tensor(case.kv_lens, dtype=torch.int32, device=dev)
+        # self-attention: one length array, so one offsets array serves queries and keys
+        self.self_attn = bool(np.array_equal(case.q_lens, case.kv_lens))
         self.qo = torch.empty(case.batch + 1, dtype=torch.int32, device=dev)
         self.ko = torch.empty(case.batch + 1, dtype=torch.int32, device=dev)
         self.status = torch.zeros(2, dtype=torch.int32, device=dev)
@@ -122,20 +124,23 @@ class Workload:
                                  self.dout, self.boff, self.boff, self.bias, self.dq, self.dk,
                                  self.dv, self.ws_b, self.nb)
             return
-        jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko, self.status[1:2])
+        ko = self.qo
+        if not self.self_attn:
+            jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko, self.status[1:2])
+            ko = self.ko
         if self.fp8:
             d = self.case.head_dim
             for x, c, sc in ((self.q, self.qc, self.qs), (self.k, self.kc, self.ks),
                              (self.v, self.vc, self.vs)):
                 jfa.jfa_quantize_mxfp8(x, x.numel() // d, d, c, sc)
             jfa.jfa_forward(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks, self.vs,
-                            self.qo, self.ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
+                            self.qo, ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
         else:
             jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo,
-                            self.ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
+                            ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
         if self.with_backward:
             jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse, self.dout,
-                             self.qo, self.ko, self.bias, self.dq, self.dk, self.dv, self.ws_b,
+                             self.qo, ko, self.bias, self.dq, self.dk, self.dv, self.ws_b,
                              self.nb)
 
     def algorithmic_bytes(self):

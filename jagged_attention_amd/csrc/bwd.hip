@@ -75,7 +75,7 @@ struct Tile {
     if constexpr (part < 2) {
 #pragma unroll
       for (int rr = 2 * part; rr < 2 * part + 2; ++rr)
-        *(u32x4*)(rows + (4 * rb + rr) * (D + 8) + 8 * cb) = v[i][rr];
+        *(u32x4*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) = v[i][rr];
     } else {
       constexpr int e2 = part - 2;
       const int pos = vt_pos(4 * rb);
@@ -85,7 +85,7 @@ struct Tile {
       *(u32x2*)(tr + (8 * cb + 2 * e2 + 1) * TS + pos) = hi;
     }
   }
-  // rows: [STEP][D + 8] row-major (may be null); tr: [D][TS] transposed, rows permuted
+  // rows: [STEP][tile_row_stride] row-major (may be null); tr: [D][TS] transposed, rows permuted
   __device__ __forceinline__ void store(__bf16* rows, __bf16* tr) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -95,7 +95,7 @@ struct Tile {
       blk_of(id, rb, cb);
       if (rows) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) *(u32x4*)(rows + (4 * rb + rr) * (D + 8) + 8 * cb) = v[i][rr];
+        for (int rr = 0; rr < 4; ++rr) *(u32x4*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) = v[i][rr];
       }
       if (tr) {
         const int pos = vt_pos(4 * rb);
@@ -129,7 +129,7 @@ struct RowTile {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int id = threadIdx.x + i * NT;
-      *(u32x4*)(rows + (id / KCH) * (D + 8) + 8 * (id % KCH)) = v[i];
+      *(u32x4*)(rows + (id / KCH) * tile_row_stride<D>() + 8 * (id % KCH)) = v[i];
     }
   }
 };
@@ -182,12 +182,12 @@ __device__ __forceinline__ void kv_interleave(int id) {
 template <int D, int NW, int BIAS>
 struct KvLds {
   static constexpr int BNK = 32 * NW;
-  static constexpr int RS = D + 8;
+  static constexpr int RS = tile_row_stride<D>();
   static constexpr int QR = 0;                            // Q rows [STEP][RS]
   static constexpr int DR = QR + STEP * RS * 2;           // dO rows
   // Q^T and dO^T operands are read from the row tiles with transposing LDS reads
   static constexpr int LS = DR + STEP * RS * 2;           // lse / scale [STEP]
-  static constexpr int DL = LS + STEP * 4;                // delta [STEP]
+  static constexpr int DL = LS + STEP * 4;                // -delta [STEP]
   static constexpr int BO = DL + STEP * 4;
   static constexpr int RP = diag_stride(STEP + BNK + 4);
   static constexpr int BS = STEP + 8;                     // dense tile [BNK][BS] bf16 (key-major)
@@ -341,7 +341,7 @@ void bwd_kv_kernel(BwdParams p) {
           // rows without a visible key have lse = -inf; all their pairs are masked to -inf,
           // so any finite value keeps exp2(-inf - lse) = 0
           reinterpret_cast<float*>(base + L::LS)[tid] = lsv == NEG_INF ? 0.f : lsv * inv_scale;
-          reinterpret_cast<float*>(base + L::DL)[tid] = dlv;
+          reinterpret_cast<float*>(base + L::DL)[tid] = -dlv;   // stored negated: dP starts at -D
         }
       }
       if constexpr (BIAS == B_RELPOS) {
@@ -450,7 +450,7 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               sacc[blk][4 * qd + e] -= l[e];
-              pacc[blk][4 * qd + e] = -dl[e];
+              pacc[blk][4 * qd + e] = dl[e];
             }
           }
       } else {
@@ -657,7 +657,7 @@ void bwd_kv_kernel(BwdParams p) {
 template <int D, int NW, int BIAS>
 struct QLds {
   static constexpr int BM = 32 * NW;
-  static constexpr int RS = D + 8;
+  static constexpr int RS = tile_row_stride<D>();
   static constexpr int KR = 0;                            // K rows [STEP][RS]
   static constexpr int VR = KR + STEP * RS * 2;           // V rows
   // the K^T operand is read from the K rows with transposing LDS reads

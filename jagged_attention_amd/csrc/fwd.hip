@@ -50,7 +50,7 @@ struct FwdLds {
   static constexpr int KRB = FP8 ? (D + 16) : 2 * (D + 8);   // K row stride in bytes
   static constexpr int K_BYTES = BN * KRB;
   static constexpr int KSC_BYTES = FP8 ? BN * 4 : 0;          // K scales: one dword per key
-  static constexpr int VS = D + 8;                             // V row stride (bf16)
+  static constexpr int VS = tile_row_stride<D>();              // V row stride (bf16)
   static constexpr int V_OFF = align16(K_BYTES + KSC_BYTES);
   static constexpr int V_BYTES = BN * VS * 2;
   static constexpr int RP = diag_stride(BM + BN + 4);          // relpos copy length (floats)

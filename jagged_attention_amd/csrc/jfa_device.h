@@ -215,6 +215,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
 // Row stride (bf16) of a wave's output staging area: 32 rows of D, padded against bank conflicts.
 template <int D>
 constexpr int out_stage_stride() { return D + 8; }
+
+// Row stride (bf16 elements) of a 64-row LDS tile that is read both along rows (16-byte reads,
+// 16 lanes per LDS cycle) and with transposing 8-byte reads (32 lanes per cycle, 8 rows x 32
+// columns).  Over 64 four-byte banks, D + 8 serves the row reads without conflicts but puts the
+// transposing reads four-way on the same banks at d = 128; D + 24 keeps the row reads and the
+// staging writes conflict-free and halves that to two-way.  At d = 64, D + 8 is already the
+// best of both.
+template <int D>
+constexpr int tile_row_stride() { return D == 128 ? D + 24 : D + 8; }
+
 template <int D>
 constexpr int out_stage_bytes() { return 32 * out_stage_stride<D>() * 2; }
 
