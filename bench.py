@@ -4,7 +4,9 @@ One step = the whole hot path over one synthetic batch: offsets from lengths, ti
 forward (with split-KV combine), softmax preprocess, dK/dV and dQ passes.  The headline
 workload is causal jagged self-attention over user histories with a relative-position bias
 (B=64, lengths log-normal median 512 clipped to [16, 4096], H=4, d=128, bf16, seed 2).
-Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
+Inputs are resident in HBM before the timed region.  The step is timed as eager launches on
+one stream; the same step captured once as a HIP graph (checked bit-exact against an eager
+step) is timed too and reported beside it.  Prints ONE JSON line.
 
 Useful FLOPs count only visible (query, key) pairs: 4*d per pair forward, 10*d backward.
 """
@@ -160,6 +162,47 @@ class Workload:
         return fwd, bwd
 
 
+def outputs(w):
+    """The step's outputs (forward and backward), for comparing a graph replay with eager."""
+    out = [w.o] + ([w.lse] if w.lse is not None else [])
+    if w.with_backward:
+        out += [w.dq, w.dk, w.dv]
+    return out
+
+
+def capture_step(w):
+    """Captures one step into a HIP graph (torch.cuda.CUDAGraph) after checking that its replay
+    reproduces an eager step bit for bit (every kernel here is deterministic)."""
+    import torch
+    torch.cuda.synchronize()
+    w.step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs(w)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w.step()
+    for t in outputs(w):
+        t.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in zip(outputs(w), want):
+        if not torch.equal(a, b):
+            raise RuntimeError("graph replay differs from the eager step")
+    return g
+
+
+def time_graph(g, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def time_steps(w, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -262,6 +305,9 @@ def bench_config(cfg, steps, warmup, seed=None, block=0):
     case = make_case(cfg, seed)
     w = Workload(case, block=block)
     sec = time_steps(w, steps, warmup)
+    # the same step replayed as one HIP graph (no per-launch host work): reported beside it
+    w.graph = capture_step(w)
+    graph = time_graph(w.graph, steps, warmup)
     flops = w.fwd_flops + w.bwd_flops
     peak = PEAK_FP8_TFLOPS if case.dtype == "mxfp8" else PEAK_BF16_TFLOPS
     fb, bb = w.algorithmic_bytes()
@@ -269,7 +315,8 @@ def bench_config(cfg, steps, warmup, seed=None, block=0):
     ceiling = min(peak, intensity * PEAK_HBM_GBS / 1000.0)
     tf = flops / sec / 1e12
     name = case.name if not block else f"block{block}-" + case.name
-    return w, dict(workload=name, seed=case.seed, ms_per_step=sec * 1e3, tflops=tf,
+    return w, dict(workload=name, seed=case.seed, ms_per_step=sec * 1e3,
+                   graph_ms_per_step=graph * 1e3, tflops=tf,
                    frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
                    frac_of_roofline=tf / ceiling, useful_gflop=flops / 1e9,
                    passes="fwd" if not w.with_backward else "fwd+bwd")
@@ -355,6 +402,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_step"], 4),
+        "graph_ms_per_step": round(head["graph_ms_per_step"], 4),
+        "launch": "eager stream launches; graph_ms_per_step replays the step as one HIP graph "
+                  "(checked bit-exact against an eager step)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

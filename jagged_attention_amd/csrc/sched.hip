@@ -29,7 +29,7 @@ constexpr int BITONIC_MAX = 1024;
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Exclusive scan of one value per thread over the workgroup; *total receives the sum.
-__device__ int64_t block_scan(int64_t v, int64_t* total, int64_t* red) {
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* total, int64_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t x = v;
 #pragma unroll
@@ -57,7 +57,7 @@ __device__ int64_t block_scan(int64_t v, int64_t* total, int64_t* red) {
 
 // out[i] = sum_{k<i} f(k) for i in [0, L]; returns the total.
 template <typename OutT, class F>
-__device__ int64_t scan_to(OutT* out, int64_t L, F f, int64_t* red) {
+__device__ __forceinline__ int64_t scan_to(OutT* out, int64_t L, F f, int64_t* red) {
   int64_t carry = 0;
   for (int64_t base = 0; base < L; base += ST) {
     const int64_t i = base + threadIdx.x;
@@ -73,7 +73,7 @@ __device__ int64_t scan_to(OutT* out, int64_t L, F f, int64_t* red) {
 }
 
 // Largest b with base[b] <= x, for base[0] = 0 <= x < base[B].
-__device__ int owner_of(const int32_t* base, int B, int64_t x) {
+__device__ __forceinline__ int owner_of(const int32_t* base, int B, int64_t x) {
   int lo = 0, hi = B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -83,7 +83,7 @@ __device__ int owner_of(const int32_t* base, int B, int64_t x) {
 }
 
 // Ascending bitonic sort of N (a power of two, at most LDS_SORT_MAX) unique keys in LDS.
-__device__ void bitonic_sort(uint32_t* s, int N) {
+__device__ __forceinline__ void bitonic_sort(uint32_t* s, int N) {
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < N / 2; i += ST) {
@@ -101,7 +101,8 @@ __device__ void bitonic_sort(uint32_t* s, int N) {
 }
 
 // Stable ascending sort of words by bits [20, 32), three 4-bit passes; result ends in b.
-__device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t* red) {
+__device__ __forceinline__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T,
+                                           int64_t* red) {
   const int tid = threadIdx.x;
   const int ipt = (n + ST - 1) / ST;
   const int lo = min(n, tid * ipt), hi = min(n, lo + ipt);
@@ -143,7 +144,8 @@ __device__ void radix_sort(uint32_t* a, uint32_t* b, int n, int32_t* T, int64_t*
 // the key bits with ballots).  A handful of barriers, where a bitonic sort of the same list
 // needs one per merge phase.  out[rank] = i.
 constexpr int CS_MAX = 4096;
-__device__ void count_sort(const int32_t* t_cost, int n, int kmax, uint32_t* out, int32_t* T,
+__device__ __forceinline__ void count_sort(const int32_t* t_cost, int n, int kmax, uint32_t* out,
+                                           int32_t* T,
                            int64_t* red) {
   constexpr int R = CS_MAX / ST;              // records per thread
   const int tid = threadIdx.x, lane = tid & 63;
@@ -206,12 +208,28 @@ struct Shared {
   int64_t sumcost;
 };
 
+// The list's work record for list record r of sample b (kernels start an item from it).
+__device__ __forceinline__ ItemRec item_of(const SchedArgs& a, int4 r, int slot,
+                                           const int32_t* qo,
+                                           const int32_t* ko) {
+  ItemRec it{};
+  it.b = r.x; it.x = r.y; it.y = r.z; it.z = r.w;
+  it.slot = slot;
+  it.qo = qo[r.x];
+  it.n = qo[r.x + 1] - it.qo;
+  it.ko = ko[r.x];
+  it.m = ko[r.x + 1] - it.ko;
+  it.boff = (a.want_bias_off && a.dense_bias) ? a.bias_off[r.x] : 0;
+  return it;
+}
+
 // Sorts gen_recs[0..n) by cost (desc, ties by generation index) into out / out_slot and the work
 // records `items` (each output may be null); the keys (inverted cost << 20 | index) are unique,
 // so the order is total.  Short lists use a bitonic sort in LDS; longer ones, whose keys arrive
 // in generation order, a stable 3-pass radix sort on the cost bits alone (in LDS up to 4096
 // entries, else in global memory).
-__device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32_t* t_cost,
+__device__ __forceinline__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n,
+                                              const int32_t* t_cost,
                               int4* out, int32_t* out_slot, ItemRec* items, const int32_t* qo,
                               const int32_t* ko) {
   const uint32_t* sorted;
@@ -256,7 +274,6 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
   for (int base = 0; base < n; base += ST * U) {
     int4 r[U];
     int slot[U];
-    int64_t boff[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = base + u * ST + threadIdx.x;
@@ -269,28 +286,111 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = base + u * ST + threadIdx.x;
-      boff[u] = (i < n && items && a.want_bias_off) ? a.bias_off[r[u].x] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * ST + threadIdx.x;
       if (i >= n) continue;
       if (out) out[i] = r[u];
       if (out_slot) out_slot[i] = slot[u];
-      if (items) {
-        ItemRec it{};
-        it.b = r[u].x; it.x = r[u].y; it.y = r[u].z; it.z = r[u].w;
-        it.slot = slot[u];
-        it.qo = qo[r[u].x];
-        it.n = qo[r[u].x + 1] - it.qo;
-        it.ko = ko[r[u].x];
-        it.m = ko[r[u].x + 1] - it.ko;
-        it.boff = boff[u];
-        items[i] = it;
-      }
+      if (items) items[i] = item_of(a, r[u], slot[u], qo, ko);
     }
   }
   __syncthreads();
+}
+
+// Fast path of a list of n <= CS_MAX records: record i is generated by rec_of(i, rec, slot,
+// cost) on thread i % ST, ranked there (cost descending, ties in index order: the same stable
+// counting rank as count_sort) and written straight to its rank, so the list makes no round
+// trip through global memory.  Returns false, having written nothing but what rec_of writes
+// itself, when the list is too long or its costs too spread for the counters; the caller then
+// takes the general path.
+template <int R, class RecOf>
+__device__ __forceinline__ bool rank_emit_r(const SchedArgs& a, Shared& sh, int n, RecOf rec_of,
+                                            int4* out,
+                            int32_t* out_slot, ItemRec* items, const int32_t* qo,
+                            const int32_t* ko) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int4 rec[R];
+  int slot[R], key[R];
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    key[k] = 0;
+    slot[k] = -1;
+    if (i < n) {
+      rec_of(i, rec[k], slot[k], key[k]);
+      c = max(c, key[k]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
+  if (lane == 0) sh.red[tid >> 6] = c;
+  __syncthreads();
+  int kmax = 1;
+  for (int w = 0; w < SW; ++w) kmax = max(kmax, (int)sh.red[w]);
+  __syncthreads();
+  const int nchunk = (n + 63) / 64;
+  if ((int64_t)kmax * nchunk > 16 * ST) return false;
+  // rank = records of higher cost + equal cost in earlier chunks + equal cost on lower lanes
+  int32_t* T = sh.T;
+  const int nent = kmax * nchunk;             // counters [key][chunk], key = kmax - cost
+  for (int i = tid; i < nent; i += ST) T[i] = 0;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int r[R], cnt[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    const bool act = i < n;
+    key[k] = act ? kmax - key[k] : 0;
+    uint64_t same = __ballot(act);
+    for (int bit = 0; (1 << bit) < kmax; ++bit) {
+      const uint64_t bal = __ballot(act && ((key[k] >> bit) & 1));
+      same &= ((key[k] >> bit) & 1) ? bal : ~bal;
+    }
+    r[k] = __popcll(same & below);
+    cnt[k] = act ? __popcll(same) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    if (i < n && r[k] == cnt[k] - 1) T[key[k] * nchunk + (i >> 6)] = cnt[k];
+  }
+  __syncthreads();
+  const int ept = (nent + ST - 1) / ST;
+  const int lo = min(nent, tid * ept), hi = min(nent, lo + ept);
+  int64_t part = 0;
+  for (int i = lo; i < hi; ++i) part += T[i];
+  int64_t tot;
+  int64_t run = block_scan(part, &tot, sh.red);
+  for (int i = lo; i < hi; ++i) {
+    const int32_t cc = T[i];
+    T[i] = (int32_t)run;
+    run += cc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = k * ST + tid;
+    if (i >= n) continue;
+    const int pos = T[key[k] * nchunk + (i >> 6)] + r[k];
+    if (out) out[pos] = rec[k];
+    if (out_slot) out_slot[pos] = slot[k];
+    if (items) items[pos] = item_of(a, rec[k], slot[k], qo, ko);
+  }
+  __syncthreads();
+  return true;
+}
+
+// R records per thread (registers only: small fully unrolled arrays)
+template <class RecOf>
+__device__ __forceinline__ bool rank_emit(const SchedArgs& a, Shared& sh, int n, RecOf rec_of,
+                                          int4* out,
+                          int32_t* out_slot, ItemRec* items, const int32_t* qo,
+                          const int32_t* ko) {
+  static_assert(CS_MAX == 4 * ST, "record count classes");
+  if (n <= ST) return rank_emit_r<1>(a, sh, n, rec_of, out, out_slot, items, qo, ko);
+  if (n <= 2 * ST) return rank_emit_r<2>(a, sh, n, rec_of, out, out_slot, items, qo, ko);
+  if (n <= CS_MAX) return rank_emit_r<4>(a, sh, n, rec_of, out, out_slot, items, qo, ko);
+  return false;
 }
 
 // D[h][i] = sum_c dO[i,h,c] * O[i,h,c] for every (query row, head): the softmax backward's
@@ -298,7 +398,7 @@ __device__ void sort_and_emit(const SchedArgs& a, Shared& sh, int n, const int32
 // overlaps the single-workgroup list building.  Each (row, head) vector is LPR consecutive
 // lanes with one 16-byte load each of O and dO; lanes combine with xor shuffles.
 template <int ES, int D>
-__device__ void delta_rows(const SchedArgs& a, int block, int nblocks) {
+__device__ __forceinline__ void delta_rows(const SchedArgs& a, int block, int nblocks) {
   constexpr int EPL = 16 / ES;                    // elements per 16-byte load
   constexpr int LPR = D / EPL;                    // lanes per (row, head) vector
   constexpr int U = 4;                            // vectors in flight per thread
@@ -432,7 +532,10 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
 
   // per-sample tile base [B+1]: in LDS (the sort's counter space, idle during generation)
   // whenever it fits, since every tile looks its sample up there by binary search
-  int32_t* s_base = (B + 1 <= 16 * ST) ? sh.T : a.s_tmp;
+  // per-sample tile base [B+1]: in LDS (the sort-key space, idle during generation) whenever
+  // it fits, since every tile looks its sample up there by binary search
+  int32_t* lds_ints = reinterpret_cast<int32_t*>(sh.sa);
+  int32_t* s_base = (B + 1 <= LDS_SORT_MAX / 2) ? lds_ints : a.s_tmp;
   int32_t* t_cost = a.t_tmp;                 // per record cost (generation order)
   int32_t* t_rb = a.t_tmp + (a.cap_t + 1);   // per tile record base
   int32_t* t_sb = a.t_tmp + 2 * (a.cap_t + 1); // per tile slot base
@@ -455,6 +558,12 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   };
   int64_t C = 0;
   int64_t nrec = 0, nslot = 0, ncomb = 0;
+  if (want_f && !overflow && s_base == lds_ints &&
+      (int64_t)(B + 1) + 3 * (ntiles + 1) <= LDS_SORT_MAX) {
+    t_rb = lds_ints + (B + 1);
+    t_sb = t_rb + (ntiles + 1);
+    t_cb = t_sb + (ntiles + 1);
+  }
   if (want_f && !overflow) {
     // total cost -> split threshold
     int64_t part = 0;
@@ -476,7 +585,30 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; }, sh.red);
     if (nrec > a.cap_f || nrec > a.cap_t || ncomb > a.cap_c || nslot > a.cap_slots) overflow = 1;
   }
+  bool done_f = false;
   if (want_f && !overflow) {
+    // record i: tile tau (record base t_rb), chunk c of its nch chunks
+    const bool split = ncomb > 0;
+    auto rec_f = [&](int i, int4& r, int& sl, int& cost) {
+      int tau = i;
+      int64_t c = 0;
+      if (split) {
+        tau = owner_of(t_rb, (int)ntiles, i);
+        c = i - t_rb[tau];
+      }
+      int b;
+      int64_t t;
+      const int64_t st = fwd_steps(tau, b, t);
+      const int64_t nch = (C > 0 && st > C) ? cdiv(st, C) : 1;
+      const int64_t kb = c * st / nch, ke = (c + 1) * st / nch;
+      r = make_int4(b, (int)t, (int)kb, (int)ke);
+      sl = nch > 1 ? (int)(t_sb[tau] + c) : -1;
+      cost = (int)max((int64_t)1, ke - kb);
+      if (nch > 1 && c == 0) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], (int)nch);
+    };
+    done_f = rank_emit(a, sh, (int)nrec, rec_f, a.fwd, a.fwd_slot, a.fwd_items, qo, ko);
+  }
+  if (want_f && !overflow && !done_f) {
     for (int64_t tau = tid; tau < ntiles; tau += ST) {
       int b; int64_t t;
       const int64_t s = fwd_steps(tau, b, t);
@@ -503,7 +635,28 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
                  sh.red);
     if (nq > a.cap_q || nq > a.cap_t) overflow = 1;
   }
+  bool done_q = false;
   if (want_q && !overflow) {
+    auto rec_q = [&](int tau, int4& r, int& sl, int& cost) {
+      const int b = owner_of(s_base, B, tau);
+      const int64_t t = tau - s_base[b];
+      const int64_t n = qlen(b), m = klen(b);
+      int64_t steps;
+      if (one_q(b)) {
+        steps = cdiv(m, tc.bq_bn);
+      } else {
+        const int64_t r1 = min((t + 1) * tc.bq_bm, n);
+        int64_t e = m;
+        if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
+        steps = cdiv(e, tc.bq_bn);
+      }
+      r = make_int4(b, (int)t, 0, (int)steps);
+      sl = -1;
+      cost = (int)max((int64_t)1, steps);
+    };
+    done_q = rank_emit(a, sh, (int)nq, rec_q, a.bq, nullptr, a.bq_items, qo, ko);
+  }
+  if (want_q && !overflow && !done_q) {
     for (int64_t tau = tid; tau < nq; tau += ST) {
       const int b = owner_of(s_base, B, tau);
       const int64_t t = tau - s_base[b];
@@ -531,7 +684,25 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
                  sh.red);
     if (nk > a.cap_k || nk > a.cap_t) overflow = 1;
   }
+  bool done_k = false;
   if (want_k && !overflow) {
+    auto rec_k = [&](int tau, int4& r, int& sl, int& cost) {
+      const int b = owner_of(s_base, B, tau);
+      const int64_t u = tau - s_base[b];
+      const int64_t n = qlen(b), m = klen(b);
+      const int64_t nqs = cdiv(n, tc.bk_bm);
+      int64_t first = 0;
+      if (a.causal && !one_k(b)) {
+        const int64_t i0 = max((int64_t)0, u * tc.bk_bn - (m - n));
+        first = i0 >= n ? nqs : i0 / tc.bk_bm;
+      }
+      r = make_int4(b, (int)u, (int)first, (int)nqs);
+      sl = -1;
+      cost = (int)max((int64_t)1, nqs - first);
+    };
+    done_k = rank_emit(a, sh, (int)nk, rec_k, a.bk, nullptr, a.bk_items, qo, ko);
+  }
+  if (want_k && !overflow && !done_k) {
     for (int64_t tau = tid; tau < nk; tau += ST) {
       const int b = owner_of(s_base, B, tau);
       const int64_t u = tau - s_base[b];
