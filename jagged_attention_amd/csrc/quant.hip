@@ -9,7 +9,8 @@
 // nearest E4M3 value, ties to even, saturating at 448; an all-zero block stores 127.
 //
 // Four lanes own one 32-element block (16 bytes each): a two-step shuffle gives the block max,
-// every lane encodes its 8 elements with integer/rounding ops, and stores 8 code bytes.
+// every lane scales its 8 elements by 2^-e, encodes them with the hardware's pack conversion
+// and stores 8 code bytes.
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -24,21 +25,15 @@ __device__ __forceinline__ int ilog2f(float a) {
   return (31 - __clz(u & 0x7fffffu)) - 149;
 }
 
-// E4M3 code of y (already scaled): nearest finite value, ties to even code, |y| >= 448 -> 0x7E.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 31) << 7;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7Eu;
-  } else if (a < 0.015625f) {                   // below 2^-6: subnormal grid of step 2^-9
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 is the smallest normal, code 0x08)
-  } else {
-    const int E = ilog2f(a);                      // -6 .. 8
-    const float q = ldexpf(a, 3 - E);             // [8, 16), exact
-    mag = (uint32_t)((E + 6) * 8) + (uint32_t)__builtin_rintf(q);   // carry moves the exponent
-  }
-  return sign | mag;
+// E4M3 codes of two scaled values y0, y1 (|y| < 512 by the choice of e): clamped to +-448
+// (saturation), then gfx950's pack conversion to OCP E4M3 with round-to-nearest-even, subnormals
+// included.  The clamp makes every value in [448, 512) encode as 448 (0x7E / 0xFE).  Returns the
+// two codes in bits [16 W, 16 W + 16) of `old`.
+template <bool W>
+__device__ __forceinline__ int e4m3_pair(float y0, float y1, int old) {
+  y0 = fminf(fmaxf(y0, -448.0f), 448.0f);
+  y1 = fminf(fmaxf(y1, -448.0f), 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, old, W);
 }
 
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restrict__ x,
@@ -67,10 +62,12 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restri
     int e = ilog2f(amax) - 8;
     e = e < -127 ? -127 : (e > 127 ? 127 : e);
     sc = (uint32_t)(e + 127);
+    // x * 2^-e is exact (a power-of-two scaling of a bf16 value within the float range)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t c = e4m3_encode(ldexpf(v[k], -e));
-      out[k >> 2] |= c << (8 * (k & 3));
+    for (int h = 0; h < 2; ++h) {
+      int word = e4m3_pair<false>(ldexpf(v[4 * h], -e), ldexpf(v[4 * h + 1], -e), 0);
+      word = e4m3_pair<true>(ldexpf(v[4 * h + 2], -e), ldexpf(v[4 * h + 3], -e), word);
+      out[h] = (uint32_t)word;
     }
   }
   *(u32x2*)(codes + blk * 32 + sub * 8) = out;

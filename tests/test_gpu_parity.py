@@ -210,6 +210,32 @@ def test_mxfp8_quantizer_bitexact():
     assert np.array_equal(codes.cpu().numpy(), want_c)
 
 
+def test_mxfp8_quantizer_golden():
+    """The hand-derived cases (ties to even, smallest subnormal, saturation, zero block) on the
+    GPU quantiser: one 32-element block per case holding amax and x."""
+    import jagged_attention_amd as jfa
+    from tests.test_oracle_pins import _golden_rows
+    rows = list(_golden_rows("mxfp8_cases.txt"))
+    blk = np.zeros((len(rows), 32), dtype=np.float32)
+    for r, (amax, x, _, _) in enumerate(rows):
+        blk[r, 0], blk[r, 1] = float(amax), float(x)
+        blk[r, 2] = -float(x)                      # the same magnitude, the other sign
+    xb = torch.from_numpy(blk).to(torch.bfloat16)
+    # every x is bf16-exact; an amax may round, but not across a power of two (same scale)
+    assert torch.equal(xb[:, 1:].float(), torch.from_numpy(blk[:, 1:]))
+    a0 = xb[:, 0].float().numpy()
+    nz = blk[:, 0] > 0
+    assert np.array_equal(np.floor(np.log2(a0[nz])), np.floor(np.log2(blk[nz, 0])))
+    codes, scales = jfa.quantize_mxfp8(xb.cuda())
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    for r, (amax, x, scale, code) in enumerate(rows):
+        c = int(code, 16)
+        assert scales[r, 0] == int(scale), (amax, x)
+        assert codes[r, 1] == c, (amax, x, hex(codes[r, 1]))
+        if float(amax) != 0.0:
+            assert codes[r, 2] == (c ^ 0x80), (amax, x, hex(codes[r, 2]))
+
+
 def test_mxfp8_forward_parity():
     import jagged_attention_amd as jfa
     ql = [300, 17, 129, 0, 64, 520]
