@@ -1,0 +1,88 @@
+"""GPU parity for problem options the workload tests leave at their defaults: an explicit QK
+scale, GDPA without the 1/kv_len weight, one and sixteen heads, a one-sample batch, and the
+two-pass backward forced on samples that would take the single pass."""
+import pytest
+import torch
+
+import oracle
+from jfa_synth import custom_case
+from tests.gpu_helpers import compare, compare_lse, device_case, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import jagged_attention_amd as jfa
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    jfa.load()
+    oracle.build()
+    return jfa
+
+
+def _run(case, *, qk_scale=0.0, kv_len_normalize=-1, bwd_fuse=-1):
+    import jagged_attention_amd as jfa
+    dc = device_case(case)
+    kw = dict(mode=case.mode, causal=case.causal, bias=dc["bias"], bias_kind=case.bias_kind,
+              num_buckets=case.num_buckets, qk_scale=qk_scale,
+              kv_len_normalize=kv_len_normalize)
+    o, lse = jfa.forward(dc["q"], dc["k"], dc["v"], dc["qo"], dc["ko"], **kw)
+    dq, dk, dv = jfa.backward(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
+                              bwd_fuse=bwd_fuse, **kw)
+    torch.cuda.synchronize()
+    okw = dict(scale=qk_scale if qk_scale > 0 else None,
+               normalize=None if kv_len_normalize < 0 else bool(kv_len_normalize))
+    o_ref, lse_ref = oracle.case_forward(case, **okw)
+    dq_ref, dk_ref, dv_ref = oracle.case_backward(case, **okw)
+    compare("O", o, o_ref, case.dtype)
+    compare_lse(lse, lse_ref, case.mode)
+    compare("dQ", dq, dq_ref, case.dtype)
+    compare("dK", dk, dk_ref, case.dtype)
+    compare("dV", dv, dv_ref, case.dtype)
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+def test_explicit_qk_scale(mode):
+    case = custom_case([200, 9, 130], [200, 9, 130], 2, 128, dtype="bf16", mode=mode,
+                       causal=True, bias_kind="relpos", seed=51)
+    say(f"[options] qk_scale=0.05 mode={mode}")
+    _run(case, qk_scale=0.05)
+
+
+@pytest.mark.parametrize("mode", ["silu", "gelu"])
+def test_gdpa_without_kv_len_weight(mode):
+    # without 1/kv_len, dP = dO.V is not damped (|dP| ~ 30 at d = 64), and dK = s sum_i dS_i Q_i
+    # takes dS rounded to bf16 as an MFMA operand: at s = 0.05 that rounding alone moves dK by
+    # ~0.02 (the bf16 bound), so the scale is 0.02 and the keys few
+    case = custom_case([70, 33, 150], [12, 40, 25], 2, 64, dtype="bf16", mode=mode,
+                       bias_kind="dense", seed=52)
+    say(f"[options] kv_len_normalize=0 mode={mode}")
+    _run(case, kv_len_normalize=0, qk_scale=0.02)
+
+
+@pytest.mark.parametrize("heads,d", [(1, 128), (16, 64)])
+def test_head_counts(heads, d):
+    case = custom_case([257, 0, 64, 31], [257, 0, 64, 31], heads, d, dtype="bf16",
+                       mode="softmax", causal=True, bias_kind="relpos", seed=53)
+    say(f"[options] heads={heads} d={d}")
+    _run(case)
+
+
+@pytest.mark.parametrize("mode", ["softmax", "gelu"])
+def test_single_sample(mode):
+    case = custom_case([1000], [1000], 1, 128, dtype="bf16", mode=mode, causal=True,
+                       bias_kind="relpos", seed=54)
+    say(f"[options] one sample mode={mode}")
+    _run(case)
+
+
+@pytest.mark.parametrize("bwd_fuse", [0, -1])
+@pytest.mark.parametrize("d,ql,kl", [(128, [40, 64, 17, 55], [300, 90, 700, 45]),
+                                     (64, [256, 100, 256], [40, 64, 9])])
+def test_single_pass_classes_against_two_pass(bwd_fuse, d, ql, kl):
+    """Samples with one query tile (d = 128, short queries) and with one key tile (d = 64,
+    short keys) take the single-pass backward by default; bwd_fuse = 0 forces two passes.
+    Both match the oracle."""
+    case = custom_case(ql, kl, 2, d, dtype="bf16", mode="silu", seed=55)
+    say(f"[options] bwd_fuse={bwd_fuse} d={d}")
+    _run(case, bwd_fuse=bwd_fuse)
