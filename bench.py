@@ -229,7 +229,7 @@ def kernel_times(w, steps):
     for name in ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
                  "jfa_fwd_bf16", "jfa_fwd_mxfp8",
                  "jfa_fwd_f32",
-                 "jfa_fwd_combine", "jfa_bwd_delta", "jfa_bwd_dkdv", "jfa_bwd_dq"):
+                 "jfa_fwd_combine", "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq"):
         ms, n = jfa.jfa_kernel_timing(name)
         if n:
             out[name] = dict(avg_ms=ms / n, launches=n)
@@ -238,8 +238,9 @@ def kernel_times(w, steps):
 
 
 # algorithmic MFMA flops per visible pair (multiples of d) for each kernel
-KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_dkdv": 8,
-                         "jfa_bwd_dq": 6}
+# (the two backward passes in one launch: 8 + 6)
+KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 14,
+                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6}
 
 
 def traffic_for(kernel):

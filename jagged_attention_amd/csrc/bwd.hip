@@ -205,12 +205,16 @@ struct KvLds {
   static constexpr int TOTAL = 2 * STAGE + (K1 ? BNK * RS * 2 + BNK * QS * 2 : 0);
 };
 
-template <int D, int NW, int MODE, int BIAS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_kv_kernel(BwdParams p) {
+// The key-stationary pass over the kv-stationary list, on the workgroup's dynamic LDS.  (The
+// dynamic LDS is named here, not passed in: a pointer argument costs the constant LDS offsets
+// and, in the one-query-tile kernels, registers enough to spill.)
+// HOME: the first item of workgroup g is item g (the pass starts the launch); otherwise every
+// item comes from a ticket.
+template <int D, int NW, int MODE, int BIAS, bool HOME>
+__device__ __forceinline__ void kv_pass(const BwdParams& p) {
+  extern __shared__ __align__(16) unsigned char lds[];
   using L = KvLds<D, NW, BIAS>;
   constexpr int BNK = L::BNK, NT = NW * 64, RS = L::RS;
-  extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int s_desc[2][IF_WORDS];
 
   if (p.hdr->status != JFA_OK) return;
@@ -237,7 +241,7 @@ void bwd_kv_kernel(BwdParams p) {
   constexpr int NPRE = D == 128 ? 0 : NDB;
   u32x4 dbr[NPRE > 0 ? NPRE : 1][2];
 
-  ItemPipe pipe{p.xtk_k, p.bk, (int)n_items, H};
+  ItemPipeT<HOME> pipe{p.xtk_k, p.bk, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -681,12 +685,12 @@ struct QLds {
   static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 : 0);
 };
 
-template <int D, int NW, int MODE, int BIAS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_q_kernel(BwdParams p) {
+// The query-stationary pass over the q-stationary list (HOME as for kv_pass).
+template <int D, int NW, int MODE, int BIAS, bool HOME>
+__device__ __forceinline__ void q_pass(const BwdParams& p) {
+  extern __shared__ __align__(16) unsigned char lds[];
   using L = QLds<D, NW, BIAS>;
   constexpr int BM = L::BM, NT = NW * 64, RS = L::RS;
-  extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int s_desc[2][IF_WORDS];
 
   if (p.hdr->status != JFA_OK) return;
@@ -707,7 +711,7 @@ void bwd_q_kernel(BwdParams p) {
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
   u32x4 dbr[NDB];                   // dense bias chunks (8 keys of one query) of the next step
 
-  ItemPipe pipe{p.xtk_q, p.bq, (int)n_items, H};
+  ItemPipeT<HOME> pipe{p.xtk_q, p.bq, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -1054,6 +1058,29 @@ void bwd_q_kernel(BwdParams p) {
   }
 }
 
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_kv_kernel(BwdParams p) {
+  kv_pass<D, NW, MODE, BIAS, true>(p);
+}
+
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_q_kernel(BwdParams p) {
+  q_pass<D, NW, MODE, BIAS, true>(p);
+}
+
+// Both passes in one persistent launch (they are independent): every workgroup first works
+// through the kv-stationary list, then takes q-stationary items by ticket, so the second list
+// fills the first one's tail and the two passes share one kernel boundary.
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_kvq_kernel(BwdParams p) {
+  kv_pass<D, NW, MODE, BIAS, true>(p);
+  __syncthreads();
+  q_pass<D, NW, MODE, BIAS, false>(p);
+}
+
 template <class K>
 hipError_t launch_persistent(K kern, size_t lds, int threads, int64_t max_items, int cu,
                              const BwdParams& p, const char* tname, hipStream_t s, int* attr) {
@@ -1084,9 +1111,20 @@ hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) 
                            max_items, cu, p, "jfa_bwd_dq", s, &attr);
 }
 
+template <int D, int NW, int MODE, int BIAS>
+hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
+  static int attr = 0;
+  constexpr size_t lds = KvLds<D, NW, BIAS>::TOTAL > QLds<D, NW, BIAS>::TOTAL
+                             ? KvLds<D, NW, BIAS>::TOTAL : QLds<D, NW, BIAS>::TOTAL;
+  return launch_persistent(bwd_kvq_kernel<D, NW, MODE, BIAS>, lds, NW * 64, max_items, cu, p,
+                           "jfa_bwd_kvq", s, &attr);
+}
+
 template <int D, int MODE, int BIAS>
 hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                         hipStream_t s) {
+  // one launch for both passes when their workgroups have the same shape
+  if (tc.bk_nw == 4 && tc.bq_nw == 4) return run_bkq<D, 4, MODE, BIAS>(p, max(mq, mk), cu, s);
   hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS>(p, mk, cu, s)
                                : run_bk<D, 2, MODE, BIAS>(p, mk, cu, s);
   if (e != hipSuccess) return e;

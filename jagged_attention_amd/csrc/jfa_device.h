@@ -332,7 +332,10 @@ constexpr int XCDS = 8;
 constexpr int XCD_TICKET_STRIDE = 32;   // dwords between per-XCD counters (own cache lines)
 static_assert(XCDS == XTK_XCDS && XCD_TICKET_STRIDE == XTK_STRIDE, "workspace counter layout");
 
-struct ItemPipe {
+// HOME: workgroup g starts on item g (no ticket); otherwise every item, the first included,
+// comes from a ticket.
+template <bool HOME>
+struct ItemPipeT {
   uint32_t* ctr;             // XCDS counters, XCD_TICKET_STRIDE dwords apart, zeroed per call
   const ItemRec* items;
   int n_items;
@@ -346,7 +349,7 @@ struct ItemPipe {
   }
   // workgroups that start on XCD x's list (they take its first entries without a ticket)
   __device__ __forceinline__ int homed(int x) const {
-    return ((int)gridDim.x - x + XCDS - 1) / XCDS;
+    return HOME ? ((int)gridDim.x - x + XCDS - 1) / XCDS : 0;
   }
   __device__ __forceinline__ void load_record(int w, int lane) {
     if (lane == IF_W) v = w;
@@ -390,10 +393,19 @@ struct ItemPipe {
   // first descriptor into dst (wave 0; the caller then synchronises the workgroup)
   __device__ __forceinline__ void start(int* dst, int lane) {
     cx = blockIdx.x % XCDS;
-    load_record(blockIdx.x, lane);
+    if constexpr (HOME) {
+      load_record(blockIdx.x, lane);
+    } else {
+      // a list that starts while other workgroups are still busy elsewhere: claim the first
+      // item like every later one, so that no item waits for a particular workgroup
+      claim(lane);
+      resolve(lane);
+    }
     publish(dst, lane);
   }
 };
+
+using ItemPipe = ItemPipeT<true>;
 
 // Item fields read back from LDS, made wave-uniform.
 __device__ __forceinline__ int item_field(const int* d, int f) {

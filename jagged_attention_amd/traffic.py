@@ -26,7 +26,8 @@ ROOT = os.path.dirname(HERE)
 
 
 # timing name -> the source file that defines the kernel
-KERNEL_SOURCE = {"jfa_bwd_dkdv": "bwd.hip", "jfa_bwd_dq": "bwd.hip", "jfa_fwd_bf16": "fwd.hip",
+KERNEL_SOURCE = {"jfa_bwd_kvq": "bwd.hip", "jfa_bwd_dkdv": "bwd.hip", "jfa_bwd_dq": "bwd.hip",
+                 "jfa_fwd_bf16": "fwd.hip",
                  "jfa_fwd_mxfp8": "fwd.hip", "jfa_fwd_combine": "fwd.hip",
                  "jfa_schedule": "sched.hip", "jfa_offsets": "sched.hip",
                  "jfa_quant_mxfp8": "quant.hip", "jfa_fwd_f32": "f32.hip",
@@ -57,14 +58,14 @@ def source_hash(kernel: str | None = None) -> str:
 # device kernel name -> the timing name bench.py reports
 def timing_name(kernel: str) -> str | None:
     k = kernel
+    if "bwd_kvq_kernel" in k:
+        return "jfa_bwd_kvq"
     if "bwd_kv_kernel" in k:
         return "jfa_bwd_dkdv"
     if "bwd_q_kernel" in k:
         return "jfa_bwd_dq"
     if "combine_kernel" in k:
         return "jfa_fwd_combine"
-    if "delta_kernel" in k:
-        return "jfa_bwd_delta"
     if "fwd_kernel" in k:
         m = re.search(r"fwd_kernel<[^>]*(true|false)>", k)
         return "jfa_fwd_mxfp8" if (m and m.group(1) == "true") else "jfa_fwd_bf16"

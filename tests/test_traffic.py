@@ -19,6 +19,8 @@ def test_timing_names():
         "jfa_fwd_bf16"
     assert traffic.timing_name("jfa::(anonymous namespace)::fwd_kernel<128, 4, 0, 1, true>") == \
         "jfa_fwd_mxfp8"
+    assert traffic.timing_name("void jfa::(anonymous namespace)::bwd_kvq_kernel<128, 4, 0, 1>"
+                               "(jfa::BwdParams)") == "jfa_bwd_kvq"
     assert traffic.timing_name("__amd_rocclr_copyBuffer") == "copy"
     assert traffic.timing_name("something_else") is None
 
