@@ -530,8 +530,6 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (a.want_bias_off)
     scan_to(a.bias_off, B, [&](int64_t b) { return qlen((int)b) * klen((int)b); }, sh.red);
 
-  // per-sample tile base [B+1]: in LDS (the sort's counter space, idle during generation)
-  // whenever it fits, since every tile looks its sample up there by binary search
   // per-sample tile base [B+1]: in LDS (the sort-key space, idle during generation) whenever
   // it fits, since every tile looks its sample up there by binary search
   int32_t* lds_ints = reinterpret_cast<int32_t*>(sh.sa);
@@ -547,14 +545,38 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   const int64_t ntiles =
       want_f ? scan_to(s_base, B, [&](int64_t b) { return cdiv(qlen((int)b), tc.bm); }, sh.red) : 0;
   if (ntiles > a.cap_t) overflow = 1;
+  // kv steps of forward tile tau, and its sample (32-bit arithmetic: the offsets check bounds
+  // every length far below 2^31)
   auto fwd_steps = [&](int64_t tau, int& b, int64_t& t) -> int64_t {
     b = owner_of(s_base, B, tau);
     t = tau - s_base[b];
-    const int64_t n = qlen(b), m = klen(b);
-    const int64_t r1 = min((t + 1) * tc.bm, n);
-    int64_t e = m;
-    if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
-    return cdiv(e, tc.bn);
+    const int n = (int)qlen(b), m = (int)klen(b);
+    const int r1 = min(((int)t + 1) * tc.bm, n);
+    int e = m;
+    if (a.causal) e = max(0, min(m, r1 + (m - n)));
+    return (e + tc.bn - 1) / tc.bn;
+  };
+  // every tile's sample and steps once, into the sort's counter space (idle until the list is
+  // ranked): the cost pass, the scans and the record generator read them from there
+  const bool tile_cache = want_f && !overflow && ntiles <= 8 * ST;
+  int32_t* t_b = sh.T;
+  int32_t* t_st = sh.T + 8 * ST;
+  if (tile_cache) {
+    for (int64_t tau = tid; tau < ntiles; tau += ST) {
+      int b;
+      int64_t t;
+      t_st[tau] = (int32_t)fwd_steps(tau, b, t);
+      t_b[tau] = b;
+    }
+    __syncthreads();
+  }
+  auto steps_of = [&](int64_t tau, int& b, int64_t& t) -> int64_t {
+    if (tile_cache) {
+      b = t_b[tau];
+      t = tau - s_base[b];
+      return t_st[tau];
+    }
+    return fwd_steps(tau, b, t);
   };
   int64_t C = 0;
   int64_t nrec = 0, nslot = 0, ncomb = 0;
@@ -569,18 +591,19 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
     int64_t part = 0;
     for (int64_t tau = tid; tau < ntiles; tau += ST) {
       int b; int64_t t;
-      part += max((int64_t)1, fwd_steps(tau, b, t));
+      part += max((int64_t)1, steps_of(tau, b, t));
     }
     int64_t tot;
     block_scan(part, &tot, sh.red);
     if (tc.slots > 0) C = max((int64_t)8, cdiv((int64_t)a.H * tot, tc.slots));
     auto nch_of = [&](int64_t tau) -> int64_t {
       int b; int64_t t;
-      const int64_t s = fwd_steps(tau, b, t);
-      return (C > 0 && s > C) ? cdiv(s, C) : 1;
+      const int st = (int)steps_of(tau, b, t);
+      return (C > 0 && st > C) ? (st + (int)C - 1) / (int)C : 1;   // C < st <= MAX_COST
     };
     nrec = scan_to(t_rb, ntiles, nch_of, sh.red);
-    nslot = scan_to(t_sb, ntiles, [&](int64_t tau) { int64_t c = nch_of(tau); return c > 1 ? c : 0; },
+    nslot = scan_to(t_sb, ntiles,
+                    [&](int64_t tau) { int64_t c = nch_of(tau); return c > 1 ? c : 0; },
                     sh.red);
     ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; }, sh.red);
     if (nrec > a.cap_f || nrec > a.cap_t || ncomb > a.cap_c || nslot > a.cap_slots) overflow = 1;
@@ -598,20 +621,21 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       }
       int b;
       int64_t t;
-      const int64_t st = fwd_steps(tau, b, t);
-      const int64_t nch = (C > 0 && st > C) ? cdiv(st, C) : 1;
-      const int64_t kb = c * st / nch, ke = (c + 1) * st / nch;
-      r = make_int4(b, (int)t, (int)kb, (int)ke);
-      sl = nch > 1 ? (int)(t_sb[tau] + c) : -1;
-      cost = (int)max((int64_t)1, ke - kb);
-      if (nch > 1 && c == 0) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], (int)nch);
+      const int st = (int)steps_of(tau, b, t);
+      const int nch = (C > 0 && st > C) ? (st + (int)C - 1) / (int)C : 1;
+      const int ci = (int)c;
+      const int kb = ci * st / nch, ke = (ci + 1) * st / nch;
+      r = make_int4(b, (int)t, kb, ke);
+      sl = nch > 1 ? t_sb[tau] + ci : -1;
+      cost = max(1, ke - kb);
+      if (nch > 1 && ci == 0) a.comb[t_cb[tau]] = make_int4(b, (int)t, t_sb[tau], nch);
     };
     done_f = rank_emit(a, sh, (int)nrec, rec_f, a.fwd, a.fwd_slot, a.fwd_items, qo, ko);
   }
   if (want_f && !overflow && !done_f) {
     for (int64_t tau = tid; tau < ntiles; tau += ST) {
       int b; int64_t t;
-      const int64_t s = fwd_steps(tau, b, t);
+      const int64_t s = steps_of(tau, b, t);
       const int64_t nch = (C > 0 && s > C) ? cdiv(s, C) : 1;
       const int64_t rb = t_rb[tau];
       for (int64_t c = 0; c < nch; ++c) {
@@ -627,11 +651,14 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   }
 
   // ================= q-stationary backward list =================
-  auto one_q = [&](int b) { return (tc.fuse & 1) && cdiv(qlen(b), tc.bq_bm) == 1; };
-  auto one_k = [&](int b) { return (tc.fuse & 2) && !one_q(b) && cdiv(klen(b), tc.bk_bn) == 1; };
+  auto one_q = [&](int b) { return (tc.fuse & 1) && qlen(b) > 0 && qlen(b) <= tc.bq_bm; };
+  auto one_k = [&](int b) {
+    return (tc.fuse & 2) && !one_q(b) && klen(b) > 0 && klen(b) <= tc.bk_bn;
+  };
   int64_t nq = 0, nk = 0;
   if (want_q && !overflow) {
-    nq = scan_to(s_base, B, [&](int64_t b) { return one_k((int)b) ? 0 : cdiv(qlen((int)b), tc.bq_bm); },
+    nq = scan_to(s_base, B,
+                 [&](int64_t b) { return one_k((int)b) ? 0 : cdiv(qlen((int)b), tc.bq_bm); },
                  sh.red);
     if (nq > a.cap_q || nq > a.cap_t) overflow = 1;
   }
@@ -639,20 +666,14 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (want_q && !overflow) {
     auto rec_q = [&](int tau, int4& r, int& sl, int& cost) {
       const int b = owner_of(s_base, B, tau);
-      const int64_t t = tau - s_base[b];
-      const int64_t n = qlen(b), m = klen(b);
-      int64_t steps;
-      if (one_q(b)) {
-        steps = cdiv(m, tc.bq_bn);
-      } else {
-        const int64_t r1 = min((t + 1) * tc.bq_bm, n);
-        int64_t e = m;
-        if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
-        steps = cdiv(e, tc.bq_bn);
-      }
-      r = make_int4(b, (int)t, 0, (int)steps);
+      const int t = tau - s_base[b];
+      const int n = (int)qlen(b), m = (int)klen(b);
+      int e = m;
+      if (!one_q(b) && a.causal) e = max(0, min(m, min((t + 1) * tc.bq_bm, n) + (m - n)));
+      const int steps = (e + tc.bq_bn - 1) / tc.bq_bn;
+      r = make_int4(b, t, 0, steps);
       sl = -1;
-      cost = (int)max((int64_t)1, steps);
+      cost = max(1, steps);
     };
     done_q = rank_emit(a, sh, (int)nq, rec_q, a.bq, nullptr, a.bq_items, qo, ko);
   }
@@ -680,7 +701,8 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
 
   // ================= kv-stationary backward list =================
   if (want_k && !overflow) {
-    nk = scan_to(s_base, B, [&](int64_t b) { return one_q((int)b) ? 0 : cdiv(klen((int)b), tc.bk_bn); },
+    nk = scan_to(s_base, B,
+                 [&](int64_t b) { return one_q((int)b) ? 0 : cdiv(klen((int)b), tc.bk_bn); },
                  sh.red);
     if (nk > a.cap_k || nk > a.cap_t) overflow = 1;
   }
@@ -688,17 +710,17 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (want_k && !overflow) {
     auto rec_k = [&](int tau, int4& r, int& sl, int& cost) {
       const int b = owner_of(s_base, B, tau);
-      const int64_t u = tau - s_base[b];
-      const int64_t n = qlen(b), m = klen(b);
-      const int64_t nqs = cdiv(n, tc.bk_bm);
-      int64_t first = 0;
+      const int u = tau - s_base[b];
+      const int n = (int)qlen(b), m = (int)klen(b);
+      const int nqs = (n + tc.bk_bm - 1) / tc.bk_bm;
+      int first = 0;
       if (a.causal && !one_k(b)) {
-        const int64_t i0 = max((int64_t)0, u * tc.bk_bn - (m - n));
+        const int i0 = max(0, u * tc.bk_bn - (m - n));
         first = i0 >= n ? nqs : i0 / tc.bk_bm;
       }
-      r = make_int4(b, (int)u, (int)first, (int)nqs);
+      r = make_int4(b, u, first, nqs);
       sl = -1;
-      cost = (int)max((int64_t)1, nqs - first);
+      cost = max(1, nqs - first);
     };
     done_k = rank_emit(a, sh, (int)nk, rec_k, a.bk, nullptr, a.bk_items, qo, ko);
   }
