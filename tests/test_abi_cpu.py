@@ -135,6 +135,12 @@ def test_other_entry_points_host_errors():
     lib = jfa.load()
     assert lib.jfa_lengths_to_offsets(None, 4, FAKE, None, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_lengths_to_offsets(FAKE, -1, FAKE, None, None) == _lib.JFA_ERR_INVALID_ARG
+    # BlockAttention offsets: block < 1, a negative batch or out_batch, null or misaligned
+    assert lib.jfa_block_offsets(FAKE, 4, 0, FAKE, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_block_offsets(FAKE, -1, 4, FAKE, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_block_offsets(FAKE, 4, 4, FAKE, -1, None, None) == _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_block_offsets(None, 4, 4, FAKE, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_block_offsets(FAKE, 4, 4, FAKE + 2, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_quantize_mxfp8(FAKE, 10, 48, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_quantize_mxfp8(FAKE + 2, 10, 64, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
     out = ctypes.c_int32(0)
