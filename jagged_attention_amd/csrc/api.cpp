@@ -149,7 +149,7 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.total_q = p.total_q;
   a.total_kv = p.total_kv;
   a.tc = tc;
-  a.want_bias_off = 1;
+  a.want_bias_off = p.bias_kind == JFA_BIAS_DENSE;   // only a dense bias is addressed by them
   a.lists = 7;
   a.hd_bytes = (int64_t)p.heads * p.head_dim * (p.dtype == JFA_F32 ? 4 : (p.dtype == JFA_BF16 ? 2 : 1));
   if (p.dtype == JFA_MXFP8_E4M3) a.hd_bytes = (int64_t)p.heads * p.head_dim * 2;   // bf16 output rows

@@ -601,11 +601,44 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int st = (int)steps_of(tau, b, t);
       return (C > 0 && st > C) ? (st + (int)C - 1) / (int)C : 1;   // C < st <= MAX_COST
     };
-    nrec = scan_to(t_rb, ntiles, nch_of, sh.red);
-    nslot = scan_to(t_sb, ntiles,
-                    [&](int64_t tau) { int64_t c = nch_of(tau); return c > 1 ? c : 0; },
-                    sh.red);
-    ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; }, sh.red);
+    // record base, slot base and combine index of every tile in one scan: the three counts
+    // share a 64-bit word in 21-bit fields (each total stays below 2^21 when the tiles are
+    // cached: at most 8192 tiles, and the split chunks are bounded by the slots)
+    if (tile_cache && 2 * (int64_t)tc.slots + ntiles < (1 << 20)) {
+      int64_t carry = 0;
+      for (int64_t base = 0; base < ntiles; base += ST) {
+        const int64_t tau = base + tid;
+        int64_t v = 0;
+        if (tau < ntiles) {
+          const int64_t c = nch_of(tau);
+          v = c | ((c > 1 ? c : 0) << 21) | ((int64_t)(c > 1) << 42);
+        }
+        int64_t tot;
+        const int64_t ex = carry + block_scan(v, &tot, sh.red);
+        if (tau < ntiles) {
+          t_rb[tau] = (int32_t)(ex & 0x1FFFFF);
+          t_sb[tau] = (int32_t)((ex >> 21) & 0x1FFFFF);
+          t_cb[tau] = (int32_t)(ex >> 42);
+        }
+        carry += tot;
+      }
+      if (tid == 0) {
+        t_rb[ntiles] = (int32_t)(carry & 0x1FFFFF);
+        t_sb[ntiles] = (int32_t)((carry >> 21) & 0x1FFFFF);
+        t_cb[ntiles] = (int32_t)(carry >> 42);
+      }
+      __syncthreads();
+      nrec = carry & 0x1FFFFF;
+      nslot = (carry >> 21) & 0x1FFFFF;
+      ncomb = carry >> 42;
+    } else {
+      nrec = scan_to(t_rb, ntiles, nch_of, sh.red);
+      nslot = scan_to(t_sb, ntiles,
+                      [&](int64_t tau) { int64_t c = nch_of(tau); return c > 1 ? c : 0; },
+                      sh.red);
+      ncomb = scan_to(t_cb, ntiles, [&](int64_t tau) { return nch_of(tau) > 1 ? 1 : 0; },
+                      sh.red);
+    }
     if (nrec > a.cap_f || nrec > a.cap_t || ncomb > a.cap_c || nslot > a.cap_slots) overflow = 1;
   }
   bool done_f = false;
