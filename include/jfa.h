@@ -81,7 +81,7 @@ typedef struct {
                                must be 0 or -1 for softmax */
   int32_t bias_kind;        /* jfa_bias_kind */
   int32_t num_buckets;      /* RELPOS table width, 1..4096 (64 for the GEM workloads) */
-  int32_t split_slots;      /* forward tail balancing: 0 = auto (concurrent workgroups of the
+  int32_t split_slots;      /* forward tail balancing: 0 = auto (the compute units of the
                                device), >0 = this many, <0 = never split a query tile */
   int32_t bwd_fuse;         /* -1 default (on where built), 0 off: single-pass backward for
                                samples with one query tile (64-row query tiles) or one key
