@@ -142,42 +142,6 @@ __device__ __forceinline__ void store_diag(float* rp, int idx, float v) {
   for (int k = 0; k < 4; ++k) rp[k * RP + idx + k] = v;
 }
 
-// Scheduling pattern for a region holding the MFMAs (and their LDS operand reads) of one
-// phase and the VALU work of another: a few reads ahead, then MFMA / read / VALU groups.
-#ifndef JFA_SCHED_VARIANT
-#define JFA_SCHED_VARIANT 1
-#endif
-template <int NM>
-__device__ __forceinline__ void kv_interleave(int id) {
-#if JFA_SCHED_VARIANT == 1
-  (void)id;
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-  }
-#elif JFA_SCHED_VARIANT == 2
-  (void)id;
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-  }
-#elif JFA_SCHED_VARIANT == 4
-  (void)id;
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-  }
-#else
-  (void)id;
-#endif
-}
-
 // ================================================= key-stationary dK, dV
 template <int D, int NW, int BIAS>
 struct KvLds {
