@@ -70,6 +70,7 @@ def lib():
         _lib.ora_relpos_bucket.restype = ctypes.c_int
         _lib.ora_forward.argtypes = [P] * 10
         _lib.ora_backward.argtypes = [P] * 12
+        _lib.ora_bias_grad.argtypes = [P] * 10
         _lib.ora_schedule.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                       P, P, P, P, P, ctypes.c_int64, P]
         _lib.ora_e4m3_decode.argtypes = [ctypes.c_int]
@@ -197,6 +198,25 @@ def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bi
     lib().ora_backward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                        _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
+
+
+def bias_grad(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
+              bias_kind="relpos", num_buckets=64, scale=None, normalize=None, block=0):
+    """Gradient of <O, dout> with respect to the bias (fp64): the relative-position table
+    [H][num_buckets], or a dense bias in its own layout."""
+    assert bias_kind in ("relpos", "dense") and bias is not None
+    _check_block(block, q_lens, kv_lens, bias_kind)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Tq, H, d = q.shape
+    qo, ko = offsets(q_lens), offsets(kv_lens)
+    B = qo.shape[0] - 1
+    bo = bias_offsets(q_lens, kv_lens)
+    bias64 = _f64(bias)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    db = np.zeros_like(bias64)
+    lib().ora_bias_grad(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
+                        _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(db))
+    return db
 
 
 def case_forward(case, **kw):

@@ -333,6 +333,83 @@ void ora_backward(const ora_problem* p, const int64_t* qo, const int64_t* ko,
   }
 }
 
+/* ------------------------------------------------------------ bias gradient */
+
+/* Gradient of <O, dO> with respect to the additive bias ("Meta GEM Training Efficiency: ...",
+ * section "Bottleneck move 1": custom biases, which a model trains).  The bias enters every
+ * score S_ij additively, so its gradient is dS_ij = dL/dS_ij on visible pairs:
+ *   softmax: dS = P (dO.V_j - D_i), D_i = dO_i.O_i;   GDPA: dS = act'(S) w (dO_i.V_j).
+ * Dense bias (bias_kind 2): dbias has the bias layout, dS per element, 0 on pairs that are not
+ * visible.  Relative-position table (bias_kind 1): dbias [H][num_buckets] accumulates dS over
+ * every visible pair of its bucket; per-(sample, head) partials are summed over samples in
+ * order, so the sum does not depend on the thread count. */
+void ora_bias_grad(const ora_problem* p, const int64_t* qo, const int64_t* ko,
+                   const double* q, const double* k, const double* v, const double* bias,
+                   const int64_t* bo, const double* dout, double* dbias) {
+  const int64_t B = p->batch, H = p->heads, d = p->head_dim, NB = p->num_buckets;
+  double* part = NULL;
+  if (p->bias_kind == 1) part = (double*)calloc((size_t)(B * H * NB), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t item = 0; item < B * H; ++item) {
+    const int64_t b = item / H;
+    const int h = (int)(item % H);
+    const int64_t n = qo[b + 1] - qo[b], m = ko[b + 1] - ko[b];
+    double* s = (double*)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+    double* oi = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t qrow = qo[b] + i;
+      const double* doi = dout + (qrow * H + h) * d;
+      int64_t nvis = 0;
+      for (int64_t j = 0; j < m; ++j) {
+        if (p->bias_kind == 2) dbias[H * bo[b] + (int64_t)h * n * m + i * m + j] = 0.0;
+        if (!visible(p, i, j, n, m)) continue;
+        s[j] = score(p, q, k, bias, bo, b, h, qrow, ko[b] + j, i, j, n, m);
+        ++nvis;
+      }
+      if (nvis == 0) continue;
+      double mx = -INFINITY, l = 0.0, D = 0.0;
+      if (p->mode == 0) {
+        for (int64_t j = 0; j < m; ++j)
+          if (visible(p, i, j, n, m) && s[j] > mx) mx = s[j];
+        for (int64_t j = 0; j < m; ++j)
+          if (visible(p, i, j, n, m)) l += exp(s[j] - mx);
+        for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+          if (!visible(p, i, j, n, m)) continue;
+          const double pij = exp(s[j] - mx) / l;
+          const double* vj = v + ((ko[b] + j) * H + h) * d;
+          for (int64_t c = 0; c < d; ++c) oi[c] += pij * vj[c];
+        }
+        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];
+      }
+      const double w = gdpa_weight(p, i, m);
+      for (int64_t j = 0; j < m; ++j) {
+        if (!visible(p, i, j, n, m)) continue;
+        const double* vj = v + ((ko[b] + j) * H + h) * d;
+        double dp = 0.0;
+        for (int64_t c = 0; c < d; ++c) dp += doi[c] * vj[c];
+        double ds;
+        if (p->mode == 0) ds = exp(s[j] - mx) / l * (dp - D);
+        else ds = act_grad(p->mode, s[j]) * w * dp;
+        if (p->bias_kind == 2) {
+          dbias[H * bo[b] + (int64_t)h * n * m + i * m + j] = ds;
+        } else if (p->bias_kind == 1) {
+          part[item * NB + ora_relpos_bucket((i + (m - n)) - j, p->num_buckets)] += ds;
+        }
+      }
+    }
+    free(s);
+    free(oi);
+  }
+  if (p->bias_kind == 1) {
+    for (int64_t x = 0; x < H * NB; ++x) dbias[x] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t k2 = 0; k2 < NB; ++k2) dbias[h * NB + k2] += part[(b * H + h) * NB + k2];
+    free(part);
+  }
+}
+
 /* ------------------------------------------------------------- tile lists */
 
 typedef struct {

@@ -518,3 +518,90 @@ def test_block_attention_special_cases(oracle_mod):
     s = (q * k).sum(-1) / math.sqrt(8)
     a = s / (1 + np.exp(-s))
     assert max_abs(og[:, 0], a[:, None] * np.asarray(g.v, np.float64)[:, 0]) < 1e-14
+
+
+# ------------------------------------------------------------ bias gradient
+
+def _torch_bias_grad(case, lens_q, lens_kv, bias, bias_kind, mode, causal, bucket_fn):
+    """d<O, dO>/d bias by torch fp64 autograd, with the bias as the leaf (per-sample SDPA or the
+    plain GDPA formula, as in the other pins)."""
+    from tests.helpers import bias_matrix, gdpa_sample, sdpa_sample, visible_mask
+    q = torch.as_tensor(np.asarray(case.q, np.float64))
+    k = torch.as_tensor(np.asarray(case.k, np.float64))
+    v = torch.as_tensor(np.asarray(case.v, np.float64))
+    do = torch.as_tensor(np.asarray(case.dout, np.float64))
+    leaf = torch.as_tensor(np.asarray(bias, np.float64)).clone().requires_grad_(True)
+    H, d = q.shape[1], q.shape[2]
+    scale = 1.0 / math.sqrt(d)
+    loss = torch.zeros((), dtype=torch.float64)
+    qo = ko = 0
+    for b, (n, m) in enumerate(zip(lens_q, lens_kv)):
+        n, m = int(n), int(m)
+        for h in range(H):
+            if n == 0 or m == 0:
+                continue
+            vis = visible_mask(n, m, causal)
+            bmat = bias_matrix(leaf, bias_kind, h, n, m, H, b, lens_q, lens_kv, bucket_fn)
+            qs, ks, vs = q[qo:qo + n, h], k[ko:ko + m, h], v[ko:ko + m, h]
+            if mode == "softmax":
+                o, _ = sdpa_sample(qs, ks, vs, bmat, vis, scale)
+                dead = ~vis.any(dim=1)
+                o = torch.where(dead[:, None], torch.zeros_like(o), o)
+            else:
+                o = gdpa_sample(qs, ks, vs, bmat, vis, scale, mode)
+            loss = loss + (o * do[qo:qo + n, h]).sum()
+        qo += n
+        ko += m
+    (g,) = torch.autograd.grad(loss, (leaf,))
+    return g.numpy()
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
+def test_bias_grad_vs_torch(oracle_mod, mode, causal, bias_kind):
+    ql, kl = ([5, 0, 9, 12], [5, 0, 9, 12]) if causal else ([4, 7, 3], [9, 2, 3])
+    case = custom_case(ql, kl, 2, 8, dtype="f32", mode=mode, causal=causal,
+                       bias_kind=bias_kind, num_buckets=64, seed=71, bias_std=0.5)
+    got = oracle_mod.bias_grad(case.q, case.k, case.v, case.dout, ql, kl, mode=mode,
+                               causal=causal, bias=case.bias, bias_kind=bias_kind)
+    want = _torch_bias_grad(case, ql, kl, case.bias, bias_kind, mode, causal,
+                            oracle_mod.relpos_bucket)
+    assert got.shape == want.shape
+    assert max_abs(got, want) < 1e-11
+    assert np.abs(want).max() > 1e-3          # the gradient is not trivially zero
+
+
+def test_bias_grad_softmax_rows_sum_to_zero(oracle_mod):
+    # softmax: sum_j dS_ij = sum_j P_ij (dP_ij - D_i) = D_i - D_i = 0 for every query row, so
+    # every head's table gradient sums to zero over the buckets, and a dense bias's gradient
+    # sums to zero along every row
+    ql = [40, 17, 1, 60]
+    case = custom_case(ql, ql, 3, 16, dtype="f32", mode="softmax", causal=True,
+                       bias_kind="relpos", seed=72, bias_std=0.5)
+    g = oracle_mod.bias_grad(case.q, case.k, case.v, case.dout, ql, ql, causal=True,
+                             bias=case.bias)
+    assert np.abs(g.sum(axis=1)).max() < 1e-12 * max(1.0, np.abs(g).max())
+    dense = custom_case(ql, ql, 2, 16, dtype="f32", mode="softmax", causal=True,
+                        bias_kind="dense", seed=73, bias_std=0.5)
+    gd = oracle_mod.bias_grad(dense.q, dense.k, dense.v, dense.dout, ql, ql, causal=True,
+                              bias=dense.bias, bias_kind="dense")
+    off = 0
+    for n in ql:
+        blk = gd[off:off + 2 * n * n].reshape(2, n, n)
+        assert np.abs(blk.sum(axis=2)).max() < 1e-12
+        off += 2 * n * n
+
+
+def test_bias_grad_block_attention_is_sum_over_blocks(oracle_mod):
+    # the table is shared by all blocks: BlockAttention's table gradient equals that of every
+    # block taken as a sample of its own, summed
+    lens, w = [11, 0, 4, 9], 4
+    case = custom_case(lens, lens, 2, 8, dtype="f32", mode="gelu", causal=True,
+                       bias_kind="relpos", seed=74, bias_std=0.5)
+    got = oracle_mod.bias_grad(case.q, case.k, case.v, case.dout, lens, lens, mode="gelu",
+                               causal=True, bias=case.bias, block=w)
+    blocks = _split_lengths(lens, w)
+    want = _torch_bias_grad(case, blocks, blocks, case.bias, "relpos", "gelu", True,
+                            oracle_mod.relpos_bucket)
+    assert max_abs(got, want) < 1e-11
