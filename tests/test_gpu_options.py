@@ -86,3 +86,28 @@ def test_single_pass_classes_against_two_pass(bwd_fuse, d, ql, kl):
     case = custom_case(ql, kl, 2, d, dtype="bf16", mode="silu", seed=55)
     say(f"[options] bwd_fuse={bwd_fuse} d={d}")
     _run(case, bwd_fuse=bwd_fuse)
+
+
+@pytest.mark.parametrize("mode,causal,bias_kind", [("softmax", True, "relpos"),
+                                                    ("silu", False, "dense")])
+def test_autograd_function(mode, causal, bias_kind):
+    """The torch.autograd.Function wrapper: gradients through loss.backward() equal the oracle's
+    backward of <O, dO>."""
+    import jagged_attention_amd as jfa
+    ql = [150, 0, 70]
+    kl = ql if causal else [90, 12, 130]
+    case = custom_case(ql, kl, 2, 128, dtype="bf16", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=56)
+    say(f"[options] autograd mode={mode}")
+    dc = device_case(case)
+    q, k, v = (dc[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    opts = dict(mode=mode, causal=causal, bias_kind=bias_kind, num_buckets=case.num_buckets)
+    o = jfa.JaggedAttention.apply(q, k, v, dc["qo"], dc["ko"], dc["bias"], opts)
+    (o.float() * dc["dout"].float()).sum().backward()
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.case_forward(case)
+    dq_ref, dk_ref, dv_ref = oracle.case_backward(case)
+    compare("O", o, o_ref, "bf16")
+    compare("dQ", q.grad, dq_ref, "bf16")
+    compare("dK", k.grad, dk_ref, "bf16")
+    compare("dV", v.grad, dv_ref, "bf16")
