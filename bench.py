@@ -243,9 +243,11 @@ KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 1
                          "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6}
 
 
-def traffic_for(kernel):
-    """HBM traffic of `kernel` per launch from the committed counter summary, if current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_for(kernel, workload):
+    """HBM traffic of `kernel` per launch on `workload` from the committed counter summary, if
+    current."""
+    from jagged_attention_amd.traffic import file_tag
+    path = os.path.join(ROOT, "profiles", f"traffic_{file_tag(workload)}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -366,7 +368,8 @@ def main():
     achieved = per_launch_flops / (cand[dom]["avg_ms"] * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if "mxfp8" in dom else PEAK_BF16_TFLOPS
     roof = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
-                unit="TFLOP/s", frac=round(achieved / peak, 4), traffic=traffic_for(dom),
+                unit="TFLOP/s", frac=round(achieved / peak, 4),
+                traffic=traffic_for(dom, w.case.name),
                 flops_per_launch=per_launch_flops, avg_ms=cand[dom]["avg_ms"])
 
     extra = {}

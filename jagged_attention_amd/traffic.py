@@ -4,7 +4,8 @@ Two counter passes of the same bench command (one with FETCH_SIZE, one with WRIT
 KiB per dispatch) are turned into bytes per launch.  Each counter is scaled by what it reads for
 a plain device copy of a known size that bench.py runs in the same process (--copy-mib), so the
 result is in the copy's units: bytes that a plain copy would move.  The summary goes to
-profiles/traffic.json (read by bench.py, valid only for the kernel sources it was taken from)
+profiles/traffic_<workload>.json (read by bench.py, valid only for the kernel sources it was
+taken from)
 and a short markdown table.
 
 Usage:
@@ -124,6 +125,11 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
     return kernels, calib
 
 
+def file_tag(workload: str) -> str:
+    """The workload name as used in profile file names."""
+    return re.sub(r"[^a-z0-9]+", "_", workload.lower()).strip("_")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("fetch_csv")
@@ -136,21 +142,21 @@ def main():
     kernels, calib = summarize(a.fetch_csv, a.write_csv, a.copy_mib << 20)
     rec = dict(source_hash=source_hash(), workload=a.workload, command=a.command,
                calibration=calib, kernels=kernels)
-    with open(os.path.join(a.out, "traffic.json"), "w") as fh:
+    with open(os.path.join(a.out, f"traffic_{file_tag(a.workload)}.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     lines = [f"# HBM traffic per launch: {a.workload}", "",
              f"Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each on `{a.command}`.",
              f"Calibration: a {a.copy_mib} MiB device copy in the same run read FETCH_SIZE "
              f"{calib['fetch_kib']:.0f} KiB and WRITE_SIZE {calib['write_kib']:.0f} KiB; factors "
              f"{calib['fetch_factor']} and {calib['write_factor']} convert the counters to bytes.",
-             f"Kernel sources (all files): {rec['source_hash']}; per kernel in traffic.json.", "",
+             f"Kernel sources (all files): {rec['source_hash']}; per kernel in the .json beside "
+             f"this file.", "",
              "| kernel | fetch MB | write MB | total MB / launch | dispatches |",
              "|---|---|---|---|---|"]
     for n, e in kernels.items():
         lines.append(f"| {n} | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} | "
                      f"{e['bytes_per_launch'] / 1e6:.1f} | {e['dispatches']} |")
-    name = re.sub(r"[^a-z0-9]+", "_", a.workload.lower()).strip("_")
-    with open(os.path.join(a.out, f"traffic_{name}.md"), "w") as fh:
+    with open(os.path.join(a.out, f"traffic_{file_tag(a.workload)}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
 
