@@ -1,6 +1,7 @@
 """GPU parity for problem options the workload tests leave at their defaults: an explicit QK
 scale, GDPA without the 1/kv_len weight, one and sixteen heads, a one-sample batch, and the
 two-pass backward forced on samples that would take the single pass."""
+import numpy as np
 import pytest
 import torch
 
@@ -111,3 +112,20 @@ def test_autograd_function(mode, causal, bias_kind):
     compare("dQ", q.grad, dq_ref, "bf16")
     compare("dK", k.grad, dk_ref, "bf16")
     compare("dV", v.grad, dv_ref, "bf16")
+
+
+@pytest.mark.parametrize("mode,causal,bias_kind", [("softmax", True, "relpos"),
+                                                    ("gelu", False, "dense")])
+def test_many_tiny_samples(mode, causal, bias_kind):
+    """5,000 samples of 0-9 rows: the scheduler's paths for more samples than its LDS offset
+    copy holds and for lists longer than its in-register ranking (sorted in global memory)."""
+    rng = np.random.default_rng(57)
+    ql = rng.integers(0, 10, size=5000)
+    # GDPA keys 8..15 as in the GELU workload: with one key its weight 1/kv_len is 1 and bf16
+    # rounding of P for the PV MFMA alone moves O by up to 0.04 (an fp64 simulation of that
+    # rounding reproduces the kernel's error exactly)
+    kl = ql if causal else rng.integers(8, 16, size=5000)
+    case = custom_case(ql, kl, 1, 64, dtype="bf16", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=57)
+    say(f"[options] 5000 tiny samples mode={mode}")
+    _run(case)
