@@ -52,11 +52,13 @@ def visible_pairs(q_lens, kv_lens, causal):
 class Workload:
     """Device buffers and preallocated outputs for one jfa_synth case."""
 
-    def __init__(self, case, with_backward=True, block=0):
+    def __init__(self, case, with_backward=True, block=0, dbias=False):
         import torch
         import jagged_attention_amd as jfa
         self.case = case
         self.block = block
+        # dbias: the backward also returns the bias gradient (jfa_backward_dbias)
+        self.want_dbias = bool(dbias) and case.bias is not None and with_backward
         dev = torch.device("cuda:0")
         self.q = case.q.to(dev)
         self.k = case.k.to(dev)
@@ -95,12 +97,13 @@ class Workload:
         self.nf = nf
         self.with_backward = self.dout is not None
         if self.with_backward:
-            nb = jfa.jfa_workspace_bytes(self.problem, True)
+            nb = jfa.jfa_workspace_bytes(self.problem, 2 if self.want_dbias else 1)
             self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
             self.nb = nb
             self.dq = torch.empty_like(self.q)
             self.dk = torch.empty_like(self.k)
             self.dv = torch.empty_like(self.v)
+            self.dbias = torch.empty_like(self.bias) if self.want_dbias else None
         if block:
             bl = np.array([min(block, n - s) for n in case.q_lens for s in range(0, n, block)],
                           dtype=np.int64)
@@ -140,7 +143,11 @@ class Workload:
         else:
             jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo,
                             ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
-        if self.with_backward:
+        if self.with_backward and self.want_dbias:
+            jfa.jfa_backward_dbias(self.problem, self.q, self.k, self.v, self.o, self.lse,
+                                   self.dout, self.qo, ko, self.bias, self.dq, self.dk, self.dv,
+                                   self.dbias, self.ws_b, self.nb)
+        elif self.with_backward:
             jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse, self.dout,
                              self.qo, ko, self.bias, self.dq, self.dk, self.dv, self.ws_b,
                              self.nb)
@@ -167,6 +174,8 @@ def outputs(w):
     out = [w.o] + ([w.lse] if w.lse is not None else [])
     if w.with_backward:
         out += [w.dq, w.dk, w.dv]
+    if w.want_dbias:
+        out.append(w.dbias)
     return out
 
 
@@ -229,7 +238,8 @@ def kernel_times(w, steps):
     for name in ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
                  "jfa_fwd_bf16", "jfa_fwd_mxfp8",
                  "jfa_fwd_f32",
-                 "jfa_fwd_combine", "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq"):
+                 "jfa_fwd_combine", "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq",
+                 "jfa_dbias_zero", "jfa_dbias_dq", "jfa_dbias_reduce"):
         ms, n = jfa.jfa_kernel_timing(name)
         if n:
             out[name] = dict(avg_ms=ms / n, launches=n)
@@ -303,10 +313,10 @@ def cpu_baseline(case, target_s=15.0):
                        f"{t:.1f} s)")
 
 
-def bench_config(cfg, steps, warmup, seed=None, block=0):
+def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False):
     from jfa_synth import make_case
     case = make_case(cfg, seed)
-    w = Workload(case, block=block)
+    w = Workload(case, block=block, dbias=dbias)
     sec = time_steps(w, steps, warmup)
     # the same step replayed as one HIP graph (no per-launch host work): reported beside it
     w.graph = capture_step(w)
@@ -318,6 +328,8 @@ def bench_config(cfg, steps, warmup, seed=None, block=0):
     ceiling = min(peak, intensity * PEAK_HBM_GBS / 1000.0)
     tf = flops / sec / 1e12
     name = case.name if not block else f"block{block}-" + case.name
+    if w.want_dbias:
+        name += "+dbias"
     return w, dict(workload=name, seed=case.seed, ms_per_step=sec * 1e3,
                    graph_ms_per_step=graph * 1e3, tflops=tf,
                    frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
@@ -389,6 +401,13 @@ def main():
         r["kernels"] = kernel_times(wx, 3)
         r["block_rows"] = BLOCK_ROWS
         extra["block_attention"] = r
+        del wx
+        torch.cuda.empty_cache()
+        # the headline step with the bias gradient (the relative-position table is trained)
+        log("[bench] bias gradient")
+        wx, r = bench_config(2, max(3, args.steps // 2), 2, dbias=True)
+        r["kernels"] = kernel_times(wx, 3)
+        extra["bias_gradient"] = r
         del wx
         torch.cuda.empty_cache()
 

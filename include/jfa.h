@@ -97,9 +97,9 @@ typedef struct {
  *          at element H * sum_{b'<b} n_b' * m_b'.  bias_h(b,i,j) = block[h][i][j].
  */
 
-/* Bytes of device workspace that jfa_forward (backward = 0) or jfa_backward (backward = 1)
- * needs for this problem; 0 if the problem is invalid.  With split_slots = 0 this queries the
- * current device. */
+/* Bytes of device workspace that jfa_forward (backward = 0), jfa_backward (backward = 1) or
+ * jfa_backward_dbias (backward = 2) needs for this problem; 0 if the problem is invalid.  With
+ * split_slots = 0 this queries the current device. */
 size_t jfa_workspace_bytes(const jfa_problem* p, int backward);
 
 /* Forward pass.  q/k/v: [rows, H, d] of the storage dtype; for MXFP8 they are E4M3 codes
@@ -120,6 +120,22 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
                         const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Backward pass that also returns the gradient of the additive bias ("Meta GEM Training
+ * Efficiency: ...", section "Bottleneck move 1": custom biases, which a model trains).  The bias
+ * enters each visible score additively, so its gradient is that pair's dS = dL/dS.  BF16 only
+ * and a bias is required (JFA_ERR_UNSUPPORTED otherwise); dbias must not be NULL.
+ *   JFA_BIAS_DENSE: dbias has the bias's own layout and dtype (bf16), dS per pair, 0 on pairs
+ *     that are not visible.
+ *   JFA_BIAS_RELPOS: dbias is fp32 [H][num_buckets], the sum of dS over the visible pairs of
+ *     each bucket, summed per query row and then over rows in a fixed order.
+ * Everything else as jfa_backward (dq, dk, dv identical up to the single-pass classes, which
+ * this call leaves off); workspace from jfa_workspace_bytes(p, 2).  Deterministic. */
+jfa_status jfa_backward_dbias(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout,
+                              const int32_t* q_offsets, const int32_t* kv_offsets,
+                              const void* bias, void* dq, void* dk, void* dv, void* dbias,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Tile sizes the kernels use for this problem, in the order
  * {bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse}: forward query/key tile rows, split slots

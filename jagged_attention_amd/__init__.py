@@ -10,7 +10,7 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # noqa: F401
-                   jfa_backward, jfa_block_offsets, jfa_build_schedule, jfa_forward,
+                   jfa_backward, jfa_backward_dbias, jfa_block_offsets, jfa_build_schedule, jfa_forward,
                    jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
                    jfa_read_device_status, jfa_set_kernel_timing, jfa_tile_config,
@@ -18,7 +18,8 @@ from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # n
 
 jfa_status_string = status_string
 
-__all__ = ["make_problem", "forward", "backward", "lengths_to_offsets", "block_offsets",
+__all__ = ["make_problem", "forward", "backward", "backward_dbias", "lengths_to_offsets",
+           "block_offsets",
            "quantize_mxfp8",
            "build_schedule", "JaggedAttention", "load"]
 
@@ -92,6 +93,27 @@ def backward(q, k, v, o, lse, dout, q_offsets, kv_offsets, *, mode: str = "softm
     jfa_backward(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
                  workspace, nbytes)
     return dq, dk, dv
+
+
+def backward_dbias(q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, *, mode: str = "softmax",
+                   causal: bool = False, bias_kind: str = "relpos", num_buckets: int = 64,
+                   qk_scale: float = 0.0, kv_len_normalize: int = -1, workspace=None):
+    """Returns (dq, dk, dv, dbias): dbias is fp32 [H, num_buckets] for a relative-position
+    table and bf16 in the bias's layout for a dense bias (bf16 inputs only)."""
+    import torch
+    problem = _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
+                          kv_len_normalize, 0)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbias = torch.empty_like(bias)
+    if workspace is None:
+        workspace, nbytes = _workspace(problem, 2, q.device)
+    else:
+        nbytes = workspace.numel()
+    jfa_backward_dbias(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
+                       dbias, workspace, nbytes)
+    return dq, dk, dv, dbias
 
 
 def lengths_to_offsets(lengths):

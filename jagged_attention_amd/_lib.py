@@ -25,7 +25,8 @@ DTYPES = {"f32": 0, "bf16": 1, "mxfp8": 2}
 BIAS_KINDS = {"none": 0, "relpos": 1, "dense": 2}
 
 # every symbol include/jfa.h declares
-EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_tile_config",
+EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_dbias",
+           "jfa_tile_config",
            "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
            "jfa_quantize_mxfp8",
            "jfa_read_device_status", "jfa_status_string", "jfa_set_kernel_timing",
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_forward.restype = ctypes.c_int
     lib.jfa_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.jfa_backward.restype = ctypes.c_int
+    lib.jfa_backward_dbias.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.jfa_backward_dbias.restype = ctypes.c_int
     lib.jfa_tile_config.argtypes = [PP, P]
     lib.jfa_tile_config.restype = ctypes.c_int
     lib.jfa_build_schedule.argtypes = [PP, P, P, P, P, P, P, P, P, I64, P, SZ, P]
@@ -119,8 +122,9 @@ def _stream(stream) -> Optional[int]:
 
 # ------------------------------------------------------- one per entry point
 
-def jfa_workspace_bytes(problem: JfaProblem, backward: bool) -> int:
-    return int(load().jfa_workspace_bytes(ctypes.byref(problem), int(bool(backward))))
+def jfa_workspace_bytes(problem: JfaProblem, backward: int) -> int:
+    """backward: 0 forward, 1 (or True) backward, 2 backward with the bias gradient."""
+    return int(load().jfa_workspace_bytes(ctypes.byref(problem), int(backward)))
 
 
 def jfa_forward(problem, q, k, v, q_scale, k_scale, v_scale, q_offsets, kv_offsets, bias, o, lse,
@@ -138,6 +142,15 @@ def jfa_backward(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq
                              _ptr(dout), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream))
     _check("jfa_backward", st)
+
+
+def jfa_backward_dbias(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
+                       dbias, workspace, workspace_bytes: int, stream=None) -> None:
+    st = load().jfa_backward_dbias(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(lse), _ptr(dout), _ptr(q_offsets), _ptr(kv_offsets),
+                                   _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+    _check("jfa_backward_dbias", st)
 
 
 def jfa_tile_config(problem: JfaProblem) -> dict:

@@ -138,6 +138,8 @@ Layout layout_of(const jfa_problem& p, const TileCfg& tc, int backward) {
     L.part_ml = take(4 * 2 * (size_t)L.cap_slots * H * tc.bm);
   }
   if (backward && p.mode == JFA_MODE_SOFTMAX) L.delta = take(4 * (size_t)H * std::max<int64_t>(p.total_q, 1));
+  if (backward == 2 && p.bias_kind == JFA_BIAS_RELPOS)
+    L.dbias_part = take(4 * 2 * (size_t)H * p.num_buckets * std::max<int64_t>(p.total_q, 1));
   L.total = off;
   return L;
 }
@@ -270,7 +272,7 @@ size_t jfa_workspace_bytes(const jfa_problem* p, int backward) {
   if (check_problem(p) != JFA_OK) return 0;
   TileCfg tc;
   if (tile_cfg(*p, &tc) != JFA_OK) return 0;
-  return layout_of(*p, tc, backward ? 1 : 0).total;
+  return layout_of(*p, tc, backward < 0 ? 0 : std::min(backward, 2)).total;
 }
 
 jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const void* v,
@@ -331,14 +333,21 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   return from_hip(e);
 }
 
-jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, const void* v,
-                        const void* o, const float* lse, const void* dout,
-                        const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
-                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+namespace {
+
+// The backward; with dbias (bias gradient wanted) the single-pass classes are off, so that every
+// pair's dS is formed in the query-stationary pass.
+jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout,
+                         const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                         void* dq, void* dk, void* dv, void* dbias, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   jfa_status st = check_problem(p);
   if (st != JFA_OK) return st;
   if (p->dtype == JFA_MXFP8_E4M3) return JFA_ERR_UNSUPPORTED;
+  if (dbias && (p->dtype != JFA_BF16 || p->bias_kind == JFA_BIAS_NONE))
+    return JFA_ERR_UNSUPPORTED;
+  if (dbias && !aligned(dbias, 4)) return JFA_ERR_INVALID_ARG;
   if (!q || !k || !v || !dout || !dq || !dk || !dv || !q_offsets || !kv_offsets || !workspace)
     return JFA_ERR_INVALID_ARG;
   if ((p->bias_kind != JFA_BIAS_NONE) != (bias != nullptr)) return JFA_ERR_INVALID_ARG;
@@ -351,7 +360,8 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   TileCfg tc;
   st = tile_cfg(*p, &tc);
   if (st != JFA_OK) return st;
-  const Layout L = layout_of(*p, tc, 1);
+  if (dbias) tc.fuse = 0;
+  const Layout L = layout_of(*p, tc, dbias ? 2 : 1);
   if (workspace_bytes < L.total) return JFA_ERR_WORKSPACE;
   const int cu = cu_count_of_current_device();
   if (cu <= 0) return JFA_ERR_LAUNCH;
@@ -385,6 +395,7 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   bp.bk = (const ItemRec*)(ws + L.bk);
   bp.xtk_q = (uint32_t*)(ws + L.xtk) + TK_BQ * XTK_XCDS * XTK_STRIDE;
   bp.xtk_k = (uint32_t*)(ws + L.xtk) + TK_BK * XTK_XCDS * XTK_STRIDE;
+  bp.batch = p->batch;
   bp.H = p->heads;
   bp.causal = p->causal;
   bp.bias_kind = p->bias_kind;
@@ -397,8 +408,36 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
   bp.scale = qk_scale_of(*p);
   bp.total_q = p->total_q;
   bp.total_kv = p->total_kv;
-  e = launch_backward(bp, tc, p->head_dim, p->dtype, L.cap_q * p->heads, L.cap_k * p->heads, cu, s);
+  if (dbias) {
+    bp.dbias = dbias;
+    bp.dbias_part = p->bias_kind == JFA_BIAS_RELPOS ? (float*)(ws + L.dbias_part) : nullptr;
+    e = launch_backward_dbias(bp, tc, p->head_dim, L.cap_q * p->heads, L.cap_k * p->heads, cu, s);
+  } else {
+    e = launch_backward(bp, tc, p->head_dim, p->dtype, L.cap_q * p->heads, L.cap_k * p->heads,
+                        cu, s);
+  }
   return from_hip(e);
+}
+
+}  // namespace
+
+jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return backward_impl(p, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
+                       nullptr, workspace, workspace_bytes, stream);
+}
+
+jfa_status jfa_backward_dbias(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout,
+                              const int32_t* q_offsets, const int32_t* kv_offsets,
+                              const void* bias, void* dq, void* dk, void* dv, void* dbias,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dbias) return JFA_ERR_INVALID_ARG;
+  return backward_impl(p, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv, dbias,
+                       workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,

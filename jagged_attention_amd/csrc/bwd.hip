@@ -649,8 +649,11 @@ struct QLds {
   static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 : 0);
 };
 
-// The query-stationary pass over the q-stationary list (HOME as for kv_pass).
-template <int D, int NW, int MODE, int BIAS, bool HOME>
+// The query-stationary pass over the q-stationary list (HOME as for kv_pass).  DB: also the
+// bias gradient, from each pair's dS as it is formed (dense: dS stored in the bias layout;
+// relative-position table: per-lane running sums by bucket, flushed into the lane's own partial
+// row, which a later kernel reduces in a fixed order).  DB runs without the single-pass classes.
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB = false>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   using L = QLds<D, NW, BIAS>;
@@ -716,6 +719,17 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       dof[ks] = as_bf16x8(ld16(rdo, qoff + 32 * ks + 16 * g));
     }
     float lse2 = 0.f, dlt = 0.f;
+    // bias gradient, relative-position table: the bucket being summed and its running sum
+    int db_k = -1;
+    float db_sum = 0.f;
+    auto db_flush = [&]() {
+      if constexpr (DB && BIAS == B_RELPOS) {
+        if (db_k >= 0) {
+          float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
+          pr[db_k] += db_sum;
+        }
+      }
+    };
     if constexpr (MODE == MODE_SOFTMAX) {
       if (qi < n) {
         lse2 = p.lse[(int64_t)h * p.total_q + qo + qi] * LOG2E;
@@ -847,6 +861,26 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
             act_pair<MODE>(x, a, da);
             d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
             p2[e] = valid ? a * wn : 0.f;
+          }
+          if constexpr (DB) {
+            const int j = j0 + blk * 32 + 8 * (ii >> 2) + 4 * g + (ii & 3);
+            if constexpr (BIAS == B_DENSE) {
+              // masked pairs store their zero; keys past the sample's end would wrap into the
+              // next row and are skipped
+              if (qi < n && j < m)
+                reinterpret_cast<__bf16*>(p.dbias)[(int64_t)H * boff + (int64_t)h * n * m +
+                                                   (int64_t)qi * m + j] = (__bf16)d2[e];
+            } else if constexpr (BIAS == B_RELPOS) {
+              if (qi < n && j < m && (!p.causal || j <= qi + delta)) {
+                const int k = relpos_bucket(qi + delta - j, p.num_buckets);
+                if (k != db_k) {
+                  db_flush();
+                  db_k = k;
+                  db_sum = 0.f;
+                }
+                db_sum += d2[e];
+              }
+            }
           }
         }
         dd[blk][pi] = pack2bf(d2[0], d2[1]);
@@ -1013,6 +1047,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
+    db_flush();
     const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
     // through the stage that the last key step left free (rows of this wave only)
     __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
@@ -1043,6 +1078,46 @@ void bwd_kvq_kernel(BwdParams p) {
   kv_pass<D, NW, MODE, BIAS, true>(p);
   __syncthreads();
   q_pass<D, NW, MODE, BIAS, false>(p);
+}
+
+// The query-stationary pass with the bias gradient (DB); the single-pass classes are off.
+template <int D, int NW, int MODE, int BIAS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_q_db_kernel(BwdParams p) {
+  q_pass<D, NW, MODE, BIAS, true, true>(p);
+}
+
+// Zeroes `count` 16-bit elements of x; with count_from (a dense bias's block offsets), the
+// count is H * count_from[B], known only on the device.  A bias gradient has to be zero on every
+// pair the passes never visit.
+__global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* x, int64_t count,
+                                                      const int64_t* count_from, int B, int H) {
+  if (count_from) count = (int64_t)H * count_from[B];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * 256)
+    x[i] = 0;
+}
+
+// dbias[h][k] = sum over query rows r, then over the two lane halves, of part[r][h][half][k]:
+// one workgroup per (head, bucket); thread t sums rows t, t + 256, ... in order, then a fixed
+// tree in LDS, so the sum does not depend on timing.
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* part, float* out,
+                                                          int64_t rows, int H, int nb) {
+  __shared__ float red[256];
+  const int h = blockIdx.x / nb, k = blockIdx.x % nb;
+  float acc = 0.f;
+  for (int64_t r = threadIdx.x; r < rows; r += 256) {
+    const float* pr = part + ((r * H + h) * 2) * (int64_t)nb + k;
+    acc += pr[0];
+    acc += pr[nb];
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[(int64_t)h * nb + k] = red[0];
 }
 
 template <class K>
@@ -1084,6 +1159,46 @@ hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s)
                            "jfa_bwd_kvq", s, &attr);
 }
 
+template <int D, int NW, int MODE, int BIAS>
+hipError_t run_bq_db(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
+  static int attr = 0;
+  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
+                           max_items, cu, p, "jfa_dbias_dq", s, &attr);
+}
+
+// Backward with the bias gradient: zero dbias (dense) or the partials (relative positions),
+// the key-stationary pass, the query-stationary pass with DB, then (relative positions) the
+// fixed-order reduction into dbias [H][num_buckets] (fp32).
+template <int D, int MODE, int BIAS>
+hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
+                      hipStream_t s) {
+  const unsigned zgrid = (unsigned)std::max(1, cu * 4);
+  timing_begin("jfa_dbias_zero", s);
+  if constexpr (BIAS == B_DENSE)
+    hipLaunchKernelGGL(zero_u16_kernel, dim3(zgrid), dim3(256), 0, s, (uint16_t*)p.dbias,
+                       (int64_t)0, p.bias_off, p.batch, p.H);
+  else
+    hipLaunchKernelGGL(zero_u16_kernel, dim3(zgrid), dim3(256), 0, s, (uint16_t*)p.dbias_part,
+                       p.total_q * p.H * 2 * p.num_buckets * 2, (const int64_t*)nullptr, 0, 0);
+  timing_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS>(p, mk, cu, s) : run_bk<D, 2, MODE, BIAS>(p, mk, cu, s);
+  if (e != hipSuccess) return e;
+  e = tc.bq_nw == 4 ? run_bq_db<D, 4, MODE, BIAS>(p, mq, cu, s)
+                    : run_bq_db<D, 2, MODE, BIAS>(p, mq, cu, s);
+  if (e != hipSuccess) return e;
+  if constexpr (BIAS == B_RELPOS) {
+    timing_begin("jfa_dbias_reduce", s);
+    hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)(p.H * p.num_buckets)), dim3(256), 0,
+                       s, (const float*)p.dbias_part, (float*)p.dbias, p.total_q, p.H,
+                       p.num_buckets);
+    timing_end(s);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 template <int D, int MODE, int BIAS>
 hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                         hipStream_t s) {
@@ -1111,6 +1226,24 @@ hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk
 hipError_t launch_backward_f32(const BwdParams& p, const TileCfg& tc, int head_dim,
                                int64_t max_q_items, int64_t max_k_items, int cu_count,
                                hipStream_t s);
+
+hipError_t launch_backward_dbias(const BwdParams& p, const TileCfg& tc, int head_dim,
+                                 int64_t max_q_items, int64_t max_k_items, int cu_count,
+                                 hipStream_t s) {
+#define JFA_BWD_DB_CASE(D_, M_)                                                                 \
+  if (head_dim == D_ && p.mode == M_)                                                           \
+    return p.bias_kind == JFA_BIAS_DENSE                                                        \
+               ? run_bwd_db<D_, M_, B_DENSE>(p, tc, max_q_items, max_k_items, cu_count, s)      \
+               : run_bwd_db<D_, M_, B_RELPOS>(p, tc, max_q_items, max_k_items, cu_count, s);
+  JFA_BWD_DB_CASE(128, MODE_SOFTMAX)
+  JFA_BWD_DB_CASE(128, MODE_SILU)
+  JFA_BWD_DB_CASE(128, MODE_GELU)
+  JFA_BWD_DB_CASE(64, MODE_SOFTMAX)
+  JFA_BWD_DB_CASE(64, MODE_SILU)
+  JFA_BWD_DB_CASE(64, MODE_GELU)
+#undef JFA_BWD_DB_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, int dtype,
                            int64_t max_q_items, int64_t max_k_items, int cu_count, hipStream_t s) {

@@ -54,6 +54,7 @@ struct Layout {
   size_t header, bias_off, s_tmp, t_tmp, gen_recs, gen_slot, words_a, words_b;
   size_t fwd, comb, bq, bk, xtk;
   size_t part_acc, part_ml, delta;
+  size_t dbias_part;   // backward with the relative-position table's gradient
   size_t total;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
 };
@@ -156,11 +157,15 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;        // [H][total_q] (softmax)
+  void* dbias;         // bias gradient (dense bias: bias layout, bf16) or null
+  float* dbias_part;   // relative-position table: per (query row, head, lane half) sums
+                       // [total_q][H][2][num_buckets], or null
   WsHeader* hdr;
   const ItemRec* bq;
   const ItemRec* bk;
   uint32_t* xtk_q;     // per-XCD work counters of the query-stationary kernel
   uint32_t* xtk_k;     // and of the key-stationary kernel
+  int32_t batch;
   int32_t H;
   int32_t causal;
   int32_t bias_kind;
@@ -184,6 +189,11 @@ hipError_t launch_forward(const FwdParams& p, const TileCfg& tc, int head_dim, i
                           int64_t max_items, int64_t max_comb_items, int cu_count, hipStream_t s);
 hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, int dtype,
                            int64_t max_q_items, int64_t max_k_items, int cu_count, hipStream_t s);
+// The backward with the bias gradient (bf16, bias present, tc.fuse == 0): dbias as for p.dbias;
+// the relative-position table's partials in p.dbias_part.
+hipError_t launch_backward_dbias(const BwdParams& p, const TileCfg& tc, int head_dim,
+                                 int64_t max_q_items, int64_t max_k_items, int cu_count,
+                                 hipStream_t s);
 hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_t* out,
                                 int32_t out_batch, int32_t* status, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,

@@ -149,3 +149,28 @@ def test_other_entry_points_host_errors():
     assert lib.jfa_kernel_timing(b"", None, ctypes.byref(n)) == _lib.JFA_ERR_INVALID_ARG
     jfa.jfa_kernel_timing_reset()
     assert jfa.jfa_kernel_timing("") == (0.0, 0)
+
+
+def _bwd_db(p, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, qo=FAKE, ko=FAKE, bias=FAKE,
+                dq=FAKE, dk=FAKE, dv=FAKE, db=FAKE, ws=FAKE, nbytes=1 << 40)
+    args.update(over)
+    return jfa.load().jfa_backward_dbias(ctypes.byref(p), args["q"], args["k"], args["v"],
+                                         args["o"], args["lse"], args["do"], args["qo"],
+                                         args["ko"], args["bias"], args["dq"], args["dk"],
+                                         args["dv"], args["db"], args["ws"], args["nbytes"], None)
+
+
+def test_backward_dbias_host_errors():
+    p = _problem(bias_kind="relpos")
+    assert _bwd_db(p, db=None) == _lib.JFA_ERR_INVALID_ARG
+    assert _bwd_db(p, bias=None) == _lib.JFA_ERR_INVALID_ARG
+    assert _bwd_db(p, db=FAKE + 2) == _lib.JFA_ERR_INVALID_ARG
+    assert _bwd_db(_problem(), bias=None) == _lib.JFA_ERR_UNSUPPORTED       # no bias to train
+    assert _bwd_db(_problem(bias_kind="relpos", dtype="f32")) == _lib.JFA_ERR_UNSUPPORTED
+    # the relative-position table's per-row partials live in the workspace
+    assert _bwd_db(p, nbytes=jfa.jfa_workspace_bytes(p, 1)) == _lib.JFA_ERR_WORKSPACE
+    assert jfa.jfa_workspace_bytes(p, 2) > jfa.jfa_workspace_bytes(p, 1)
+    d = _problem(bias_kind="dense")
+    assert jfa.jfa_workspace_bytes(d, 2) == jfa.jfa_workspace_bytes(d, 1)
+    assert _bwd_db(d, nbytes=16) == _lib.JFA_ERR_WORKSPACE

@@ -1,0 +1,117 @@
+"""GPU parity for the bias gradient (jfa_backward_dbias) against the oracle's ``bias_grad``.
+
+The bias is a trained parameter ("Meta GEM Training Efficiency: ...", section "Bottleneck
+move 1": custom biases), so the backward also returns dL/dbias: per pair for a dense bias (bf16,
+in the bias's layout), summed by bucket for the relative-position table (fp32 [H, buckets]).
+
+Bounds: the dense gradient is bf16 per pair, so the bf16 bounds apply as for dQ/dK/dV.  A table
+entry sums dS over up to a few hundred thousand pairs; its error scales with the magnitude of
+the sum, so the max-abs bound is 2e-2 * max(1, max |exact|), with rel-L2 1e-2 as for bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jfa_synth import custom_case
+from tests.gpu_helpers import compare, device_case, say
+from tests.helpers import max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+LENS_Q = [300, 17, 129, 0, 64, 700, 5]
+LENS_KV = [300, 40, 129, 9, 0, 700, 200]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import jagged_attention_amd as jfa
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    jfa.load()
+    oracle.build()
+    return jfa
+
+
+def _run(case, dc):
+    import jagged_attention_amd as jfa
+    kw = dict(mode=case.mode, causal=case.causal, bias_kind=case.bias_kind,
+              num_buckets=case.num_buckets)
+    o, lse = jfa.forward(dc["q"], dc["k"], dc["v"], dc["qo"], dc["ko"], bias=dc["bias"], **kw)
+    out = jfa.backward_dbias(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
+                             dc["bias"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_table(got, want):
+    g = got.detach().double().cpu().numpy()
+    ma, rl = max_abs(g, want), rel_l2(g, want)
+    bound = 2e-2 * max(1.0, float(np.abs(want).max()))
+    say(f"  dbias table: max-abs {ma:.3e} (bound {bound:.3e}) rel-L2 {rl:.3e}")
+    assert ma <= bound and rl <= 1e-2
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_bias_grad_parity(mode, causal, bias_kind, d):
+    lq, lk = (LENS_Q, LENS_Q) if causal else (LENS_Q, LENS_KV)
+    case = custom_case(lq, lk, 2, d, dtype="bf16", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=90 + d)
+    say(f"[bias grad] mode={mode} causal={causal} bias={bias_kind} d={d}")
+    dc = device_case(case)
+    dq, dk, dv, db = _run(case, dc)
+    okw = dict(mode=mode, causal=causal, bias=case.bias, bias_kind=bias_kind,
+               num_buckets=case.num_buckets)
+    db_ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                              **okw)
+    if bias_kind == "dense":
+        assert db.dtype == torch.bfloat16 and db.shape == dc["bias"].shape
+        compare("dbias", db, db_ref, "bf16")
+    else:
+        assert db.dtype == torch.float32 and tuple(db.shape) == (2, case.num_buckets)
+        _check_table(db, db_ref)
+    dq_ref, dk_ref, dv_ref = oracle.backward(case.q, case.k, case.v, case.dout, case.q_lens,
+                                             case.kv_lens, **okw)
+    compare("dQ", dq, dq_ref, "bf16")
+    compare("dK", dk, dk_ref, "bf16")
+    compare("dV", dv, dv_ref, "bf16")
+
+
+@pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
+def test_bias_grad_deterministic_and_overwrites(bias_kind):
+    """Two calls give bitwise-identical results, whatever the output buffer held before."""
+    import jagged_attention_amd as jfa
+    case = custom_case(LENS_Q, LENS_Q, 2, 128, dtype="bf16", mode="softmax", causal=True,
+                       bias_kind=bias_kind, seed=7)
+    say(f"[bias grad determinism] bias={bias_kind}")
+    dc = device_case(case)
+    a = _run(case, dc)
+    b = _run(case, dc)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    # the dense gradient is zero on every pair that is not visible (here: above the diagonal);
+    # the mask comes from the indices, since a visible pair's exact dS can be 0 as well (a row
+    # with one visible key has P = 1 and dS = dP - D = 0)
+    if bias_kind == "dense":
+        db = a[3].float().cpu().numpy()
+        hidden = []
+        for n in LENS_Q:
+            i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+            hidden.append(np.tile((j > i).ravel(), 2))
+        hidden = np.concatenate(hidden)
+        assert hidden.shape == db.shape and hidden.sum() > 0
+        assert np.all(db[hidden] == 0)
+
+
+def test_bias_grad_rejects_unsupported():
+    import jagged_attention_amd as jfa
+    case = custom_case([64], [64], 1, 64, dtype="f32", mode="softmax", bias_kind="relpos", seed=3)
+    dc = device_case(case)
+    o, lse = jfa.forward(dc["q"], dc["k"], dc["v"], dc["qo"], dc["ko"], bias=dc["bias"],
+                         bias_kind="relpos")
+    with pytest.raises(jfa.JfaError):
+        jfa.backward_dbias(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
+                           dc["bias"], bias_kind="relpos")
