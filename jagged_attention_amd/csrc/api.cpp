@@ -138,8 +138,11 @@ Layout layout_of(const jfa_problem& p, const TileCfg& tc, int backward) {
     L.part_ml = take(4 * 2 * (size_t)L.cap_slots * H * tc.bm);
   }
   if (backward && p.mode == JFA_MODE_SOFTMAX) L.delta = take(4 * (size_t)H * std::max<int64_t>(p.total_q, 1));
-  if (backward == 2 && p.bias_kind == JFA_BIAS_RELPOS)
-    L.dbias_part = take(4 * 2 * (size_t)H * p.num_buckets * std::max<int64_t>(p.total_q, 1));
+  if (backward == 2 && p.bias_kind == JFA_BIAS_RELPOS) {
+    const size_t cols = (size_t)H * dbias_halves(p.num_buckets) * p.num_buckets;
+    L.dbias_part = take(4 * cols * std::max<int64_t>(p.total_q, 1));
+    L.dbias_chunk = take(4 * cols * dbias_chunks(p.heads, p.num_buckets, p.total_q));
+  }
   L.total = off;
   return L;
 }
@@ -411,6 +414,7 @@ jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, con
   if (dbias) {
     bp.dbias = dbias;
     bp.dbias_part = p->bias_kind == JFA_BIAS_RELPOS ? (float*)(ws + L.dbias_part) : nullptr;
+    bp.dbias_chunk = p->bias_kind == JFA_BIAS_RELPOS ? (float*)(ws + L.dbias_chunk) : nullptr;
     e = launch_backward_dbias(bp, tc, p->head_dim, L.cap_q * p->heads, L.cap_k * p->heads, cu, s);
   } else {
     e = launch_backward(bp, tc, p->head_dim, p->dtype, L.cap_q * p->heads, L.cap_k * p->heads,

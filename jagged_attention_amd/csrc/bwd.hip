@@ -647,12 +647,21 @@ struct QLds {
   static constexpr int Q1_P = Q1_DR + BM * RS * 2;
   static constexpr int Q1_DS = Q1_P + BM * PS * 2;
   static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 : 0);
+  // bias gradient of a relative-position table of at most DB_NB buckets: per-lane bucket sums,
+  // [DB_NB][64] floats per wave (bucket-major, so the 64 lanes hit 64 banks), in place of the
+  // single-pass class's area, which that pass does not use
+  static constexpr int DBA = 2 * STAGE;
+  static constexpr int TOTAL_DB = BIAS == B_RELPOS ? (TOTAL > DBA + NW * DB_NB * 64 * 4
+                                                          ? TOTAL : DBA + NW * DB_NB * 64 * 4)
+                                                   : TOTAL;
+  static_assert(TOTAL_DB <= 160 * 1024, "LDS of the bias-gradient pass");
 };
 
 // The query-stationary pass over the q-stationary list (HOME as for kv_pass).  DB: also the
 // bias gradient, from each pair's dS as it is formed (dense: dS stored in the bias layout;
-// relative-position table: per-lane running sums by bucket, flushed into the lane's own partial
-// row, which a later kernel reduces in a fixed order).  DB runs without the single-pass classes.
+// relative-position table: per-lane running sums by bucket, flushed on a change of bucket into
+// the lane's own slots, in LDS for at most DB_NB buckets and else in its partial row in memory;
+// later kernels reduce the rows in a fixed order).  DB runs without the single-pass classes.
 template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB = false>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -680,6 +689,11 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 
   ItemPipeT<HOME> pipe{p.xtk_q, p.bq, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
+  // relative-position gradient in LDS: this lane's slot of bucket k is dbl[64 k]
+  const bool db_lds = DB && BIAS == B_RELPOS && p.num_buckets <= DB_NB;
+  float* dbl = reinterpret_cast<float*>(lds + L::DBA) + wave * DB_NB * 64 + lane;
+  if (db_lds)
+    for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
     const int* dsc = s_desc[buf];
@@ -725,8 +739,12 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     auto db_flush = [&]() {
       if constexpr (DB && BIAS == B_RELPOS) {
         if (db_k >= 0) {
-          float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
-          pr[db_k] += db_sum;
+          if (db_lds) {
+            dbl[64 * db_k] += db_sum;
+          } else {
+            float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
+            pr[db_k] += db_sum;
+          }
         }
       }
     };
@@ -1048,6 +1066,19 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     db_flush();
+    if constexpr (DB && BIAS == B_RELPOS) {
+      if (db_lds) {
+        // the row's two lane halves, summed in that order, into its partial row [H][buckets];
+        // then the slots start again from zero
+        __syncthreads();
+        if (g == 0 && qi < n) {
+          float* pr = p.dbias_part + ((int64_t)(qo + qi) * H + h) * p.num_buckets;
+          for (int k = 0; k < p.num_buckets; ++k) pr[k] = dbl[64 * k] + dbl[64 * k + 32];
+        }
+        __syncthreads();
+        for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
+      }
+    }
     const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
     // through the stage that the last key step left free (rows of this wave only)
     __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
@@ -1098,19 +1129,41 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* x, int64_t coun
     x[i] = 0;
 }
 
-// dbias[h][k] = sum over query rows r, then over the two lane halves, of part[r][h][half][k]:
-// one workgroup per (head, bucket); thread t sums rows t, t + 256, ... in order, then a fixed
-// tree in LDS, so the sum does not depend on timing.
-__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* part, float* out,
-                                                          int64_t rows, int H, int nb) {
+// Reduction of the partial rows part[rows][cols] (cols = H * halves * buckets) in a fixed order.
+// Stage 1: chunk c (rows_per_chunk consecutive rows) into out1[c][cols]; thread x owns columns
+// x, x + 256, ... and keeps 8 running sums (rows r with r % 8 = j), added in j order at the end.
+__global__ __launch_bounds__(256) void dbias_rows_kernel(const float* part, float* out1,
+                                                        int64_t rows, int cols,
+                                                        int64_t rows_per_chunk) {
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_chunk;
+  const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int64_t r = r0;
+    for (; r + 8 <= r1; r += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] += part[(r + j) * cols + c];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (r + j < r1) a[j] += part[(r + j) * cols + c];
+    float acc = a[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) acc += a[j];
+    out1[(int64_t)blockIdx.x * cols + c] = acc;
+  }
+}
+
+// Stage 2: dbias[h][k] = sum over chunks and lane halves of out1; one workgroup per (h, k):
+// thread x sums chunks x, x + 256, ... (halves in order within a chunk), then a fixed tree.
+__global__ __launch_bounds__(256) void dbias_chunks_kernel(const float* out1, float* out,
+                                                          int chunks, int H, int halves, int nb) {
   __shared__ float red[256];
   const int h = blockIdx.x / nb, k = blockIdx.x % nb;
+  const int cols = H * halves * nb;
   float acc = 0.f;
-  for (int64_t r = threadIdx.x; r < rows; r += 256) {
-    const float* pr = part + ((r * H + h) * 2) * (int64_t)nb + k;
-    acc += pr[0];
-    acc += pr[nb];
-  }
+  for (int c = threadIdx.x; c < chunks; c += 256)
+    for (int s = 0; s < halves; ++s) acc += out1[(int64_t)c * cols + (h * halves + s) * nb + k];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -1162,7 +1215,7 @@ hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s)
 template <int D, int NW, int MODE, int BIAS>
 hipError_t run_bq_db(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
   static int attr = 0;
-  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
+  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL_DB, NW * 64,
                            max_items, cu, p, "jfa_dbias_dq", s, &attr);
 }
 
@@ -1179,7 +1232,8 @@ hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t
                        (int64_t)0, p.bias_off, p.batch, p.H);
   else
     hipLaunchKernelGGL(zero_u16_kernel, dim3(zgrid), dim3(256), 0, s, (uint16_t*)p.dbias_part,
-                       p.total_q * p.H * 2 * p.num_buckets * 2, (const int64_t*)nullptr, 0, 0);
+                       p.total_q * p.H * dbias_halves(p.num_buckets) * p.num_buckets * 2,
+                       (const int64_t*)nullptr, 0, 0);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1189,9 +1243,15 @@ hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t
                     : run_bq_db<D, 2, MODE, BIAS>(p, mq, cu, s);
   if (e != hipSuccess) return e;
   if constexpr (BIAS == B_RELPOS) {
+    const int halves = dbias_halves(p.num_buckets);
+    const int cols = p.H * halves * p.num_buckets;
+    const int chunks = dbias_chunks(p.H, p.num_buckets, p.total_q);
+    const int64_t per = (p.total_q + chunks - 1) / chunks;
     timing_begin("jfa_dbias_reduce", s);
-    hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)(p.H * p.num_buckets)), dim3(256), 0,
-                       s, (const float*)p.dbias_part, (float*)p.dbias, p.total_q, p.H,
+    hipLaunchKernelGGL(dbias_rows_kernel, dim3((unsigned)chunks), dim3(256), 0, s,
+                       (const float*)p.dbias_part, p.dbias_chunk, p.total_q, cols, per);
+    hipLaunchKernelGGL(dbias_chunks_kernel, dim3((unsigned)(p.H * p.num_buckets)), dim3(256), 0,
+                       s, (const float*)p.dbias_chunk, (float*)p.dbias, chunks, p.H, halves,
                        p.num_buckets);
     timing_end(s);
     e = hipGetLastError();

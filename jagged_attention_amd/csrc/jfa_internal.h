@@ -54,7 +54,7 @@ struct Layout {
   size_t header, bias_off, s_tmp, t_tmp, gen_recs, gen_slot, words_a, words_b;
   size_t fwd, comb, bq, bk, xtk;
   size_t part_acc, part_ml, delta;
-  size_t dbias_part;   // backward with the relative-position table's gradient
+  size_t dbias_part, dbias_chunk;   // backward with the relative-position table's gradient
   size_t total;
   int64_t cap_f, cap_c, cap_q, cap_k, cap_t, cap_slots;
 };
@@ -158,8 +158,9 @@ struct BwdParams {
   void* dv;
   float* delta;        // [H][total_q] (softmax)
   void* dbias;         // bias gradient (dense bias: bias layout, bf16) or null
-  float* dbias_part;   // relative-position table: per (query row, head, lane half) sums
-                       // [total_q][H][2][num_buckets], or null
+  float* dbias_part;   // relative-position table: per-row sums [total_q][H][halves][buckets]
+                       // (halves = dbias_halves(buckets)), or null
+  float* dbias_chunk;  // and their per-chunk sums [dbias_chunks(...)][H][halves][buckets]
   WsHeader* hdr;
   const ItemRec* bq;
   const ItemRec* bk;
@@ -179,6 +180,20 @@ struct BwdParams {
   int64_t total_q;
   int64_t total_kv;
 };
+
+// Bias gradient of a relative-position table: tables of at most DB_NB buckets are summed per
+// lane in LDS and leave one partial row per query row and head (halves 1); wider tables leave
+// one per lane half (halves 2).  The rows are reduced in `dbias_chunks` chunks (at most 512,
+// and at most 4M floats of chunk sums).
+constexpr int DB_NB = 64;
+inline int dbias_halves(int nb) { return nb <= DB_NB ? 1 : 2; }
+inline int dbias_chunks(int H, int nb, int64_t rows) {
+  const int64_t cols = (int64_t)H * dbias_halves(nb) * nb;
+  int64_t c = (int64_t)(4 << 20) / cols;
+  if (c > 512) c = 512;
+  if (c > rows) c = rows;
+  return c < 1 ? 1 : (int)c;
+}
 
 // ---------------------------------------------------------- launchers
 // Each returns hipSuccess or the first launch error.  `grid_slots` sizes persistent grids.

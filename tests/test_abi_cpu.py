@@ -171,6 +171,8 @@ def test_backward_dbias_host_errors():
     # the relative-position table's per-row partials live in the workspace
     assert _bwd_db(p, nbytes=jfa.jfa_workspace_bytes(p, 1)) == _lib.JFA_ERR_WORKSPACE
     assert jfa.jfa_workspace_bytes(p, 2) > jfa.jfa_workspace_bytes(p, 1)
+    wide = _problem(bias_kind="relpos", num_buckets=300)     # partial rows per lane half
+    assert jfa.jfa_workspace_bytes(wide, 2) > jfa.jfa_workspace_bytes(wide, 1)
     d = _problem(bias_kind="dense")
     assert jfa.jfa_workspace_bytes(d, 2) == jfa.jfa_workspace_bytes(d, 1)
     assert _bwd_db(d, nbytes=16) == _lib.JFA_ERR_WORKSPACE

@@ -32,7 +32,7 @@ def _lib():
     return jfa
 
 
-def _run(case, dc):
+def _run(case, dc, with_o=False):
     import jagged_attention_amd as jfa
     kw = dict(mode=case.mode, causal=case.causal, bias_kind=case.bias_kind,
               num_buckets=case.num_buckets)
@@ -40,7 +40,7 @@ def _run(case, dc):
     out = jfa.backward_dbias(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
                              dc["bias"], **kw)
     torch.cuda.synchronize()
-    return out
+    return (out, o) if with_o else out
 
 
 def _check_table(got, want):
@@ -77,6 +77,40 @@ def test_bias_grad_parity(mode, causal, bias_kind, d):
     compare("dQ", dq, dq_ref, "bf16")
     compare("dK", dk, dk_ref, "bf16")
     compare("dV", dv, dv_ref, "bf16")
+
+
+@pytest.mark.parametrize("num_buckets", [1, 17, 64, 65, 300])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bias_grad_table_widths(num_buckets, causal):
+    """Tables of at most 64 buckets are summed in LDS, wider ones in memory (two lane halves per
+    row); both against the oracle, with the two-stage reduction over a few thousand rows."""
+    lens = [1500, 3, 700, 64, 2000, 129]
+    case = custom_case(lens, lens, 3, 64, dtype="bf16", mode="gelu" if causal else "softmax",
+                       causal=causal, bias_kind="relpos", num_buckets=num_buckets, seed=11)
+    say(f"[bias grad table] buckets={num_buckets} causal={causal}")
+    dc = device_case(case)
+    out, o = _run(case, dc, with_o=True)
+    db = out[3]
+    db_ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                              mode=case.mode, causal=causal, bias=case.bias, bias_kind="relpos",
+                              num_buckets=num_buckets)
+    assert tuple(db.shape) == (3, num_buckets)
+    if case.mode == "softmax" and num_buckets == 1:
+        # one bucket under softmax: a constant added to a whole row leaves the output alone, so
+        # the exact gradient is 0; what remains is the backward's D = rowsum(dO * O) taken from
+        # the stored bf16 O, |sum over the row's pairs of P (D_exact - D)| = |dO . (O - O_bf16)|
+        # per row, which bounds the sum over rows
+        o_ref, _ = oracle.forward(case.q, case.k, case.v, case.q_lens, case.kv_lens,
+                                  mode="softmax", causal=causal, bias=case.bias,
+                                  bias_kind="relpos", num_buckets=1)
+        do = case.dout.double().numpy()
+        resid = np.abs(np.einsum("rhd,rhd->rh", do, o.double().cpu().numpy() - o_ref))
+        bound = resid.sum(axis=0) * 1.05 + 1e-3
+        got = np.abs(db.double().cpu().numpy()[:, 0])
+        say(f"  one bucket: |dbias| {got} bound {bound} (exact {db_ref[:, 0]})")
+        assert np.all(np.abs(db_ref) < 1e-9) and np.all(got <= bound)
+        return
+    _check_table(db, db_ref)
 
 
 @pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
