@@ -250,7 +250,7 @@ def kernel_times(w, steps):
 # algorithmic MFMA flops per visible pair (multiples of d) for each kernel
 # (the two backward passes in one launch: 8 + 6)
 KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 14,
-                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6}
+                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6, "jfa_dbias_dq": 6}
 
 
 def traffic_for(kernel, workload):
@@ -345,6 +345,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--dbias", action="store_true",
+                    help="the main workload's backward also returns the bias gradient")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -369,7 +371,7 @@ def main():
         del src, dst
         log(f"[bench] calibration copy: {args.copy_mib} MiB x 3")
     log(f"[bench] headline workload {args.config}: warmup {args.warmup}, steps {args.steps}")
-    w, head = bench_config(args.config, args.steps, args.warmup)
+    w, head = bench_config(args.config, args.steps, args.warmup, dbias=args.dbias)
     log(f"[bench] {head['workload']}: {head['ms_per_step']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s")
     kt = kernel_times(w, max(3, args.steps // 2))
     log(f"[bench] kernel times: {json.dumps(kt)}")

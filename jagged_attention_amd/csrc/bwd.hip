@@ -889,7 +889,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                 reinterpret_cast<__bf16*>(p.dbias)[(int64_t)H * boff + (int64_t)h * n * m +
                                                    (int64_t)qi * m + j] = (__bf16)d2[e];
             } else if constexpr (BIAS == B_RELPOS) {
-              if (qi < n && j < m && (!p.causal || j <= qi + delta)) {
+              // `valid` is exactly qi < n, j < m and (causal) j <= qi + delta
+              if (valid) {
                 const int k = relpos_bucket(qi + delta - j, p.num_buckets);
                 if (k != db_k) {
                   db_flush();
