@@ -605,3 +605,36 @@ def test_bias_grad_block_attention_is_sum_over_blocks(oracle_mod):
     want = _torch_bias_grad(case, blocks, blocks, case.bias, "relpos", "gelu", True,
                             oracle_mod.relpos_bucket)
     assert max_abs(got, want) < 1e-11
+
+
+# ------------------------------------------------- fused normalisation + quantisation (row F4)
+
+def test_rmsnorm_closed_forms(oracle_mod):
+    """RMS normalisation against values worked by hand: a group [3, 4, 0, ...] of 32 has mean
+    square 25/32, so y = x * sqrt(32/25); a constant group c gives c / sqrt(c^2 + eps)."""
+    x = np.zeros((1, 32))
+    x[0, :2] = [3.0, 4.0]
+    y = oracle_mod.rmsnorm(x, eps=0.0)
+    assert np.allclose(y[0, :2], [3.0 * np.sqrt(32 / 25), 4.0 * np.sqrt(32 / 25)], rtol=1e-15)
+    assert np.all(y[0, 2:] == 0)
+    c = np.full((1, 64), -2.5)
+    y = oracle_mod.rmsnorm(c, eps=0.75)
+    assert np.allclose(y, -2.5 / np.sqrt(6.25 + 0.75), rtol=1e-15)
+    # the gain multiplies channel by channel (not transposed, not per group)
+    w = np.arange(1, 65, dtype=np.float64)
+    assert np.allclose(oracle_mod.rmsnorm(c, w, eps=0.75), -2.5 / np.sqrt(7.0) * w, rtol=1e-15)
+
+
+def test_rmsnorm_invariants(oracle_mod):
+    """Unit mean square per group (eps = 0, unit gain), invariance to a positive scale of the
+    group, groups of n inside a longer last dimension normalised on their own."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 3, 128))
+    y = oracle_mod.rmsnorm(x, eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+    assert np.allclose(oracle_mod.rmsnorm(7.5 * x, eps=0.0), y, rtol=1e-13)
+    x2 = x.copy()
+    x2[..., 64:] *= 100.0                       # groups of 64: the second half scales alone
+    y64 = oracle_mod.rmsnorm(x2, n=64, eps=0.0)
+    assert np.allclose(y64[..., :64], oracle_mod.rmsnorm(x[..., :64], eps=0.0), rtol=1e-13)
+    assert np.allclose(y64[..., 64:], oracle_mod.rmsnorm(x[..., 64:], eps=0.0), rtol=1e-13)
