@@ -337,6 +337,50 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False):
                    passes="fwd" if not w.with_backward else "fwd+bwd")
 
 
+def bench_norm_quant(cfg=5, reps=10):
+    """The fused RMS normalisation + MXFP8 quantiser (one group per row and head, n = d) on the
+    MXFP8 workload's Q, K and V, against the plain quantiser on the same tensors (HIP events)."""
+    import torch
+    import jagged_attention_amd as jfa
+    from jfa_synth import make_case
+    case = make_case(cfg)
+    d = case.head_dim
+    xs = [t.to("cuda:0") for t in (case.q, case.k, case.v)]
+    outs = [(torch.empty(x.shape, dtype=torch.uint8, device=x.device),
+             torch.empty(tuple(x.shape[:-1]) + (d // 32,), dtype=torch.uint8, device=x.device))
+            for x in xs]
+    w = torch.ones(d, dtype=torch.float32, device="cuda:0")
+    elems = sum(x.numel() for x in xs)
+
+    def run(fused):
+        for x, (c, sc) in zip(xs, outs):
+            if fused:
+                jfa.jfa_rmsnorm_quantize_mxfp8(x, w, x.numel() // d, d, 1e-6, c, sc)
+            else:
+                jfa.jfa_quantize_mxfp8(x, x.numel() // d, d, c, sc)
+
+    res = {}
+    for name, fused in (("jfa_norm_quant_mxfp8", True), ("jfa_quant_mxfp8", False)):
+        run(fused)
+        torch.cuda.synchronize()
+        jfa.jfa_kernel_timing_reset()
+        jfa.jfa_set_kernel_timing(True)
+        for _ in range(reps):
+            run(fused)
+        torch.cuda.synchronize()
+        jfa.jfa_set_kernel_timing(False)
+        ms, n = jfa.jfa_kernel_timing(name)
+        jfa.jfa_kernel_timing_reset()
+        sec = ms / reps * 1e-3                        # Q, K and V, one launch each
+        gbs = elems * (2 + 1 + 1 / 32) / sec / 1e9    # bf16 read, codes + scales written
+        res[name] = dict(us_for_qkv=round(sec * 1e6, 1), launches=n, gbs=round(gbs, 1),
+                         frac_of_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    del xs, outs
+    torch.cuda.empty_cache()
+    return dict(workload=case.name + "-qkv-norm-quant", elements=elems, group=d,
+                algorithmic_bytes_per_element=2 + 1 + 1 / 32, **res)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +449,9 @@ def main():
         extra["block_attention"] = r
         del wx
         torch.cuda.empty_cache()
+        # fused normalisation + MXFP8 quantisation of the MXFP8 workload's inputs
+        log("[bench] fused norm + quant")
+        extra["norm_quant"] = bench_norm_quant()
         # the headline step with the bias gradient (the relative-position table is trained)
         log("[bench] bias gradient")
         wx, r = bench_config(2, max(3, args.steps // 2), 2, dbias=True)

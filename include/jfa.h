@@ -191,6 +191,19 @@ jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t bloc
 jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
                               uint8_t* scales, void* stream);
 
+/* RMS normalisation fused with the MXFP8 quantiser, producing MXFP8 attention inputs in one pass
+ * over memory ("Meta GEM Training Efficiency: ...", section "Bottleneck move 2": quantisation
+ * fused into the preceding normalisation, so that scale generation and casting cost no extra
+ * pass).  x: bf16 [groups, n] (device), n in {32, 64, 128, 256, 512}: a head's d values
+ * (groups = rows * H) or a token's H * d.  weight: fp32 [n] per-channel gain, or NULL for 1.
+ * Each group becomes y = x / sqrt(mean(x^2) + eps) * weight (fp32), and y is quantised exactly
+ * as jfa_quantize_mxfp8 does: codes [groups, n], scales [groups, n / 32].  eps >= 0.  Other
+ * sizes, a negative count, NULL or misaligned pointers (x 16 B, codes 8 B, weight 16 B) are
+ * JFA_ERR_INVALID_ARG. */
+jfa_status jfa_rmsnorm_quantize_mxfp8(const void* x_bf16, const float* weight, int64_t groups,
+                                      int32_t n, float eps, uint8_t* codes, uint8_t* scales,
+                                      void* stream);
+
 /* Waits for `stream` and returns the device status word of the last call that used this
  * workspace (JFA_OK or JFA_ERR_DEVICE_DATA) in *status_out. */
 jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* status_out);

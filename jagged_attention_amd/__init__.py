@@ -13,6 +13,7 @@ from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # n
                    jfa_backward, jfa_backward_dbias, jfa_block_offsets, jfa_build_schedule, jfa_forward,
                    jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
+                   jfa_rmsnorm_quantize_mxfp8,
                    jfa_read_device_status, jfa_set_kernel_timing, jfa_tile_config,
                    jfa_workspace_bytes, load, status_string)
 
@@ -20,7 +21,7 @@ jfa_status_string = status_string
 
 __all__ = ["make_problem", "forward", "backward", "backward_dbias", "lengths_to_offsets",
            "block_offsets",
-           "quantize_mxfp8",
+           "quantize_mxfp8", "rmsnorm_quantize_mxfp8",
            "build_schedule", "JaggedAttention", "load"]
 
 
@@ -146,6 +147,20 @@ def quantize_mxfp8(x):
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     scales = torch.empty(tuple(x.shape[:-1]) + (d // 32,), dtype=torch.uint8, device=x.device)
     jfa_quantize_mxfp8(x, rows, d, codes, scales)
+    return codes, scales
+
+
+def rmsnorm_quantize_mxfp8(x, weight=None, n: Optional[int] = None, eps: float = 1e-6):
+    """bf16 [..., d] -> RMS-normalised over groups of n consecutive elements (default: the last
+    dimension), times weight (fp32 [n] or None), then MXFP8: (codes uint8 [..., d], scales
+    uint8 [..., d/32])."""
+    import torch
+    n = x.shape[-1] if n is None else n
+    groups = x.numel() // n
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (x.shape[-1] // 32,), dtype=torch.uint8,
+                         device=x.device)
+    jfa_rmsnorm_quantize_mxfp8(x, weight, groups, n, eps, codes, scales)
     return codes, scales
 
 

@@ -28,7 +28,7 @@ BIAS_KINDS = {"none": 0, "relpos": 1, "dense": 2}
 EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_dbias",
            "jfa_tile_config",
            "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
-           "jfa_quantize_mxfp8",
+           "jfa_quantize_mxfp8", "jfa_rmsnorm_quantize_mxfp8",
            "jfa_read_device_status", "jfa_status_string", "jfa_set_kernel_timing",
            "jfa_kernel_timing", "jfa_kernel_timing_reset")
 
@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_block_offsets.restype = ctypes.c_int
     lib.jfa_quantize_mxfp8.argtypes = [P, I64, I32, P, P, P]
     lib.jfa_quantize_mxfp8.restype = ctypes.c_int
+    lib.jfa_rmsnorm_quantize_mxfp8.argtypes = [P, P, I64, I32, ctypes.c_float, P, P, P]
+    lib.jfa_rmsnorm_quantize_mxfp8.restype = ctypes.c_int
     lib.jfa_read_device_status.argtypes = [P, P, ctypes.POINTER(I32)]
     lib.jfa_read_device_status.restype = ctypes.c_int
     lib.jfa_status_string.argtypes = [ctypes.c_int]
@@ -186,6 +188,14 @@ def jfa_quantize_mxfp8(x, rows: int, d: int, codes, scales, stream=None) -> None
     st = load().jfa_quantize_mxfp8(_ptr(x), int(rows), int(d), _ptr(codes), _ptr(scales),
                                    _stream(stream))
     _check("jfa_quantize_mxfp8", st)
+
+
+def jfa_rmsnorm_quantize_mxfp8(x, weight, groups: int, n: int, eps: float, codes, scales,
+                               stream=None) -> None:
+    st = load().jfa_rmsnorm_quantize_mxfp8(_ptr(x), _ptr(weight), int(groups), int(n),
+                                           float(eps), _ptr(codes), _ptr(scales),
+                                           _stream(stream))
+    _check("jfa_rmsnorm_quantize_mxfp8", st)
 
 
 def jfa_read_device_status(workspace, stream=None) -> int:

@@ -501,6 +501,18 @@ jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8
   return from_hip(launch_quantize_mxfp8(x_bf16, rows, d, codes, scales, (hipStream_t)stream));
 }
 
+jfa_status jfa_rmsnorm_quantize_mxfp8(const void* x_bf16, const float* weight, int64_t groups,
+                                      int32_t n, float eps, uint8_t* codes, uint8_t* scales,
+                                      void* stream) {
+  if (!x_bf16 || !codes || !scales || groups < 0) return JFA_ERR_INVALID_ARG;
+  if (n != 32 && n != 64 && n != 128 && n != 256 && n != 512) return JFA_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return JFA_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 8) || (weight && !aligned(weight, 16)))
+    return JFA_ERR_INVALID_ARG;
+  return from_hip(launch_rmsnorm_quantize_mxfp8(x_bf16, weight, groups, n, eps, codes, scales,
+                                                (hipStream_t)stream));
+}
+
 jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* status_out) {
   if (!workspace || !status_out) return JFA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;

@@ -213,6 +213,9 @@ hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_
                                 int32_t out_batch, int32_t* status, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);
+hipError_t launch_rmsnorm_quantize_mxfp8(const void* x, const float* w, int64_t groups, int32_t n,
+                                         float eps, uint8_t* codes, uint8_t* scales,
+                                         hipStream_t s);
 
 // Kernel timing hooks (api.cpp): bracket a launch with events when timing is enabled.
 void timing_begin(const char* name, hipStream_t s);

@@ -74,7 +74,90 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restri
   if (sub == 0) scales[blk] = (uint8_t)sc;
 }
 
+// RMS normalisation fused with the MXFP8 quantiser: quantisation folded into the normalisation
+// that produces the attention inputs ("Meta GEM Training Efficiency: ...", section "Bottleneck
+// move 2": activation quantisation fused into the upstream normalisation, so that scale
+// generation and casting add no pass over memory).  Each group of n = 8 LPG consecutive elements
+// (a head's d values, or a token's H d) becomes y = x / sqrt(mean(x^2) + eps) * w, and y is
+// quantised as above.  LPG lanes own a group (8 elements each); the sum of squares is a fixed
+// in-lane order then an xor butterfly, which gives every lane the same fp32 value.
+template <int LPG>
+__global__ __launch_bounds__(256) void rmsnorm_quant_mxfp8_kernel(
+    const __bf16* __restrict__ x, const float* __restrict__ w, float eps, int64_t groups,
+    uint8_t* codes, uint8_t* scales) {
+  constexpr int N = 8 * LPG;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t grp = tid / LPG;
+  const int sub = (int)(tid % LPG);
+  const bool ok = grp < groups;
+  u32x4 raw = {0, 0, 0, 0};
+  if (ok) raw = *(const u32x4*)(x + grp * N + sub * 8);
+  // this lane's 8 gains, issued with the data load (two 16-byte loads; w is 16-byte aligned)
+  u32x4 wa = {0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u}, wb = wa;
+  if (w) {
+    wa = *(const u32x4*)(w + sub * 8);
+    wb = *(const u32x4*)(w + sub * 8 + 4);
+  }
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(raw[e] << 16);
+    v[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+  for (int off = 1; off < LPG; off <<= 1) ss += __shfl_xor(ss, off);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / N) + eps);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float we = __uint_as_float(e < 4 ? wa[e & 3] : wb[e & 3]);
+    v[e] = v[e] * rstd * we;
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  if (!ok) return;
+  uint32_t sc = 127;
+  u32x2 out = {0, 0};
+  if (amax > 0.f) {
+    int e = ilog2f(amax) - 8;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    sc = (uint32_t)(e + 127);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int word = e4m3_pair<false>(ldexpf(v[4 * h], -e), ldexpf(v[4 * h + 1], -e), 0);
+      word = e4m3_pair<true>(ldexpf(v[4 * h + 2], -e), ldexpf(v[4 * h + 3], -e), word);
+      out[h] = (uint32_t)word;
+    }
+  }
+  const int64_t el = grp * N + sub * 8;
+  *(u32x2*)(codes + el) = out;
+  if ((sub & 3) == 0) scales[el / 32] = (uint8_t)sc;
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm_quantize_mxfp8(const void* x, const float* w, int64_t groups, int32_t n,
+                                         float eps, uint8_t* codes, uint8_t* scales,
+                                         hipStream_t s) {
+  if (groups == 0) return hipSuccess;
+  const int64_t threads = groups * (n / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  timing_begin("jfa_norm_quant_mxfp8", s);
+  switch (n) {
+    case 32: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<4>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
+    case 64: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<8>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
+    case 128: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<16>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
+    case 256: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<32>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
+    case 512: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<64>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
+    default: timing_end(s); return hipErrorInvalidValue;
+  }
+  timing_end(s);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s) {

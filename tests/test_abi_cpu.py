@@ -176,3 +176,16 @@ def test_backward_dbias_host_errors():
     d = _problem(bias_kind="dense")
     assert jfa.jfa_workspace_bytes(d, 2) == jfa.jfa_workspace_bytes(d, 1)
     assert _bwd_db(d, nbytes=16) == _lib.JFA_ERR_WORKSPACE
+
+
+def test_norm_quant_host_errors():
+    lib = jfa.load()
+    f = lib.jfa_rmsnorm_quantize_mxfp8
+    assert f(FAKE, None, 4, 96, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG    # n
+    assert f(FAKE, None, 4, 1024, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG  # n
+    assert f(FAKE, None, -1, 128, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
+    assert f(FAKE, None, 4, 128, -1.0, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG   # eps
+    assert f(FAKE, None, 4, 128, float("nan"), FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
+    assert f(None, None, 4, 128, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
+    assert f(FAKE + 8, None, 4, 128, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4, 4, 128, 1e-6, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
