@@ -740,7 +740,11 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       if constexpr (DB && BIAS == B_RELPOS) {
         if (db_k >= 0) {
           if (db_lds) {
-            dbl[64 * db_k] += db_sum;
+            // an LDS add with no result (ds_add_f32): no wait inside the loop; the slot is this
+            // lane's own and a wave's LDS operations apply in program order, so the sum's order
+            // is fixed
+            __hip_atomic_fetch_add(dbl + 64 * db_k, db_sum, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
           } else {
             float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
             pr[db_k] += db_sum;
