@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from jfa_synth import custom_case
-from tests.gpu_helpers import compare, device_case, say
+from tests.gpu_helpers import bf16_half_ulp, compare, device_case, say
 from tests.helpers import max_abs, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -43,6 +43,41 @@ def _run(case, dc, with_o=False):
     return (out, o) if with_o else out
 
 
+def d_residue(case, o_gpu, bias=None, num_buckets=None):
+    """Softmax: |dO_i . (O_i - O_bf16,i)| per (query row, head). The backward forms
+    D = rowsum(dO * O) from the stored bf16 O, and a pair's dS = P (dP - D) carries P times this
+    (P <= 1); 0 for GDPA, which has no D."""
+    if case.mode != "softmax":
+        return np.zeros((case.total_q, case.heads))
+    o_ref, _ = oracle.forward(case.q, case.k, case.v, case.q_lens, case.kv_lens, mode="softmax",
+                              causal=case.causal, bias=case.bias if bias is None else bias,
+                              bias_kind=case.bias_kind,
+                              num_buckets=num_buckets or case.num_buckets)
+    do = case.dout.double().numpy()
+    return np.abs(np.einsum("rhd,rhd->rh", do, o_gpu.double().cpu().numpy() - o_ref))
+
+
+def check_dense(db, ref, case, resid):
+    """Dense dbias against the oracle: element-wise |got - exact| <= 2e-2 + half a bf16 ulp of
+    the exact value + the pair's row residue (d_residue), and rel-L2 <= 1e-2."""
+    H = case.heads
+    slack = []
+    qo = 0
+    for n, m in zip(case.q_lens, case.kv_lens):
+        n, m = int(n), int(m)
+        for h in range(H):
+            slack.append(np.repeat(resid[qo:qo + n, h], m))
+        qo += n
+    slack = np.concatenate(slack) if slack else np.zeros(0)
+    g = db.detach().float().cpu().double().numpy()
+    assert slack.shape == g.shape == ref.shape
+    err = np.abs(g - ref) - bf16_half_ulp(ref) - slack
+    rl = rel_l2(g, ref)
+    say(f"  dense dbias: max-abs {max_abs(g, ref):.3e}, beyond rounding and D residue "
+        f"{err.max():.3e}, rel-L2 {rl:.3e}")
+    assert np.all(np.isfinite(g)) and err.max() <= 2e-2 and rl <= 1e-2
+
+
 def _check_table(got, want):
     g = got.detach().double().cpu().numpy()
     ma, rl = max_abs(g, want), rel_l2(g, want)
@@ -61,14 +96,14 @@ def test_bias_grad_parity(mode, causal, bias_kind, d):
                        bias_kind=bias_kind, seed=90 + d)
     say(f"[bias grad] mode={mode} causal={causal} bias={bias_kind} d={d}")
     dc = device_case(case)
-    dq, dk, dv, db = _run(case, dc)
+    (dq, dk, dv, db), o = _run(case, dc, with_o=True)
     okw = dict(mode=mode, causal=causal, bias=case.bias, bias_kind=bias_kind,
                num_buckets=case.num_buckets)
     db_ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
                               **okw)
     if bias_kind == "dense":
         assert db.dtype == torch.bfloat16 and db.shape == dc["bias"].shape
-        compare("dbias", db, db_ref, "bf16")
+        check_dense(db, db_ref, case, d_residue(case, o))
     else:
         assert db.dtype == torch.float32 and tuple(db.shape) == (2, case.num_buckets)
         _check_table(db, db_ref)
@@ -149,3 +184,50 @@ def test_bias_grad_rejects_unsupported():
     with pytest.raises(jfa.JfaError):
         jfa.backward_dbias(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], dc["qo"], dc["ko"],
                            dc["bias"], bias_kind="relpos")
+
+
+@pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
+def test_bias_grad_block_attention(bias_kind):
+    """The bias gradient of BlockAttention: the library's refined offsets in front of
+    jfa_backward_dbias, against the oracle's block-diagonal bias gradient on the original
+    samples (a dense bias is laid out over the blocks)."""
+    import jagged_attention_amd as jfa
+    lens = [300, 17, 129, 0, 64, 700]
+    w = 100
+    case = custom_case(lens, lens, 2, 128, dtype="bf16", mode="silu", causal=True,
+                       bias_kind="relpos", seed=61)
+    say(f"[bias grad block attention] bias={bias_kind} w={w}")
+    dc = device_case(case)
+    boff, nb, st = jfa.block_offsets(dc["qo"], w, case.total_q)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    blocks = [min(w, n - s) for n in lens for s in range(0, n, w)]
+    if bias_kind == "dense":
+        g = torch.Generator().manual_seed(62)
+        bias = (0.1 * torch.randn(2 * sum(b * b for b in blocks), generator=g)).to(torch.bfloat16)
+    else:
+        bias = case.bias
+    kw = dict(mode="silu", causal=True, bias_kind=bias_kind, num_buckets=case.num_buckets)
+    bd = bias.cuda()
+    o, lse = jfa.forward(dc["q"], dc["k"], dc["v"], boff, boff, bias=bd, **kw)
+    dq, dk, dv, db = jfa.backward_dbias(dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], boff,
+                                        boff, bd, **kw)
+    torch.cuda.synchronize()
+    if bias_kind == "dense":
+        # the oracle's dense layout is per sample; over the blocks taken as samples it is the
+        # refined batch's layout
+        bl = np.array(blocks)
+        ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, bl, bl, mode="silu",
+                               causal=True, bias=bias, bias_kind="dense")
+        compare("dbias", db, ref, "bf16")
+    else:
+        ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                               mode="silu", causal=True, bias=bias, bias_kind="relpos",
+                               num_buckets=case.num_buckets, block=w)
+        _check_table(db, ref)
+        dq_ref, dk_ref, _ = oracle.backward(case.q, case.k, case.v, case.dout, case.q_lens,
+                                            case.kv_lens, mode="silu", causal=True,
+                                            bias=bias, bias_kind="relpos",
+                                            num_buckets=case.num_buckets, block=w)
+        compare("dQ", dq, dq_ref, "bf16")
+        compare("dK", dk, dk_ref, "bf16")

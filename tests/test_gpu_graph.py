@@ -7,6 +7,7 @@ import torch
 import oracle
 from jfa_synth import custom_case
 from tests.gpu_helpers import compare, say
+from tests.test_gpu_bias_grad import check_dense, d_residue
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +87,61 @@ def test_graph_replay_matches_eager(mode, causal, bias_kind, split):
         for a, b in zip(outs, want):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
         assert int(st[0].item()) == 0 and int(st[1].item()) == 0
+
+
+@pytest.mark.parametrize("bias_kind", ["relpos", "dense"])
+def test_graph_replay_bias_gradient(bias_kind):
+    """jfa_backward_dbias inside a captured graph: its zeroing is a fill kernel (no memset node),
+    so every replay, with eager library work in between, reproduces the eager dQ, dK, dV and
+    dbias bit for bit, after each output was filled with NaN."""
+    import jagged_attention_amd as jfa
+    lens = [700, 0, 129, 64, 1500]
+    case = custom_case(lens, lens, 2, 128, dtype="bf16", mode="softmax", causal=True,
+                       bias_kind=bias_kind, seed=78)
+    say(f"[graph dbias] bias={bias_kind}")
+    dev = torch.device("cuda:0")
+    ql = torch.as_tensor(case.q_lens, dtype=torch.int32, device=dev)
+    q, k, v, do = (t.to(dev).contiguous() for t in (case.q, case.k, case.v, case.dout))
+    bias = case.bias.to(dev).contiguous()
+    B, H, d = case.batch, case.heads, case.head_dim
+    p = jfa.make_problem(B, H, d, case.total_q, case.total_kv, mode="softmax", causal=True,
+                         bias_kind=bias_kind)
+    wf = torch.empty(jfa.jfa_workspace_bytes(p, 0), dtype=torch.uint8, device=dev)
+    wb = torch.empty(jfa.jfa_workspace_bytes(p, 2), dtype=torch.uint8, device=dev)
+    qo = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, case.total_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    db = torch.empty_like(bias)
+
+    def step():
+        jfa.jfa_lengths_to_offsets(ql, B, qo, st[0:1])
+        jfa.jfa_forward(p, q, k, v, None, None, None, qo, qo, bias, o, lse, wf, wf.numel())
+        jfa.jfa_backward_dbias(p, q, k, v, o, lse, do, qo, qo, bias, dq, dk, dv, db, wb,
+                               wb.numel())
+
+    outs = [o, lse, dq, dk, dv, db]
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    db_ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                              mode="softmax", causal=True, bias=case.bias, bias_kind=bias_kind)
+    if bias_kind == "dense":
+        check_dense(db, db_ref, case, d_residue(case, o))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = custom_case([33, 90], [33, 90], 2, 128, dtype="bf16", seed=5, with_dout=False)
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        oq = other.q.to(dev)
+        qo2, _ = jfa.lengths_to_offsets(torch.as_tensor(other.q_lens, dtype=torch.int32,
+                                                        device=dev))
+        jfa.forward(oq, other.k.to(dev), other.v.to(dev), qo2, qo2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
