@@ -35,7 +35,7 @@ def _lognormal_lengths(rng: np.random.Generator, n: int, median: float, lo: int,
 
 
 # name -> description of one workload (the five jagged-attention workloads)
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="tiny-selfattn-softmax-f32", batch=4, heads=2, head_dim=64, dtype="f32",
             mode="softmax", causal=False, bias_kind="none", forward_only=False),
     2: dict(name="causal-selfattn-relpos-bf16", batch=64, heads=4, head_dim=128, dtype="bf16",
@@ -51,7 +51,7 @@ CONFIGS = {
 
 def lengths_for(cfg: int, rng: np.random.Generator, batch: Optional[int] = None):
     """Per-sample (q_len, kv_len) for workload ``cfg``; ``batch`` overrides B."""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     B = c["batch"] if batch is None else batch
     if cfg == 1:
         q = rng.integers(1, 129, size=B).astype(np.int32)
@@ -149,7 +149,7 @@ def custom_case(q_lens, kv_lens, heads: int, head_dim: int, *, dtype: str = "bf1
 
 def make_case(cfg: int, seed: Optional[int] = None, batch: Optional[int] = None) -> Case:
     """Workload ``cfg`` (1..5) drawn with ``seed`` (default: the workload number)."""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     seed = cfg if seed is None else seed
     rng = np.random.default_rng(seed)
     q_lens, kv_lens = lengths_for(cfg, rng, batch)
