@@ -4,18 +4,18 @@ One step = the whole hot path over one synthetic batch: offsets from lengths, ti
 forward (with split-KV combine), softmax preprocess, dK/dV and dQ passes.  The headline
 workload is causal jagged self-attention over user histories with a relative-position bias
 (B=64, lengths log-normal median 512 clipped to [16, 4096], H=4, d=128, bf16, seed 2).
-Inputs are resident in HBM before the timed region.  The step is timed as eager launches on
-one stream; the same step captured once as a HIP graph (checked bit-exact against an eager
-step) is timed too and reported beside it.  Prints ONE JSON line.
+Inputs are resident in HBM before the timed region.  Every step is timed with HIP events on
+the stream, after a 512 MB write that flushes the 256 MB MALL; the median over the steps is the
+reported time (p10 and p90 beside it, and back-to-back steps as a secondary).  The same step
+captured once as a HIP graph (checked bit-exact against an eager step) is timed too.  Prints
+ONE JSON line.
 
 Useful FLOPs count only visible (query, key) pairs: 4*d per pair forward, 10*d backward.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -117,7 +117,7 @@ class Workload:
 
     def step(self):
         import jagged_attention_amd as jfa
-        jfa.jfa_lengths_to_offsets(self.q_lens, self.case.batch, self.qo, self.status[0:1])
+        jfa.jfa_lengths_to_offsets(self.q_lens, self.case.batch, self.qo, status=self.status[0:1])
         if self.block:
             # self-attention split into blocks: one offsets array, refined, on both sides
             jfa.jfa_block_offsets(self.qo, self.case.batch, self.block, self.boff, self.batch,
@@ -131,7 +131,8 @@ class Workload:
             return
         ko = self.qo
         if not self.self_attn:
-            jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko, self.status[1:2])
+            jfa.jfa_lengths_to_offsets(self.kv_lens, self.case.batch, self.ko,
+                                       status=self.status[1:2])
             ko = self.ko
         if self.fp8:
             d = self.case.head_dim
@@ -153,7 +154,9 @@ class Workload:
                              self.nb)
 
     def algorithmic_bytes(self):
-        """HBM bytes the method must move per step (inputs once, outputs once)."""
+        """HBM bytes the method must move per step (inputs once, outputs once): forward reads
+        Q, K, V (and the bias) and writes O (+ LSE for softmax); backward reads Q, K, V, dO
+        (+ O and LSE for softmax, + the bias) and writes dQ, dK, dV."""
         c = self.case
         el = 1 if c.dtype == "mxfp8" else (4 if c.dtype == "f32" else 2)
         sc = (1.0 / 32) if c.dtype == "mxfp8" else 0.0
@@ -165,8 +168,20 @@ class Workload:
         fwd = qb + 2 * kb + bias + ob + lse
         bwd = 0
         if self.with_backward:
-            bwd = qb + 2 * kb + bias + 2 * ob + lse + qb + 2 * kb   # read q,k,v,o,do,lse,bias; write dq,dk,dv
+            reads = qb + 2 * kb + bias + ob + ((ob + lse) if c.mode == "softmax" else 0)
+            bwd = reads + qb + 2 * kb                 # dQ, dK, dV written in the input dtype
         return fwd, bwd
+
+    def padded_flops(self):
+        """FLOPs of the same batch padded to its longest sample (what a dense kernel would
+        execute): every sample takes max q_len queries and max kv_len keys."""
+        c = self.case
+        n = int(np.max(c.q_lens)) if c.batch else 0
+        m = int(np.max(c.kv_lens)) if c.batch else 0
+        pairs = c.batch * c.heads * int(visible_pairs(np.array([n]), np.array([m]),
+                                                      c.causal)[0])
+        per = (4.0 + (10.0 if self.with_backward else 0.0)) * c.head_dim
+        return per * pairs
 
 
 def outputs(w):
@@ -200,40 +215,68 @@ def capture_step(w):
     return g
 
 
-def time_graph(g, steps, warmup):
+FLUSH_BYTES = 512 << 20           # twice the 256 MB MALL (Infinity Cache) of MI355X
+
+
+class Flusher:
+    """Writes a 512 MB scratch buffer on the current stream, so no input of the next step is
+    left in the MALL or the L2s (a fill kernel: every line of it is written)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(self.k)
+
+
+def _timed(fn, steps, warmup, flush=None):
+    """Per-step device times (ms) of fn() from HIP events on the current stream; with flush, the
+    MALL is flushed before every step, outside the events."""
     import torch
     for _ in range(warmup):
-        g.replay()
+        fn()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return np.array([a.elapsed_time(b) for a, b in ev])
 
 
-def time_steps(w, steps, warmup):
-    import torch
-    for _ in range(warmup):
-        w.step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        w.step()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+def stats(ms):
+    return dict(median=float(np.median(ms)), p10=float(np.percentile(ms, 10)),
+                p90=float(np.percentile(ms, 90)), mean=float(np.mean(ms)))
 
 
-def kernel_times(w, steps):
-    """Average device time per launch of each library kernel (HIP events on its stream)."""
+def time_graph(g, steps, warmup, flush=None):
+    return _timed(g.replay, steps, warmup, flush)
+
+
+def time_steps(w, steps, warmup, flush=None):
+    return _timed(w.step, steps, warmup, flush)
+
+
+def kernel_times(w, steps, flush=None):
+    """Average device time per launch of each library kernel (HIP events the library records
+    on its own stream around every launch), over `steps` steps, each after a MALL flush."""
     import torch
     import jagged_attention_amd as jfa
     jfa.jfa_kernel_timing_reset()
-    jfa.jfa_set_kernel_timing(True)
     for _ in range(steps):
+        if flush is not None:
+            flush()
+        jfa.jfa_set_kernel_timing(True)
         w.step()
+        jfa.jfa_set_kernel_timing(False)
     torch.cuda.synchronize()
-    jfa.jfa_set_kernel_timing(False)
     out = {}
     for name in ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
                  "jfa_fwd_bf16", "jfa_fwd_mxfp8",
@@ -247,10 +290,15 @@ def kernel_times(w, steps):
     return out
 
 
-# algorithmic MFMA flops per visible pair (multiples of d) for each kernel
-# (the two backward passes in one launch: 8 + 6)
-KERNEL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 14,
-                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6, "jfa_dbias_dq": 6}
+# MFMA flops per visible pair (multiples of d) credited to each kernel.  Useful work: 4 d
+# forward (QK^T, PV) and 10 d backward (S recompute, dP, dV, dQ, dK); the key-stationary pass
+# does S, dP, dV, dK (8 d), the query-stationary pass adds only dQ (2 d) of useful work, so when
+# both run in one launch it is credited 10 d.  Executed work counts the query-stationary pass's
+# recompute of S and dP too (6 d; 14 d for the shared launch).
+USEFUL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 10,
+                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 2, "jfa_dbias_dq": 2}
+EXECUTED_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 14,
+                           "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6, "jfa_dbias_dq": 6}
 
 
 def traffic_for(kernel, workload):
@@ -271,70 +319,119 @@ def traffic_for(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, target_s=15.0):
-    """The oracle (fp64, all host threads) on a bounded sample of the headline workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_timing(case, target_s):
+    """The oracle (fp64, all host threads) on a bounded sample of `case`: samples taken in batch
+    order while the estimated time fits `target_s` (calibrated on the cheapest samples).
+    Returns useful TFLOP/s of the fwd (+bwd) pass and the sample description."""
     import oracle
     oracle.build()
-    order = np.arange(case.batch)
-    pairs = visible_pairs(case.q_lens, case.kv_lens, True)
-    # calibrate on the shortest samples, then take samples (in order) up to the time target
-    qo = np.concatenate([[0], np.cumsum(case.q_lens)])
-
-    def sub(idx):
-        idx = np.asarray(idx)
-        ql = case.q_lens[idx]
-        rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in idx])
-        q, k, v, do = (t[rows] for t in (case.q, case.k, case.v, case.dout))
-        return ql, q, k, v, do
+    back = case.dout is not None
+    pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal)
+    per_pair = (4.0 + (10.0 if back else 0.0)) * case.head_dim * case.heads
+    qo = np.concatenate([[0], np.cumsum(case.q_lens.astype(np.int64))])
+    ko = np.concatenate([[0], np.cumsum(case.kv_lens.astype(np.int64))])
+    H = case.heads
+    bo = np.concatenate([[0], np.cumsum(case.q_lens.astype(np.int64) *
+                                        case.kv_lens.astype(np.int64))]) * H
 
     def run(idx):
-        ql, q, k, v, do = sub(idx)
+        idx = np.asarray(idx, dtype=np.int64)
+        rq = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in idx] + [np.zeros(0, np.int64)])
+        rk = np.concatenate([np.arange(ko[b], ko[b + 1]) for b in idx] + [np.zeros(0, np.int64)])
+        bias = case.bias
+        if case.bias_kind == "dense":
+            bias = np.concatenate([case.bias[int(bo[b]):int(bo[b + 1])].float().numpy()
+                                   for b in idx] + [np.zeros(0, np.float32)])
+        kw = dict(mode=case.mode, causal=case.causal, bias=bias, bias_kind=case.bias_kind,
+                  num_buckets=case.num_buckets)
+        q, k, v = case.q[rq], case.k[rk], case.v[rk]
         t0 = time.perf_counter()
-        oracle.forward(q, k, v, ql, ql, causal=True, bias=case.bias, bias_kind="relpos")
-        oracle.backward(q, k, v, do, ql, ql, causal=True, bias=case.bias, bias_kind="relpos")
+        oracle.forward(q, k, v, case.q_lens[idx], case.kv_lens[idx], **kw)
+        if back:
+            oracle.backward(q, k, v, case.dout[rq], case.q_lens[idx], case.kv_lens[idx], **kw)
         return time.perf_counter() - t0
 
-    small = order[np.argsort(pairs)][:8]
-    t_cal = run(small)
-    rate = (14.0 * 128 * 4 * pairs[small].sum()) / max(t_cal, 1e-6)      # useful flop/s
+    order = np.arange(case.batch)
+    cheap = order[np.argsort(pairs, kind="stable")][:min(8, case.batch)]
+    t_cal = run(cheap)
+    rate = per_pair * max(int(pairs[cheap].sum()), 1) / max(t_cal, 1e-6)   # flop/s
     budget = rate * target_s
     chosen, acc = [], 0.0
     for b in order:
-        f = 14.0 * 128 * 4 * pairs[b]
+        f = per_pair * pairs[b]
         if acc + f > budget and chosen:
             continue
-        chosen.append(b)
+        chosen.append(int(b))
         acc += f
     t = run(chosen)
-    flops = 14.0 * 128 * 4 * pairs[chosen].sum()
-    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"{len(chosen)} of {case.batch} samples of the headline workload "
-                       f"({int(pairs[chosen].sum())} visible pairs per head, fwd+bwd fp64, "
-                       f"{t:.1f} s)")
+    flops = per_pair * pairs[chosen].sum()
+    return dict(value=float(flops / t / 1e12), unit="TFLOP/s", cores=oracle.max_threads(),
+                kind="oracle", cpu_model=cpu_model(),
+                sample=f"{len(chosen)} of {case.batch} samples of {case.name} in batch order "
+                       f"({int(pairs[chosen].sum()) * H} visible (query, key, head) triples, "
+                       f"{'fwd+bwd' if back else 'fwd'} in fp64, {t:.1f} s)")
 
 
-def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False):
+def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None):
     from jfa_synth import make_case
     case = make_case(cfg, seed)
     w = Workload(case, block=block, dbias=dbias)
-    sec = time_steps(w, steps, warmup)
+    t_fl = stats(time_steps(w, steps, warmup, flush))          # MALL flushed before every step
+    t_hot = stats(time_steps(w, steps, 1))                     # back to back (secondary)
     # the same step replayed as one HIP graph (no per-launch host work): reported beside it
     w.graph = capture_step(w)
-    graph = time_graph(w.graph, steps, warmup)
+    t_graph = stats(time_graph(w.graph, steps, 1, flush))
     flops = w.fwd_flops + w.bwd_flops
     peak = PEAK_FP8_TFLOPS if case.dtype == "mxfp8" else PEAK_BF16_TFLOPS
     fb, bb = w.algorithmic_bytes()
     intensity = flops / (fb + bb)
     ceiling = min(peak, intensity * PEAK_HBM_GBS / 1000.0)
+    sec = t_fl["median"] * 1e-3
     tf = flops / sec / 1e12
+    padded = w.padded_flops()
     name = case.name if not block else f"block{block}-" + case.name
     if w.want_dbias:
         name += "+dbias"
-    return w, dict(workload=name, seed=case.seed, ms_per_step=sec * 1e3,
-                   graph_ms_per_step=graph * 1e3, tflops=tf,
+    return w, dict(workload=name, seed=case.seed, ms_per_step=t_fl["median"],
+                   ms_p10=t_fl["p10"], ms_p90=t_fl["p90"],
+                   unflushed_ms_per_step=t_hot["median"],
+                   graph_ms_per_step=t_graph["median"], tflops=tf,
                    frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
                    frac_of_roofline=tf / ceiling, useful_gflop=flops / 1e9,
+                   algorithmic_mb=(fb + bb) / 1e6,
+                   padded_gflop=padded / 1e9,
+                   padding_waste_frac=(1.0 - flops / padded) if padded > 0 else 0.0,
                    passes="fwd" if not w.with_backward else "fwd+bwd")
+
+
+def roofline_of(w, kt):
+    """Roofline record of the dominant MFMA kernel of the step (largest total time)."""
+    cand = {k: v for k, v in kt.items() if k in USEFUL_FLOPS_PER_PAIR}
+    if not cand:
+        return None
+    dom = max(cand, key=lambda k: cand[k]["avg_ms"] * cand[k]["launches"])
+    d = w.case.head_dim
+    useful = USEFUL_FLOPS_PER_PAIR[dom] * d * w.pairs
+    executed = EXECUTED_FLOPS_PER_PAIR[dom] * d * w.pairs
+    sec = cand[dom]["avg_ms"] * 1e-3
+    achieved = useful / sec / 1e12
+    peak = PEAK_FP8_TFLOPS if "mxfp8" in dom else PEAK_BF16_TFLOPS
+    return dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
+                unit="TFLOP/s", frac=round(achieved / peak, 4),
+                traffic=traffic_for(dom, w.case.name), flops_per_launch=useful,
+                executed_flops_per_launch=executed,
+                executed_frac=round(executed / sec / 1e12 / peak, 4),
+                avg_ms=cand[dom]["avg_ms"])
 
 
 def bench_norm_quant(cfg=5, reps=10):
@@ -386,7 +483,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
     ap.add_argument("--dbias", action="store_true",
@@ -414,21 +511,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"[bench] calibration copy: {args.copy_mib} MiB x 3")
+    flush = Flusher()
     log(f"[bench] headline workload {args.config}: warmup {args.warmup}, steps {args.steps}")
-    w, head = bench_config(args.config, args.steps, args.warmup, dbias=args.dbias)
-    log(f"[bench] {head['workload']}: {head['ms_per_step']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s")
-    kt = kernel_times(w, max(3, args.steps // 2))
+    w, head = bench_config(args.config, args.steps, args.warmup, dbias=args.dbias, flush=flush)
+    log(f"[bench] {head['workload']}: {head['ms_per_step']:.3f} ms/step (p10 "
+        f"{head['ms_p10']:.3f}, p90 {head['ms_p90']:.3f}), {head['tflops']:.1f} TFLOP/s")
+    kt = kernel_times(w, max(3, args.steps // 2), flush)
     log(f"[bench] kernel times: {json.dumps(kt)}")
-    # dominant MFMA kernel of the step
-    cand = {k: v for k, v in kt.items() if k in KERNEL_FLOPS_PER_PAIR}
-    dom = max(cand, key=lambda k: cand[k]["avg_ms"] * cand[k]["launches"])
-    per_launch_flops = KERNEL_FLOPS_PER_PAIR[dom] * w.case.head_dim * w.pairs
-    achieved = per_launch_flops / (cand[dom]["avg_ms"] * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if "mxfp8" in dom else PEAK_BF16_TFLOPS
-    roof = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
-                unit="TFLOP/s", frac=round(achieved / peak, 4),
-                traffic=traffic_for(dom, w.case.name),
-                flops_per_launch=per_launch_flops, avg_ms=cand[dom]["avg_ms"])
+    roof = roofline_of(w, kt)
 
     extra = {}
     if not args.no_extra:
@@ -436,15 +526,30 @@ def main():
             if cfg == args.config:
                 continue
             log(f"[bench] workload {cfg}")
-            wx, r = bench_config(cfg, max(3, args.steps // 2), 2)
-            r["kernels"] = kernel_times(wx, 3)
+            wx, r = bench_config(cfg, max(3, args.steps // 2), 2, flush=flush)
+            r["kernels"] = kernel_times(wx, 3, flush)
+            r["roofline"] = roofline_of(wx, r["kernels"])
+            if cfg == 5:
+                # low-precision gate: the MXFP8 step (its three quantiser launches included)
+                # against the bf16 forward on the same batch
+                import copy
+                cb = copy.copy(wx.case)
+                cb.dtype = "bf16"
+                del wx
+                torch.cuda.empty_cache()
+                wb = Workload(cb, with_backward=False)
+                tb = stats(time_steps(wb, max(3, args.steps // 2), 2, flush))
+                r["bf16_forward_ms"] = tb["median"]
+                r["mxfp8_step_speedup_vs_bf16"] = tb["median"] / r["ms_per_step"]
+                r["bf16_kernels"] = kernel_times(wb, 3, flush)
+                wx = wb
             extra[f"workload_{cfg}"] = r
             del wx
             torch.cuda.empty_cache()
         # BlockAttention: the headline batch with every sample split into blocks of 256 rows
         log("[bench] block attention")
-        wx, r = bench_config(2, max(3, args.steps // 2), 2, block=BLOCK_ROWS)
-        r["kernels"] = kernel_times(wx, 3)
+        wx, r = bench_config(2, max(3, args.steps // 2), 2, block=BLOCK_ROWS, flush=flush)
+        r["kernels"] = kernel_times(wx, 3, flush)
         r["block_rows"] = BLOCK_ROWS
         extra["block_attention"] = r
         del wx
@@ -454,8 +559,8 @@ def main():
         extra["norm_quant"] = bench_norm_quant()
         # the headline step with the bias gradient (the relative-position table is trained)
         log("[bench] bias gradient")
-        wx, r = bench_config(2, max(3, args.steps // 2), 2, dbias=True)
-        r["kernels"] = kernel_times(wx, 3)
+        wx, r = bench_config(2, max(3, args.steps // 2), 2, dbias=True, flush=flush)
+        r["kernels"] = kernel_times(wx, 3, flush)
         extra["bias_gradient"] = r
         del wx
         torch.cuda.empty_cache()
@@ -463,7 +568,18 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("[bench] oracle CPU baseline")
-        cpu = cpu_baseline(w.case)
+        cpu = oracle_timing(w.case, 15.0)
+        if not args.no_extra:
+            from jfa_synth import make_case
+            for cfg in (1, 2, 3, 4, 5):
+                if cfg == args.config:
+                    continue                  # the headline's oracle is cpu_baseline
+                c = make_case(cfg)
+                o = oracle_timing(c, 4.0)
+                tgt = extra.setdefault(f"workload_{cfg}", {})
+                tgt["oracle"] = o
+                if "tflops" in tgt:
+                    tgt["gpu_over_oracle"] = tgt["tflops"] / o["value"]
 
     case = w.case
     line = {
@@ -474,9 +590,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_step"], 4),
+        "ms_p10": round(head["ms_p10"], 4),
+        "ms_p90": round(head["ms_p90"], 4),
+        "unflushed_ms_per_step": round(head["unflushed_ms_per_step"], 4),
         "graph_ms_per_step": round(head["graph_ms_per_step"], 4),
-        "launch": "eager stream launches; graph_ms_per_step replays the step as one HIP graph "
-                  "(checked bit-exact against an eager step)",
+        "timing": "median of per-step HIP events, a 512 MB write flushing the MALL before each "
+                  "step; unflushed_ms_per_step: back-to-back steps; graph_ms_per_step: the step "
+                  "replayed as one HIP graph (checked bit-exact against an eager step)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -488,6 +608,9 @@ def main():
                    else "see jfa_synth", "mode": case.mode, "causal": case.causal,
                    "bias": case.bias_kind, "seed": case.seed, "parallelism": "single GPU"},
         "mfma_peak_frac": round(head["frac_of_mfma_peak"], 4),
+        "useful_gflop": round(head["useful_gflop"], 3),
+        "padded_gflop": round(head["padded_gflop"], 3),
+        "padding_waste_frac": round(head["padding_waste_frac"], 4),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kt,

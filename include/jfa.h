@@ -158,11 +158,23 @@ jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
                               int64_t capacity, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Offsets from lengths: offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] (device
- * int32 arrays, B+1 and B entries).  status (device int32, may be NULL) receives 0, or
- * JFA_ERR_DEVICE_DATA for a negative length or a total above INT32_MAX. */
+/* Offsets from lengths ("Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a
+ * Different Stack", FAQ "What is a jagged tensor?": values plus offsets; section "Bottleneck
+ * move 1": custom biases over asymmetric query/key-value lengths).
+ *   offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b]   (device int32, B+1 and B entries)
+ *   bias_offsets_or_null (device int64 [B+1], may be NULL): the dense-bias block offsets,
+ *     bias_offsets[0] = 0, bias_offsets[b+1] = bias_offsets[b] + lengths[b] * kv_len[b], where
+ *     kv_len = kv_lengths_or_null (device int32 [B]) or, when that is NULL, lengths itself
+ *     (self-attention).  Sample b's dense-bias block [H][n][m] starts at element
+ *     H * bias_offsets[b]; the attention calls derive the same offsets from q/kv offsets
+ *     themselves, so this output is for callers that lay out or slice a dense bias.
+ * status (device int32, may be NULL) receives 0, or JFA_ERR_DEVICE_DATA for a negative length
+ * (either array) or a row total above INT32_MAX; then neither offsets array is written.
+ * Host errors: NULL lengths/offsets, batch < 0, misaligned pointers -> JFA_ERR_INVALID_ARG. */
 jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t* offsets,
-                                  int32_t* status, void* stream);
+                                  int64_t* bias_offsets_or_null,
+                                  const int32_t* kv_lengths_or_null, int32_t* status,
+                                  void* stream);
 
 /* BlockAttention ("Meta GEM Training Efficiency: Why LLM-Scale Recommenders Need a Different
  * Stack", section "Bottleneck move 1": eligible long-sequence attention becomes independent

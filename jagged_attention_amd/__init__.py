@@ -20,6 +20,7 @@ from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # n
 jfa_status_string = status_string
 
 __all__ = ["make_problem", "forward", "backward", "backward_dbias", "lengths_to_offsets",
+           "bias_offsets",
            "block_offsets",
            "quantize_mxfp8", "rmsnorm_quantize_mxfp8",
            "build_schedule", "JaggedAttention", "load"]
@@ -122,8 +123,20 @@ def lengths_to_offsets(lengths):
     import torch
     off = torch.empty(lengths.shape[0] + 1, dtype=torch.int32, device=lengths.device)
     status = torch.empty(1, dtype=torch.int32, device=lengths.device)
-    jfa_lengths_to_offsets(lengths, lengths.shape[0], off, status)
+    jfa_lengths_to_offsets(lengths, lengths.shape[0], off, status=status)
     return off, status
+
+
+def bias_offsets(q_lengths, kv_lengths=None):
+    """int32 lengths [B] (and kv lengths [B], default: the same) on the GPU -> (offsets int32
+    [B+1], dense-bias block offsets int64 [B+1], status int32 [1])."""
+    import torch
+    dev = q_lengths.device
+    off = torch.empty(q_lengths.shape[0] + 1, dtype=torch.int32, device=dev)
+    boff = torch.empty(q_lengths.shape[0] + 1, dtype=torch.int64, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    jfa_lengths_to_offsets(q_lengths, q_lengths.shape[0], off, boff, kv_lengths, status)
+    return off, boff, status
 
 
 def block_offsets(offsets, block: int, total_rows: int):
@@ -204,8 +217,18 @@ def _autograd():
         def backward(ctx, do):
             q, k, v, o, lse, qo, ko = ctx.saved_tensors
             opts = {key: val for key, val in ctx.opts.items() if key != "split_slots"}
-            dq, dk, dv = backward(q, k, v, o, lse if ctx.has_lse else None, do.contiguous(), qo,
-                                  ko, bias=ctx.bias, **opts)
+            lse = lse if ctx.has_lse else None
+            if ctx.bias is not None and ctx.needs_input_grad[5]:
+                # a trained bias: its gradient comes from the backward with dbias (bf16 only)
+                if q.dtype != torch.bfloat16:
+                    raise NotImplementedError(
+                        "the bias gradient is built for bf16 inputs; got " + str(q.dtype))
+                dopts = {key: val for key, val in opts.items() if key != "bwd_fuse"}
+                dq, dk, dv, dbias = backward_dbias(q, k, v, o, lse, do.contiguous(), qo, ko,
+                                                   ctx.bias, **dopts)
+                return dq, dk, dv, None, None, dbias, None
+            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), qo, ko, bias=ctx.bias,
+                                  **opts)
             return dq, dk, dv, None, None, None, None
 
     return JaggedAttention

@@ -75,7 +75,7 @@ def load() -> ctypes.CDLL:
     lib.jfa_tile_config.restype = ctypes.c_int
     lib.jfa_build_schedule.argtypes = [PP, P, P, P, P, P, P, P, P, I64, P, SZ, P]
     lib.jfa_build_schedule.restype = ctypes.c_int
-    lib.jfa_lengths_to_offsets.argtypes = [P, I32, P, P, P]
+    lib.jfa_lengths_to_offsets.argtypes = [P, I32, P, P, P, P, P]
     lib.jfa_lengths_to_offsets.restype = ctypes.c_int
     lib.jfa_block_offsets.argtypes = [P, I32, I32, P, I32, P, P]
     lib.jfa_block_offsets.restype = ctypes.c_int
@@ -171,8 +171,10 @@ def jfa_build_schedule(problem, q_offsets, kv_offsets, fwd, fwd_slot, comb, bwd_
     _check("jfa_build_schedule", st)
 
 
-def jfa_lengths_to_offsets(lengths, batch: int, offsets, status=None, stream=None) -> None:
-    st = load().jfa_lengths_to_offsets(_ptr(lengths), int(batch), _ptr(offsets), _ptr(status),
+def jfa_lengths_to_offsets(lengths, batch: int, offsets, bias_offsets=None, kv_lengths=None,
+                           status=None, stream=None) -> None:
+    st = load().jfa_lengths_to_offsets(_ptr(lengths), int(batch), _ptr(offsets),
+                                       _ptr(bias_offsets), _ptr(kv_lengths), _ptr(status),
                                        _stream(stream))
     _check("jfa_lengths_to_offsets", st)
 

@@ -222,6 +222,21 @@ void timing_end(hipStream_t s) {
   g_timing_open = -1;
 }
 
+hipError_t ensure_dyn_lds(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::unordered_map<std::string, int> done;   // (device, kernel, bytes) already set
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const std::string key = std::to_string(dev) + ":" + std::to_string((uintptr_t)kernel) + ":" +
+                          std::to_string(bytes);
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.count(key)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[key] = 1;
+  return e;
+}
+
 int resident_grid(const void* kernel, int threads, size_t dyn_lds, int cu_count) {
   static std::mutex mu;
   static std::unordered_map<std::string, int> cache;
@@ -476,11 +491,16 @@ jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,
 }
 
 jfa_status jfa_lengths_to_offsets(const int32_t* lengths, int32_t batch, int32_t* offsets,
-                                  int32_t* status, void* stream) {
+                                  int64_t* bias_offsets_or_null,
+                                  const int32_t* kv_lengths_or_null, int32_t* status,
+                                  void* stream) {
   if (!lengths || !offsets || batch < 0) return JFA_ERR_INVALID_ARG;
-  if (!aligned(lengths, 4) || !aligned(offsets, 4) || (status && !aligned(status, 4)))
+  if (!aligned(lengths, 4) || !aligned(offsets, 4) || (status && !aligned(status, 4)) ||
+      (bias_offsets_or_null && !aligned(bias_offsets_or_null, 8)) ||
+      (kv_lengths_or_null && !aligned(kv_lengths_or_null, 4)))
     return JFA_ERR_INVALID_ARG;
-  return from_hip(launch_lengths_to_offsets(lengths, batch, offsets, status, (hipStream_t)stream));
+  return from_hip(launch_lengths_to_offsets(lengths, kv_lengths_or_null, batch, offsets,
+                                            bias_offsets_or_null, status, (hipStream_t)stream));
 }
 
 jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t block,

@@ -559,12 +559,9 @@ hipError_t run_fwd(const FwdParams& p, int64_t max_items, int64_t max_comb, int 
   using L = FwdLds<D, NW, BIAS, FP8>;
   const size_t lds = L::TOTAL;
   auto kern = fwd_kernel<D, NW, MODE, BIAS, FP8>;
-  static int attr_done = 0;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    hipError_t e = ensure_dyn_lds((const void*)kern, lds);
     if (e != hipSuccess) return e;
-    attr_done = 1;
   }
   int grid = resident_grid((const void*)kern, NW * 64, lds, cu_count);
   if ((int64_t)grid > max_items) grid = (int)max(max_items, (int64_t)1);

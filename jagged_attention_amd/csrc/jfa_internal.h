@@ -198,7 +198,8 @@ inline int dbias_chunks(int H, int nb, int64_t rows) {
 // ---------------------------------------------------------- launchers
 // Each returns hipSuccess or the first launch error.  `grid_slots` sizes persistent grids.
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s);
-hipError_t launch_lengths_to_offsets(const int32_t* len, int32_t B, int32_t* off, int32_t* status,
+hipError_t launch_lengths_to_offsets(const int32_t* len, const int32_t* kv_len, int32_t B,
+                                     int32_t* off, int64_t* bias_off, int32_t* status,
                                      hipStream_t s);
 hipError_t launch_forward(const FwdParams& p, const TileCfg& tc, int head_dim, int mode, int dtype,
                           int64_t max_items, int64_t max_comb_items, int cu_count, hipStream_t s);
@@ -209,6 +210,26 @@ hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, 
 hipError_t launch_backward_dbias(const BwdParams& p, const TileCfg& tc, int head_dim,
                                  int64_t max_q_items, int64_t max_k_items, int cu_count,
                                  hipStream_t s);
+// The MFMA backward of one (head dim, mode) pair (bwd_inst.hip, one translation unit per pair);
+// dbias: the variant with the bias gradient (bf16, bias present, tc.fuse == 0).
+template <int D, int MODE>
+hipError_t launch_bwd_dm(const BwdParams& p, const TileCfg& tc, int64_t max_q_items,
+                         int64_t max_k_items, int cu_count, hipStream_t s, bool dbias);
+#define JFA_DECLARE_BWD_DM(D_, M_)                                                         \
+  template <>                                                                              \
+  hipError_t launch_bwd_dm<D_, M_>(const BwdParams&, const TileCfg&, int64_t, int64_t, int, \
+                                   hipStream_t, bool);
+JFA_DECLARE_BWD_DM(128, 0)
+JFA_DECLARE_BWD_DM(128, 1)
+JFA_DECLARE_BWD_DM(128, 2)
+JFA_DECLARE_BWD_DM(64, 0)
+JFA_DECLARE_BWD_DM(64, 1)
+JFA_DECLARE_BWD_DM(64, 2)
+#undef JFA_DECLARE_BWD_DM
+
+// Sets a kernel's dynamic-LDS limit once per device (thread-safe).
+hipError_t ensure_dyn_lds(const void* kernel, size_t bytes);
+
 hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_t* out,
                                 int32_t out_batch, int32_t* status, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,

@@ -819,35 +819,57 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (role == 0 && a.xtk && tid < XTK_KINDS * XTK_XCDS) a.xtk[tid * XTK_STRIDE] = 0;
 }
 
-// offsets[b+1] = offsets[b] + lengths[b], in int64 with an int32 range check.
-__global__ __launch_bounds__(ST) void lengths_to_offsets_kernel(const int32_t* len, int32_t B,
-                                                                int32_t* off, int32_t* status) {
+// offsets[b+1] = offsets[b] + lengths[b], in int64 with an int32 range check; with bias_off,
+// also the dense-bias block offsets bias_off[b+1] = bias_off[b] + lengths[b] * kv_lengths[b]
+// (kv_lengths = lengths when null), in int64.  Nothing is written when a length is negative or
+// the row total leaves int32.
+__global__ __launch_bounds__(ST) void lengths_to_offsets_kernel(const int32_t* len,
+                                                                const int32_t* kv_len, int32_t B,
+                                                                int32_t* off, int64_t* bias_off,
+                                                                int32_t* status) {
   __shared__ int64_t red[SW];
   __shared__ int32_t flag;
   if (threadIdx.x == 0) flag = 0;
   __syncthreads();
-  int64_t carry = 0;
+  // pass 1: validate (negative lengths, row total past int32)
+  int64_t total = 0;
   int bad = 0;
   for (int64_t base = 0; base < B; base += ST) {
     const int64_t i = base + threadIdx.x;
     const int64_t v = i < B ? (int64_t)len[i] : 0;
-    if (v < 0) bad = 1;
+    const int64_t kv = (i < B && kv_len) ? (int64_t)kv_len[i] : 0;
+    if (v < 0 || kv < 0) bad = 1;
     int64_t tot;
-    const int64_t ex = block_scan(v, &tot, red);
-    if (i < B) {
-      const int64_t o = carry + ex;
-      if (o > INT32_MAX) bad = 1;
-      off[i] = (int32_t)o;
-    }
-    carry += tot;
+    block_scan(v, &tot, red);
+    total += tot;
   }
-  if (threadIdx.x == 0) {
-    if (carry > INT32_MAX) bad = 1;
-    off[B] = (int32_t)carry;
-  }
+  if (total > INT32_MAX) bad = 1;
   if (bad) atomicOr(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && status) *status = flag ? JFA_ERR_DEVICE_DATA : JFA_OK;
+  const bool ok = flag == 0;
+  if (ok) {
+    int64_t carry = 0, bcarry = 0;
+    for (int64_t base = 0; base < B; base += ST) {
+      const int64_t i = base + threadIdx.x;
+      const int64_t v = i < B ? (int64_t)len[i] : 0;
+      int64_t tot;
+      const int64_t ex = block_scan(v, &tot, red);
+      if (i < B) off[i] = (int32_t)(carry + ex);
+      carry += tot;
+      if (bias_off) {
+        const int64_t kv = i < B ? (kv_len ? (int64_t)kv_len[i] : v) : 0;
+        int64_t btot;
+        const int64_t bex = block_scan(v * kv, &btot, red);
+        if (i < B) bias_off[i] = bcarry + bex;
+        bcarry += btot;
+      }
+    }
+    if (threadIdx.x == 0) {
+      off[B] = (int32_t)carry;
+      if (bias_off) bias_off[B] = bcarry;
+    }
+  }
+  if (threadIdx.x == 0 && status) *status = ok ? JFA_OK : JFA_ERR_DEVICE_DATA;
 }
 
 // BlockAttention's refined offsets: sample b (rows [off[b], off[b+1])) becomes ceil(n_b / W)
@@ -908,13 +930,10 @@ hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
-  static bool attr_set = false;
   const size_t lds = sizeof(Shared);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)schedule_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    hipError_t e = ensure_dyn_lds((const void*)schedule_kernel, lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int roles = a.parallel ? __builtin_popcount(a.lists & 7) : 1;
   timing_begin("jfa_schedule", s);
@@ -924,10 +943,12 @@ hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_lengths_to_offsets(const int32_t* len, int32_t B, int32_t* off, int32_t* status,
+hipError_t launch_lengths_to_offsets(const int32_t* len, const int32_t* kv_len, int32_t B,
+                                     int32_t* off, int64_t* bias_off, int32_t* status,
                                      hipStream_t s) {
   timing_begin("jfa_offsets", s);
-  hipLaunchKernelGGL(lengths_to_offsets_kernel, dim3(1), dim3(ST), 0, s, len, B, off, status);
+  hipLaunchKernelGGL(lengths_to_offsets_kernel, dim3(1), dim3(ST), 0, s, len, kv_len, B, off,
+                     bias_off, status);
   timing_end(s);
   return hipGetLastError();
 }

@@ -27,7 +27,8 @@ ROOT = os.path.dirname(HERE)
 
 
 # timing name -> the source file that defines the kernel
-KERNEL_SOURCE = {"jfa_bwd_kvq": "bwd.hip", "jfa_bwd_dkdv": "bwd.hip", "jfa_bwd_dq": "bwd.hip",
+KERNEL_SOURCE = {"jfa_bwd_kvq": "bwd_inst.hip", "jfa_bwd_dkdv": "bwd_inst.hip",
+                 "jfa_bwd_dq": "bwd_inst.hip", "jfa_dbias_dq": "bwd_inst.hip",
                  "jfa_fwd_bf16": "fwd.hip",
                  "jfa_fwd_mxfp8": "fwd.hip", "jfa_fwd_combine": "fwd.hip",
                  "jfa_schedule": "sched.hip", "jfa_offsets": "sched.hip",
@@ -63,6 +64,8 @@ def timing_name(kernel: str) -> str | None:
         return "jfa_bwd_kvq"
     if "bwd_kv_kernel" in k:
         return "jfa_bwd_dkdv"
+    if "bwd_q_db_kernel" in k:
+        return "jfa_dbias_dq"
     if "bwd_q_kernel" in k:
         return "jfa_bwd_dq"
     if "combine_kernel" in k:

@@ -71,6 +71,7 @@ def lib():
         _lib.ora_forward.argtypes = [P] * 10
         _lib.ora_backward.argtypes = [P] * 12
         _lib.ora_bias_grad.argtypes = [P] * 10
+        _lib.ora_abs_terms.argtypes = [P] * 13
         _lib.ora_schedule.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                       P, P, P, P, P, ctypes.c_int64, P]
         _lib.ora_e4m3_decode.argtypes = [ctypes.c_int]
@@ -217,6 +218,40 @@ def bias_grad(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, b
     lib().ora_bias_grad(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                         _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(db))
     return db
+
+
+def abs_terms(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
+              bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
+    """Absolute-value contractions (fp64) behind each output element: dict with "O" = sum_j
+    |P_ij||V_j|, "dV" = sum_i |P_ij||dO_i|, "dQ" = scale sum_j |dS_ij||K_j|, "dK" = scale
+    sum_i |dS_ij||Q_i| (GDPA's P includes its weight w).  Rounding P or dS to a format with
+    relative error u moves each output by at most u times its term (see ``ora_abs_terms``).
+    dout None: only "O"."""
+    _check_block(block, q_lens, kv_lens, bias_kind)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    dout = None if dout is None else _f64(dout)
+    Tq, H, d = q.shape
+    qo, ko = offsets(q_lens), offsets(kv_lens)
+    B = qo.shape[0] - 1
+    bo = bias_offsets(q_lens, kv_lens)
+    bias64 = _f64(bias) if bias is not None else None
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    c_o = np.zeros_like(q)
+    c_dq, c_dk, c_dv = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)) \
+        if dout is not None else (None, None, None)
+    lib().ora_abs_terms(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
+                        _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(c_o), _ptr(c_dq), _ptr(c_dk),
+                        _ptr(c_dv))
+    out = {"O": c_o}
+    if dout is not None:
+        out.update(dQ=c_dq, dK=c_dk, dV=c_dv)
+    return out
+
+
+def case_abs_terms(case, **kw):
+    return abs_terms(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                     mode=case.mode, causal=case.causal, bias=case.bias,
+                     bias_kind=case.bias_kind, num_buckets=case.num_buckets, **kw)
 
 
 def case_forward(case, **kw):

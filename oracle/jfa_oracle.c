@@ -333,6 +333,101 @@ void ora_backward(const ora_problem* p, const int64_t* qo, const int64_t* ko,
   }
 }
 
+/* ------------------------------------------------ operand-rounding magnitudes */
+
+/* Absolute-value contractions behind each output element, for bounding the error that comes
+ * from rounding an operand of a product to a narrower format (relative error at most u per
+ * element): the output's error from rounding P (or dS) is then at most u times
+ *   cO[i]  = sum_j |P_ij| |V_j|            (GDPA: P_ij = w act(S_ij))
+ *   cdV[j] = sum_i |P_ij| |dO_i|
+ *   cdQ[i] = scale * sum_j |dS_ij| |K_j|
+ *   cdK[j] = scale * sum_i |dS_ij| |Q_i|
+ * over visible pairs, with P and dS exactly as in ora_forward / ora_backward (fp64).  Outputs
+ * have the layouts of o, dv, dq, dk and are fully written; dout may be NULL (then only cO). */
+void ora_abs_terms(const ora_problem* p, const int64_t* qo, const int64_t* ko,
+                   const double* q, const double* k, const double* v, const double* bias,
+                   const int64_t* bo, const double* dout, double* c_o, double* c_dq,
+                   double* c_dk, double* c_dv) {
+  const int64_t B = p->batch, H = p->heads, d = p->head_dim;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t item = 0; item < B * H; ++item) {
+    const int64_t b = item / H;
+    const int h = (int)(item % H);
+    const int64_t n = qo[b + 1] - qo[b], m = ko[b + 1] - ko[b];
+    for (int64_t i = 0; i < n; ++i) {
+      memset(c_o + ((qo[b] + i) * H + h) * d, 0, sizeof(double) * (size_t)d);
+      if (dout) memset(c_dq + ((qo[b] + i) * H + h) * d, 0, sizeof(double) * (size_t)d);
+    }
+    if (dout)
+      for (int64_t j = 0; j < m; ++j) {
+        memset(c_dk + ((ko[b] + j) * H + h) * d, 0, sizeof(double) * (size_t)d);
+        memset(c_dv + ((ko[b] + j) * H + h) * d, 0, sizeof(double) * (size_t)d);
+      }
+    double* s = (double*)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+    double* pr = (double*)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t qrow = qo[b] + i;
+      const double* qi = q + (qrow * H + h) * d;
+      int64_t nvis = 0;
+      for (int64_t j = 0; j < m; ++j) {
+        if (!visible(p, i, j, n, m)) continue;
+        s[j] = score(p, q, k, bias, bo, b, h, qrow, ko[b] + j, i, j, n, m);
+        ++nvis;
+      }
+      if (nvis == 0) continue;
+      /* P row (softmax: normalised exponentials; GDPA: w act(S)) */
+      double mx = -INFINITY, l = 0.0;
+      const double w = gdpa_weight(p, i, m);
+      if (p->mode == 0) {
+        for (int64_t j = 0; j < m; ++j)
+          if (visible(p, i, j, n, m) && s[j] > mx) mx = s[j];
+        for (int64_t j = 0; j < m; ++j)
+          if (visible(p, i, j, n, m)) l += exp(s[j] - mx);
+      }
+      for (int64_t j = 0; j < m; ++j) {
+        if (!visible(p, i, j, n, m)) continue;
+        pr[j] = p->mode == 0 ? exp(s[j] - mx) / l : w * act(p->mode, s[j]);
+      }
+      double* coi = c_o + (qrow * H + h) * d;
+      for (int64_t j = 0; j < m; ++j) {
+        if (!visible(p, i, j, n, m)) continue;
+        const double* vj = v + ((ko[b] + j) * H + h) * d;
+        for (int64_t c = 0; c < d; ++c) coi[c] += fabs(pr[j]) * fabs(vj[c]);
+      }
+      if (!dout) continue;
+      const double* doi = dout + (qrow * H + h) * d;
+      double D = 0.0;
+      if (p->mode == 0) {
+        /* D = dO . O with O = sum_j P_ij V_j */
+        for (int64_t c = 0; c < d; ++c) {
+          double oc = 0.0;
+          for (int64_t j = 0; j < m; ++j)
+            if (visible(p, i, j, n, m)) oc += pr[j] * v[((ko[b] + j) * H + h) * d + c];
+          D += doi[c] * oc;
+        }
+      }
+      double* cdqi = c_dq + (qrow * H + h) * d;
+      for (int64_t j = 0; j < m; ++j) {
+        if (!visible(p, i, j, n, m)) continue;
+        const double* kj = k + ((ko[b] + j) * H + h) * d;
+        const double* vj = v + ((ko[b] + j) * H + h) * d;
+        double* cdkj = c_dk + ((ko[b] + j) * H + h) * d;
+        double* cdvj = c_dv + ((ko[b] + j) * H + h) * d;
+        double dp = 0.0;
+        for (int64_t c = 0; c < d; ++c) dp += doi[c] * vj[c];
+        const double ds = p->mode == 0 ? pr[j] * (dp - D) : act_grad(p->mode, s[j]) * w * dp;
+        for (int64_t c = 0; c < d; ++c) {
+          cdvj[c] += fabs(pr[j]) * fabs(doi[c]);
+          cdqi[c] += p->scale * fabs(ds) * fabs(kj[c]);
+          cdkj[c] += p->scale * fabs(ds) * fabs(qi[c]);
+        }
+      }
+    }
+    free(s);
+    free(pr);
+  }
+}
+
 /* ------------------------------------------------------------ bias gradient */
 
 /* Gradient of <O, dO> with respect to the additive bias ("Meta GEM Training Efficiency: ...",

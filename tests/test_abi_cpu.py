@@ -133,8 +133,15 @@ def test_backward_host_errors():
 
 def test_other_entry_points_host_errors():
     lib = jfa.load()
-    assert lib.jfa_lengths_to_offsets(None, 4, FAKE, None, None) == _lib.JFA_ERR_INVALID_ARG
-    assert lib.jfa_lengths_to_offsets(FAKE, -1, FAKE, None, None) == _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_lengths_to_offsets(None, 4, FAKE, None, None, None, None) == \
+        _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_lengths_to_offsets(FAKE, -1, FAKE, None, None, None, None) == \
+        _lib.JFA_ERR_INVALID_ARG
+    # the int64 bias offsets must be 8-byte aligned, the kv lengths 4-byte aligned
+    assert lib.jfa_lengths_to_offsets(FAKE, 4, FAKE, FAKE + 4, None, None, None) == \
+        _lib.JFA_ERR_INVALID_ARG
+    assert lib.jfa_lengths_to_offsets(FAKE, 4, FAKE, FAKE, FAKE + 2, None, None) == \
+        _lib.JFA_ERR_INVALID_ARG
     # BlockAttention offsets: block < 1, a negative batch or out_batch, null or misaligned
     assert lib.jfa_block_offsets(FAKE, 4, 0, FAKE, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_block_offsets(FAKE, -1, 4, FAKE, 8, None, None) == _lib.JFA_ERR_INVALID_ARG

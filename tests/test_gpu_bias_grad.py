@@ -231,3 +231,63 @@ def test_bias_grad_block_attention(bias_kind):
                                             num_buckets=case.num_buckets, block=w)
         compare("dQ", dq, dq_ref, "bf16")
         compare("dK", dk, dk_ref, "bf16")
+
+
+@pytest.mark.parametrize("mode,causal,bias_kind", [("softmax", True, "relpos"),
+                                                    ("gelu", False, "dense")])
+def test_autograd_bias_gradient(mode, causal, bias_kind):
+    """A trainable bias through the torch.autograd.Function: bias.grad is the oracle's
+    dL/dbias for L = <O, dO>, beside dQ, dK, dV."""
+    import jagged_attention_amd as jfa
+    lq = [150, 0, 70, 9]
+    lk = lq if causal else [90, 12, 130, 3]
+    case = custom_case(lq, lk, 2, 128, dtype="bf16", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=96)
+    say(f"[bias grad] autograd mode={mode} bias={bias_kind}")
+    dc = device_case(case)
+    q, k, v = (dc[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    bias = dc["bias"].clone().requires_grad_(True)
+    opts = dict(mode=mode, causal=causal, bias_kind=bias_kind, num_buckets=case.num_buckets)
+    o = jfa.JaggedAttention.apply(q, k, v, dc["qo"], dc["ko"], bias, opts)
+    (o.float() * dc["dout"].float()).sum().backward()
+    torch.cuda.synchronize()
+    okw = dict(mode=mode, causal=causal, bias=case.bias, bias_kind=bias_kind,
+               num_buckets=case.num_buckets)
+    db_ref = oracle.bias_grad(case.q, case.k, case.v, case.dout, case.q_lens, case.kv_lens,
+                              **okw)
+    assert bias.grad is not None and bias.grad.dtype == bias.dtype
+    if bias_kind == "dense":
+        check_dense(bias.grad, db_ref, case, d_residue(case, o.detach()))
+    else:
+        _check_table(bias.grad, db_ref)
+    dq_ref, dk_ref, dv_ref = oracle.backward(case.q, case.k, case.v, case.dout, case.q_lens,
+                                             case.kv_lens, **okw)
+    compare("dQ", q.grad, dq_ref, "bf16")
+    compare("dK", k.grad, dk_ref, "bf16")
+    compare("dV", v.grad, dv_ref, "bf16")
+
+
+def test_malformed_offsets_leave_dbias_untouched():
+    """Offsets the scheduler rejects (non-monotone) on a workspace and dbias prefilled with
+    garbage: the call reports JFA_ERR_DEVICE_DATA and writes neither dbias nor the gradients
+    (the zeroing kernel takes its count from bias offsets that were never written)."""
+    import jagged_attention_amd as jfa
+    for bias_kind in ("dense", "relpos"):
+        case = custom_case([40, 30], [40, 30], 2, 128, dtype="bf16", mode="softmax",
+                           causal=True, bias_kind=bias_kind, seed=97)
+        say(f"[bias grad] malformed offsets bias={bias_kind}")
+        dc = device_case(case)
+        bad = torch.tensor([0, 50, 30], dtype=torch.int32, device="cuda:0")   # decreasing
+        p = jfa.make_problem(2, 2, 128, case.total_q, case.total_kv, mode="softmax",
+                             causal=True, bias_kind=bias_kind)
+        nb = jfa.jfa_workspace_bytes(p, 2)
+        ws = torch.full((nb,), 0x7F, dtype=torch.uint8, device="cuda:0")
+        o = torch.zeros_like(dc["q"])
+        lse = torch.zeros((2, case.total_q), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = (torch.full_like(dc[x], 3.0) for x in ("q", "k", "v"))
+        db = torch.full_like(dc["bias"], 5.0)
+        jfa.jfa_backward_dbias(p, dc["q"], dc["k"], dc["v"], o, lse, dc["dout"], bad, bad,
+                               dc["bias"], dq, dk, dv, db, ws, nb)
+        assert jfa.jfa_read_device_status(ws) == jfa._lib.JFA_ERR_DEVICE_DATA
+        assert bool((db == 5.0).all()), bias_kind
+        assert bool((dq == 3.0).all() and (dk == 3.0).all() and (dv == 3.0).all())

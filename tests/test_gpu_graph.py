@@ -26,10 +26,7 @@ def _lib():
 def test_graph_replay_matches_eager(mode, causal, bias_kind, split):
     import jagged_attention_amd as jfa
     lens = [700, 0, 129, 64, 1500]
-    # key lengths >= 8 as in the GDPA workloads: with one key and 64 queries GDPA's weight
-    # 1/kv_len is 1, |dK| reaches ~20, and rounding dS to bf16 for the dK MFMA alone moves it by
-    # ~0.02 (an fp64 simulation of that rounding reproduces the kernel's error exactly)
-    kl = lens if causal else [300, 16, 64, 8, 90]
+    kl = lens if causal else [300, 16, 64, 1, 90]
     case = custom_case(lens, kl, 2, 128, dtype="bf16", mode=mode, causal=causal,
                        bias_kind=bias_kind, seed=77)
     say(f"[graph] mode={mode} causal={causal} bias={bias_kind} split={split}")
@@ -54,8 +51,8 @@ def test_graph_replay_matches_eager(mode, causal, bias_kind, split):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
     def step():
-        jfa.jfa_lengths_to_offsets(ql, B, qo, st[0:1])
-        jfa.jfa_lengths_to_offsets(kvl, B, ko, st[1:2])
+        jfa.jfa_lengths_to_offsets(ql, B, qo, status=st[0:1])
+        jfa.jfa_lengths_to_offsets(kvl, B, ko, status=st[1:2])
         jfa.jfa_forward(pf, q, k, v, None, None, None, qo, ko, bias, o, lse, wf, wf.numel())
         jfa.jfa_backward(pb, q, k, v, o, lse, do, qo, ko, bias, dq, dk, dv, wb, wb.numel())
 
@@ -65,9 +62,10 @@ def test_graph_replay_matches_eager(mode, causal, bias_kind, split):
     want = [t.clone() for t in outs]
     o_ref, _ = oracle.case_forward(case)
     dq_ref, dk_ref, dv_ref = oracle.case_backward(case)
+    c = oracle.case_abs_terms(case)     # bf16 operand rounding (one sample has a single key)
     for name, got, ref in (("O", o, o_ref), ("dQ", dq, dq_ref), ("dK", dk, dk_ref),
                            ("dV", dv, dv_ref)):
-        compare(name, got, ref, "bf16")
+        compare(name, got, ref, "bf16", cond=c[name])
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -116,7 +114,7 @@ def test_graph_replay_bias_gradient(bias_kind):
     db = torch.empty_like(bias)
 
     def step():
-        jfa.jfa_lengths_to_offsets(ql, B, qo, st[0:1])
+        jfa.jfa_lengths_to_offsets(ql, B, qo, status=st[0:1])
         jfa.jfa_forward(p, q, k, v, None, None, None, qo, qo, bias, o, lse, wf, wf.numel())
         jfa.jfa_backward_dbias(p, q, k, v, o, lse, do, qo, qo, bias, dq, dk, dv, db, wb,
                                wb.numel())

@@ -39,6 +39,34 @@ def test_lengths_to_offsets_bitexact():
     assert int(st.item()) == jfa._lib.JFA_ERR_DEVICE_DATA
 
 
+@pytest.mark.parametrize("asym", [False, True])
+def test_bias_offsets_bitexact(asym):
+    """Row offsets and the int64 dense-bias block offsets (running sum of q_len * kv_len) against
+    the oracle, including totals far beyond 2^31 elements."""
+    import jagged_attention_amd as jfa
+    rng = np.random.default_rng(2 + asym)
+    for B in (1, 7, 1025, 3000):
+        ql = rng.integers(0, 5000, size=B).astype(np.int32)
+        kl = rng.integers(0, 5000, size=B).astype(np.int32) if asym else ql
+        ql[rng.integers(0, B)] = 0
+        off, boff, st = jfa.bias_offsets(torch.as_tensor(ql).cuda(),
+                                         torch.as_tensor(kl).cuda() if asym else None)
+        assert int(st.item()) == 0
+        assert np.array_equal(off.cpu().numpy().astype(np.int64), oracle.offsets(ql)), B
+        want = oracle.bias_offsets(ql, kl)
+        assert np.array_equal(boff.cpu().numpy(), want), B
+        if B == 3000:
+            assert want[-1] > 2 ** 31
+    # a negative kv length is malformed: status set, neither array written
+    off = torch.full((4,), 7, dtype=torch.int32).cuda()
+    boff = torch.full((4,), 7, dtype=torch.int64).cuda()
+    st = torch.zeros(1, dtype=torch.int32).cuda()
+    jfa.jfa_lengths_to_offsets(torch.tensor([3, 1, 2], dtype=torch.int32).cuda(), 3, off, boff,
+                               torch.tensor([3, -1, 2], dtype=torch.int32).cuda(), st)
+    assert int(st.item()) == jfa._lib.JFA_ERR_DEVICE_DATA
+    assert off.cpu().tolist() == [7] * 4 and boff.cpu().tolist() == [7] * 4
+
+
 # ------------------------------------------------------------ tile lists
 
 SCHED_BATCHES = [

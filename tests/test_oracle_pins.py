@@ -638,3 +638,63 @@ def test_rmsnorm_invariants(oracle_mod):
     y64 = oracle_mod.rmsnorm(x2, n=64, eps=0.0)
     assert np.allclose(y64[..., :64], oracle_mod.rmsnorm(x[..., :64], eps=0.0), rtol=1e-13)
     assert np.allclose(y64[..., 64:], oracle_mod.rmsnorm(x[..., 64:], eps=0.0), rtol=1e-13)
+
+
+# ------------------------------------------------ operand-rounding magnitudes
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal,bias_kind", [(False, "none"), (True, "relpos"), (False, "dense")])
+def test_abs_terms_bound_outputs(oracle_mod, mode, causal, bias_kind):
+    """Triangle inequality: every term is at least the magnitude of the output it bounds."""
+    ql, kl = ([5, 0, 9, 1, 12], [5, 0, 9, 1, 12]) if causal else ([4, 7, 3, 6], [9, 2, 3, 1])
+    case = custom_case(ql, kl, 2, 16, dtype="f32", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=140, bias_std=0.5)
+    c = oracle_mod.case_abs_terms(case)
+    o, _ = oracle_mod.case_forward(case)
+    dq, dk, dv = oracle_mod.case_backward(case)
+    for name, x in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert np.all(c[name] >= np.abs(x) * (1 - 1e-12) - 1e-300), name
+    # a term is zero exactly where nothing is visible: the empty sample's rows
+    assert np.all(c["O"][5:5] == 0)
+
+
+def test_abs_terms_equal_outputs_when_signs_agree(oracle_mod):
+    """Where no cancellation is possible the term equals the output's magnitude: softmax with
+    V >= 0 (P >= 0) gives cO = O, with dO >= 0 gives cdV = dV; one key per sample gives
+    |dQ| = cdQ (a single term), one query per sample gives |dK| = cdK, and GDPA with one key
+    gives |O| = cO."""
+    case = custom_case([6, 3, 8], [4, 9, 5], 2, 16, dtype="f32", mode="softmax",
+                       bias_kind="dense", seed=141, bias_std=0.5)
+    case.v = case.v.abs()
+    case.dout = case.dout.abs()
+    c = oracle_mod.case_abs_terms(case)
+    o, _ = oracle_mod.case_forward(case)
+    _, _, dv = oracle_mod.case_backward(case)
+    assert max_abs(c["O"], o) < 1e-12 and max_abs(c["dV"], dv) < 1e-12
+    for mode in ("softmax", "silu", "gelu"):
+        one_k = custom_case([5, 3, 7], [1, 1, 1], 2, 16, dtype="f32", mode=mode,
+                            bias_kind="relpos", seed=142, bias_std=0.5)
+        c = oracle_mod.case_abs_terms(one_k)
+        dq, _, _ = oracle_mod.case_backward(one_k)
+        assert max_abs(c["dQ"], np.abs(dq)) < 1e-12, mode
+        if mode != "softmax":
+            o, _ = oracle_mod.case_forward(one_k)
+            assert max_abs(c["O"], np.abs(o)) < 1e-12, mode
+        one_q = custom_case([1, 1, 1], [5, 3, 7], 2, 16, dtype="f32", mode=mode,
+                            bias_kind="dense", seed=143, bias_std=0.5)
+        c = oracle_mod.case_abs_terms(one_q)
+        _, dk, _ = oracle_mod.case_backward(one_q)
+        assert max_abs(c["dK"], np.abs(dk)) < 1e-12, mode
+
+
+def test_abs_terms_scale_with_operands(oracle_mod):
+    """cO is linear in |V| and cdV in |dO| at fixed P; cdQ and cdK depend on V and dO only
+    through dS (scaling V by 4 and dO by 1/4, both exact, leaves dP, dS and P unchanged)."""
+    case = custom_case([6, 3], [4, 9], 2, 16, dtype="f32", mode="silu", seed=144)
+    c1 = oracle_mod.case_abs_terms(case)
+    case.v = case.v * 4.0
+    case.dout = case.dout / 4.0
+    c2 = oracle_mod.case_abs_terms(case)
+    assert rel_l2(c2["O"], 4.0 * c1["O"]) < 1e-12
+    assert rel_l2(c2["dQ"], c1["dQ"]) < 1e-12 and rel_l2(c2["dK"], c1["dK"]) < 1e-12
+    assert rel_l2(c2["dV"], c1["dV"] / 4.0) < 1e-12
