@@ -44,14 +44,15 @@ class _Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_double),
                 ("normalize", ctypes.c_int32), ("bias_kind", ctypes.c_int32),
-                ("num_buckets", ctypes.c_int32), ("block", ctypes.c_int32)]
+                ("num_buckets", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class _SchedParams(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("slots", ctypes.c_int32),
                 ("bq_bm", ctypes.c_int32), ("bq_bn", ctypes.c_int32),
                 ("bk_bn", ctypes.c_int32), ("bk_bm", ctypes.c_int32),
-                ("fuse", ctypes.c_int32)]
+                ("fuse", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -145,13 +146,15 @@ def relpos_bucket(delta: int, num_buckets: int = 64) -> int:
 
 # ------------------------------------------------------------ attention
 
-def _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block=0):
+def _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block=0,
+             window=0):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if normalize is None:
         normalize = mode != "softmax"
+    assert int(window) >= 0
     return _Problem(B, H, d, MODES[mode], int(bool(causal)), float(scale), int(bool(normalize)),
-                    BIAS[bias_kind], int(num_buckets), int(block))
+                    BIAS[bias_kind], int(num_buckets), int(block), int(window))
 
 
 def _check_block(block, q_lens, kv_lens, bias_kind):
@@ -163,9 +166,10 @@ def _check_block(block, q_lens, kv_lens, bias_kind):
 
 
 def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-            bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
+            bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0, window=0):
     """Returns (o [Tq,H,d] fp64, lse [H,Tq] fp64 or None for GDPA).  block > 0: BlockAttention
-    with blocks of that many rows."""
+    with blocks of that many rows; window > 0: sliding window, key j visible to query i only
+    when |i + (kv_len - q_len) - j| < window (and j <= i + kv_len - q_len when causal)."""
     _check_block(block, q_lens, kv_lens, bias_kind)
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, H, d = q.shape
@@ -176,7 +180,8 @@ def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None
     bias64 = _f64(bias) if bias is not None else None
     if bias_kind != "none":
         assert bias64 is not None
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block,
+                 window)
     o = np.zeros_like(q)
     lse = np.full((H, Tq), np.nan) if mode == "softmax" else None
     lib().ora_forward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
@@ -185,7 +190,7 @@ def forward(q, k, v, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None
 
 
 def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-             bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
+             bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0, window=0):
     """Returns (dq, dk, dv) in fp64: the gradients of <O, dout>."""
     _check_block(block, q_lens, kv_lens, bias_kind)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -194,7 +199,8 @@ def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bi
     B = qo.shape[0] - 1
     bo = bias_offsets(q_lens, kv_lens)
     bias64 = _f64(bias) if bias is not None else None
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block,
+                 window)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     lib().ora_backward(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                        _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
@@ -202,7 +208,7 @@ def backward(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bi
 
 
 def bias_grad(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-              bias_kind="relpos", num_buckets=64, scale=None, normalize=None, block=0):
+              bias_kind="relpos", num_buckets=64, scale=None, normalize=None, block=0, window=0):
     """Gradient of <O, dout> with respect to the bias (fp64): the relative-position table
     [H][num_buckets], or a dense bias in its own layout."""
     assert bias_kind in ("relpos", "dense") and bias is not None
@@ -213,7 +219,8 @@ def bias_grad(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, b
     B = qo.shape[0] - 1
     bo = bias_offsets(q_lens, kv_lens)
     bias64 = _f64(bias)
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block,
+                 window)
     db = np.zeros_like(bias64)
     lib().ora_bias_grad(ctypes.byref(p), _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                         _ptr(bias64), _ptr(bo), _ptr(dout), _ptr(db))
@@ -221,7 +228,7 @@ def bias_grad(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, b
 
 
 def abs_terms(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, bias=None,
-              bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0):
+              bias_kind="none", num_buckets=64, scale=None, normalize=None, block=0, window=0):
     """Absolute-value contractions (fp64) behind each output element: dict with "O" = sum_j
     |P_ij||V_j|, "dV" = sum_i |P_ij||dO_i|, "dQ" = scale sum_j |dS_ij||K_j|, "dK" = scale
     sum_i |dS_ij||Q_i| (GDPA's P includes its weight w).  Rounding P or dS to a format with
@@ -235,7 +242,8 @@ def abs_terms(q, k, v, dout, q_lens, kv_lens, *, mode="softmax", causal=False, b
     B = qo.shape[0] - 1
     bo = bias_offsets(q_lens, kv_lens)
     bias64 = _f64(bias) if bias is not None else None
-    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block)
+    p = _problem(B, H, d, mode, causal, scale, normalize, bias_kind, num_buckets, block,
+                 window)
     c_o = np.zeros_like(q)
     c_dq, c_dk, c_dv = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)) \
         if dout is not None else (None, None, None)
@@ -270,11 +278,13 @@ def case_backward(case, **kw):
 # ------------------------------------------------------------- tile lists
 
 def schedule(q_offsets, kv_offsets, heads: int, causal: bool, *, bm: int, bn: int, slots: int,
-             bq_bm: int, bq_bn: int, bk_bn: int, bk_bm: int, fuse: int = 3) -> dict:
+             bq_bm: int, bq_bn: int, bk_bn: int, bk_bm: int, fuse: int = 3,
+             window: int = 0) -> dict:
     """Forward / combine / backward tile lists (see ``ora_schedule`` in the C source).
 
     fuse: single-pass backward classes, bit 0 for samples with one query tile, bit 1 for
-    samples with one key tile (True means both)."""
+    samples with one key tile (True means both).  window: the attention's sliding window
+    (0 = none); tiles then cover only the steps some of their rows can see."""
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
     ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
     B = qo.shape[0] - 1
@@ -289,7 +299,7 @@ def schedule(q_offsets, kv_offsets, heads: int, causal: bool, *, bm: int, bn: in
     bk = np.zeros((cap, 4), np.int32)
     counts = np.zeros(5, np.int64)
     fuse = 3 if fuse is True else int(fuse)
-    sp = _SchedParams(bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse)
+    sp = _SchedParams(bm, bn, slots, bq_bm, bq_bn, bk_bn, bk_bm, fuse, int(window))
     rc = lib().ora_schedule(_ptr(qo), _ptr(ko), B, heads, int(bool(causal)), ctypes.byref(sp),
                             _ptr(fwd), _ptr(fslot), _ptr(comb), _ptr(bq), _ptr(bk), cap,
                             _ptr(counts))

@@ -46,6 +46,9 @@ typedef struct {
   int32_t block;       /* BlockAttention: >0 splits every sample (q_len = kv_len) into
                           consecutive blocks of this many rows that attend only within
                           themselves; 0 = full attention over the sample */
+  int32_t window;      /* sliding window: >0 limits query i to keys j with
+                          |i + (kv_len - q_len) - j| < window (with causal: the window keys
+                          ending at its own position); 0 = no window */
 } ora_problem;
 
 /* ---------------------------------------------------------------- threads */
@@ -160,6 +163,14 @@ static double act_grad(int mode, double x) {
  * key j interact only when they fall in the same block of p->block consecutive rows. */
 static int visible(const ora_problem* p, int64_t i, int64_t j, int64_t n, int64_t m) {
   if (p->block > 0 && i / p->block != j / p->block) return 0;
+  /* sliding window ("GEM Training: How Meta Doubled ...", "Challenge 1": long sequences with a
+   * short attention window; "Meta Enhances GEM Training Efficiency ...", "Leveraging Compute
+   * Efficiency through Customized Kernels": attention over windows): the key must lie fewer
+   * than `window` positions from the query's aligned position i + (m - n) */
+  if (p->window > 0) {
+    const int64_t dist = (i + (m - n)) - j;
+    if (dist >= p->window || -dist >= p->window) return 0;
+  }
   return !p->causal || j <= i + (m - n);
 }
 
@@ -514,6 +525,7 @@ typedef struct {
   int32_t bk_bn, bk_bm;  /* key-stationary backward: key rows per tile, query rows per step */
   int32_t fuse;          /* single backward pass: bit 0 for samples with one query tile, bit 1 for
                             samples with one key tile (and not one query tile) */
+  int32_t window;        /* sliding window of the attention (0 = none), as in ora_problem */
 } ora_sched_params;
 
 typedef struct { int32_t b, t, lo, hi; } ora_rec;
@@ -533,14 +545,51 @@ static int rec_cmp(const void* pa, const void* pb) {
   return 0;
 }
 
-/* Number of key rows that some query of tile rows [r0, r1) may see. */
-static int64_t kv_extent(int causal, int64_t r1, int64_t n, int64_t m) {
-  if (!causal) return m;
-  int64_t e = r1 + (m - n);
-  if (e < 0) e = 0;
+/* Keys [*lo, *hi) that some query of rows [r0, r1) may see (causal, window); returns 0 when
+ * there are none.  Query i sees key j iff j <= i + (m - n) (causal) and, with a window W,
+ * i + (m - n) - W < j < i + (m - n) + W. */
+static int kv_range(int causal, int32_t window, int64_t r0, int64_t r1, int64_t n, int64_t m,
+                    int64_t* lo, int64_t* hi) {
+  const int64_t dl = m - n;
+  int64_t a = 0, e = m;
+  if (window > 0) {
+    a = r0 + dl - window + 1;
+    e = r1 - 1 + dl + window;
+  }
+  if (causal && r1 + dl < e) e = r1 + dl;
+  if (a < 0) a = 0;
   if (e > m) e = m;
-  (void)n;
-  return e;
+  *lo = a;
+  *hi = e;
+  return e > a;
+}
+
+/* Queries [*lo, *hi) that may see some key of columns [c0, c1). */
+static int q_range(int causal, int32_t window, int64_t c0, int64_t c1, int64_t n, int64_t m,
+                   int64_t* lo, int64_t* hi) {
+  const int64_t dl = m - n;
+  int64_t a = 0, e = n;
+  if (window > 0) {
+    a = c0 - dl - window + 1;
+    e = c1 - 1 - dl + window;
+  }
+  if (causal && c0 - dl > a) a = c0 - dl;
+  if (a < 0) a = 0;
+  if (e > n) e = n;
+  *lo = a;
+  *hi = e;
+  return e > a;
+}
+
+/* Step range [*s0, *s1) of `step`-row steps covering [lo, hi), or the empty range at `empty`. */
+static void step_range(int nonempty, int64_t lo, int64_t hi, int64_t step, int64_t empty,
+                       int64_t* s0, int64_t* s1) {
+  if (nonempty) {
+    *s0 = lo / step;
+    *s1 = ceil_div64(hi, step);
+  } else {
+    *s0 = *s1 = empty;
+  }
 }
 
 /*
@@ -567,7 +616,10 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
     const int64_t nqt = ceil_div64(n, sp->bm);
     for (int64_t t = 0; t < nqt; ++t) {
       int64_t r1 = (t + 1) * sp->bm < n ? (t + 1) * sp->bm : n;
-      int64_t nkv = ceil_div64(kv_extent(causal, r1, n, m), sp->bn);
+      int64_t lo, hi, s0, s1;
+      const int any = kv_range(causal, sp->window, t * sp->bm, r1, n, m, &lo, &hi);
+      step_range(any, lo, hi, sp->bn, 0, &s0, &s1);
+      const int64_t nkv = s1 - s0;
       sumcost += nkv > 1 ? nkv : 1;
       ++ntiles;
     }
@@ -585,7 +637,10 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
     const int64_t nqt = ceil_div64(n, sp->bm);
     for (int64_t t = 0; t < nqt; ++t) {
       int64_t r1 = (t + 1) * sp->bm < n ? (t + 1) * sp->bm : n;
-      int64_t nkv = ceil_div64(kv_extent(causal, r1, n, m), sp->bn);
+      int64_t lo, hi, s0, s1;
+      const int any = kv_range(causal, sp->window, t * sp->bm, r1, n, m, &lo, &hi);
+      step_range(any, lo, hi, sp->bn, 0, &s0, &s1);
+      const int64_t nkv = s1 - s0;
       if (C > 0 && nkv > C) {
         int64_t nch = ceil_div64(nkv, C);
         if (nc >= cap) { free(recs); free(slot_of); return -2; }
@@ -593,7 +648,8 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
         comb[4 * nc + 2] = (int32_t)slot; comb[4 * nc + 3] = (int32_t)nch;
         ++nc;
         for (int64_t c = 0; c < nch; ++c) {
-          ora_rec r = {b, (int32_t)t, (int32_t)(c * nkv / nch), (int32_t)((c + 1) * nkv / nch)};
+          ora_rec r = {b, (int32_t)t, (int32_t)(s0 + c * nkv / nch),
+                       (int32_t)(s0 + (c + 1) * nkv / nch)};
           recs = (ora_rec*)realloc(recs, sizeof(ora_rec) * (size_t)(nf + 1));
           slot_of = (int32_t*)realloc(slot_of, sizeof(int32_t) * (size_t)(nf + 1));
           recs[nf] = r;
@@ -604,7 +660,7 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
       } else {
         recs = (ora_rec*)realloc(recs, sizeof(ora_rec) * (size_t)(nf + 1));
         slot_of = (int32_t*)realloc(slot_of, sizeof(int32_t) * (size_t)(nf + 1));
-        ora_rec r = {b, (int32_t)t, 0, (int32_t)nkv};
+        ora_rec r = {b, (int32_t)t, (int32_t)s0, (int32_t)s1};
         recs[nf] = r;
         slot_of[nf] = -1;
         ++nf;
@@ -637,27 +693,33 @@ int ora_schedule(const int64_t* qo, const int64_t* ko, int32_t B, int32_t H, int
     if (!one_k) {            /* q-stationary pass: every query tile */
       for (int64_t t = 0; t < nqt; ++t) {
         int64_t r1 = (t + 1) * sp->bq_bm < n ? (t + 1) * sp->bq_bm : n;
-        int64_t nkv = ceil_div64(kv_extent(causal, r1, n, m), sp->bq_bn);
+        int64_t lo, hi, s0, s1;
+        const int any = kv_range(causal, sp->window, t * sp->bq_bm, r1, n, m, &lo, &hi);
+        step_range(any, lo, hi, sp->bq_bn, 0, &s0, &s1);
         /* a single pass also owns dK/dV, so it visits every key tile (unseen keys get zeros) */
-        if (one_q) nkv = ceil_div64(m, sp->bq_bn);
+        if (one_q) {
+          s0 = 0;
+          s1 = ceil_div64(m, sp->bq_bn);
+        }
         rq = (ora_rec*)realloc(rq, sizeof(ora_rec) * (size_t)(nq + 1));
-        ora_rec r = {b, (int32_t)t, 0, (int32_t)nkv};
+        ora_rec r = {b, (int32_t)t, (int32_t)s0, (int32_t)s1};
         rq[nq++] = r;
       }
     }
     if (!one_q) {            /* kv-stationary pass: every key tile */
       const int64_t nqs = ceil_div64(n, sp->bk_bm);
       for (int64_t u = 0; u < nkt; ++u) {
-        int64_t first = 0;
+        int64_t c1 = (u + 1) * sp->bk_bn < m ? (u + 1) * sp->bk_bn : m;
+        int64_t lo, hi, s0, s1;
+        const int any = q_range(causal, sp->window, u * sp->bk_bn, c1, n, m, &lo, &hi);
+        step_range(any, lo, hi, sp->bk_bm, nqs, &s0, &s1);
         /* a single pass also owns dQ, so it visits every query tile (unseeing queries get zeros) */
-        if (causal && !one_k) {
-          /* the first query that sees key u*bk_bn is i = u*bk_bn - (m - n) */
-          int64_t i0 = u * sp->bk_bn - (m - n);
-          if (i0 < 0) i0 = 0;
-          first = i0 >= n ? nqs : i0 / sp->bk_bm;
+        if (one_k) {
+          s0 = 0;
+          s1 = nqs;
         }
         rk = (ora_rec*)realloc(rk, sizeof(ora_rec) * (size_t)(nk + 1));
-        ora_rec r = {b, (int32_t)u, (int32_t)first, (int32_t)nqs};
+        ora_rec r = {b, (int32_t)u, (int32_t)s0, (int32_t)s1};
         rk[nk++] = r;
       }
     }

@@ -41,12 +41,17 @@ def bias_matrix(bias, bias_kind, h, n, m, H, b_index, q_lens, kv_lens, bucket_fn
     return blk[h].clone()
 
 
-def visible_mask(n, m, causal):
+def visible_mask(n, m, causal, window=0):
+    """[n, m] visibility: causal bottom-right (j <= i + m - n); a sliding window keeps keys with
+    |i + m - n - j| < window (a band of the dense matrix)."""
     i = torch.arange(n)[:, None]
     j = torch.arange(m)[None, :]
-    if not causal:
-        return torch.ones(n, m, dtype=torch.bool)
-    return j <= i + (m - n)
+    vis = torch.ones(n, m, dtype=torch.bool)
+    if causal:
+        vis = vis & (j <= i + (m - n))
+    if window:
+        vis = vis & ((i + (m - n) - j).abs() < window)
+    return vis
 
 
 def sdpa_sample(q, k, v, bmat, vis, scale):
@@ -74,7 +79,7 @@ def gdpa_sample(q, k, v, bmat, vis, scale, mode, normalize=True):
 
 
 def torch_reference(case_q, case_k, case_v, q_lens, kv_lens, mode, causal, bias, bias_kind,
-                    bucket_fn, scale=None, dout=None, num_buckets=64):
+                    bucket_fn, scale=None, dout=None, num_buckets=64, window=0):
     """Per-sample fp64 torch reference, with autograd gradients when dout is given.
 
     Returns dict(o, lse, dq, dk, dv) as fp64 numpy arrays (lse NaN for GDPA)."""
@@ -99,7 +104,7 @@ def torch_reference(case_q, case_k, case_v, q_lens, kv_lens, mode, causal, bias,
             if n == 0:
                 continue
             qs, ks, vs = q[qo:qo + n, h], k[ko:ko + m, h], v[ko:ko + m, h]
-            vis = visible_mask(n, m, causal)
+            vis = visible_mask(n, m, causal, window)
             bmat = bias_matrix(bias, bias_kind, h, n, m, H, b, q_lens, kv_lens, bucket_fn,
                                num_buckets)
             if mode == "softmax":

@@ -698,3 +698,130 @@ def test_abs_terms_scale_with_operands(oracle_mod):
     assert rel_l2(c2["O"], 4.0 * c1["O"]) < 1e-12
     assert rel_l2(c2["dQ"], c1["dQ"]) < 1e-12 and rel_l2(c2["dK"], c1["dK"]) < 1e-12
     assert rel_l2(c2["dV"], c1["dV"] / 4.0) < 1e-12
+
+
+# ------------------------------------------------------------ sliding window
+
+WINDOW_CASES = [
+    # q_lens, kv_lens, H, d, window
+    ([9, 0, 13, 1, 20], [9, 0, 13, 1, 20], 2, 8, 3),
+    ([4, 11, 6], [9, 5, 6], 2, 8, 2),          # asymmetric: aligned position i + (m - n)
+    ([7, 16], [7, 16], 1, 8, 1),
+    ([12], [5], 1, 8, 7),
+]
+
+
+@pytest.mark.parametrize("mode", ["softmax", "silu", "gelu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bias_kind", ["none", "relpos", "dense"])
+@pytest.mark.parametrize("ci", range(len(WINDOW_CASES)))
+def test_window_vs_torch(oracle_mod, mode, causal, bias_kind, ci):
+    """Sliding window against torch fp64 SDPA / autograd with a band mask."""
+    ql, kl, H, d, W = WINDOW_CASES[ci]
+    case = custom_case(ql, kl, H, d, dtype="f32", mode=mode, causal=causal,
+                       bias_kind=bias_kind, seed=150 + ci, bias_std=0.5)
+    o, lse = oracle_mod.case_forward(case, window=W)
+    dq, dk, dv = oracle_mod.case_backward(case, window=W)
+    ref = torch_reference(case.q, case.k, case.v, case.q_lens, case.kv_lens, mode, causal,
+                          case.bias, bias_kind, oracle_mod.relpos_bucket, dout=case.dout,
+                          window=W)
+    assert max_abs(o, ref["o"]) < 1e-12
+    if mode == "softmax":
+        finite = np.isfinite(ref["lse"])
+        assert np.array_equal(np.isfinite(lse), finite)
+        assert max_abs(lse[finite], ref["lse"][finite]) < 1e-12
+    for got, want in ((dq, ref["dq"]), (dk, ref["dk"]), (dv, ref["dv"])):
+        assert max_abs(got, want) < 1e-11
+
+
+def test_window_special_cases(oracle_mod):
+    """A window no shorter than every sample changes nothing (bit-identical); a causal window of
+    one key gives softmax O_i = V_(i + m - n) (0 where that key does not exist), dQ = dK = 0 and
+    dV_j = dO_(j - m + n); GDPA O_i = w act(S_i,i+m-n) V_(i+m-n)."""
+    ql, kl = [9, 14, 3], [9, 10, 5]
+    for mode in ("softmax", "gelu"):
+        for causal in (False, True):
+            case = custom_case(ql, kl, 2, 8, dtype="f32", mode=mode, causal=causal,
+                               bias_kind="relpos", seed=160, bias_std=0.5)
+            o0, l0 = oracle_mod.case_forward(case)
+            o1, l1 = oracle_mod.case_forward(case, window=100)
+            assert np.array_equal(o0, o1)
+            g0 = oracle_mod.case_backward(case)
+            g1 = oracle_mod.case_backward(case, window=100)
+            assert all(np.array_equal(a, b) for a, b in zip(g0, g1))
+    case = custom_case(ql, kl, 2, 8, dtype="f32", mode="softmax", causal=True, seed=161)
+    o, lse = oracle_mod.case_forward(case, window=1)
+    dq, dk, dv = oracle_mod.case_backward(case, window=1)
+    v, do = case.v.double().numpy(), case.dout.double().numpy()
+    qo, ko = 0, 0
+    want_o = np.zeros_like(o)
+    want_dv = np.zeros_like(dv)
+    for n, m in zip(ql, kl):
+        for i in range(n):
+            j = i + m - n
+            if 0 <= j < m:
+                want_o[qo + i] = v[ko + j]
+                want_dv[ko + j] = do[qo + i]
+        qo += n
+        ko += m
+    assert max_abs(o, want_o) < 1e-15 and max_abs(dv, want_dv) < 1e-15
+    assert np.all(dq == 0) and np.all(dk == 0)
+    # rows whose only key would lie before the sample (i + m - n < 0) see nothing
+    assert lse[0, 9 + 0] == -np.inf and np.all(o[9:13] == 0)
+
+
+def _vis_w(n, m, causal, W, i, j):
+    d = i + (m - n) - j
+    return (not causal or d >= 0) and (W == 0 or abs(d) < W)
+
+
+def _pairs_w(n, m, causal, W, r0, r1, c0, c1):
+    return sum(1 for i in range(max(r0, 0), min(r1, n)) for j in range(max(c0, 0), min(c1, m))
+               if _vis_w(n, m, causal, W, i, j))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_schedule_window_bruteforce(oracle_mod, seed):
+    """With a window every list entry covers exactly the steps its tile can see: its first and
+    last steps hold a visible pair, the steps outside its range hold none (forward, both
+    backward lists); chunks of a split tile still tile the range; order stays longest first."""
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.integers(1, 9))
+    ql = rng.integers(0, 400, size=B).astype(np.int32)
+    kl = ql.copy() if seed % 2 == 0 else rng.integers(0, 400, size=B).astype(np.int32)
+    causal = seed % 3 != 1
+    W = int(rng.choice([1, 5, 40, 64, 100, 333]))
+    bm, bn = 64 * int(rng.integers(1, 3)), 64
+    slots = int(rng.integers(1, 30)) if seed % 4 else 0
+    qo, ko = oracle_mod.offsets(ql), oracle_mod.offsets(kl)
+    s = oracle_mod.schedule(qo, ko, 2, causal, bm=bm, bn=bn, slots=slots, bq_bm=64, bq_bn=64,
+                            bk_bn=128, bk_bm=64, fuse=0, window=W)
+    fwd = s["fwd"]
+    cost = np.maximum(1, fwd[:, 3] - fwd[:, 2])
+    keys = [(-c, b, t, kb) for c, (b, t, kb, _) in zip(cost, fwd)]
+    assert keys == sorted(keys) and len(set(keys)) == len(keys)
+
+    def check_range(n, m, rows, lo, hi, step, along_keys):
+        # [lo, hi) steps of `step` rows along keys (or queries) for the row (column) block rows
+        r0, r1 = rows
+        def cnt(a, b):
+            return _pairs_w(n, m, causal, W, r0, r1, a, b) if along_keys else \
+                _pairs_w(n, m, causal, W, a, b, r0, r1)
+        total = cnt(0, 1 << 30)
+        if hi > lo:
+            assert cnt(lo * step, hi * step) == total
+            assert cnt(lo * step, (lo + 1) * step) > 0 and cnt((hi - 1) * step, hi * step) > 0
+        else:
+            assert total == 0
+
+    for b in range(B):
+        n, m = int(ql[b]), int(kl[b])
+        for t in range(-(-n // bm)):
+            parts = sorted([tuple(r[2:]) for r in fwd if r[0] == b and r[1] == t])
+            for a, c in zip(parts, parts[1:]):
+                assert a[1] == c[0]
+            check_range(n, m, (t * bm, (t + 1) * bm), parts[0][0], parts[-1][1], bn, True)
+        for _, t, lo, hi in (r for r in s["bwd_q"] if r[0] == b):
+            check_range(n, m, (t * 64, (t + 1) * 64), lo, hi, 64, True)
+        for _, u, lo, hi in (r for r in s["bwd_kv"] if r[0] == b):
+            check_range(n, m, (u * 128, (u + 1) * 128), lo, hi, 64, False)
