@@ -29,34 +29,40 @@ METRIC = "jagged attention fwd+bwd useful TFLOP/s and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-BLOCK_ROWS = 256                 # BlockAttention block size of the extra workload
+BLOCK_ROWS = 256                 # BlockAttention block size / sliding window of the extra lines
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def visible_pairs(q_lens, kv_lens, causal):
+def visible_pairs(q_lens, kv_lens, causal, window=0):
+    """Visible (query, key) pairs per sample: key j is visible to query i iff j <= i + (m - n)
+    (causal) and |i + (m - n) - j| < window (window > 0)."""
     n = q_lens.astype(np.int64)
     m = kv_lens.astype(np.int64)
-    if not causal:
+    if not causal and not window:
         return n * m
-    # key j visible to query i iff j <= i + (m - n): sum over i of clamp(i + m - n + 1, 0, m)
     out = np.zeros_like(n)
     for b in range(len(n)):
-        i = np.arange(n[b])
-        out[b] = np.clip(i + m[b] - n[b] + 1, 0, m[b]).sum()
+        a = np.arange(n[b]) + m[b] - n[b]          # aligned position of every query
+        lo = np.zeros_like(a) if not window else a - window + 1
+        hi = np.full_like(a, m[b]) if not window else a + window
+        if causal:
+            hi = np.minimum(hi, a + 1)
+        out[b] = np.clip(np.minimum(hi, m[b]) - np.maximum(lo, 0), 0, None).sum()
     return out
 
 
 class Workload:
     """Device buffers and preallocated outputs for one jfa_synth case."""
 
-    def __init__(self, case, with_backward=True, block=0, dbias=False):
+    def __init__(self, case, with_backward=True, block=0, dbias=False, window=0):
         import torch
         import jagged_attention_amd as jfa
         self.case = case
         self.block = block
+        self.window = window
         # dbias: the backward also returns the bias gradient (jfa_backward_dbias)
         self.want_dbias = bool(dbias) and case.bias is not None and with_backward
         dev = torch.device("cuda:0")
@@ -87,7 +93,8 @@ class Workload:
         self.problem = jfa.make_problem(batch, case.heads, case.head_dim, case.total_q,
                                         case.total_kv, mode=case.mode,
                                         dtype=case.dtype, causal=case.causal,
-                                        bias_kind=case.bias_kind, num_buckets=case.num_buckets)
+                                        bias_kind=case.bias_kind, num_buckets=case.num_buckets,
+                                        window=window)
         odt = torch.float32 if case.dtype == "f32" else torch.bfloat16
         self.o = torch.empty(self.q.shape, dtype=odt, device=dev)
         self.lse = torch.empty((case.heads, case.total_q), dtype=torch.float32, device=dev) \
@@ -109,7 +116,7 @@ class Workload:
                           dtype=np.int64)
             pairs = visible_pairs(bl, bl, case.causal) * case.heads
         else:
-            pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal) * case.heads
+            pairs = visible_pairs(case.q_lens, case.kv_lens, case.causal, window) * case.heads
         self.pairs = int(pairs.sum())
         d = case.head_dim
         self.fwd_flops = 4.0 * d * self.pairs
@@ -382,10 +389,10 @@ def oracle_timing(case, target_s):
                        f"{'fwd+bwd' if back else 'fwd'} in fp64, {t:.1f} s)")
 
 
-def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None):
+def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None, window=0):
     from jfa_synth import make_case
     case = make_case(cfg, seed)
-    w = Workload(case, block=block, dbias=dbias)
+    w = Workload(case, block=block, dbias=dbias, window=window)
     t_fl = stats(time_steps(w, steps, warmup, flush))          # MALL flushed before every step
     t_hot = stats(time_steps(w, steps, 1))                     # back to back (secondary)
     # the same step replayed as one HIP graph (no per-launch host work): reported beside it
@@ -400,6 +407,8 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None
     tf = flops / sec / 1e12
     padded = w.padded_flops()
     name = case.name if not block else f"block{block}-" + case.name
+    if window:
+        name = f"window{window}-" + name
     if w.want_dbias:
         name += "+dbias"
     return w, dict(workload=name, seed=case.seed, ms_per_step=t_fl["median"],
@@ -552,6 +561,15 @@ def main():
         r["kernels"] = kernel_times(wx, 3, flush)
         r["block_rows"] = BLOCK_ROWS
         extra["block_attention"] = r
+        del wx
+        torch.cuda.empty_cache()
+        # sliding window: the headline batch, every query seeing its last 256 keys
+        log("[bench] sliding window")
+        wx, r = bench_config(2, max(3, args.steps // 2), 2, window=BLOCK_ROWS, flush=flush)
+        r["kernels"] = kernel_times(wx, 3, flush)
+        r["roofline"] = roofline_of(wx, r["kernels"])
+        r["window"] = BLOCK_ROWS
+        extra["sliding_window"] = r
         del wx
         torch.cuda.empty_cache()
         # fused normalisation + MXFP8 quantisation of the MXFP8 workload's inputs

@@ -15,7 +15,8 @@
  *
  * For sample b with n = q_len, m = kv_len, query i < n, key j < m, head h:
  *   S_ij = qk_scale * <Q[qo_b+i,h,:], K[ko_b+j,h,:]> + bias_h(b,i,j)
- *   visible(i,j) = !causal || j <= i + (m - n)      (bottom-right aligned)
+ *   visible(i,j) = (!causal || j <= i + (m - n))     (bottom-right aligned)
+ *                  && (window == 0 || |i + (m - n) - j| < window)   (sliding window)
  *   softmax: O_i = sum_j softmax_j(S_i.) V_j over visible j; LSE_i = log sum_j exp S_ij
  *   GDPA:    O_i = w * sum_{visible j} act(S_ij) V_j, w = 1/m if kv_len_normalize else 1,
  *            act = SiLU (x*sigmoid x) or GELU (erf form)
@@ -86,6 +87,16 @@ typedef struct {
   int32_t bwd_fuse;         /* -1 default (on where built), 0 off: single-pass backward for
                                samples with one query tile (64-row query tiles) or one key
                                tile (d = 64) */
+  int32_t window;           /* sliding window ("GEM Training: How Meta Doubled the Efficiency of
+                               Its LLM-Scale Ads Foundation Model", "Challenge 1": long sequences
+                               with a short attention window; "Meta Enhances GEM Training
+                               Efficiency ...", "Leveraging Compute Efficiency through Customized
+                               Kernels": attention over windows).  0 = none; W > 0 keeps key j
+                               for query i only when |i + (kv_len - q_len) - j| < W, i.e. the W
+                               keys ending at the query's aligned position under causal, a band
+                               of 2W - 1 keys otherwise.  GDPA's weight stays 1/kv_len.  Tiles
+                               visit only the key (query) steps their rows can see.  Negative is
+                               invalid. */
 } jfa_problem;
 
 /*

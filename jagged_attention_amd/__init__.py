@@ -29,13 +29,14 @@ __all__ = ["make_problem", "forward", "backward", "backward_dbias", "lengths_to_
 def make_problem(batch: int, heads: int, head_dim: int, total_q: int, total_kv: int, *,
                  mode: str = "softmax", dtype: str = "bf16", causal: bool = False,
                  qk_scale: float = 0.0, kv_len_normalize: int = -1, bias_kind: str = "none",
-                 num_buckets: int = 64, split_slots: int = 0, bwd_fuse: int = -1) -> JfaProblem:
+                 num_buckets: int = 64, split_slots: int = 0, bwd_fuse: int = -1,
+                 window: int = 0) -> JfaProblem:
     return JfaProblem(batch=batch, heads=heads, head_dim=head_dim, total_q=total_q,
                       total_kv=total_kv, mode=MODES[mode], dtype=DTYPES[dtype],
                       causal=int(bool(causal)), qk_scale=float(qk_scale),
                       kv_len_normalize=int(kv_len_normalize), bias_kind=BIAS_KINDS[bias_kind],
                       num_buckets=int(num_buckets), split_slots=int(split_slots),
-                      bwd_fuse=int(bwd_fuse))
+                      bwd_fuse=int(bwd_fuse), window=int(window))
 
 
 def _workspace(problem: JfaProblem, backward: bool, device):
@@ -47,24 +48,27 @@ def _workspace(problem: JfaProblem, backward: bool, device):
 
 
 def _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
-                kv_len_normalize, split_slots, dtype=None, bwd_fuse=-1) -> JfaProblem:
+                kv_len_normalize, split_slots, dtype=None, bwd_fuse=-1,
+                window=0) -> JfaProblem:
     import torch
     if dtype is None:
         dtype = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "mxfp8"}[q.dtype]
     return make_problem(q_offsets.shape[0] - 1, q.shape[1], q.shape[2], q.shape[0], k.shape[0],
                         mode=mode, dtype=dtype, causal=causal, qk_scale=qk_scale,
                         kv_len_normalize=kv_len_normalize, bias_kind=bias_kind,
-                        num_buckets=num_buckets, split_slots=split_slots, bwd_fuse=bwd_fuse)
+                        num_buckets=num_buckets, split_slots=split_slots, bwd_fuse=bwd_fuse,
+                        window=window)
 
 
 def forward(q, k, v, q_offsets, kv_offsets, *, mode: str = "softmax", causal: bool = False,
             bias=None, bias_kind: str = "none", num_buckets: int = 64, qk_scale: float = 0.0,
             kv_len_normalize: int = -1, split_slots: int = 0, q_scale=None, k_scale=None,
-            v_scale=None, workspace=None, out=None):
-    """Returns (o, lse); lse is None for GDPA.  MXFP8: q/k/v are uint8 codes plus scales."""
+            v_scale=None, workspace=None, out=None, window: int = 0):
+    """Returns (o, lse); lse is None for GDPA.  MXFP8: q/k/v are uint8 codes plus scales.
+    window > 0: sliding-window attention (see jfa_problem.window)."""
     import torch
     problem = _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
-                          kv_len_normalize, split_slots)
+                          kv_len_normalize, split_slots, window=window)
     odtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     o = out if out is not None else torch.empty(q.shape, dtype=odtype, device=q.device)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device) \
@@ -80,11 +84,12 @@ def forward(q, k, v, q_offsets, kv_offsets, *, mode: str = "softmax", causal: bo
 
 def backward(q, k, v, o, lse, dout, q_offsets, kv_offsets, *, mode: str = "softmax",
              causal: bool = False, bias=None, bias_kind: str = "none", num_buckets: int = 64,
-             qk_scale: float = 0.0, kv_len_normalize: int = -1, workspace=None, bwd_fuse=-1):
+             qk_scale: float = 0.0, kv_len_normalize: int = -1, workspace=None, bwd_fuse=-1,
+             window: int = 0):
     """Returns (dq, dk, dv), the gradients of <O, dout>."""
     import torch
     problem = _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
-                          kv_len_normalize, 0, bwd_fuse=bwd_fuse)
+                          kv_len_normalize, 0, bwd_fuse=bwd_fuse, window=window)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -99,12 +104,13 @@ def backward(q, k, v, o, lse, dout, q_offsets, kv_offsets, *, mode: str = "softm
 
 def backward_dbias(q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, *, mode: str = "softmax",
                    causal: bool = False, bias_kind: str = "relpos", num_buckets: int = 64,
-                   qk_scale: float = 0.0, kv_len_normalize: int = -1, workspace=None):
+                   qk_scale: float = 0.0, kv_len_normalize: int = -1, workspace=None,
+                   window: int = 0):
     """Returns (dq, dk, dv, dbias): dbias is fp32 [H, num_buckets] for a relative-position
     table and bf16 in the bias's layout for a dense bias (bf16 inputs only)."""
     import torch
     problem = _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
-                          kv_len_normalize, 0)
+                          kv_len_normalize, 0, window=window)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

@@ -41,7 +41,8 @@ class JfaProblem(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("qk_scale", ctypes.c_float), ("kv_len_normalize", ctypes.c_int32),
                 ("bias_kind", ctypes.c_int32), ("num_buckets", ctypes.c_int32),
-                ("split_slots", ctypes.c_int32), ("bwd_fuse", ctypes.c_int32)]
+                ("split_slots", ctypes.c_int32), ("bwd_fuse", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class JfaError(RuntimeError):

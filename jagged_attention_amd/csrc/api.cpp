@@ -47,6 +47,7 @@ jfa_status check_problem(const jfa_problem* p) {
   if (p->mode == JFA_MODE_SOFTMAX && p->kv_len_normalize == 1) return JFA_ERR_INVALID_ARG;
   if (!std::isfinite(p->qk_scale) || p->qk_scale < 0.f) return JFA_ERR_INVALID_ARG;
   if (p->bwd_fuse < -1 || p->bwd_fuse > 1) return JFA_ERR_INVALID_ARG;
+  if (p->window < 0) return JFA_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
   if ((int64_t)p->heads * p->head_dim > (1 << 20)) return JFA_ERR_UNSUPPORTED;
   return JFA_OK;
@@ -155,6 +156,7 @@ SchedArgs sched_args(const jfa_problem& p, const TileCfg& tc, const Layout& L, c
   a.B = p.batch;
   a.H = p.heads;
   a.causal = p.causal;
+  a.window = p.window;
   a.total_q = p.total_q;
   a.total_kv = p.total_kv;
   a.tc = tc;
@@ -341,6 +343,7 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   fp.part_ml = L.cap_slots > 0 ? (float*)(ws + L.part_ml) : nullptr;
   fp.H = p->heads;
   fp.causal = p->causal;
+  fp.window = p->window;
   fp.bias_kind = p->bias_kind;
   fp.num_buckets = p->num_buckets;
   fp.normalize = normalize_of(*p);
@@ -416,6 +419,7 @@ jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, con
   bp.batch = p->batch;
   bp.H = p->heads;
   bp.causal = p->causal;
+  bp.window = p->window;
   bp.bias_kind = p->bias_kind;
   bp.num_buckets = p->num_buckets;
   bp.normalize = normalize_of(*p);

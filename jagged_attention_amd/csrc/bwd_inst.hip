@@ -181,7 +181,7 @@ struct KvLds {
 // and, in the one-query-tile kernels, registers enough to spill.)
 // HOME: the first item of workgroup g is item g (the pass starts the launch); otherwise every
 // item comes from a ticket.
-template <int D, int NW, int MODE, int BIAS, bool HOME>
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool WIN>
 __device__ __forceinline__ void kv_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   using L = KvLds<D, NW, BIAS>;
@@ -352,7 +352,12 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
     auto compute_step = [&](int it, int qs, int nst) {
       const int q0 = qs * STEP;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
-      if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0)) {
+      // nothing visible between this step's queries and the wave's keys (past the sample,
+      // before the causal diagonal, or outside the window band)
+      const int W = WIN ? p.window : 0;
+      if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0) ||
+          (WIN && (q0 > jw0 + 31 - delta + W - 1 ||
+                   (!p.causal && q0 + STEP - 1 < jw0 - delta - W + 1)))) {
         if (nst >= 0) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, nst); });
         if (L::K1 && one_k) {     // these keys contribute nothing to this step's dQ
           uint32_t* ds = reinterpret_cast<uint32_t*>(
@@ -401,10 +406,17 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       // pairs that are not visible start at -inf, so P = 0 and dS = 0 with no per-element test
       // later: query offset o = blk*32 + 8(i/4) + i%4 (+4g) is visible iff qlo <= o < qhi
       const bool need_mask = (q0 + STEP > n) || (jw0 + 32 > m) ||
-                             (p.causal && q0 + delta < jw0 + 31);
+                             (p.causal && q0 + delta < jw0 + 31) ||
+                             (WIN && (q0 + STEP - 1 >= jw0 - delta + W ||
+                                      (!p.causal && q0 <= jw0 + 31 - delta - W)));
       if (need_mask) {
-        const int qhi = j < m ? n - q0 - 4 * g : -1;
-        const int qlo = p.causal ? j - delta - q0 - 4 * g : -1;
+        // queries [qlo, qhi) (offsets in the step, less 4g) see key j
+        int qhi = j < m ? n - q0 - 4 * g : -1;
+        int qlo = p.causal ? j - delta - q0 - 4 * g : -1;
+        if constexpr (WIN) {
+          if (j < m) qhi = min(n, j - delta + W) - q0 - 4 * g;
+          if (!p.causal) qlo = j - delta - W + 1 - q0 - 4 * g;
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -669,7 +681,7 @@ struct QLds {
 // relative-position table: per-lane running sums by bucket, flushed on a change of bucket into
 // the lane's own slots, in LDS for at most DB_NB buckets and else in its partial row in memory;
 // later kernels reduce the rows in a fixed order).  DB runs without the single-pass classes.
-template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB = false>
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   using L = QLds<D, NW, BIAS>;
@@ -707,7 +719,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     const int w = item_field(dsc, IF_W);
     if (w >= n_items) break;
     const int h = w % H;
-    const int t = item_field(dsc, IF_X), steps = item_field(dsc, IF_Z);
+    // key steps [kb0, kb0 + steps) of query tile t
+    const int t = item_field(dsc, IF_X), kb0 = WIN ? item_field(dsc, IF_Y) : 0;
+    const int steps = item_field(dsc, IF_Z) - kb0;
     const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
     const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
     const int64_t boff = item_boff(dsc);
@@ -717,8 +731,12 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
     const int q0 = t * BM, qw0 = q0 + wave * 32;
     const int qil = wave * 32 + l32, qi = q0 + qil;
-    int wave_kend = m;
+    // keys [wave_kbeg, wave_kend) hold every pair this wave's rows can see
+    const int W = WIN ? p.window : 0;
+    int wave_kend = m, wave_kbeg = 0;
     if (p.causal) wave_kend = max(0, min(m, min(n, qw0 + 32) + delta));
+    else if (WIN) wave_kend = max(0, min(m, min(n, qw0 + 32) - 1 + delta + W));
+    if (WIN) wave_kbeg = max(0, qw0 + delta - W + 1);
     const bool wave_rows = qw0 < n;
 
     const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
@@ -814,9 +832,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     };
 
     auto compute_step = [&](int it) {
-      const int j0 = it * STEP;
+      const int j0 = (kb0 + it) * STEP;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
-      if (!wave_rows || j0 >= wave_kend) {
+      if (!wave_rows || j0 >= wave_kend || (WIN && j0 + STEP <= wave_kbeg)) {
         if (L::Q1 && one_q) {     // this wave's queries contribute nothing to this step's dK, dV
           uint32_t* pq = reinterpret_cast<uint32_t*>(
               reinterpret_cast<__bf16*>(lds + L::Q1_P) + qil * L::PS);
@@ -869,8 +887,16 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
       const bool need_mask = (j0 + STEP > m) || (p.causal && j0 + STEP - 1 > qw0 + delta) ||
-                             (qw0 + 32 > n);
-      const int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
+                             (qw0 + 32 > n) ||
+                             (WIN && (j0 <= qw0 + 31 + delta - W ||
+                                      (!p.causal && j0 + STEP - 1 >= qw0 + delta + W)));
+      // keys [kbeg, kend) are visible to query qi: offsets [lo, lim) of this lane's elements
+      int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
+      int lo = 0;
+      if constexpr (WIN) {
+        if (qi < n && !p.causal) kend = min(m, qi + delta + W);
+        lo = qi + delta - W + 1 - j0 - 4 * g;
+      }
       const int lim = kend - j0 - 4 * g;
       uint32_t dd[2][8], pq2[2][8];
       // B(blk) pair pi: dS and P of elements 2 pi, 2 pi + 1 of block blk
@@ -879,7 +905,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int ii = 2 * pi + e;
-          const bool valid = !need_mask || (blk * 32 + 8 * (ii >> 2) + (ii & 3) < lim);
+          const int off = blk * 32 + 8 * (ii >> 2) + (ii & 3);
+          const bool valid = !need_mask || (off < lim && (!WIN || off >= lo));
           const float x = sacc[blk][ii] * c_log;
           if constexpr (MODE == MODE_SOFTMAX) {
             const float pr = valid ? fast_exp2(x - lse2) : 0.f;
@@ -1006,7 +1033,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
         __bf16* ost = reinterpret_cast<__bf16*>(lds + (kt & 1) * L::STAGE +
                                                 wave * out_stage_bytes<D>());
         const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
-        const uint32_t row0 = (uint32_t)(kt * STEP + 32 * wave) * row_bytes;
+        const uint32_t row0 = (uint32_t)((kb0 + kt) * STEP + 32 * wave) * row_bytes;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {       // 0: dV = P^T dO, 1: dK = s dS^T Q
           const __bf16* xa = which ? qr1 : dr1;
@@ -1034,8 +1061,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     };
 
     if (steps > 0) {
-      load_step(0);
-      store_step(0, 0);
+      load_step(kb0);
+      store_step(0, kb0);
     }
     // the query fragments (loaded with the first tiles) are complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -1059,13 +1086,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     for (int it = 0; it + 1 < steps; ++it) {
       if (it == claim_it && wave == 0) pipe.claim(lane);
       if (it == resolve_it && wave == 0) pipe.resolve(lane);
-      load_step(it + 1);
+      load_step(kb0 + it + 1);
       compute_step(it);
       if (one_q) {
         __syncthreads();
         dkdv_step(it);
       }
-      store_step((it + 1) & 1, it + 1);
+      store_step((it + 1) & 1, kb0 + it + 1);
       __syncthreads();
     }
     if (steps > 0) compute_step(steps - 1);
@@ -1100,34 +1127,34 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   }
 }
 
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_kv_kernel(BwdParams p) {
-  kv_pass<D, NW, MODE, BIAS, true>(p);
+  kv_pass<D, NW, MODE, BIAS, true, WIN>(p);
 }
 
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_kernel(BwdParams p) {
-  q_pass<D, NW, MODE, BIAS, true>(p);
+  q_pass<D, NW, MODE, BIAS, true, false, WIN>(p);
 }
 
 // Both passes in one persistent launch (they are independent): every workgroup first works
 // through the kv-stationary list, then takes q-stationary items by ticket, so the second list
 // fills the first one's tail and the two passes share one kernel boundary.
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_kvq_kernel(BwdParams p) {
-  kv_pass<D, NW, MODE, BIAS, true>(p);
+  kv_pass<D, NW, MODE, BIAS, true, WIN>(p);
   __syncthreads();
-  q_pass<D, NW, MODE, BIAS, false>(p);
+  q_pass<D, NW, MODE, BIAS, false, false, WIN>(p);
 }
 
 // The query-stationary pass with the bias gradient (DB); the single-pass classes are off.
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_db_kernel(BwdParams p) {
-  q_pass<D, NW, MODE, BIAS, true, true>(p);
+  q_pass<D, NW, MODE, BIAS, true, true, WIN>(p);
 }
 
 // Zeroes `count` 16-bit elements of x; with count_from (a dense bias's block offsets), the
@@ -1204,35 +1231,35 @@ hipError_t launch_persistent(K kern, size_t lds, int threads, int64_t max_items,
   return hipGetLastError();
 }
 
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 hipError_t run_bk(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_kv_kernel<D, NW, MODE, BIAS>, KvLds<D, NW, BIAS>::TOTAL, NW * 64,
+  return launch_persistent(bwd_kv_kernel<D, NW, MODE, BIAS, WIN>, KvLds<D, NW, BIAS>::TOTAL, NW * 64,
                            max_items, cu, p, "jfa_bwd_dkdv", s);
 }
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
+  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS, WIN>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
                            max_items, cu, p, "jfa_bwd_dq", s);
 }
 
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
   constexpr size_t lds = KvLds<D, NW, BIAS>::TOTAL > QLds<D, NW, BIAS>::TOTAL
                              ? KvLds<D, NW, BIAS>::TOTAL : QLds<D, NW, BIAS>::TOTAL;
-  return launch_persistent(bwd_kvq_kernel<D, NW, MODE, BIAS>, lds, NW * 64, max_items, cu, p,
+  return launch_persistent(bwd_kvq_kernel<D, NW, MODE, BIAS, WIN>, lds, NW * 64, max_items, cu, p,
                            "jfa_bwd_kvq", s);
 }
 
-template <int D, int NW, int MODE, int BIAS>
+template <int D, int NW, int MODE, int BIAS, bool WIN>
 hipError_t run_bq_db(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS>, QLds<D, NW, BIAS>::TOTAL_DB, NW * 64,
+  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS, WIN>, QLds<D, NW, BIAS>::TOTAL_DB, NW * 64,
                            max_items, cu, p, "jfa_dbias_dq", s);
 }
 
 // Backward with the bias gradient: zero dbias (dense) or the partials (relative positions),
 // the key-stationary pass, the query-stationary pass with DB, then (relative positions) the
 // fixed-order reduction into dbias [H][num_buckets] (fp32).
-template <int D, int MODE, int BIAS>
+template <int D, int MODE, int BIAS, bool WIN>
 hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                       hipStream_t s) {
   const unsigned zgrid = (unsigned)std::max(1, cu * 4);
@@ -1249,10 +1276,10 @@ hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS>(p, mk, cu, s) : run_bk<D, 2, MODE, BIAS>(p, mk, cu, s);
+  e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS, WIN>(p, mk, cu, s) : run_bk<D, 2, MODE, BIAS, WIN>(p, mk, cu, s);
   if (e != hipSuccess) return e;
-  e = tc.bq_nw == 4 ? run_bq_db<D, 4, MODE, BIAS>(p, mq, cu, s)
-                    : run_bq_db<D, 2, MODE, BIAS>(p, mq, cu, s);
+  e = tc.bq_nw == 4 ? run_bq_db<D, 4, MODE, BIAS, WIN>(p, mq, cu, s)
+                    : run_bq_db<D, 2, MODE, BIAS, WIN>(p, mq, cu, s);
   if (e != hipSuccess) return e;
   if constexpr (BIAS == B_RELPOS) {
     const int halves = dbias_halves(p.num_buckets);
@@ -1272,25 +1299,25 @@ hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t
   return e;
 }
 
-template <int D, int MODE, int BIAS>
+template <int D, int MODE, int BIAS, bool WIN>
 hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                         hipStream_t s) {
   // one launch for both passes when their workgroups have the same shape
-  if (tc.bk_nw == 4 && tc.bq_nw == 4) return run_bkq<D, 4, MODE, BIAS>(p, max(mq, mk), cu, s);
-  hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS>(p, mk, cu, s)
-                               : run_bk<D, 2, MODE, BIAS>(p, mk, cu, s);
+  if (tc.bk_nw == 4 && tc.bq_nw == 4) return run_bkq<D, 4, MODE, BIAS, WIN>(p, max(mq, mk), cu, s);
+  hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS, WIN>(p, mk, cu, s)
+                               : run_bk<D, 2, MODE, BIAS, WIN>(p, mk, cu, s);
   if (e != hipSuccess) return e;
-  return tc.bq_nw == 4 ? run_bq<D, 4, MODE, BIAS>(p, mq, cu, s) : run_bq<D, 2, MODE, BIAS>(p, mq, cu, s);
+  return tc.bq_nw == 4 ? run_bq<D, 4, MODE, BIAS, WIN>(p, mq, cu, s) : run_bq<D, 2, MODE, BIAS, WIN>(p, mq, cu, s);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool WIN>
 hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                    hipStream_t s) {
   // D (softmax) was computed by the scheduler launch
   switch (p.bias_kind) {
-    case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS>(p, tc, mq, mk, cu, s);
-    case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE>(p, tc, mq, mk, cu, s);
-    default: return run_bwd_bias<D, MODE, B_NONE>(p, tc, mq, mk, cu, s);
+    case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS, WIN>(p, tc, mq, mk, cu, s);
+    case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE, WIN>(p, tc, mq, mk, cu, s);
+    default: return run_bwd_bias<D, MODE, B_NONE, WIN>(p, tc, mq, mk, cu, s);
   }
 }
 
@@ -1301,11 +1328,16 @@ template <>
 hipError_t launch_bwd_dm<JFA_BWD_D, JFA_BWD_MODE>(const BwdParams& p, const TileCfg& tc,
                                                   int64_t mq, int64_t mk, int cu, hipStream_t s,
                                                   bool dbias) {
-  if (dbias)
-    return p.bias_kind == JFA_BIAS_DENSE
-               ? run_bwd_db<JFA_BWD_D, JFA_BWD_MODE, B_DENSE>(p, tc, mq, mk, cu, s)
-               : run_bwd_db<JFA_BWD_D, JFA_BWD_MODE, B_RELPOS>(p, tc, mq, mk, cu, s);
-  return run_bwd<JFA_BWD_D, JFA_BWD_MODE>(p, tc, mq, mk, cu, s);
+  constexpr int D = JFA_BWD_D, M = JFA_BWD_MODE;
+  const bool win = p.window > 0;
+  if (dbias) {
+    if (p.bias_kind == JFA_BIAS_DENSE)
+      return win ? run_bwd_db<D, M, B_DENSE, true>(p, tc, mq, mk, cu, s)
+                 : run_bwd_db<D, M, B_DENSE, false>(p, tc, mq, mk, cu, s);
+    return win ? run_bwd_db<D, M, B_RELPOS, true>(p, tc, mq, mk, cu, s)
+               : run_bwd_db<D, M, B_RELPOS, false>(p, tc, mq, mk, cu, s);
+  }
+  return win ? run_bwd<D, M, true>(p, tc, mq, mk, cu, s) : run_bwd<D, M, false>(p, tc, mq, mk, cu, s);
 }
 
 }  // namespace jfa

@@ -24,6 +24,13 @@ __device__ __forceinline__ float bias_at(const FwdParams& p, int64_t bias_base, 
   return 0.f;
 }
 
+// Sliding window: key j is out of query i's window (aligned position i + delta) when
+// |i + delta - j| >= window (window 0: no window).
+__device__ __forceinline__ bool out_of_window(int window, int i, int j, int delta) {
+  const int d = i + delta - j;
+  return window > 0 && (d >= window || -d >= window);
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   __shared__ float ks[F32_BN][D + 1];
@@ -65,6 +72,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
       for (int jj = 0; jj < jend; ++jj) {
         const int j = j0 + jj;
         if (p.causal && j > qi + (m - n)) break;
+        if (out_of_window(p.window, qi, j, m - n)) continue;
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) s = fmaf(qv[c], ks[jj][c], s);
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(NT) void bwd_q_f32_kernel(BwdParams p) {
     const ItemRec& it = p.bq[w / H];
     const int4 rec = make_int4(it.b, it.x, it.y, it.z);
     const int h = (int)(w % H);
-    const int b = rec.x, t = rec.y, steps = rec.w;
+    const int b = rec.x, t = rec.y, kb = rec.z, ke = rec.w;
     const int qo = p.q_off[b], n = p.q_off[b + 1] - qo;
     const int ko = p.kv_off[b], m = p.kv_off[b + 1] - ko;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(NT) void bwd_q_f32_kernel(BwdParams p) {
       lse = p.lse[(int64_t)h * p.total_q + qo + qi];
       dl = p.delta[(int64_t)h * p.total_q + qo + qi];
     }
-    for (int kt = 0; kt < steps; ++kt) {
+    for (int kt = kb; kt < ke; ++kt) {
       const int j0 = kt * F32_BN;
       __syncthreads();
       for (int e = threadIdx.x; e < F32_BN * D; e += NT) {
@@ -162,6 +170,7 @@ __global__ __launch_bounds__(NT) void bwd_q_f32_kernel(BwdParams p) {
       for (int jj = 0; jj < jend; ++jj) {
         const int j = j0 + jj;
         if (p.causal && j > qi + (m - n)) break;
+        if (out_of_window(p.window, qi, j, m - n)) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
@@ -237,6 +246,7 @@ __global__ __launch_bounds__(NT) void bwd_kv_f32_kernel(BwdParams p) {
       for (int ii = 0; ii < iend; ++ii) {
         const int i = i0 + ii;
         if (p.causal && j > i + (m - n)) continue;
+        if (out_of_window(p.window, i, j, m - n)) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {

@@ -66,7 +66,8 @@ struct FwdLds {
 
 // Occupancy: two workgroups per CU.  With 4 waves per workgroup that is 2 waves per SIMD
 // (256 registers each); with 2 waves it is one wave per SIMD, which may use all 512.
-template <int D, int NW, int MODE, int BIAS, bool FP8>
+// WIN: a sliding window is set (its bounds only cost registers and VALU where it is).
+template <int D, int NW, int MODE, int BIAS, bool FP8, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2)))
 void fwd_kernel(FwdParams p) {
   using L = FwdLds<D, NW, BIAS, FP8>;
@@ -126,8 +127,12 @@ void fwd_kernel(FwdParams p) {
     const int qw0 = q0 + wave * 32;
     const int qil = wave * 32 + l32;        // tile-local query row of this lane
     const int qi = q0 + qil;                // sample-local query row
-    int wave_kend = m;
+    // keys [wave_kbeg, wave_kend) hold every pair this wave's rows can see
+    const int W = WIN ? p.window : 0;
+    int wave_kend = m, wave_kbeg = 0;
     if (p.causal) wave_kend = max(0, min(m, min(n, qw0 + 32) + delta));
+    else if (WIN) wave_kend = max(0, min(m, min(n, qw0 + 32) - 1 + delta + W));
+    if (WIN) wave_kbeg = max(0, qw0 + delta - W + 1);
     const bool wave_rows = qw0 < n;
 
     // per-(sample, head) buffer resources: rows past the sample's end read as zero
@@ -311,7 +316,7 @@ void fwd_kernel(FwdParams p) {
       const int kt = kb + it;
       const int j0 = kt * BN;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
-      if (wave_rows && j0 < wave_kend) {
+      if (wave_rows && j0 < wave_kend && (!WIN || j0 + BN > wave_kbeg)) {
         // ---- accumulator init = bias / scale (element (blk, i): key blk*32 + 8(i/4) + 4g + i%4)
         f32x16 sacc[2];
         if constexpr (BIAS == B_RELPOS) {
@@ -370,17 +375,32 @@ void fwd_kernel(FwdParams p) {
           }
         }
 
-        // ---- mask (only tiles that cross the sample end or the causal diagonal): element
-        //      (blk, i) is visible iff its key offset blk*32 + 8(i/4) + i%4 < lim
-        const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta);
+        // ---- mask (only tiles that cross the sample end, the causal diagonal or a window
+        //      edge): element (blk, i) is visible iff its key offset blk*32 + 8(i/4) + i%4
+        //      lies in [lo, lim)
+        const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta) ||
+                               (WIN && (j0 <= qw0 + 31 + delta - W ||
+                                        (!p.causal && j0 + BN - 1 >= qw0 + delta + W)));
         if (need_mask) {
-          const int kend = p.causal ? min(m, qi + delta + 1) : m;
-          const int lim = kend - j0 - 4 * g;
+          if constexpr (WIN) {
+            int kend = p.causal ? min(m, qi + delta + 1) : min(m, qi + delta + W);
+            const int lim = kend - j0 - 4 * g, lo = qi + delta - W + 1 - j0 - 4 * g;
 #pragma unroll
-          for (int blk = 0; blk < 2; ++blk)
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (blk * 32 + 8 * (i >> 2) + (i & 3) >= lim) sacc[blk][i] = NEG_INF;
+              for (int i = 0; i < 16; ++i) {
+                const int o = blk * 32 + 8 * (i >> 2) + (i & 3);
+                if (o >= lim || o < lo) sacc[blk][i] = NEG_INF;
+              }
+          } else {
+            const int kend = p.causal ? min(m, qi + delta + 1) : m;
+            const int lim = kend - j0 - 4 * g;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (blk * 32 + 8 * (i >> 2) + (i & 3) >= lim) sacc[blk][i] = NEG_INF;
+          }
         }
 
         // ---- probabilities P^T (bf16 pairs, in MFMA B-operand order)
@@ -553,12 +573,12 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, int MODE, int BIAS, bool FP8>
+template <int D, int NW, int MODE, int BIAS, bool FP8, bool WIN>
 hipError_t run_fwd(const FwdParams& p, int64_t max_items, int64_t max_comb, int cu_count,
                    hipStream_t s) {
   using L = FwdLds<D, NW, BIAS, FP8>;
   const size_t lds = L::TOTAL;
-  auto kern = fwd_kernel<D, NW, MODE, BIAS, FP8>;
+  auto kern = fwd_kernel<D, NW, MODE, BIAS, FP8, WIN>;
   {
     hipError_t e = ensure_dyn_lds((const void*)kern, lds);
     if (e != hipSuccess) return e;
@@ -579,13 +599,19 @@ hipError_t run_fwd(const FwdParams& p, int64_t max_items, int64_t max_comb, int 
   return hipGetLastError();
 }
 
+template <int D, int NW, int MODE, bool FP8, bool WIN>
+hipError_t run_fwd_win(const FwdParams& p, int64_t mi, int64_t mc, int cu, hipStream_t s) {
+  switch (p.bias_kind) {
+    case JFA_BIAS_RELPOS: return run_fwd<D, NW, MODE, B_RELPOS, FP8, WIN>(p, mi, mc, cu, s);
+    case JFA_BIAS_DENSE: return run_fwd<D, NW, MODE, B_DENSE, FP8, WIN>(p, mi, mc, cu, s);
+    default: return run_fwd<D, NW, MODE, B_NONE, FP8, WIN>(p, mi, mc, cu, s);
+  }
+}
+
 template <int D, int NW, int MODE, bool FP8>
 hipError_t run_fwd_bias(const FwdParams& p, int64_t mi, int64_t mc, int cu, hipStream_t s) {
-  switch (p.bias_kind) {
-    case JFA_BIAS_RELPOS: return run_fwd<D, NW, MODE, B_RELPOS, FP8>(p, mi, mc, cu, s);
-    case JFA_BIAS_DENSE: return run_fwd<D, NW, MODE, B_DENSE, FP8>(p, mi, mc, cu, s);
-    default: return run_fwd<D, NW, MODE, B_NONE, FP8>(p, mi, mc, cu, s);
-  }
+  return p.window > 0 ? run_fwd_win<D, NW, MODE, FP8, true>(p, mi, mc, cu, s)
+                      : run_fwd_win<D, NW, MODE, FP8, false>(p, mi, mc, cu, s);
 }
 
 template <int D, int NW, bool FP8>

@@ -23,6 +23,49 @@ constexpr int BK_BM = 64;
 // Upper bound of a record's cost (kv or q steps) that the list sort accepts.
 constexpr int MAX_COST = 4095;
 
+// Step range [s0, s1) of `step`-row key steps that query rows [r0, r1) of a sample with n
+// queries and m keys can see: key j is visible to query i iff j <= i + (m - n) (causal) and,
+// with a window W > 0, i + (m - n) - W < j < i + (m - n) + W.  Empty: s0 = s1 = `empty`.
+__host__ __device__ inline void visible_key_steps(int causal, int window, int64_t r0, int64_t r1,
+                                                  int64_t n, int64_t m, int step, int64_t empty,
+                                                  int64_t& s0, int64_t& s1) {
+  const int64_t dl = m - n;
+  int64_t a = 0, e = m;
+  if (window > 0) {
+    a = r0 + dl - window + 1;
+    e = r1 - 1 + dl + window;
+  }
+  if (causal && r1 + dl < e) e = r1 + dl;
+  if (a < 0) a = 0;
+  if (e > m) e = m;
+  if (e > a) {
+    s0 = a / step;
+    s1 = (e + step - 1) / step;
+  } else {
+    s0 = s1 = empty;
+  }
+}
+// Step range of `step`-row query steps that keys [c0, c1) can be seen from (same rule).
+__host__ __device__ inline void visible_query_steps(int causal, int window, int64_t c0,
+                                                    int64_t c1, int64_t n, int64_t m, int step,
+                                                    int64_t empty, int64_t& s0, int64_t& s1) {
+  const int64_t dl = m - n;
+  int64_t a = 0, e = n;
+  if (window > 0) {
+    a = c0 - dl - window + 1;
+    e = c1 - 1 - dl + window;
+  }
+  if (causal && c0 - dl > a) a = c0 - dl;
+  if (a < 0) a = 0;
+  if (e > n) e = n;
+  if (e > a) {
+    s0 = a / step;
+    s1 = (e + step - 1) / step;
+  } else {
+    s0 = s1 = empty;
+  }
+}
+
 // ------------------------------------------------------------ workspace
 // Header at the start of every workspace (device memory, 256 bytes).
 struct WsHeader {
@@ -76,6 +119,7 @@ struct SchedArgs {
   const int32_t* q_off;
   const int32_t* kv_off;
   int32_t B, H, causal;
+  int32_t window;      // sliding window (0 = none)
   int64_t total_q, total_kv;
   TileCfg tc;
   int want_bias_off;
@@ -135,6 +179,7 @@ struct FwdParams {
   float* part_ml;
   int32_t H;
   int32_t causal;
+  int32_t window;     // sliding window (0 = none)
   int32_t bias_kind;
   int32_t num_buckets;
   int32_t normalize;
@@ -169,6 +214,7 @@ struct BwdParams {
   int32_t batch;
   int32_t H;
   int32_t causal;
+  int32_t window;      // sliding window (0 = none)
   int32_t bias_kind;
   int32_t num_buckets;
   int32_t normalize;

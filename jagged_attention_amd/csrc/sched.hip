@@ -547,11 +547,24 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   if (ntiles > a.cap_t) overflow = 1;
   // kv steps of forward tile tau, and its sample (32-bit arithmetic: the offsets check bounds
   // every length far below 2^31)
+  // first kv step of forward tile t of sample b (0 without a sliding window)
+  auto fwd_first = [&](int b, int64_t t) -> int64_t {
+    if (a.window <= 0) return 0;
+    int64_t s0, s1;
+    visible_key_steps(a.causal, a.window, t * tc.bm, min((t + 1) * tc.bm, qlen(b)), qlen(b),
+                      klen(b), tc.bn, 0, s0, s1);
+    return s0;
+  };
   auto fwd_steps = [&](int64_t tau, int& b, int64_t& t) -> int64_t {
     b = owner_of(s_base, B, tau);
     t = tau - s_base[b];
     const int n = (int)qlen(b), m = (int)klen(b);
     const int r1 = min(((int)t + 1) * tc.bm, n);
+    if (a.window > 0) {
+      int64_t s0, s1;
+      visible_key_steps(a.causal, a.window, t * tc.bm, r1, n, m, tc.bn, 0, s0, s1);
+      return s1 - s0;
+    }
     int e = m;
     if (a.causal) e = max(0, min(m, r1 + (m - n)));
     return (e + tc.bn - 1) / tc.bn;
@@ -657,7 +670,8 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int st = (int)steps_of(tau, b, t);
       const int nch = (C > 0 && st > C) ? (st + (int)C - 1) / (int)C : 1;
       const int ci = (int)c;
-      const int kb = ci * st / nch, ke = (ci + 1) * st / nch;
+      const int k0 = (int)fwd_first(b, t);
+      const int kb = k0 + ci * st / nch, ke = k0 + (ci + 1) * st / nch;
       r = make_int4(b, (int)t, kb, ke);
       sl = nch > 1 ? t_sb[tau] + ci : -1;
       cost = max(1, ke - kb);
@@ -671,8 +685,9 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int64_t s = steps_of(tau, b, t);
       const int64_t nch = (C > 0 && s > C) ? cdiv(s, C) : 1;
       const int64_t rb = t_rb[tau];
+      const int64_t k0 = fwd_first(b, t);
       for (int64_t c = 0; c < nch; ++c) {
-        const int64_t kb = c * s / nch, ke = (c + 1) * s / nch;
+        const int64_t kb = k0 + c * s / nch, ke = k0 + (c + 1) * s / nch;
         a.gen_recs[rb + c] = make_int4(b, (int)t, (int)kb, (int)ke);
         a.gen_slot[rb + c] = nch > 1 ? (int32_t)(t_sb[tau] + c) : -1;
         t_cost[rb + c] = (int32_t)max((int64_t)1, ke - kb);
@@ -701,12 +716,15 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int b = owner_of(s_base, B, tau);
       const int t = tau - s_base[b];
       const int n = (int)qlen(b), m = (int)klen(b);
-      int e = m;
-      if (!one_q(b) && a.causal) e = max(0, min(m, min((t + 1) * tc.bq_bm, n) + (m - n)));
-      const int steps = (e + tc.bq_bn - 1) / tc.bq_bn;
-      r = make_int4(b, t, 0, steps);
+      int64_t s0 = 0, s1 = (m + tc.bq_bn - 1) / tc.bq_bn;
+      // a single pass also owns dK/dV, so it visits every key tile (unseen keys get zeros)
+      if (!one_q(b))
+        visible_key_steps(a.causal, a.window, (int64_t)t * tc.bq_bm,
+                          min((int64_t)(t + 1) * tc.bq_bm, (int64_t)n), n, m, tc.bq_bn, 0, s0,
+                          s1);
+      r = make_int4(b, t, (int)s0, (int)s1);
       sl = -1;
-      cost = max(1, steps);
+      cost = max(1, (int)(s1 - s0));
     };
     done_q = rank_emit(a, sh, (int)nq, rec_q, a.bq, nullptr, a.bq_items, qo, ko);
   }
@@ -715,18 +733,13 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int b = owner_of(s_base, B, tau);
       const int64_t t = tau - s_base[b];
       const int64_t n = qlen(b), m = klen(b);
-      int64_t steps;
-      if (one_q(b)) {
-        steps = cdiv(m, tc.bq_bn);
-      } else {
-        const int64_t r1 = min((t + 1) * tc.bq_bm, n);
-        int64_t e = m;
-        if (a.causal) e = max((int64_t)0, min(m, r1 + (m - n)));
-        steps = cdiv(e, tc.bq_bn);
-      }
-      a.gen_recs[tau] = make_int4(b, (int)t, 0, (int)steps);
+      int64_t s0 = 0, s1 = cdiv(m, tc.bq_bn);
+      if (!one_q(b))
+        visible_key_steps(a.causal, a.window, t * tc.bq_bm, min((t + 1) * tc.bq_bm, n), n, m,
+                          tc.bq_bn, 0, s0, s1);
+      a.gen_recs[tau] = make_int4(b, (int)t, (int)s0, (int)s1);
       a.gen_slot[tau] = -1;
-      t_cost[tau] = (int32_t)max((int64_t)1, steps);
+      t_cost[tau] = (int32_t)max((int64_t)1, s1 - s0);
     }
     __syncthreads();
     sort_and_emit(a, sh, (int)nq, t_cost, a.bq, nullptr, a.bq_items, qo, ko);
@@ -746,14 +759,15 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int u = tau - s_base[b];
       const int n = (int)qlen(b), m = (int)klen(b);
       const int nqs = (n + tc.bk_bm - 1) / tc.bk_bm;
-      int first = 0;
-      if (a.causal && !one_k(b)) {
-        const int i0 = max(0, u * tc.bk_bn - (m - n));
-        first = i0 >= n ? nqs : i0 / tc.bk_bm;
-      }
-      r = make_int4(b, u, first, nqs);
+      int64_t s0 = 0, s1 = nqs;
+      // a single pass also owns dQ, so it visits every query tile (unseeing queries get zeros)
+      if (!one_k(b))
+        visible_query_steps(a.causal, a.window, (int64_t)u * tc.bk_bn,
+                            min((int64_t)(u + 1) * tc.bk_bn, (int64_t)m), n, m, tc.bk_bm, nqs,
+                            s0, s1);
+      r = make_int4(b, u, (int)s0, (int)s1);
       sl = -1;
-      cost = max(1, nqs - first);
+      cost = max(1, (int)(s1 - s0));
     };
     done_k = rank_emit(a, sh, (int)nk, rec_k, a.bk, nullptr, a.bk_items, qo, ko);
   }
@@ -763,14 +777,13 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
       const int64_t u = tau - s_base[b];
       const int64_t n = qlen(b), m = klen(b);
       const int64_t nqs = cdiv(n, tc.bk_bm);
-      int64_t first = 0;
-      if (a.causal && !one_k(b)) {
-        const int64_t i0 = max((int64_t)0, u * tc.bk_bn - (m - n));
-        first = i0 >= n ? nqs : i0 / tc.bk_bm;
-      }
-      a.gen_recs[tau] = make_int4(b, (int)u, (int)first, (int)nqs);
+      int64_t s0 = 0, s1 = nqs;
+      if (!one_k(b))
+        visible_query_steps(a.causal, a.window, u * tc.bk_bn, min((u + 1) * tc.bk_bn, m), n, m,
+                            tc.bk_bm, nqs, s0, s1);
+      a.gen_recs[tau] = make_int4(b, (int)u, (int)s0, (int)s1);
       a.gen_slot[tau] = -1;
-      t_cost[tau] = (int32_t)max((int64_t)1, nqs - first);
+      t_cost[tau] = (int32_t)max((int64_t)1, s1 - s0);
     }
     __syncthreads();
     sort_and_emit(a, sh, (int)nk, t_cost, a.bk, nullptr, a.bk_items, qo, ko);

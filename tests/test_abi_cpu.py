@@ -41,6 +41,14 @@ def _problem(**kw):
     return jfa.make_problem(b, h, d, tq, tk, **args)
 
 
+def test_negative_window_is_invalid():
+    p = _problem(window=-1)
+    assert jfa.jfa_workspace_bytes(p, False) == 0
+    assert jfa.load().jfa_tile_config(ctypes.byref(p), (ctypes.c_int32 * 8)()) == \
+        _lib.JFA_ERR_INVALID_ARG
+    assert jfa.jfa_workspace_bytes(_problem(window=7), False) > 0
+
+
 def test_tile_config_and_workspace_host_only():
     p = _problem()
     tc = jfa.jfa_tile_config(p)
