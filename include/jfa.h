@@ -227,6 +227,26 @@ jfa_status jfa_rmsnorm_quantize_mxfp8(const void* x_bf16, const float* weight, i
                                       int32_t n, float eps, uint8_t* codes, uint8_t* scales,
                                       void* stream);
 
+/* Size of the fixed device array that jfa_forward_noalloc uses as its workspace (64 MiB per
+ * GPU, held from the library's first use of that GPU until the process ends). */
+#define JFA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* jfa_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * as jfa_forward (bit for bit), without the workspace: the library's fixed per-GPU array of
+ * JFA_NOALLOC_SCRATCH_BYTES serves instead.  Nothing is allocated or freed.  Problems whose
+ * workspace (jfa_workspace_bytes(p, 0)) exceeds that size return JFA_ERR_WORKSPACE before
+ * anything is enqueued; other errors as jfa_forward.  Every call on a GPU shares that GPU's
+ * array and rewrites what it reads from it, so calls ordered on one stream are independent,
+ * while calls that overlap on one GPU (several streams or threads at once) race.  The device
+ * status of the last call is in the array and is not readable through
+ * jfa_read_device_status; malformed offsets still make the kernels write nothing. */
+jfa_status jfa_forward_noalloc(const jfa_problem* p, const void* q, const void* k,
+                               const void* v, const uint8_t* q_scale, const uint8_t* k_scale,
+                               const uint8_t* v_scale, const int32_t* q_offsets,
+                               const int32_t* kv_offsets, const void* bias, void* o,
+                               float* lse, void* stream);
+
 /* Waits for `stream` and returns the device status word of the last call that used this
  * workspace (JFA_OK or JFA_ERR_DEVICE_DATA) in *status_out. */
 jfa_status jfa_read_device_status(const void* workspace, void* stream, int32_t* status_out);

@@ -11,6 +11,7 @@ from typing import Optional
 from . import _lib
 from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # noqa: F401
                    jfa_backward, jfa_backward_dbias, jfa_block_offsets, jfa_build_schedule, jfa_forward,
+                   jfa_forward_noalloc,
                    jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
                    jfa_rmsnorm_quantize_mxfp8,

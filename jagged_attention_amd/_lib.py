@@ -20,12 +20,15 @@ JFA_ERR_WORKSPACE = -3
 JFA_ERR_LAUNCH = -4
 JFA_ERR_DEVICE_DATA = -5
 
+NOALLOC_SCRATCH_BYTES = 64 << 20     # JFA_NOALLOC_SCRATCH_BYTES
+
 MODES = {"softmax": 0, "silu": 1, "gelu": 2}
 DTYPES = {"f32": 0, "bf16": 1, "mxfp8": 2}
 BIAS_KINDS = {"none": 0, "relpos": 1, "dense": 2}
 
 # every symbol include/jfa.h declares
-EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_dbias",
+EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_forward_noalloc", "jfa_backward",
+           "jfa_backward_dbias",
            "jfa_tile_config",
            "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
            "jfa_quantize_mxfp8", "jfa_rmsnorm_quantize_mxfp8",
@@ -68,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_workspace_bytes.restype = SZ
     lib.jfa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.jfa_forward.restype = ctypes.c_int
+    lib.jfa_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.jfa_forward_noalloc.restype = ctypes.c_int
     lib.jfa_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.jfa_backward.restype = ctypes.c_int
     lib.jfa_backward_dbias.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -137,6 +142,15 @@ def jfa_forward(problem, q, k, v, q_scale, k_scale, v_scale, q_offsets, kv_offse
                             _ptr(bias), _ptr(o), _ptr(lse), _ptr(workspace), workspace_bytes,
                             _stream(stream))
     _check("jfa_forward", st)
+
+
+def jfa_forward_noalloc(problem, q, k, v, q_scale, k_scale, v_scale, q_offsets, kv_offsets, bias,
+                        o, lse, stream=None) -> None:
+    st = load().jfa_forward_noalloc(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(o),
+                                    _ptr(lse), _stream(stream))
+    _check("jfa_forward_noalloc", st)
 
 
 def jfa_backward(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
