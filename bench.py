@@ -84,6 +84,8 @@ class Workload:
             self.qc, self.qs = jfa.quantize_mxfp8(self.q)
             self.kc, self.ks = jfa.quantize_mxfp8(self.k)
             self.vc, self.vs = jfa.quantize_mxfp8(self.v)
+            if self.dout is not None:
+                self.doc, self.dos = jfa.quantize_mxfp8(self.dout)
         batch = case.batch
         if block:
             # BlockAttention: the attention calls run on the refined batch of blocks
@@ -107,7 +109,7 @@ class Workload:
             nb = jfa.jfa_workspace_bytes(self.problem, 2 if self.want_dbias else 1)
             self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
             self.nb = nb
-            self.dq = torch.empty_like(self.q)
+            self.dq = torch.empty_like(self.q)       # bf16 also for MXFP8 inputs
             self.dk = torch.empty_like(self.k)
             self.dv = torch.empty_like(self.v)
             self.dbias = torch.empty_like(self.bias) if self.want_dbias else None
@@ -143,14 +145,22 @@ class Workload:
             ko = self.ko
         if self.fp8:
             d = self.case.head_dim
-            for x, c, sc in ((self.q, self.qc, self.qs), (self.k, self.kc, self.ks),
-                             (self.v, self.vc, self.vs)):
+            todo = [(self.q, self.qc, self.qs), (self.k, self.kc, self.ks),
+                    (self.v, self.vc, self.vs)]
+            if self.with_backward:
+                todo.append((self.dout, self.doc, self.dos))
+            for x, c, sc in todo:
                 jfa.jfa_quantize_mxfp8(x, x.numel() // d, d, c, sc)
             jfa.jfa_forward(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks, self.vs,
                             self.qo, ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
-        else:
-            jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo,
-                            ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
+            if self.with_backward:
+                jfa.jfa_backward_mxfp8(self.problem, self.qc, self.kc, self.vc, self.qs,
+                                       self.ks, self.vs, self.o, self.lse, self.doc, self.dos,
+                                       self.qo, ko, self.bias, self.dq, self.dk, self.dv,
+                                       self.ws_b, self.nb)
+            return
+        jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo, ko,
+                        self.bias, self.o, self.lse, self.ws_f, self.nf)
         if self.with_backward and self.want_dbias:
             jfa.jfa_backward_dbias(self.problem, self.q, self.k, self.v, self.o, self.lse,
                                    self.dout, self.qo, ko, self.bias, self.dq, self.dk, self.dv,
@@ -175,8 +185,11 @@ class Workload:
         fwd = qb + 2 * kb + bias + ob + lse
         bwd = 0
         if self.with_backward:
-            reads = qb + 2 * kb + bias + ob + ((ob + lse) if c.mode == "softmax" else 0)
-            bwd = reads + qb + 2 * kb                 # dQ, dK, dV written in the input dtype
+            # dO in the input format (codes + scales for MXFP8), O and the gradients bf16/fp32
+            ib = 2 if c.dtype == "mxfp8" else el
+            reads = 2 * qb + 2 * kb + bias + ((ob + lse) if c.mode == "softmax" else 0)
+            grads = (c.total_q + 2 * c.total_kv) * c.heads * c.head_dim * ib
+            bwd = reads + grads
         return fwd, bwd
 
     def padded_flops(self):
@@ -289,6 +302,7 @@ def kernel_times(w, steps, flush=None):
                  "jfa_fwd_bf16", "jfa_fwd_mxfp8",
                  "jfa_fwd_f32",
                  "jfa_fwd_combine", "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq",
+                 "jfa_bwd_kvq_mxfp8", "jfa_bwd_dkdv_mxfp8", "jfa_bwd_dq_mxfp8",
                  "jfa_dbias_zero", "jfa_dbias_dq", "jfa_dbias_reduce"):
         ms, n = jfa.jfa_kernel_timing(name)
         if n:
@@ -303,9 +317,16 @@ def kernel_times(w, steps, flush=None):
 # both run in one launch it is credited 10 d.  Executed work counts the query-stationary pass's
 # recompute of S and dP too (6 d; 14 d for the shared launch).
 USEFUL_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 10,
-                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 2, "jfa_dbias_dq": 2}
+                         "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 2, "jfa_dbias_dq": 2,
+                         "jfa_bwd_kvq_mxfp8": 10, "jfa_bwd_dkdv_mxfp8": 8,
+                         "jfa_bwd_dq_mxfp8": 2}
 EXECUTED_FLOPS_PER_PAIR = {"jfa_fwd_bf16": 4, "jfa_fwd_mxfp8": 4, "jfa_bwd_kvq": 14,
-                           "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6, "jfa_dbias_dq": 6}
+                           "jfa_bwd_dkdv": 8, "jfa_bwd_dq": 6, "jfa_dbias_dq": 6,
+                           "jfa_bwd_kvq_mxfp8": 14, "jfa_bwd_dkdv_mxfp8": 8,
+                           "jfa_bwd_dq_mxfp8": 6}
+# kernels whose products run on the fp8 MFMA (QK^T of the MXFP8 forward); every other product,
+# the MXFP8 backward's included, runs on bf16 MFMA
+FP8_MFMA_KERNELS = ("jfa_fwd_mxfp8",)
 
 
 def traffic_for(kernel, workload):
@@ -389,9 +410,10 @@ def oracle_timing(case, target_s):
                        f"{'fwd+bwd' if back else 'fwd'} in fp64, {t:.1f} s)")
 
 
-def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None, window=0):
+def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None, window=0,
+                 with_dout=None):
     from jfa_synth import make_case
-    case = make_case(cfg, seed)
+    case = make_case(cfg, seed, with_dout=with_dout)
     w = Workload(case, block=block, dbias=dbias, window=window)
     t_fl = stats(time_steps(w, steps, warmup, flush))          # MALL flushed before every step
     t_hot = stats(time_steps(w, steps, 1))                     # back to back (secondary)
@@ -409,6 +431,8 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None
     name = case.name if not block else f"block{block}-" + case.name
     if window:
         name = f"window{window}-" + name
+    if case.dtype == "mxfp8" and w.with_backward:
+        name += "+bwd"
     if w.want_dbias:
         name += "+dbias"
     return w, dict(workload=name, seed=case.seed, ms_per_step=t_fl["median"],
@@ -434,7 +458,7 @@ def roofline_of(w, kt):
     executed = EXECUTED_FLOPS_PER_PAIR[dom] * d * w.pairs
     sec = cand[dom]["avg_ms"] * 1e-3
     achieved = useful / sec / 1e12
-    peak = PEAK_FP8_TFLOPS if "mxfp8" in dom else PEAK_BF16_TFLOPS
+    peak = PEAK_FP8_TFLOPS if dom in FP8_MFMA_KERNELS else PEAK_BF16_TFLOPS
     return dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
                 unit="TFLOP/s", frac=round(achieved / peak, 4),
                 traffic=traffic_for(dom, w.case.name), flops_per_launch=useful,
@@ -561,6 +585,16 @@ def main():
         r["kernels"] = kernel_times(wx, 3, flush)
         r["block_rows"] = BLOCK_ROWS
         extra["block_attention"] = r
+        del wx
+        torch.cuda.empty_cache()
+        # MXFP8 training step: the MXFP8 workload with dO, quantiser (Q, K, V, dO), forward and
+        # the MXFP8 backward
+        log("[bench] mxfp8 fwd+bwd")
+        wx, r = bench_config(5, max(3, args.steps // 2), 2, flush=flush, with_dout=True)
+        r["kernels"] = kernel_times(wx, 3, flush)
+        r["roofline"] = roofline_of(wx, r["kernels"])
+        r["frac_of_bf16_mfma_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+        extra["mxfp8_fwd_bwd"] = r
         del wx
         torch.cuda.empty_cache()
         # sliding window: the headline batch, every query seeing its last 256 keys

@@ -75,7 +75,8 @@ typedef struct {
   int64_t total_kv;         /* rows of K / V (equals kv_offsets[B]; checked on the device) */
   int32_t mode;             /* jfa_mode */
   int32_t dtype;            /* jfa_dtype: storage type of Q, K, V (and O, dO, dQ, dK, dV
-                               for F32/BF16).  MXFP8 is forward only: O is bf16. */
+                               for F32/BF16).  MXFP8: Q, K, V (and dO) are codes + scales;
+                               O, dQ, dK, dV are bf16. */
   int32_t causal;           /* 0 or 1; visible iff j <= i + (kv_len - q_len) */
   float qk_scale;           /* > 0, or 0 to select 1/sqrt(d); negative is invalid */
   int32_t kv_len_normalize; /* -1 default (on for SiLU/GELU, off for softmax), 0, 1;
@@ -123,14 +124,36 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
                        void* o, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* Backward pass (F32 and BF16).  o and lse are the forward's outputs (softmax; may be NULL
- * for GDPA); dout like o.  Writes every row of dq [total_q, H, d], dk and dv [total_kv, H, d].
- * Deterministic: repeated calls give bitwise-identical results. */
+/* Backward pass (F32 and BF16; MXFP8 inputs go through jfa_backward_mxfp8, and this call
+ * returns JFA_ERR_UNSUPPORTED for them).  o and lse are the forward's outputs (softmax; may be
+ * NULL for GDPA); dout like o.  Writes every row of dq [total_q, H, d], dk and dv
+ * [total_kv, H, d].  Deterministic: repeated calls give bitwise-identical results. */
 jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, const void* v,
                         const void* o, const float* lse, const void* dout,
                         const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Backward pass on MXFP8 inputs ("Meta Enhances GEM Training Efficiency with Advanced LLM-Scale
+ * Innovations", section "Leveraging Compute Efficiency through Customized Kernels": MXFP8
+ * attention in training; "Meta GEM Training Efficiency: ...", section "Bottleneck move 2":
+ * selective higher precision where the gradient is sensitive).  p->dtype = JFA_MXFP8_E4M3.
+ * q, k, v, dout: E4M3 codes [rows, H, d] (uint8) with E8M0 scales q_scale, k_scale, v_scale,
+ * dout_scale [rows, H, d/32], as jfa_quantize_mxfp8 writes them (dout quantised by the caller
+ * like the forward's inputs); o (bf16) and lse as jfa_forward returned them.  dq, dk, dv are
+ * bf16.  The four inputs are read as codes and scales (1 + 1/32 bytes per element) and
+ * dequantised exactly to bf16 on the way to LDS; all five products run on bf16 MFMA with fp32
+ * accumulation, and P and dS stay bf16 (never requantised).  The result is the gradient of
+ * <O, dO> at the dequantised inputs.  Deterministic; bias, window and the single-pass classes
+ * as jfa_backward; workspace from jfa_workspace_bytes(p, 1).  NULL scales are
+ * JFA_ERR_INVALID_ARG; another dtype in p is JFA_ERR_INVALID_ARG. */
+jfa_status jfa_backward_mxfp8(const jfa_problem* p, const uint8_t* q, const uint8_t* k,
+                              const uint8_t* v, const uint8_t* q_scale, const uint8_t* k_scale,
+                              const uint8_t* v_scale, const void* o, const float* lse,
+                              const uint8_t* dout, const uint8_t* dout_scale,
+                              const int32_t* q_offsets, const int32_t* kv_offsets,
+                              const void* bias, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Backward pass that also returns the gradient of the additive bias ("Meta GEM Training
  * Efficiency: ...", section "Bottleneck move 1": custom biases, which a model trains).  The bias

@@ -11,7 +11,7 @@ from typing import Optional
 from . import _lib
 from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # noqa: F401
                    jfa_backward, jfa_backward_dbias, jfa_block_offsets, jfa_build_schedule, jfa_forward,
-                   jfa_forward_noalloc,
+                   jfa_forward_noalloc, jfa_backward_mxfp8,
                    jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
                    jfa_rmsnorm_quantize_mxfp8,
@@ -20,7 +20,8 @@ from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # n
 
 jfa_status_string = status_string
 
-__all__ = ["make_problem", "forward", "backward", "backward_dbias", "lengths_to_offsets",
+__all__ = ["make_problem", "forward", "backward", "backward_mxfp8", "backward_dbias",
+           "lengths_to_offsets",
            "bias_offsets",
            "block_offsets",
            "quantize_mxfp8", "rmsnorm_quantize_mxfp8",
@@ -100,6 +101,27 @@ def backward(q, k, v, o, lse, dout, q_offsets, kv_offsets, *, mode: str = "softm
         nbytes = workspace.numel()
     jfa_backward(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
                  workspace, nbytes)
+    return dq, dk, dv
+
+
+def backward_mxfp8(q, k, v, q_scale, k_scale, v_scale, o, lse, dout, dout_scale, q_offsets,
+                   kv_offsets, *, mode: str = "softmax", causal: bool = False, bias=None,
+                   bias_kind: str = "none", num_buckets: int = 64, qk_scale: float = 0.0,
+                   kv_len_normalize: int = -1, workspace=None, bwd_fuse=-1, window: int = 0):
+    """MXFP8 backward: q, k, v, dout are E4M3 codes with their E8M0 scales (jfa_quantize_mxfp8);
+    o, lse from the MXFP8 forward.  Returns bf16 (dq, dk, dv)."""
+    import torch
+    problem = _problem_of(q, k, q_offsets, mode, causal, bias_kind, num_buckets, qk_scale,
+                          kv_len_normalize, 0, dtype="mxfp8", bwd_fuse=bwd_fuse, window=window)
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace, nbytes = _workspace(problem, True, q.device)
+    else:
+        nbytes = workspace.numel()
+    jfa_backward_mxfp8(problem, q, k, v, q_scale, k_scale, v_scale, o, lse, dout, dout_scale,
+                       q_offsets, kv_offsets, bias, dq, dk, dv, workspace, nbytes)
     return dq, dk, dv
 
 

@@ -28,7 +28,7 @@ BIAS_KINDS = {"none": 0, "relpos": 1, "dense": 2}
 
 # every symbol include/jfa.h declares
 EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_forward_noalloc", "jfa_backward",
-           "jfa_backward_dbias",
+           "jfa_backward_mxfp8", "jfa_backward_dbias",
            "jfa_tile_config",
            "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
            "jfa_quantize_mxfp8", "jfa_rmsnorm_quantize_mxfp8",
@@ -75,6 +75,9 @@ def load() -> ctypes.CDLL:
     lib.jfa_forward_noalloc.restype = ctypes.c_int
     lib.jfa_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.jfa_backward.restype = ctypes.c_int
+    lib.jfa_backward_mxfp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       SZ, P]
+    lib.jfa_backward_mxfp8.restype = ctypes.c_int
     lib.jfa_backward_dbias.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.jfa_backward_dbias.restype = ctypes.c_int
     lib.jfa_tile_config.argtypes = [PP, P]
@@ -159,6 +162,17 @@ def jfa_backward(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq
                              _ptr(dout), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream))
     _check("jfa_backward", st)
+
+
+def jfa_backward_mxfp8(problem, q, k, v, q_scale, k_scale, v_scale, o, lse, dout, dout_scale,
+                       q_offsets, kv_offsets, bias, dq, dk, dv, workspace, workspace_bytes: int,
+                       stream=None) -> None:
+    st = load().jfa_backward_mxfp8(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+                                   _ptr(lse), _ptr(dout), _ptr(dout_scale), _ptr(q_offsets),
+                                   _ptr(kv_offsets), _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+    _check("jfa_backward_mxfp8", st)
 
 
 def jfa_backward_dbias(problem, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,

@@ -2,8 +2,8 @@
 
 Usage: python -m jagged_attention_amd.build [--incremental]   (or build() from Python).
 Every HIP source is compiled separately (in parallel) under _build/, then linked.  The MFMA
-backward (bwd_inst.hip) is compiled once per (head dim, mode) pair, so its instances build in
-parallel.  --incremental reuses objects newer than every source and header they depend on.
+backward (bwd_inst.hip) is compiled once per (head dim, mode, input format), so its instances
+build in parallel.  --incremental reuses objects newer than every source and header they depend on.
 """
 from __future__ import annotations
 
@@ -28,8 +28,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 
 # translation units compiled once per variant: source -> [(object suffix, extra flags)]
 VARIANTS = {
-    "bwd_inst.hip": [(f"d{d}_m{m}", [f"-DJFA_BWD_D={d}", f"-DJFA_BWD_MODE={m}"])
-                     for d in (128, 64) for m in (0, 1, 2)],
+    "bwd_inst.hip": [(f"d{d}_m{m}_f{f}", [f"-DJFA_BWD_D={d}", f"-DJFA_BWD_MODE={m}",
+                                          f"-DJFA_BWD_FP8={f}"])
+                     for d in (128, 64) for m in (0, 1, 2) for f in (0, 1)],
 }
 
 

@@ -356,16 +356,27 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
 
 namespace {
 
+// MXFP8 scales of the backward's inputs (null for bf16 / fp32).
+struct Fp8Scales {
+  const uint8_t* q = nullptr;
+  const uint8_t* k = nullptr;
+  const uint8_t* v = nullptr;
+  const uint8_t* dout = nullptr;
+};
+
 // The backward; with dbias (bias gradient wanted) the single-pass classes are off, so that every
-// pair's dS is formed in the query-stationary pass.
+// pair's dS is formed in the query-stationary pass.  sc: MXFP8 inputs (dtype JFA_MXFP8_E4M3).
 jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, const void* v,
                          const void* o, const float* lse, const void* dout,
                          const int32_t* q_offsets, const int32_t* kv_offsets, const void* bias,
                          void* dq, void* dk, void* dv, void* dbias, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const Fp8Scales* sc) {
   jfa_status st = check_problem(p);
   if (st != JFA_OK) return st;
-  if (p->dtype == JFA_MXFP8_E4M3) return JFA_ERR_UNSUPPORTED;
+  const bool fp8 = p->dtype == JFA_MXFP8_E4M3;
+  if (fp8 && !sc) return JFA_ERR_UNSUPPORTED;       // MXFP8 inputs come with their scales
+  if (!fp8 && sc) return JFA_ERR_INVALID_ARG;
+  if (fp8 && (!sc->q || !sc->k || !sc->v || !sc->dout)) return JFA_ERR_INVALID_ARG;
   if (dbias && (p->dtype != JFA_BF16 || p->bias_kind == JFA_BIAS_NONE))
     return JFA_ERR_UNSUPPORTED;
   if (dbias && !aligned(dbias, 4)) return JFA_ERR_INVALID_ARG;
@@ -399,6 +410,7 @@ jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, con
     a.d_delta = (float*)(ws + L.delta);
     a.d_head_dim = p->head_dim;
     a.d_esize = p->dtype == JFA_F32 ? 4 : 2;
+    a.d_dout_sc = fp8 ? sc->dout : nullptr;
     a.delta_blocks = std::max(1, cu - 2);
   }
   hipError_t e = launch_schedule(a, s);
@@ -406,6 +418,9 @@ jfa_status backward_impl(const jfa_problem* p, const void* q, const void* k, con
 
   BwdParams bp{};
   bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse; bp.dout = dout;
+  if (fp8) {
+    bp.q_sc = sc->q; bp.k_sc = sc->k; bp.v_sc = sc->v; bp.do_sc = sc->dout;
+  }
   bp.q_off = q_offsets; bp.kv_off = kv_offsets;
   bp.bias = bias;
   bp.bias_off = (const int64_t*)(ws + L.bias_off);
@@ -450,7 +465,25 @@ jfa_status jfa_backward(const jfa_problem* p, const void* q, const void* k, cons
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         void* stream) {
   return backward_impl(p, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
-                       nullptr, workspace, workspace_bytes, stream);
+                       nullptr, workspace, workspace_bytes, stream, nullptr);
+}
+
+jfa_status jfa_backward_mxfp8(const jfa_problem* p, const uint8_t* q, const uint8_t* k,
+                              const uint8_t* v, const uint8_t* q_scale, const uint8_t* k_scale,
+                              const uint8_t* v_scale, const void* o, const float* lse,
+                              const uint8_t* dout, const uint8_t* dout_scale,
+                              const int32_t* q_offsets, const int32_t* kv_offsets,
+                              const void* bias, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!p) return JFA_ERR_INVALID_ARG;
+  if (p->dtype != JFA_MXFP8_E4M3) return JFA_ERR_INVALID_ARG;
+  Fp8Scales sc;
+  sc.q = q_scale;
+  sc.k = k_scale;
+  sc.v = v_scale;
+  sc.dout = dout_scale;
+  return backward_impl(p, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv,
+                       nullptr, workspace, workspace_bytes, stream, &sc);
 }
 
 jfa_status jfa_backward_dbias(const jfa_problem* p, const void* q, const void* k, const void* v,
@@ -460,7 +493,7 @@ jfa_status jfa_backward_dbias(const jfa_problem* p, const void* q, const void* k
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!dbias) return JFA_ERR_INVALID_ARG;
   return backward_impl(p, q, k, v, o, lse, dout, q_offsets, kv_offsets, bias, dq, dk, dv, dbias,
-                       workspace, workspace_bytes, stream);
+                       workspace, workspace_bytes, stream, nullptr);
 }
 
 jfa_status jfa_build_schedule(const jfa_problem* p, const int32_t* q_offsets,

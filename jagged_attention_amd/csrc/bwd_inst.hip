@@ -29,9 +29,10 @@
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
-#if !defined(JFA_BWD_D) || !defined(JFA_BWD_MODE)
-#error "compile with -DJFA_BWD_D=<64|128> -DJFA_BWD_MODE=<0|1|2>"
+#if !defined(JFA_BWD_D) || !defined(JFA_BWD_MODE) || !defined(JFA_BWD_FP8)
+#error "compile with -DJFA_BWD_D=<64|128> -DJFA_BWD_MODE=<0|1|2> -DJFA_BWD_FP8=<0|1>"
 #endif
+#include <type_traits>
 
 namespace jfa {
 namespace {
@@ -141,6 +142,103 @@ struct RowTile {
   }
 };
 
+// MXFP8 inputs: the same STEP x D tile staging as Tile (4 rows x 8 dims per block, row-major
+// stores only), loading 8 E4M3 codes and the row's E8M0 scale per row and block and storing
+// them dequantised to bf16 (exact), so the MFMAs and every LDS layout stay those of bf16.
+template <int D, int NT>
+struct Fp8Tile {
+  static constexpr int NBLK = (STEP / 4) * (D / 8);
+  static constexpr int NB = (NBLK + NT - 1) / NT;
+  static constexpr int PARTS = 6 * NB;
+  u32x2 c[NB][4];
+  uint32_t sc[NB][4];
+
+  // rc: codes (row stride crow bytes), rs: scales (row stride srow bytes)
+  __device__ __forceinline__ void load(rsrc_t rc, rsrc_t rs, uint32_t crow, uint32_t srow,
+                                       int r0) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int id = threadIdx.x + i * NT;
+      if (NBLK % NT != 0 && id >= NBLK) break;
+      int rb, cb;
+      blk_of(id, rb, cb);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t row = (uint32_t)(r0 + 4 * rb + rr);
+        c[i][rr] = ld8(rc, row * crow + 8 * cb);
+        sc[i][rr] = ld1(rs, row * srow + (8 * cb) / 32);
+      }
+    }
+  }
+  // parts 0, 1 of block I write its rows 2 PART, 2 PART + 1; parts 2..5 (the transposed copies
+  // of Tile) are not used with MXFP8 inputs
+  template <int P>
+  __device__ __forceinline__ void store_part(__bf16* rows, __bf16* tr) const {
+    constexpr int i = P / 6, part = P % 6;
+    static_assert(part < 2, "row stores only");
+    const int id = threadIdx.x + i * NT;
+    if (NBLK % NT != 0 && id >= NBLK) return;
+    int rb, cb;
+    blk_of(id, rb, cb);
+#pragma unroll
+    for (int rr = 2 * part; rr < 2 * part + 2; ++rr)
+      *(bf16x8*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) =
+          dequant8_bf16(c[i][rr], sc[i][rr]);
+  }
+  __device__ __forceinline__ void store(__bf16* rows) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int id = threadIdx.x + i * NT;
+      if (NBLK % NT != 0 && id >= NBLK) break;
+      int rb, cb;
+      blk_of(id, rb, cb);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *(bf16x8*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) =
+            dequant8_bf16(c[i][rr], sc[i][rr]);
+    }
+  }
+};
+
+// RowTile's staging for MXFP8 inputs: 8 codes per thread and chunk, dequantised on the store.
+template <int D, int NT>
+struct Fp8RowTile {
+  static constexpr int KCH = D / 8;
+  static constexpr int NL = STEP * KCH / NT;
+  static_assert(STEP * KCH % NT == 0, "row tile staging");
+  u32x2 c[NL];
+  uint32_t sc[NL];
+  __device__ __forceinline__ void load(rsrc_t rc, rsrc_t rs, uint32_t crow, uint32_t srow,
+                                       int r0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int id = threadIdx.x + i * NT;
+      const uint32_t row = (uint32_t)(r0 + id / KCH);
+      c[i] = ld8(rc, row * crow + 8 * (id % KCH));
+      sc[i] = ld1(rs, row * srow + (8 * (id % KCH)) / 32);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* rows) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int id = threadIdx.x + i * NT;
+      *(bf16x8*)(rows + (id / KCH) * tile_row_stride<D>() + 8 * (id % KCH)) =
+          dequant8_bf16(c[i], sc[i]);
+    }
+  }
+};
+
+// A lane's 8 consecutive elements of one (row, head) vector as an MFMA operand: bf16 loaded
+// directly, or MXFP8 codes and their block scale dequantised (byte offsets of element e0).
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8 load_frag8(rsrc_t r, rsrc_t rs, uint32_t row, uint32_t row_b,
+                                             uint32_t srow, int e0) {
+  if constexpr (FP8)
+    return dequant8_bf16(ld8(r, row * row_b + e0), ld1(rs, row * srow + e0 / 32));
+  else
+    return as_bf16x8(ld16(r, row * row_b + 2 * e0));
+}
+
 // Four copies of a diagonal bias table, copy k shifted by k floats, so that any run of 4
 // consecutive entries is one aligned 16-byte read from the copy k = (4 - start % 4) % 4.
 template <int RP>
@@ -181,7 +279,7 @@ struct KvLds {
 // and, in the one-query-tile kernels, registers enough to spill.)
 // HOME: the first item of workgroup g is item g (the pass starts the launch); otherwise every
 // item comes from a ticket.
-template <int D, int NW, int MODE, int BIAS, bool HOME, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool WIN, bool FP8>
 __device__ __forceinline__ void kv_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   using L = KvLds<D, NW, BIAS>;
@@ -199,9 +297,12 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
                       4 * (lane & 3);
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
   const float inv_scale = 1.0f / p.scale;
-  const uint32_t row_bytes = (uint32_t)H * D * 2;
+  const uint32_t row_bytes = (uint32_t)H * D * 2;          // bf16 rows (outputs, bf16 inputs)
+  constexpr int ES = FP8 ? 1 : 2;                           // bytes per input element
+  const uint32_t in_row = (uint32_t)H * D * ES;             // input row stride
+  const uint32_t sc_row = (uint32_t)H * (D / 32);           // MXFP8 scale row stride
 
-  Tile<D, NT> tq, tdo;
+  std::conditional_t<FP8, Fp8Tile<D, NT>, Tile<D, NT>> tq, tdo;
   float lsv = 0.f, dlv = 0.f;       // lse / delta entry staged by threads < STEP
   float rpv = 0.f;                  // relpos table entry
   // Dense bias: NDB units per thread and step, each two 16-byte chunks (8 keys of queries q and
@@ -235,10 +336,21 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
 
     const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
     const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
-    const rsrc_t rk = make_rsrc((const __bf16*)p.k + ((int64_t)ko * H + h) * D, kv_bytes);
-    const rsrc_t rv = make_rsrc((const __bf16*)p.v + ((int64_t)ko * H + h) * D, kv_bytes);
-    const rsrc_t rq = make_rsrc((const __bf16*)p.q + ((int64_t)qo * H + h) * D, q_bytes);
-    const rsrc_t rdo = make_rsrc((const __bf16*)p.dout + ((int64_t)qo * H + h) * D, q_bytes);
+    const uint32_t kv_in = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * ES : 0;
+    const uint32_t q_in = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * ES : 0;
+    const rsrc_t rk = make_rsrc((const uint8_t*)p.k + ((int64_t)ko * H + h) * D * ES, kv_in);
+    const rsrc_t rv = make_rsrc((const uint8_t*)p.v + ((int64_t)ko * H + h) * D * ES, kv_in);
+    const rsrc_t rq = make_rsrc((const uint8_t*)p.q + ((int64_t)qo * H + h) * D * ES, q_in);
+    const rsrc_t rdo = make_rsrc((const uint8_t*)p.dout + ((int64_t)qo * H + h) * D * ES, q_in);
+    rsrc_t rks = rk, rvs = rv, rqs = rq, rdos = rdo;
+    if constexpr (FP8) {
+      const uint32_t kv_s = m > 0 ? ((uint32_t)(m - 1) * H + 1) * (D / 32) : 0;
+      const uint32_t q_s = n > 0 ? ((uint32_t)(n - 1) * H + 1) * (D / 32) : 0;
+      rks = make_rsrc(p.k_sc + ((int64_t)ko * H + h) * (D / 32), kv_s);
+      rvs = make_rsrc(p.v_sc + ((int64_t)ko * H + h) * (D / 32), kv_s);
+      rqs = make_rsrc(p.q_sc + ((int64_t)qo * H + h) * (D / 32), q_s);
+      rdos = make_rsrc(p.do_sc + ((int64_t)qo * H + h) * (D / 32), q_s);
+    }
     rsrc_t rls = rq, rdl = rq, rb = rq;
     if constexpr (MODE == MODE_SOFTMAX) {
       rls = make_rsrc(p.lse + (int64_t)h * p.total_q + qo, (uint32_t)n * 4u);
@@ -252,8 +364,8 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = as_bf16x8(ld16(rk, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
-      vf[ks] = as_bf16x8(ld16(rv, (uint32_t)j * row_bytes + 32 * ks + 16 * g));
+      kf[ks] = load_frag8<D, FP8>(rk, rks, (uint32_t)j, in_row, sc_row, 16 * ks + 8 * g);
+      vf[ks] = load_frag8<D, FP8>(rv, rvs, (uint32_t)j, in_row, sc_row, 16 * ks + 8 * g);
     }
 
     f32x16 dk[D / 32], dv[D / 32];
@@ -285,8 +397,13 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
           dlv = __uint_as_float(ld4(rdl, (uint32_t)(q0 + tid) * 4u));
         }
       }
-      tq.load(rq, row_bytes, q0);
-      tdo.load(rdo, row_bytes, q0);
+      if constexpr (FP8) {
+        tq.load(rq, rqs, in_row, sc_row, q0);
+        tdo.load(rdo, rdos, in_row, sc_row, q0);
+      } else {
+        tq.load(rq, row_bytes, q0);
+        tdo.load(rdo, row_bytes, q0);
+      }
       if constexpr (BIAS == B_DENSE) {
 #pragma unroll
         for (int i = 0; i < NPRE; ++i) {
@@ -296,7 +413,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       }
     };
     // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
-    constexpr int TP = Tile<D, NT>::PARTS;
+    constexpr int TP = decltype(tq)::PARTS;
     auto store_tile_piece = [&](auto pc, int st) {
       constexpr int P = decltype(pc)::value;
       unsigned char* base = lds + st * L::STAGE;
@@ -681,7 +798,7 @@ struct QLds {
 // relative-position table: per-lane running sums by bucket, flushed on a change of bucket into
 // the lane's own slots, in LDS for at most DB_NB buckets and else in its partial row in memory;
 // later kernels reduce the rows in a fixed order).  DB runs without the single-pass classes.
-template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN, bool FP8>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   using L = QLds<D, NW, BIAS>;
@@ -698,10 +815,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                       4 * (lane & 3);
   const float c_log = MODE == MODE_SOFTMAX ? p.scale * LOG2E : p.scale;
   const float inv_scale = 1.0f / p.scale;
-  const uint32_t row_bytes = (uint32_t)H * D * 2;
+  const uint32_t row_bytes = (uint32_t)H * D * 2;          // bf16 rows (outputs, bf16 inputs)
+  constexpr int ES = FP8 ? 1 : 2;                           // bytes per input element
+  const uint32_t in_row = (uint32_t)H * D * ES;             // input row stride
+  const uint32_t sc_row = (uint32_t)H * (D / 32);           // MXFP8 scale row stride
 
-  Tile<D, NT> tk;
-  RowTile<D, NT> tv;
+  std::conditional_t<FP8, Fp8Tile<D, NT>, Tile<D, NT>> tk;
+  std::conditional_t<FP8, Fp8RowTile<D, NT>, RowTile<D, NT>> tv;
   float rpv = 0.f;
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
   u32x4 dbr[NDB];                   // dense bias chunks (8 keys of one query) of the next step
@@ -741,21 +861,31 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 
     const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
     const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * 2 : 0;
-    const rsrc_t rk = make_rsrc((const __bf16*)p.k + ((int64_t)ko * H + h) * D, kv_bytes);
-    const rsrc_t rv = make_rsrc((const __bf16*)p.v + ((int64_t)ko * H + h) * D, kv_bytes);
-    const rsrc_t rq = make_rsrc((const __bf16*)p.q + ((int64_t)qo * H + h) * D, q_bytes);
-    const rsrc_t rdo = make_rsrc((const __bf16*)p.dout + ((int64_t)qo * H + h) * D, q_bytes);
+    const uint32_t kv_in = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * ES : 0;
+    const uint32_t q_in = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * ES : 0;
+    const rsrc_t rk = make_rsrc((const uint8_t*)p.k + ((int64_t)ko * H + h) * D * ES, kv_in);
+    const rsrc_t rv = make_rsrc((const uint8_t*)p.v + ((int64_t)ko * H + h) * D * ES, kv_in);
+    const rsrc_t rq = make_rsrc((const uint8_t*)p.q + ((int64_t)qo * H + h) * D * ES, q_in);
+    const rsrc_t rdo = make_rsrc((const uint8_t*)p.dout + ((int64_t)qo * H + h) * D * ES, q_in);
+    rsrc_t rks = rk, rvs = rv, rqs = rq, rdos = rdo;
+    if constexpr (FP8) {
+      const uint32_t kv_s = m > 0 ? ((uint32_t)(m - 1) * H + 1) * (D / 32) : 0;
+      const uint32_t q_s = n > 0 ? ((uint32_t)(n - 1) * H + 1) * (D / 32) : 0;
+      rks = make_rsrc(p.k_sc + ((int64_t)ko * H + h) * (D / 32), kv_s);
+      rvs = make_rsrc(p.v_sc + ((int64_t)ko * H + h) * (D / 32), kv_s);
+      rqs = make_rsrc(p.q_sc + ((int64_t)qo * H + h) * (D / 32), q_s);
+      rdos = make_rsrc(p.do_sc + ((int64_t)qo * H + h) * (D / 32), q_s);
+    }
     rsrc_t rb = rq;
     if constexpr (BIAS == B_DENSE)
       rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * boff + (int64_t)h * n * m,
                      (uint32_t)n * (uint32_t)m * 2u);
 
     bf16x8 qf[D / 16], dof[D / 16];
-    const uint32_t qoff = (uint32_t)qi * row_bytes;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = as_bf16x8(ld16(rq, qoff + 32 * ks + 16 * g));
-      dof[ks] = as_bf16x8(ld16(rdo, qoff + 32 * ks + 16 * g));
+      qf[ks] = load_frag8<D, FP8>(rq, rqs, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
+      dof[ks] = load_frag8<D, FP8>(rdo, rdos, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
     }
     float lse2 = 0.f, dlt = 0.f;
     // bias gradient, relative-position table: the bucket being summed and its running sum
@@ -799,8 +929,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                                        relpos_bucket(dist, p.num_buckets)];
         }
       }
-      tk.load(rk, row_bytes, j0);
-      tv.load(rv, row_bytes, j0);
+      if constexpr (FP8) {
+        tk.load(rk, rks, in_row, sc_row, j0);
+        tv.load(rv, rvs, in_row, sc_row, j0);
+      } else {
+        tk.load(rk, row_bytes, j0);
+        tv.load(rv, row_bytes, j0);
+      }
       if constexpr (BIAS == B_DENSE) {
         // [BM][STEP] block as chunks of 8 keys, consecutive lanes along a row
 #pragma unroll
@@ -816,7 +951,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     auto store_step = [&](int st, int kt) {
       unsigned char* base = lds + st * L::STAGE;
       const int j0 = kt * STEP;
-      tk.store(reinterpret_cast<__bf16*>(base + L::KR), nullptr);
+      if constexpr (FP8) tk.store(reinterpret_cast<__bf16*>(base + L::KR));
+      else tk.store(reinterpret_cast<__bf16*>(base + L::KR), nullptr);
       tv.store(reinterpret_cast<__bf16*>(base + L::VR));
       if constexpr (BIAS == B_RELPOS) {
         if (tid < BM + STEP - 1)
@@ -1127,34 +1263,34 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   }
 }
 
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_kv_kernel(BwdParams p) {
-  kv_pass<D, NW, MODE, BIAS, true, WIN>(p);
+  kv_pass<D, NW, MODE, BIAS, true, WIN, FP8>(p);
 }
 
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_kernel(BwdParams p) {
-  q_pass<D, NW, MODE, BIAS, true, false, WIN>(p);
+  q_pass<D, NW, MODE, BIAS, true, false, WIN, FP8>(p);
 }
 
 // Both passes in one persistent launch (they are independent): every workgroup first works
 // through the kv-stationary list, then takes q-stationary items by ticket, so the second list
 // fills the first one's tail and the two passes share one kernel boundary.
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_kvq_kernel(BwdParams p) {
-  kv_pass<D, NW, MODE, BIAS, true, WIN>(p);
+  kv_pass<D, NW, MODE, BIAS, true, WIN, FP8>(p);
   __syncthreads();
-  q_pass<D, NW, MODE, BIAS, false, false, WIN>(p);
+  q_pass<D, NW, MODE, BIAS, false, false, WIN, FP8>(p);
 }
 
 // The query-stationary pass with the bias gradient (DB); the single-pass classes are off.
 template <int D, int NW, int MODE, int BIAS, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_db_kernel(BwdParams p) {
-  q_pass<D, NW, MODE, BIAS, true, true, WIN>(p);
+  q_pass<D, NW, MODE, BIAS, true, true, WIN, false>(p);
 }
 
 // Zeroes `count` 16-bit elements of x; with count_from (a dense bias's block offsets), the
@@ -1231,23 +1367,24 @@ hipError_t launch_persistent(K kern, size_t lds, int threads, int64_t max_items,
   return hipGetLastError();
 }
 
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8 = false>
 hipError_t run_bk(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_kv_kernel<D, NW, MODE, BIAS, WIN>, KvLds<D, NW, BIAS>::TOTAL, NW * 64,
-                           max_items, cu, p, "jfa_bwd_dkdv", s);
+  return launch_persistent(bwd_kv_kernel<D, NW, MODE, BIAS, WIN, FP8>, KvLds<D, NW, BIAS>::TOTAL,
+                           NW * 64, max_items, cu, p,
+                           FP8 ? "jfa_bwd_dkdv_mxfp8" : "jfa_bwd_dkdv", s);
 }
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8 = false>
 hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS, WIN>, QLds<D, NW, BIAS>::TOTAL, NW * 64,
-                           max_items, cu, p, "jfa_bwd_dq", s);
+  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS, WIN, FP8>, QLds<D, NW, BIAS>::TOTAL,
+                           NW * 64, max_items, cu, p, FP8 ? "jfa_bwd_dq_mxfp8" : "jfa_bwd_dq", s);
 }
 
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8 = false>
 hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
   constexpr size_t lds = KvLds<D, NW, BIAS>::TOTAL > QLds<D, NW, BIAS>::TOTAL
                              ? KvLds<D, NW, BIAS>::TOTAL : QLds<D, NW, BIAS>::TOTAL;
-  return launch_persistent(bwd_kvq_kernel<D, NW, MODE, BIAS, WIN>, lds, NW * 64, max_items, cu, p,
-                           "jfa_bwd_kvq", s);
+  return launch_persistent(bwd_kvq_kernel<D, NW, MODE, BIAS, WIN, FP8>, lds, NW * 64, max_items,
+                           cu, p, FP8 ? "jfa_bwd_kvq_mxfp8" : "jfa_bwd_kvq", s);
 }
 
 template <int D, int NW, int MODE, int BIAS, bool WIN>
@@ -1299,45 +1436,52 @@ hipError_t run_bwd_db(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t
   return e;
 }
 
-template <int D, int MODE, int BIAS, bool WIN>
+template <int D, int MODE, int BIAS, bool WIN, bool FP8>
 hipError_t run_bwd_bias(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                         hipStream_t s) {
   // one launch for both passes when their workgroups have the same shape
-  if (tc.bk_nw == 4 && tc.bq_nw == 4) return run_bkq<D, 4, MODE, BIAS, WIN>(p, max(mq, mk), cu, s);
-  hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS, WIN>(p, mk, cu, s)
-                               : run_bk<D, 2, MODE, BIAS, WIN>(p, mk, cu, s);
+  if (tc.bk_nw == 4 && tc.bq_nw == 4)
+    return run_bkq<D, 4, MODE, BIAS, WIN, FP8>(p, max(mq, mk), cu, s);
+  hipError_t e = tc.bk_nw == 4 ? run_bk<D, 4, MODE, BIAS, WIN, FP8>(p, mk, cu, s)
+                               : run_bk<D, 2, MODE, BIAS, WIN, FP8>(p, mk, cu, s);
   if (e != hipSuccess) return e;
-  return tc.bq_nw == 4 ? run_bq<D, 4, MODE, BIAS, WIN>(p, mq, cu, s) : run_bq<D, 2, MODE, BIAS, WIN>(p, mq, cu, s);
+  return tc.bq_nw == 4 ? run_bq<D, 4, MODE, BIAS, WIN, FP8>(p, mq, cu, s)
+                       : run_bq<D, 2, MODE, BIAS, WIN, FP8>(p, mq, cu, s);
 }
 
-template <int D, int MODE, bool WIN>
+template <int D, int MODE, bool WIN, bool FP8>
 hipError_t run_bwd(const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu,
                    hipStream_t s) {
   // D (softmax) was computed by the scheduler launch
   switch (p.bias_kind) {
-    case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS, WIN>(p, tc, mq, mk, cu, s);
-    case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE, WIN>(p, tc, mq, mk, cu, s);
-    default: return run_bwd_bias<D, MODE, B_NONE, WIN>(p, tc, mq, mk, cu, s);
+    case JFA_BIAS_RELPOS: return run_bwd_bias<D, MODE, B_RELPOS, WIN, FP8>(p, tc, mq, mk, cu, s);
+    case JFA_BIAS_DENSE: return run_bwd_bias<D, MODE, B_DENSE, WIN, FP8>(p, tc, mq, mk, cu, s);
+    default: return run_bwd_bias<D, MODE, B_NONE, WIN, FP8>(p, tc, mq, mk, cu, s);
   }
 }
 
 }  // namespace
 
-// The launcher of one (head dim, mode) pair, defined by the translation unit compiled for it.
+// The launcher of one (head dim, mode, input format) triple, defined by the translation unit
+// compiled for it.
 template <>
-hipError_t launch_bwd_dm<JFA_BWD_D, JFA_BWD_MODE>(const BwdParams& p, const TileCfg& tc,
-                                                  int64_t mq, int64_t mk, int cu, hipStream_t s,
-                                                  bool dbias) {
+hipError_t launch_bwd_dm<JFA_BWD_D, JFA_BWD_MODE, (JFA_BWD_FP8 != 0)>(
+    const BwdParams& p, const TileCfg& tc, int64_t mq, int64_t mk, int cu, hipStream_t s,
+    bool dbias) {
   constexpr int D = JFA_BWD_D, M = JFA_BWD_MODE;
+  constexpr bool FP8 = JFA_BWD_FP8 != 0;
   const bool win = p.window > 0;
-  if (dbias) {
+  if constexpr (FP8) {
+    if (dbias) return hipErrorInvalidValue;        // the bias gradient is built for bf16 inputs
+  } else if (dbias) {
     if (p.bias_kind == JFA_BIAS_DENSE)
       return win ? run_bwd_db<D, M, B_DENSE, true>(p, tc, mq, mk, cu, s)
                  : run_bwd_db<D, M, B_DENSE, false>(p, tc, mq, mk, cu, s);
     return win ? run_bwd_db<D, M, B_RELPOS, true>(p, tc, mq, mk, cu, s)
                : run_bwd_db<D, M, B_RELPOS, false>(p, tc, mq, mk, cu, s);
   }
-  return win ? run_bwd<D, M, true>(p, tc, mq, mk, cu, s) : run_bwd<D, M, false>(p, tc, mq, mk, cu, s);
+  return win ? run_bwd<D, M, true, FP8>(p, tc, mq, mk, cu, s)
+             : run_bwd<D, M, false, FP8>(p, tc, mq, mk, cu, s);
 }
 
 }  // namespace jfa

@@ -147,6 +147,21 @@ __device__ __forceinline__ float e8m0_to_f(uint32_t s) {
   return s == 0 ? 5.877471754111438e-39f : __uint_as_float(s << 23);
 }
 
+// Eight E4M3 codes (the bytes of c, lowest first) times 2^(s - 127), as eight bf16: the
+// hardware's scaled conversion, exact for the scale codes of normal data (an E4M3 value has 4
+// significant bits and bf16 8).
+__device__ __forceinline__ bf16x8 dequant8_bf16(u32x2 c, uint32_t s) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const float sc = e8m0_to_f(s);
+  const bf2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false);
+  const bf2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true);
+  const bf2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false);
+  const bf2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true);
+  const u32x4 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, e)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // Position of row k (0..63) of a tile stored transposed for the contraction of a 32x32x16
 // MFMA whose other operand comes from a 32x32 accumulator: within each group of 16, row
 // 8a + 4g + b sits at 8g + 4a + b, so the 8 contraction indices of MFMA lane half g (the

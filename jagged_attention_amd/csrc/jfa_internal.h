@@ -154,6 +154,7 @@ struct SchedArgs {
   int32_t delta_blocks;
   int32_t d_head_dim;
   int32_t d_esize;      // bytes per element of O / dO (2 bf16, 4 fp32)
+  const uint8_t* d_dout_sc;   // MXFP8 dO: E4M3 codes in d_dout, E8M0 scales here (O is bf16)
 };
 
 // ----------------------------------------------------- kernel parameters
@@ -188,9 +189,13 @@ struct FwdParams {
 };
 
 struct BwdParams {
-  const void* q;
+  const void* q;          // bf16 / fp32 values, or MXFP8 codes (then the scales below)
   const void* k;
   const void* v;
+  const uint8_t* q_sc;    // MXFP8 E8M0 scales [rows][H][d/32] of q, k, v and dout (else null)
+  const uint8_t* k_sc;
+  const uint8_t* v_sc;
+  const uint8_t* do_sc;
   const void* o;
   const float* lse;
   const void* dout;
@@ -256,21 +261,28 @@ hipError_t launch_backward(const BwdParams& p, const TileCfg& tc, int head_dim, 
 hipError_t launch_backward_dbias(const BwdParams& p, const TileCfg& tc, int head_dim,
                                  int64_t max_q_items, int64_t max_k_items, int cu_count,
                                  hipStream_t s);
-// The MFMA backward of one (head dim, mode) pair (bwd_inst.hip, one translation unit per pair);
-// dbias: the variant with the bias gradient (bf16, bias present, tc.fuse == 0).
-template <int D, int MODE>
+// The MFMA backward of one (head dim, mode, input format) triple (bwd_inst.hip, one translation
+// unit per triple; FP8: MXFP8 inputs); dbias: the variant with the bias gradient (bf16 inputs,
+// bias present, tc.fuse == 0).
+template <int D, int MODE, bool FP8>
 hipError_t launch_bwd_dm(const BwdParams& p, const TileCfg& tc, int64_t max_q_items,
                          int64_t max_k_items, int cu_count, hipStream_t s, bool dbias);
-#define JFA_DECLARE_BWD_DM(D_, M_)                                                         \
-  template <>                                                                              \
-  hipError_t launch_bwd_dm<D_, M_>(const BwdParams&, const TileCfg&, int64_t, int64_t, int, \
-                                   hipStream_t, bool);
-JFA_DECLARE_BWD_DM(128, 0)
-JFA_DECLARE_BWD_DM(128, 1)
-JFA_DECLARE_BWD_DM(128, 2)
-JFA_DECLARE_BWD_DM(64, 0)
-JFA_DECLARE_BWD_DM(64, 1)
-JFA_DECLARE_BWD_DM(64, 2)
+#define JFA_DECLARE_BWD_DM(D_, M_, F_)                                                      \
+  template <>                                                                               \
+  hipError_t launch_bwd_dm<D_, M_, F_>(const BwdParams&, const TileCfg&, int64_t, int64_t, \
+                                       int, hipStream_t, bool);
+JFA_DECLARE_BWD_DM(128, 0, false)
+JFA_DECLARE_BWD_DM(128, 1, false)
+JFA_DECLARE_BWD_DM(128, 2, false)
+JFA_DECLARE_BWD_DM(64, 0, false)
+JFA_DECLARE_BWD_DM(64, 1, false)
+JFA_DECLARE_BWD_DM(64, 2, false)
+JFA_DECLARE_BWD_DM(128, 0, true)
+JFA_DECLARE_BWD_DM(128, 1, true)
+JFA_DECLARE_BWD_DM(128, 2, true)
+JFA_DECLARE_BWD_DM(64, 0, true)
+JFA_DECLARE_BWD_DM(64, 1, true)
+JFA_DECLARE_BWD_DM(64, 2, true)
 #undef JFA_DECLARE_BWD_DM
 
 // Sets a kernel's dynamic-LDS limit once per device (thread-safe).

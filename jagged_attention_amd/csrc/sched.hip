@@ -446,6 +446,59 @@ __device__ __forceinline__ void delta_rows(const SchedArgs& a, int block, int nb
   }
 }
 
+// The same D with MXFP8 dO (O stays bf16): each lane takes 8 elements of a (row, head) vector,
+// 16 bytes of O and 8 codes of dO with their E8M0 block scale, dequantised exactly in fp32.
+template <int D>
+__device__ __forceinline__ void delta_rows_fp8(const SchedArgs& a, int block, int nblocks) {
+  constexpr int LPR = D / 8;                      // lanes per (row, head) vector
+  constexpr int U = 4;
+  const int64_t nchunks = a.total_q * a.H * LPR;
+  const int64_t stride = (int64_t)nblocks * ST;
+  const uint8_t* o = (const uint8_t*)a.d_o;
+  const uint8_t* g = (const uint8_t*)a.d_dout;
+  for (int64_t base = (int64_t)block * ST + threadIdx.x; base < nchunks; base += U * stride) {
+    u32x4 x[U];
+    uint2 y[U];
+    uint32_t sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * stride;
+      if (c < nchunks) {
+        x[u] = *(const u32x4*)(o + c * 16);
+        y[u] = *(const uint2*)(g + c * 8);
+        sc[u] = a.d_dout_sc[c / 4];               // 32 elements (4 chunks) per scale
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * stride;
+      float acc = 0.f;
+      if (c < nchunks) {
+        // 2^(s - 127) as a float (s = 0: 2^-127, a subnormal)
+        const float f = sc[u] == 0 ? 5.877471754111438e-39f : __uint_as_float(sc[u] << 23);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t code = ((e < 4 ? y[u].x : y[u].y) >> (8 * (e & 3))) & 255u;
+          // E4M3: sign, 4-bit exponent (bias 7), 3-bit mantissa, subnormals at exponent 0
+          const uint32_t ex = (code >> 3) & 15u, mt = code & 7u;
+          float v = ex ? __uint_as_float(((ex + 120u) << 23) | (mt << 20))
+                       : (float)mt * 0.001953125f;
+          v = (code & 128u) ? -v : v;
+          const uint32_t ow = x[u][e >> 1];
+          const float ov = __uint_as_float((e & 1) ? (ow & 0xffff0000u) : (ow << 16));
+          acc = fmaf(ov, v * f, acc);
+        }
+      }
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (c < nchunks && (threadIdx.x % LPR) == 0) {
+        const int64_t rh = c / LPR;
+        a.d_delta[(rh % a.H) * a.total_q + rh / a.H] = acc;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
@@ -458,7 +511,10 @@ __global__ __launch_bounds__(ST) void schedule_kernel(SchedArgs a) {
   const int nroles = a.parallel ? __popc(a.lists & 7) : 1;
   if ((int)blockIdx.x >= nroles) {
     const int blk = blockIdx.x - nroles, nblk = gridDim.x - nroles;
-    if (a.d_esize == 2) {
+    if (a.d_dout_sc) {
+      if (a.d_head_dim == 128) delta_rows_fp8<128>(a, blk, nblk);
+      else delta_rows_fp8<64>(a, blk, nblk);
+    } else if (a.d_esize == 2) {
       if (a.d_head_dim == 128) delta_rows<2, 128>(a, blk, nblk);
       else delta_rows<2, 64>(a, blk, nblk);
     } else {

@@ -147,14 +147,17 @@ def custom_case(q_lens, kv_lens, heads: int, head_dim: int, *, dtype: str = "bf1
                 forward_only=not with_dout, seed=seed)
 
 
-def make_case(cfg: int, seed: Optional[int] = None, batch: Optional[int] = None) -> Case:
-    """Workload ``cfg`` (1..5) drawn with ``seed`` (default: the workload number)."""
+def make_case(cfg: int, seed: Optional[int] = None, batch: Optional[int] = None,
+              with_dout: Optional[bool] = None) -> Case:
+    """Workload ``cfg`` (1..5) drawn with ``seed`` (default: the workload number).  with_dout
+    overrides whether dO is drawn (last, so Q, K, V and the bias do not change)."""
     c = WORKLOADS[cfg]
     seed = cfg if seed is None else seed
     rng = np.random.default_rng(seed)
     q_lens, kv_lens = lengths_for(cfg, rng, batch)
+    want_dout = (not c["forward_only"]) if with_dout is None else bool(with_dout)
     case = custom_case(q_lens, kv_lens, c["heads"], c["head_dim"], dtype=c["dtype"],
                        mode=c["mode"], causal=c["causal"], bias_kind=c["bias_kind"],
-                       seed=seed, with_dout=not c["forward_only"], name=c["name"], rng=rng)
+                       seed=seed, with_dout=want_dout, name=c["name"], rng=rng)
     case.extra["config"] = cfg
     return case
