@@ -432,7 +432,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
         if (tid < STEP) {
           // rows without a visible key have lse = -inf; all their pairs are masked to -inf,
           // so any finite value keeps exp2(-inf - lse) = 0
-          reinterpret_cast<float*>(base + L::LS)[tid] = lsv == NEG_INF ? 0.f : lsv * inv_scale;
+          reinterpret_cast<float*>(base + L::LS)[tid] = lsv == NEG_INF ? 0.f : lsv * LOG2E;
           reinterpret_cast<float*>(base + L::DL)[tid] = -dlv;   // stored negated: dP starts at -D
         }
       }
@@ -542,20 +542,17 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
             if (o < qlo || o >= qhi) sacc[blk][i] = NEG_INF;
           }
       }
-      // softmax: S starts at bias/scale - lse/scale and dP at -delta, so that the VALU work per
-      // pair is P = exp2(S c), dS = P dP (masked pairs stay at -inf)
+      // softmax: dP starts at -delta (loaded straight into the accumulator), so that the VALU
+      // work per pair is P = exp2(S c - lse log2 e) (one fma and the exp), dS = P dP (masked
+      // pairs stay at -inf); the lse of the lane's queries is read from LDS beside the MFMAs
       if constexpr (MODE == MODE_SOFTMAX) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 l = *(const f32x4*)(lsl + blk * 32 + 8 * qd + 4 * g);
             const f32x4 dl = *(const f32x4*)(dll + blk * 32 + 8 * qd + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sacc[blk][4 * qd + e] -= l[e];
-              pacc[blk][4 * qd + e] = dl[e];
-            }
+            for (int e = 0; e < 4; ++e) pacc[blk][4 * qd + e] = dl[e];
           }
       } else {
 #pragma unroll
@@ -585,12 +582,21 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
         return u32x4{lo[0], lo[1], hi[0], hi[1]};
       };
       uint32_t pp[2][8], dd[2][8];
+      // lse log2 e of this lane's queries of half h, quad qd (softmax)
+      f32x4 lq[2][4];
+      auto load_lse = [&](int h) {
+        if constexpr (MODE == MODE_SOFTMAX) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            lq[h][qd] = *(const f32x4*)(lsl + h * 32 + 8 * qd + 4 * g);
+        }
+      };
       // B(h) element i (query offset blk*32 + 8(i/4) + i%4 with blk = h)
       float pv_t = 0.f, ds_t = 0.f;
       auto valu_b = [&](int h, int i) {
         float pv, dsv;
         if constexpr (MODE == MODE_SOFTMAX) {
-          pv = fast_exp2(sacc[h][i] * c_log);
+          pv = fast_exp2(fmaf(sacc[h][i], c_log, -lq[h][i >> 2][i & 3]));
           dsv = pv * pacc[h][i];
         } else {
           const bool vis = sacc[h][i] != NEG_INF;
@@ -630,6 +636,9 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       static_for<0, NS>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         if constexpr (s + PF < NS) ring[(s + PF) % RING] = opnd(s + PF);
+        // each half's lse a phase before its exps
+        if constexpr (s == NA / 2) load_lse(0);
+        if constexpr (s == NA + NA / 2) load_lse(1);
         mfma_s(s, ring[s % RING]);
         // B(0) under A(1), B(1) under C(0): one element per MFMA (16 elements per half)
         constexpr int EPM = 16 / NA;     // elements per MFMA (1 at d = 128, 2 at d = 64)
