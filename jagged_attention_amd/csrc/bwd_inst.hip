@@ -311,7 +311,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
   constexpr int KCHK = BNK / 8;
   constexpr int NDB = BIAS == B_DENSE ? (STEP / 2) * KCHK / NT : 1;
   constexpr int NPRE = D == 128 ? 0 : NDB;
-  u32x4 dbr[NPRE > 0 ? NPRE : 1][2];
+  BiasRaw dbr[NPRE > 0 ? NPRE : 1][2];
 
   ItemPipeT<HOME> pipe{p.xtk_k, p.bk, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
@@ -323,6 +323,12 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
     const int h = w % H;
     const int u = item_field(dsc, IF_X), qs_first = item_field(dsc, IF_Y);
     const int qs_end = item_field(dsc, IF_Z);
+    // the next item: a short item takes its ticket now and reads its record right after this
+    // item's first loads (both round trips overlap those loads); a longer one claims it
+    // CLAIM_AHEAD steps before its end
+    const int nsteps = qs_end - qs_first;
+    const bool short_item = nsteps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
     const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
     const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
     const int64_t boff = item_boff(dsc);
@@ -374,12 +380,19 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
 
-    auto dense_chunk = [&](int i, int q0, int half) -> u32x4 {
+    // chunk (i, half) of this thread for query step q0: byte offset and valid element count
+    auto dense_at = [&](int i, int q0, int half, uint32_t& off, int& valid) {
       const int id = tid + i * NT;
       const int qa = q0 + 2 * (id / KCHK) + half, k0 = j0 + 8 * (id % KCHK);
-      const int valid = qa < n ? min(8, m - k0) : 0;
-      return bias_chunk(rb, ((uint32_t)qa * (uint32_t)m + (uint32_t)k0) * 2u, valid,
-                        (uint32_t)n * (uint32_t)m * 2u);
+      valid = qa < n ? min(8, m - k0) : 0;
+      off = ((uint32_t)qa * (uint32_t)m + (uint32_t)k0) * 2u;
+    };
+    const uint32_t bias_bytes = (uint32_t)n * (uint32_t)m * 2u;
+    auto dense_chunk = [&](int i, int q0, int half) -> u32x4 {
+      uint32_t off;
+      int valid;
+      dense_at(i, q0, half, off, valid);
+      return bias_chunk(rb, off, valid, bias_bytes);
     };
     auto load_step = [&](int qs) {
       const int q0 = qs * STEP;
@@ -406,10 +419,14 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       }
       if constexpr (BIAS == B_DENSE) {
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i) {
-          dbr[i][0] = dense_chunk(i, q0, 0);
-          dbr[i][1] = dense_chunk(i, q0, 1);
-        }
+        for (int i = 0; i < NPRE; ++i)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            uint32_t off;
+            int valid;
+            dense_at(i, q0, half, off, valid);
+            dbr[i][half] = bias_chunk_load(rb, off, valid, bias_bytes);
+          }
       }
     };
     // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
@@ -445,8 +462,18 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
           const int id = tid + i * NT;
-          const u32x4 a = i < NPRE ? dbr[i][0] : dense_chunk(i, qs * STEP, 0);
-          const u32x4 c = i < NPRE ? dbr[i][1] : dense_chunk(i, qs * STEP, 1);
+          u32x4 a, c;
+          if (i < NPRE) {
+            uint32_t off;
+            int valid;
+            dense_at(i, q0, 0, off, valid);
+            a = bias_chunk_finish(dbr[i][0], off, valid, bias_bytes);
+            dense_at(i, q0, 1, off, valid);
+            c = bias_chunk_finish(dbr[i][1], off, valid, bias_bytes);
+          } else {
+            a = dense_chunk(i, q0, 0);
+            c = dense_chunk(i, q0, 1);
+          }
           __bf16* dst = bt + 8 * (id % KCHK) * L::BS + 2 * (id / KCHK);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
@@ -713,11 +740,9 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       }
     };
 
-    const int nsteps = qs_end - qs_first;
-    if (nsteps > 0) {
-      load_step(qs_first);
-      store_step(0, qs_first, true);
-    }
+    if (nsteps > 0) load_step(qs_first);
+    if (short_item && wave == 0) pipe.resolve(lane);
+    if (nsteps > 0) store_step(0, qs_first, true);
     // the key fragments (loaded with the first tiles) are complete before the query loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     if (L::K1 && one_k) {
@@ -727,9 +752,6 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       for (int ks = 0; ks < D / 16; ++ks) *(bf16x8*)(kr1 + 16 * ks + 8 * g) = kf[ks];
     }
     __syncthreads();
-    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
-    const bool short_item = nsteps <= CLAIM_AHEAD;
-    if (short_item && wave == 0) pipe.claim(lane);
     const int claim_it = short_item ? -1 : nsteps - CLAIM_AHEAD;
     const int resolve_it = short_item ? -1 : nsteps - 2;
     for (int it = 0; it + 1 < nsteps; ++it) {
@@ -749,7 +771,6 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       __syncthreads();
       dq_step(qs_end - 1);
     }
-    if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
@@ -833,7 +854,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   std::conditional_t<FP8, Fp8RowTile<D, NT>, RowTile<D, NT>> tv;
   float rpv = 0.f;
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
-  u32x4 dbr[NDB];                   // dense bias chunks (8 keys of one query) of the next step
+  BiasRaw dbr[NDB];                 // dense bias chunks (8 keys of one query) of the next step
+  constexpr bool BIAS_RAW = !(D == 128 && (DB || WIN));
 
   ItemPipeT<HOME> pipe{p.xtk_q, p.bq, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
@@ -851,6 +873,10 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     // key steps [kb0, kb0 + steps) of query tile t
     const int t = item_field(dsc, IF_X), kb0 = WIN ? item_field(dsc, IF_Y) : 0;
     const int steps = item_field(dsc, IF_Z) - kb0;
+    // the next item: a short item takes its ticket now and reads its record right after this
+    // item's first loads; a longer one claims it CLAIM_AHEAD steps before its end
+    const bool short_item = steps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
     const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
     const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
     const int64_t boff = item_boff(dsc);
@@ -929,6 +955,14 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
+    // chunk i of this thread for key step j0: byte offset and valid element count
+    const uint32_t bias_bytes = (uint32_t)n * (uint32_t)m * 2u;
+    auto dense_at = [&](int i, int j0, uint32_t& off, int& valid) {
+      const int id = tid + i * NT;
+      const int qq = q0 + id / (STEP / 8), k0 = j0 + 8 * (id % (STEP / 8));
+      valid = qq < n ? min(8, m - k0) : 0;
+      off = ((uint32_t)qq * (uint32_t)m + (uint32_t)k0) * 2u;
+    };
     auto load_step = [&](int kt) {
       const int j0 = kt * STEP;
       if constexpr (BIAS == B_RELPOS) {
@@ -949,11 +983,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
         // [BM][STEP] block as chunks of 8 keys, consecutive lanes along a row
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
-          const int id = tid + i * NT;
-          const int qq = q0 + id / (STEP / 8), k0 = j0 + 8 * (id % (STEP / 8));
-          const int valid = qq < n ? min(8, m - k0) : 0;
-          dbr[i] = bias_chunk(rb, ((uint32_t)qq * (uint32_t)m + (uint32_t)k0) * 2u, valid,
-                        (uint32_t)n * (uint32_t)m * 2u);
+          uint32_t off;
+          int valid;
+          dense_at(i, j0, off, valid);
+          // (the bias-gradient and window kernels at d = 128 have no registers for the raw
+          // loads: they assemble the chunk at once)
+          if constexpr (!BIAS_RAW) dbr[i].x = bias_chunk(rb, off, valid, bias_bytes);
+          else dbr[i] = bias_chunk_load(rb, off, valid, bias_bytes);
         }
       }
     };
@@ -971,7 +1007,11 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
           const int id = tid + i * NT;
-          *(u32x4*)(bt + (id / (STEP / 8)) * L::BS + 8 * (id % (STEP / 8))) = dbr[i];
+          uint32_t off;
+          int valid;
+          dense_at(i, j0, off, valid);
+          *(u32x4*)(bt + (id / (STEP / 8)) * L::BS + 8 * (id % (STEP / 8))) =
+              BIAS_RAW ? bias_chunk_finish(dbr[i], off, valid, bias_bytes) : dbr[i].x;
         }
       }
     };
@@ -1205,10 +1245,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       }
     };
 
-    if (steps > 0) {
-      load_step(kb0);
-      store_step(0, kb0);
-    }
+    if (steps > 0) load_step(kb0);
+    if (short_item && wave == 0) pipe.resolve(lane);
+    if (steps > 0) store_step(0, kb0);
     // the query fragments (loaded with the first tiles) are complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     if (L::Q1 && one_q) {
@@ -1223,9 +1262,6 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       }
     }
     __syncthreads();
-    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
-    const bool short_item = steps <= CLAIM_AHEAD;
-    if (short_item && wave == 0) pipe.claim(lane);
     const int claim_it = short_item ? -1 : steps - CLAIM_AHEAD;
     const int resolve_it = short_item ? -1 : steps - 2;
     for (int it = 0; it + 1 < steps; ++it) {
@@ -1245,7 +1281,6 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       __syncthreads();
       dkdv_step(steps - 1);
     }
-    if (short_item && wave == 0) pipe.resolve(lane);
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 

@@ -105,25 +105,163 @@ void fwd_kernel(FwdParams p) {
   uint32_t vsc[FP8 ? V_LOADS : 1][4];
   float rp_val = 0.f;                                        // relpos table entry of this thread
   // Dense bias: NDB 16-byte chunks (8 keys of one query row) per thread and step, prefetched
-  // into registers with the K/V tiles unless registers run short (then loaded while staging).
+  // into registers with the K/V tiles.
   constexpr int NDB = BIAS == B_DENSE ? BM * (BN / 8) / NT : 1;
-  constexpr int NPRE = (D == 128 && NW == 4) ? 0 : NDB;
-  u32x4 dbr[NPRE > 0 ? NPRE : 1];
+  static_assert(!(BIAS == B_DENSE && D == 128 && NW == 4), "dense bias takes 64-row tiles");
+  BiasRaw dbr[NDB];
+
+  // Cross-item prefetch: the query fragment and first tiles of the next item are loaded before
+  // the last key step of the current one, so that a run of short items keeps loads in flight
+  // behind their compute and epilogues.  It needs registers for a second query fragment, which
+  // the 4-wave kernel at d = 128 does not have.
+  constexpr bool XPF = !(D == 128 && NW == 4);
+
+  // what one item's loads read, from its descriptor (wave-uniform)
+  struct Src {
+    rsrc_t rk, rv, rq, rks, rvs, rqs, rb;
+    int h, q0, n, m, kb, ke;
+  };
+  auto make_src = [&](const int* d) -> Src {
+    Src s;
+    s.h = item_field(d, IF_W) % H;
+    s.q0 = item_field(d, IF_X) * BM;
+    s.kb = item_field(d, IF_Y);
+    s.ke = item_field(d, IF_Z);
+    s.n = item_field(d, IF_N);
+    s.m = item_field(d, IF_M);
+    const int qo = item_field(d, IF_QO), ko = item_field(d, IF_KO);
+    // per-(sample, head) buffer resources: rows past the sample's end read as zero
+    const uint32_t kv_bytes = s.m > 0 ? ((uint32_t)(s.m - 1) * H + 1) * D * ES : 0;
+    const uint32_t q_bytes = s.n > 0 ? ((uint32_t)(s.n - 1) * H + 1) * D * ES : 0;
+    s.rk = make_rsrc((const uint8_t*)p.k + ((int64_t)ko * H + s.h) * D * ES, kv_bytes);
+    s.rv = make_rsrc((const uint8_t*)p.v + ((int64_t)ko * H + s.h) * D * ES, kv_bytes);
+    s.rq = make_rsrc((const uint8_t*)p.q + ((int64_t)qo * H + s.h) * D * ES, q_bytes);
+    s.rks = s.rk;
+    s.rvs = s.rv;
+    s.rqs = s.rq;
+    if constexpr (FP8) {
+      const uint32_t kvs = s.m > 0 ? ((uint32_t)(s.m - 1) * H + 1) * (D / 32) : 0;
+      const uint32_t qs = s.n > 0 ? ((uint32_t)(s.n - 1) * H + 1) * (D / 32) : 0;
+      s.rks = make_rsrc(p.k_sc + ((int64_t)ko * H + s.h) * (D / 32), kvs);
+      s.rvs = make_rsrc(p.v_sc + ((int64_t)ko * H + s.h) * (D / 32), kvs);
+      s.rqs = make_rsrc(p.q_sc + ((int64_t)qo * H + s.h) * (D / 32), qs);
+    }
+    s.rb = s.rk;
+    if constexpr (BIAS == B_DENSE)
+      s.rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * item_boff(d) +
+                           (int64_t)s.h * s.n * s.m,
+                       (uint32_t)s.n * (uint32_t)s.m * 2u);
+    return s;
+  };
+
+  // ---- query fragment (B operand: column = query row, k = head dim), loaded into the *_in
+  //      registers and copied to the working set once complete
+  constexpr int QK = FP8 ? D / 64 : D / 16;
+  i32x8 qf8_in[FP8 ? QK : 1];
+  int qsc_in[FP8 ? QK : 1];
+  bf16x8 qf_in[FP8 ? 1 : QK];
+  auto load_q = [&](const Src& s) {
+    const uint32_t qrow = (uint32_t)(s.q0 + wave * 32 + l32);
+    const uint32_t qoff = qrow * row_bytes;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) {
+        const u32x4 lo = ld16(s.rq, qoff + 64 * ks + 16 * g);
+        const u32x4 hi = ld16(s.rq, qoff + 64 * ks + 32 + 16 * g);
+        i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        qf8_in[ks] = v;
+        qsc_in[ks] = (int)ld1(s.rqs, qrow * sc_row_bytes + 2 * ks + g);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) qf_in[ks] = as_bf16x8(ld16(s.rq, qoff + 32 * ks + 16 * g));
+    }
+  };
+
+  // ---- staging: global -> registers for key step kt of an item
+  // [BM][BN] block of the dense bias as chunks of 8 keys, consecutive lanes along a row
+  // chunk i of this thread: byte offset and valid element count in the item's bias matrix
+  auto dense_at = [&](const Src& s, int i, int j0, uint32_t& off, int& valid) {
+    const int id = tid + i * NT;
+    const int qq = s.q0 + id / (BN / 8), k0 = j0 + 8 * (id % (BN / 8));
+    valid = qq < s.n ? min(8, s.m - k0) : 0;
+    off = ((uint32_t)qq * (uint32_t)s.m + (uint32_t)k0) * 2u;
+  };
+  auto load_step = [&](const Src& s, int kt) {
+    const int j0 = kt * BN;
+    if constexpr (BIAS == B_DENSE) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) {
+        uint32_t off;
+        int valid;
+        dense_at(s, i, j0, off, valid);
+        dbr[i] = bias_chunk_load(s.rb, off, valid, (uint32_t)s.n * (uint32_t)s.m * 2u);
+      }
+    }
+    if constexpr (BIAS == B_RELPOS) {
+      // diagonal table: T[x] = bias(dist = q0 + delta - j0 + BM - 1 - x), issued first so
+      // that waiting for it never waits for the tile loads behind it
+      if (tid < BM + BN - 1) {
+        const int dist = s.q0 + (s.m - s.n) - j0 + BM - 1 - tid;
+        const float* tab = (const float*)p.bias + (int64_t)s.h * p.num_buckets;
+        rp_val = tab[relpos_bucket(dist, p.num_buckets)];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < K_LOADS; ++i) {
+      const int id = tid + i * NT;
+      const int r = id / KCH, c = id % KCH;
+      kreg[i] = ld16(s.rk, (uint32_t)(j0 + r) * row_bytes + 16 * c);
+    }
+    if constexpr (FP8) {
+      if (tid < BN) {
+        const uint32_t base = (uint32_t)(j0 + tid) * sc_row_bytes;
+        uint32_t wv = 0;
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) wv |= ld1(s.rks, base + e) << (8 * e);
+        kscreg = wv;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_LOADS; ++i) {
+      const int id = tid + i * NT;
+      if (VBLK % NT != 0 && id >= VBLK) break;
+      const int cb = id % (D / 8), rbk = id / (D / 8);   // lanes along a row
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t row = (uint32_t)(j0 + 4 * rbk + rr);
+        if constexpr (FP8) {
+          v8[i][rr] = ld8(s.rv, row * row_bytes + 8 * cb);
+          vsc[i][rr] = ld1(s.rvs, row * sc_row_bytes + (8 * cb) / 32);
+        } else {
+          v16[i][rr] = ld16(s.rv, row * row_bytes + 16 * cb);
+        }
+      }
+    }
+  };
 
   ItemPipe pipe{p.xtk, p.items, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   __syncthreads();
+  bool pref = false;       // this item's query fragment and first tiles are already loading
   for (int buf = 0;; buf ^= 1) {
     const int* dsc = s_desc[buf];
     const int w = item_field(dsc, IF_W);
     if (w >= n_items) break;
-    const int h = w % H;
-    const int t = item_field(dsc, IF_X), kb = item_field(dsc, IF_Y), ke = item_field(dsc, IF_Z);
+    const Src cur = make_src(dsc);
+    const int h = cur.h;
+    const int kb = cur.kb, ke = cur.ke;
     const int slot = item_field(dsc, IF_SLOT);
-    const int qo = item_field(dsc, IF_QO), n = item_field(dsc, IF_N);
-    const int ko = item_field(dsc, IF_KO), m = item_field(dsc, IF_M);
+    const int qo = item_field(dsc, IF_QO), n = cur.n, m = cur.m;
     const int delta = m - n;
-    const int q0 = t * BM;
+    // the next item: a short item takes its ticket now and reads its record right after this
+    // item's first loads, so that both round trips overlap those loads; a longer one claims it
+    // CLAIM_AHEAD steps before its end
+    const int nsteps = ke - kb;
+    const bool short_item = nsteps <= CLAIM_AHEAD;
+    if (short_item && wave == 0) pipe.claim(lane);
+    const int q0 = cur.q0;
     const int qw0 = q0 + wave * 32;
     const int qil = wave * 32 + l32;        // tile-local query row of this lane
     const int qi = q0 + qil;                // sample-local query row
@@ -135,46 +273,9 @@ void fwd_kernel(FwdParams p) {
     if (WIN) wave_kbeg = max(0, qw0 + delta - W + 1);
     const bool wave_rows = qw0 < n;
 
-    // per-(sample, head) buffer resources: rows past the sample's end read as zero
-    const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * ES : 0;
-    const uint32_t q_bytes = n > 0 ? ((uint32_t)(n - 1) * H + 1) * D * ES : 0;
-    const rsrc_t rk = make_rsrc((const uint8_t*)p.k + ((int64_t)ko * H + h) * D * ES, kv_bytes);
-    const rsrc_t rv = make_rsrc((const uint8_t*)p.v + ((int64_t)ko * H + h) * D * ES, kv_bytes);
-    const rsrc_t rq = make_rsrc((const uint8_t*)p.q + ((int64_t)qo * H + h) * D * ES, q_bytes);
-    rsrc_t rks = rk, rvs = rv, rqs = rq;
-    if constexpr (FP8) {
-      const uint32_t kvs = m > 0 ? ((uint32_t)(m - 1) * H + 1) * (D / 32) : 0;
-      const uint32_t qs = n > 0 ? ((uint32_t)(n - 1) * H + 1) * (D / 32) : 0;
-      rks = make_rsrc(p.k_sc + ((int64_t)ko * H + h) * (D / 32), kvs);
-      rvs = make_rsrc(p.v_sc + ((int64_t)ko * H + h) * (D / 32), kvs);
-      rqs = make_rsrc(p.q_sc + ((int64_t)qo * H + h) * (D / 32), qs);
-    }
-    rsrc_t rb = rk;
-    if constexpr (BIAS == B_DENSE)
-      rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * item_boff(dsc) + (int64_t)h * n * m,
-                     (uint32_t)n * (uint32_t)m * 2u);
-
-    // ---- query fragment: B operand (column = query row, k = head dim)
-    constexpr int QK = FP8 ? D / 64 : D / 16;
-    i32x8 qf8[FP8 ? QK : 1];
-    int qsc[FP8 ? QK : 1];
-    bf16x8 qf[FP8 ? 1 : QK];
-    {
-      const uint32_t qoff = (uint32_t)qi * row_bytes;
-      if constexpr (FP8) {
-#pragma unroll
-        for (int ks = 0; ks < QK; ++ks) {
-          const u32x4 lo = ld16(rq, qoff + 64 * ks + 16 * g);
-          const u32x4 hi = ld16(rq, qoff + 64 * ks + 32 + 16 * g);
-          i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          qf8[ks] = v;
-          qsc[ks] = (int)ld1(rqs, (uint32_t)qi * sc_row_bytes + 2 * ks + g);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(rq, qoff + 32 * ks + 16 * g));
-      }
+    if (!pref) {
+      load_q(cur);
+      if (nsteps > 0) load_step(cur, kb);
     }
 
     f32x16 acc[D / 32];
@@ -183,63 +284,6 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     float m_run = NEG_INF, l_run = 0.f;
-
-    // ---- staging: global -> registers for key step kt
-    // [BM][BN] block of the dense bias as chunks of 8 keys, consecutive lanes along a row
-    auto dense_chunk = [&](int i, int j0) -> u32x4 {
-      const int id = tid + i * NT;
-      const int qq = q0 + id / (BN / 8), k0 = j0 + 8 * (id % (BN / 8));
-      const int valid = qq < n ? min(8, m - k0) : 0;
-      return bias_chunk(rb, ((uint32_t)qq * (uint32_t)m + (uint32_t)k0) * 2u, valid,
-                        (uint32_t)n * (uint32_t)m * 2u);
-    };
-    auto load_step = [&](int kt) {
-      const int j0 = kt * BN;
-      if constexpr (BIAS == B_DENSE) {
-#pragma unroll
-        for (int i = 0; i < NPRE; ++i) dbr[i] = dense_chunk(i, j0);
-      }
-      if constexpr (BIAS == B_RELPOS) {
-        // diagonal table: T[x] = bias(dist = q0 + delta - j0 + BM - 1 - x), issued first so
-        // that waiting for it never waits for the tile loads behind it
-        if (tid < BM + BN - 1) {
-          const int dist = q0 + delta - j0 + BM - 1 - tid;
-          const float* tab = (const float*)p.bias + (int64_t)h * p.num_buckets;
-          rp_val = tab[relpos_bucket(dist, p.num_buckets)];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < K_LOADS; ++i) {
-        const int id = tid + i * NT;
-        const int r = id / KCH, c = id % KCH;
-        kreg[i] = ld16(rk, (uint32_t)(j0 + r) * row_bytes + 16 * c);
-      }
-      if constexpr (FP8) {
-        if (tid < BN) {
-          const uint32_t base = (uint32_t)(j0 + tid) * sc_row_bytes;
-          uint32_t wv = 0;
-#pragma unroll
-          for (int e = 0; e < D / 32; ++e) wv |= ld1(rks, base + e) << (8 * e);
-          kscreg = wv;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < V_LOADS; ++i) {
-        const int id = tid + i * NT;
-        if (VBLK % NT != 0 && id >= VBLK) break;
-        const int cb = id % (D / 8), rbk = id / (D / 8);   // lanes along a row
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t row = (uint32_t)(j0 + 4 * rbk + rr);
-          if constexpr (FP8) {
-            v8[i][rr] = ld8(rv, row * row_bytes + 8 * cb);
-            vsc[i][rr] = ld1(rvs, row * sc_row_bytes + (8 * cb) / 32);
-          } else {
-            v16[i][rr] = ld16(rv, row * row_bytes + 16 * cb);
-          }
-        }
-      }
-    };
 
     // ---- staging: registers -> LDS stage `st`
     auto store_step = [&](int st, int kt) {
@@ -293,23 +337,39 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
           const int id = tid + i * NT;
+          uint32_t off;
+          int valid;
+          dense_at(cur, i, kt * BN, off, valid);
           *(u32x4*)(bt + (id / (BN / 8)) * L::BS + 8 * (id % (BN / 8))) =
-              i < NPRE ? dbr[i] : dense_chunk(i, kt * BN);
+              bias_chunk_finish(dbr[i], off, valid, (uint32_t)n * (uint32_t)m * 2u);
         }
       }
     };
 
-    const int nsteps = ke - kb;
-    if (nsteps > 0) {
-      load_step(kb);
-      store_step(0, kb);
-    }
+    if (short_item && wave == 0) pipe.resolve(lane);
+    if (nsteps > 0) store_step(0, kb);
+    if (short_item && wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
     // the query fragment (loaded with the first tiles) is complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // the working copy (with prefetch, the *_in registers take the next item's fragment
+    // during the last key step)
+    constexpr int QW8 = XPF && FP8 ? QK : 1, QW = XPF && !FP8 ? QK : 1;
+    i32x8 qf8_w[QW8];
+    int qsc_w[QW8];
+    bf16x8 qf_w[QW];
+    if constexpr (XPF) {
+#pragma unroll
+      for (int ks = 0; ks < QW8; ++ks) {
+        qf8_w[ks] = qf8_in[ks];
+        qsc_w[ks] = qsc_in[ks];
+      }
+#pragma unroll
+      for (int ks = 0; ks < QW; ++ks) qf_w[ks] = qf_in[ks];
+    }
+    auto& qf8 = [&]() -> auto& { if constexpr (XPF) return qf8_w; else return qf8_in; }();
+    auto& qsc = [&]() -> auto& { if constexpr (XPF) return qsc_w; else return qsc_in; }();
+    auto& qf = [&]() -> auto& { if constexpr (XPF) return qf_w; else return qf_in; }();
     __syncthreads();
-    // the next item: short items claim it now, longer ones CLAIM_AHEAD steps before their end
-    const bool short_item = nsteps <= CLAIM_AHEAD;
-    if (short_item && wave == 0) pipe.claim(lane);
     // one key step on LDS stage it&1 (the loop is peeled so that its loads and stores are
     // unconditional: no load can be pending across the back edge)
     auto compute_step = [&](int it) {
@@ -469,21 +529,31 @@ void fwd_kernel(FwdParams p) {
         }
       }
     };
+    // a longer item claims the next one CLAIM_AHEAD steps before its end and publishes its
+    // descriptor before the barrier ahead of its last step, where the prefetch reads it
     const int claim_it = short_item ? -1 : nsteps - CLAIM_AHEAD;
-    const int resolve_it = short_item ? -1 : nsteps - 2;
+    const int resolve_it = short_item ? -1 : nsteps - 3;
+    const int publish_it = short_item ? -1 : nsteps - 2;
     for (int it = 0; it + 1 < nsteps; ++it) {
       if (it == claim_it && wave == 0) pipe.claim(lane);
       if (it == resolve_it && wave == 0) pipe.resolve(lane);
-      load_step(kb + it + 1);
+      load_step(cur, kb + it + 1);
       compute_step(it);
+      if (it == publish_it && wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
       store_step((it + 1) & 1, kb + it + 1);
       __syncthreads();
     }
+    pref = false;
+    if constexpr (XPF) {
+      const int* nd = s_desc[buf ^ 1];
+      if (item_field(nd, IF_W) < n_items) {
+        const Src nx = make_src(nd);
+        load_q(nx);
+        if (nx.ke > nx.kb) load_step(nx, nx.kb);
+        pref = true;
+      }
+    }
     if (nsteps > 0) compute_step(nsteps - 1);
-    if (short_item && wave == 0) pipe.resolve(lane);
-    // publish the next descriptor before the epilogue's stores: waiting for its record load
-    // after them would also wait for the stores to complete
-    if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     // ---- epilogue
     float l_tot = l_run;
@@ -603,7 +673,10 @@ template <int D, int NW, int MODE, bool FP8, bool WIN>
 hipError_t run_fwd_win(const FwdParams& p, int64_t mi, int64_t mc, int cu, hipStream_t s) {
   switch (p.bias_kind) {
     case JFA_BIAS_RELPOS: return run_fwd<D, NW, MODE, B_RELPOS, FP8, WIN>(p, mi, mc, cu, s);
-    case JFA_BIAS_DENSE: return run_fwd<D, NW, MODE, B_DENSE, FP8, WIN>(p, mi, mc, cu, s);
+    case JFA_BIAS_DENSE:
+      // the tile configuration takes 64-row tiles for a dense bias at d = 128
+      if constexpr (D == 128 && NW == 4) return hipErrorInvalidValue;
+      else return run_fwd<D, NW, MODE, B_DENSE, FP8, WIN>(p, mi, mc, cu, s);
     default: return run_fwd<D, NW, MODE, B_NONE, FP8, WIN>(p, mi, mc, cu, s);
   }
 }

@@ -285,35 +285,51 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return p
 // five dwords that cover the chunk, shifted by one element when `off` is not dword-aligned:
 // sub-dword loads of the same bytes cost several times more.  The range check drops a dword
 // that only partly lies in the buffer, so a final element in such a dword is loaded alone.
-__device__ __forceinline__ u32x4 bias_chunk(rsrc_t r, uint32_t off, int valid, uint32_t size) {
-  u32x4 v = {0u, 0u, 0u, 0u};
+// The work is split in two: bias_chunk_load only issues the loads (into raw registers, so that
+// a prefetch does not wait for them), bias_chunk_finish assembles the chunk once they are
+// needed; both take the same (off, valid, size).
+struct BiasRaw {
+  u32x4 x;          // the four dwords from off rounded down to a dword
+  uint32_t y;       // the dword after them
+  uint32_t z;       // the final element of the buffer, when it sits in a partial dword
+};
+__device__ __forceinline__ bool bias_chunk_tail(uint32_t off, int valid, uint32_t size) {
+  return valid > 0 && (size & 2u) && off + 2u * (uint32_t)(valid - 1) + 2u == size;
+}
+__device__ __forceinline__ BiasRaw bias_chunk_load(rsrc_t r, uint32_t off, int valid,
+                                                   uint32_t size) {
+  BiasRaw b{{0u, 0u, 0u, 0u}, 0u, 0u};
   if (valid > 0) {
     const uint32_t base = off & ~3u;
-    const u32x4 x = ld16(r, base);
-    const uint32_t y = ld4(r, base + 16);
-    if (off & 2u) {
-      v[0] = __builtin_amdgcn_alignbyte(x[1], x[0], 2);
-      v[1] = __builtin_amdgcn_alignbyte(x[2], x[1], 2);
-      v[2] = __builtin_amdgcn_alignbyte(x[3], x[2], 2);
-      v[3] = __builtin_amdgcn_alignbyte(y, x[3], 2);
-    } else {
-      v = x;
-    }
-    const uint32_t last = off + 2u * (uint32_t)(valid - 1);
-    if ((size & 2u) && last + 2u == size) {
-      const int e = valid - 1;
-      const uint32_t sh = 16u * (uint32_t)(e & 1);
-      v[e >> 1] = (v[e >> 1] & ~(0xFFFFu << sh)) | (ld2(r, last) << sh);
-    }
+    b.x = ld16(r, base);
+    b.y = ld4(r, base + 16);
+    if (bias_chunk_tail(off, valid, size)) b.z = ld2(r, off + 2u * (uint32_t)(valid - 1));
   }
-  if (valid < 8) {
+  return b;
+}
+__device__ __forceinline__ u32x4 bias_chunk_finish(const BiasRaw& b, uint32_t off, int valid,
+                                                   uint32_t size) {
+  u32x4 v = b.x;
+  if (off & 2u) {
+    v[0] = __builtin_amdgcn_alignbyte(b.x[1], b.x[0], 2);
+    v[1] = __builtin_amdgcn_alignbyte(b.x[2], b.x[1], 2);
+    v[2] = __builtin_amdgcn_alignbyte(b.x[3], b.x[2], 2);
+    v[3] = __builtin_amdgcn_alignbyte(b.y, b.x[3], 2);
+  }
+  if (bias_chunk_tail(off, valid, size)) {
+    const int e = valid - 1;
+    const uint32_t sh = 16u * (uint32_t)(e & 1);
+    v[e >> 1] = (v[e >> 1] & ~(0xFFFFu << sh)) | (b.z << sh);
+  }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t keep = 2 * w + 1 < valid ? 0xFFFFFFFFu : (2 * w < valid ? 0xFFFFu : 0u);
-      v[w] &= keep;
-    }
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t keep = 2 * w + 1 < valid ? 0xFFFFFFFFu : (2 * w < valid ? 0xFFFFu : 0u);
+    v[w] &= keep;
   }
   return v;
+}
+__device__ __forceinline__ u32x4 bias_chunk(rsrc_t r, uint32_t off, int valid, uint32_t size) {
+  return bias_chunk_finish(bias_chunk_load(r, off, valid, size), off, valid, size);
 }
 
 // Sum of the two bf16 halves of `w` added to `acc` (fp32).
