@@ -305,6 +305,9 @@ jfa_status jfa_forward(const jfa_problem* p, const void* q, const void* k, const
   const bool fp8 = p->dtype == JFA_MXFP8_E4M3;
   if (!q || !k || !v || !o || !q_offsets || !kv_offsets || !workspace) return JFA_ERR_INVALID_ARG;
   if (fp8 && (!q_scale || !k_scale || !v_scale)) return JFA_ERR_INVALID_ARG;
+  // a key's scale bytes are read as one word
+  if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return JFA_ERR_INVALID_ARG;
   if ((p->bias_kind != JFA_BIAS_NONE) != (bias != nullptr)) return JFA_ERR_INVALID_ARG;
   if (p->mode == JFA_MODE_SOFTMAX && !lse) return JFA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -477,6 +480,9 @@ jfa_status jfa_backward_mxfp8(const jfa_problem* p, const uint8_t* q, const uint
                               size_t workspace_bytes, void* stream) {
   if (!p) return JFA_ERR_INVALID_ARG;
   if (p->dtype != JFA_MXFP8_E4M3) return JFA_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      !aligned(dout_scale, 4))
+    return JFA_ERR_INVALID_ARG;
   Fp8Scales sc;
   sc.q = q_scale;
   sc.k = k_scale;

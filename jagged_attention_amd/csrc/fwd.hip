@@ -216,11 +216,11 @@ void fwd_kernel(FwdParams p) {
     }
     if constexpr (FP8) {
       if (tid < BN) {
+        // the key's D/32 scale bytes are contiguous and aligned: one load, block e in byte e
+        // (assembling them from byte loads would wait for the loads here)
         const uint32_t base = (uint32_t)(j0 + tid) * sc_row_bytes;
-        uint32_t wv = 0;
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e) wv |= ld1(s.rks, base + e) << (8 * e);
-        kscreg = wv;
+        static_assert(D == 128 || D == 64, "scale word");
+        kscreg = D == 128 ? ld4(s.rks, base) : ld2(s.rks, base);
       }
     }
 #pragma unroll
