@@ -44,6 +44,8 @@ constexpr int TS = STEP + 8;   // stride (bf16) of a transposed tile row
 constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 
 // --------------------------------------------------------------- tile staging
+// The NT threads that stage a tile are the first NT of the workgroup or, in a workgroup of more
+// threads, any NT consecutive ones (thread index taken modulo NT).
 // A STEP x D bf16 tile is moved as blocks of 4 rows x 8 dims (one 16-byte load per row).
 // Block id -> (row block rb, dim block cb): within each 16 ids, 4 row blocks x 4 dim blocks,
 // so that a quarter wave's row-major writes cover all banks.
@@ -61,7 +63,7 @@ struct Tile {
   __device__ __forceinline__ void load(rsrc_t r, uint32_t row_bytes, int r0) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       if (NBLK % NT != 0 && id >= NBLK) break;
       int rb, cb;
       blk_of(id, rb, cb);
@@ -76,7 +78,7 @@ struct Tile {
   template <int P>
   __device__ __forceinline__ void store_part(__bf16* rows, __bf16* tr) const {
     constexpr int i = P / 6, part = P % 6;
-    const int id = threadIdx.x + i * NT;
+    const int id = (int)(threadIdx.x % NT) + i * NT;
     if (NBLK % NT != 0 && id >= NBLK) return;
     int rb, cb;
     blk_of(id, rb, cb);
@@ -97,7 +99,7 @@ struct Tile {
   __device__ __forceinline__ void store(__bf16* rows, __bf16* tr) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       if (NBLK % NT != 0 && id >= NBLK) break;
       int rb, cb;
       blk_of(id, rb, cb);
@@ -129,14 +131,14 @@ struct RowTile {
   __device__ __forceinline__ void load(rsrc_t r, uint32_t row_bytes, int r0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       v[i] = ld16(r, (uint32_t)(r0 + id / KCH) * row_bytes + 16 * (id % KCH));
     }
   }
   __device__ __forceinline__ void store(__bf16* rows) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       *(u32x4*)(rows + (id / KCH) * tile_row_stride<D>() + 8 * (id % KCH)) = v[i];
     }
   }
@@ -158,7 +160,7 @@ struct Fp8Tile {
                                        int r0) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       if (NBLK % NT != 0 && id >= NBLK) break;
       int rb, cb;
       blk_of(id, rb, cb);
@@ -176,7 +178,7 @@ struct Fp8Tile {
   __device__ __forceinline__ void store_part(__bf16* rows, __bf16* tr) const {
     constexpr int i = P / 6, part = P % 6;
     static_assert(part < 2, "row stores only");
-    const int id = threadIdx.x + i * NT;
+    const int id = (int)(threadIdx.x % NT) + i * NT;
     if (NBLK % NT != 0 && id >= NBLK) return;
     int rb, cb;
     blk_of(id, rb, cb);
@@ -188,7 +190,7 @@ struct Fp8Tile {
   __device__ __forceinline__ void store(__bf16* rows) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       if (NBLK % NT != 0 && id >= NBLK) break;
       int rb, cb;
       blk_of(id, rb, cb);
@@ -212,7 +214,7 @@ struct Fp8RowTile {
                                        int r0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       const uint32_t row = (uint32_t)(r0 + id / KCH);
       c[i] = ld8(rc, row * crow + 8 * (id % KCH));
       sc[i] = ld1(rs, row * srow + (8 * (id % KCH)) / 32);
@@ -221,7 +223,7 @@ struct Fp8RowTile {
   __device__ __forceinline__ void store(__bf16* rows) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = (int)(threadIdx.x % NT) + i * NT;
       *(bf16x8*)(rows + (id / KCH) * tile_row_stride<D>() + 8 * (id % KCH)) =
           dequant8_bf16(c[i], sc[i]);
     }
@@ -788,7 +790,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
 }
 
 // ================================================= query-stationary dQ
-template <int D, int NW, int BIAS>
+template <int D, int NW, int BIAS, bool SPLIT = false>
 struct QLds {
   static constexpr int BM = 32 * NW;
   static constexpr int RS = tile_row_stride<D>();
@@ -812,7 +814,11 @@ struct QLds {
   static constexpr int Q1_DR = Q1_QR + BM * RS * 2;
   static constexpr int Q1_P = Q1_DR + BM * RS * 2;
   static constexpr int Q1_DS = Q1_P + BM * PS * 2;
-  static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 : 0);
+  // SPLIT (two more waves compute the dK / dV of the previous step while the query waves work
+  // on the current one): P / dS double-buffered, PDS bytes apart
+  static constexpr int PDS = SPLIT ? 2 * BM * PS * 2 : 0;
+  static constexpr int TOTAL = 2 * STAGE + (Q1 ? 2 * BM * RS * 2 + 2 * BM * PS * 2 + PDS : 0);
+  static_assert(!SPLIT || (Q1 && TOTAL <= 160 * 1024 - 512), "LDS of the split pass");
   // bias gradient of a relative-position table of at most DB_NB buckets: per-lane bucket sums,
   // [DB_NB][64] floats per wave (bucket-major, so the 64 lanes hit 64 banks), in place of the
   // single-pass class's area, which that pass does not use
@@ -828,15 +834,28 @@ struct QLds {
 // relative-position table: per-lane running sums by bucket, flushed on a change of bucket into
 // the lane's own slots, in LDS for at most DB_NB buckets and else in its partial row in memory;
 // later kernels reduce the rows in a fixed order).  DB runs without the single-pass classes.
-template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN, bool FP8>
+//
+// SPLIT: a workgroup of 4 waves for 64-row tiles.  Waves 0, 1 own the query rows (S, dP, dS, dQ
+// as above); waves 2, 3 stage the K / V tiles and, for a one-query-tile sample, compute the dK,
+// dV rows of the previous key step from its P / dS while the query waves work on the current
+// one, so every SIMD has a wave.
+template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN, bool FP8,
+          bool SPLIT = false>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
-  using L = QLds<D, NW, BIAS>;
-  constexpr int BM = L::BM, NT = NW * 64, RS = L::RS;
+  constexpr int QW = SPLIT ? 2 : NW;                 // waves that own query rows
+  static_assert(!SPLIT || (NW == 4 && !DB && !FP8 && BIAS != B_DENSE), "split pass");
+  using L = QLds<D, QW, BIAS, SPLIT>;
+  constexpr int BM = L::BM, RS = L::RS;
+  constexpr int NT = SPLIT ? 128 : NW * 64;          // threads that stage K / V (and the bias)
   __shared__ int s_desc[2][IF_WORDS];
 
   if (p.hdr->status != JFA_OK) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool qrole = !SPLIT || wave < QW;             // owns query rows
+  const bool srole = !SPLIT || wave >= QW;            // stages the tiles
+  const int tid = SPLIT ? (int)threadIdx.x - 128 : (int)threadIdx.x;   // staging thread index
+  const int kvw = SPLIT ? wave - QW : wave;           // key block of the dK / dV step
   const int g = lane >> 5, l32 = lane & 31;
   const int H = p.H;
   const int64_t n_items = (int64_t)p.hdr->counts[2] * H;
@@ -917,10 +936,12 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                      (uint32_t)n * (uint32_t)m * 2u);
 
     bf16x8 qf[D / 16], dof[D / 16];
+    if (qrole) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = load_frag8<D, FP8>(rq, rqs, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
-      dof[ks] = load_frag8<D, FP8>(rdo, rdos, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        qf[ks] = load_frag8<D, FP8>(rq, rqs, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
+        dof[ks] = load_frag8<D, FP8>(rdo, rdos, (uint32_t)qi, in_row, sc_row, 16 * ks + 8 * g);
+      }
     }
     float lse2 = 0.f, dlt = 0.f;
     // bias gradient, relative-position table: the bucket being summed and its running sum
@@ -943,7 +964,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       }
     };
     if constexpr (MODE == MODE_SOFTMAX) {
-      if (qi < n) {
+      if (qrole && qi < n) {
         lse2 = p.lse[(int64_t)h * p.total_q + qo + qi] * LOG2E;
         dlt = p.delta[(int64_t)h * p.total_q + qo + qi];
       }
@@ -1022,9 +1043,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       if (!wave_rows || j0 >= wave_kend || (WIN && j0 + STEP <= wave_kbeg)) {
         if (L::Q1 && one_q) {     // this wave's queries contribute nothing to this step's dK, dV
           uint32_t* pq = reinterpret_cast<uint32_t*>(
-              reinterpret_cast<__bf16*>(lds + L::Q1_P) + qil * L::PS);
+              reinterpret_cast<__bf16*>(lds + L::Q1_P + (it & 1) * L::PDS) + qil * L::PS);
           uint32_t* dq = reinterpret_cast<uint32_t*>(
-              reinterpret_cast<__bf16*>(lds + L::Q1_DS) + qil * L::PS);
+              reinterpret_cast<__bf16*>(lds + L::Q1_DS + (it & 1) * L::PDS) + qil * L::PS);
 #pragma unroll
           for (int i = 0; i < STEP / 2 / 2; ++i) {
             pq[2 * i + g] = 0u;
@@ -1188,8 +1209,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       if (L::Q1 && one_q) {
         // P and dS [query][key] of this step: pair p of block blk holds keys k, k + 1 with
         // k = 32 blk + 8(p/2) + 4g + 2(p%2)
-        __bf16* pr = reinterpret_cast<__bf16*>(lds + L::Q1_P) + qil * L::PS;
-        __bf16* dr = reinterpret_cast<__bf16*>(lds + L::Q1_DS) + qil * L::PS;
+        __bf16* pr = reinterpret_cast<__bf16*>(lds + L::Q1_P + (it & 1) * L::PDS) + qil * L::PS;
+        __bf16* dr = reinterpret_cast<__bf16*>(lds + L::Q1_DS + (it & 1) * L::PDS) + qil * L::PS;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -1203,22 +1224,23 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 
     // dK, dV of a key step of a one-query-tile sample: dV^T = dO^T P and dK^T = scale Q^T dS
     // over the tile's queries, operands read with transposing LDS reads in natural query order
-    // (k = 8g + j <-> query 16 kc + 8g + j).  Wave w owns keys 32w .. 32w + 31 of the step and
-    // writes their rows through its staging area in the step's (now idle) LDS stage.
+    // (k = 8g + j <-> query 16 kc + 8g + j).  Key wave w owns keys 32w .. 32w + 31 of the step
+    // and writes their rows through its staging area in the step's (now idle) LDS stage or
+    // (SPLIT, where no stage is idle) straight from the accumulators, 4 dims per lane and store.
     auto dkdv_step = [&](int kt) {
       if constexpr (L::Q1) {
         const __bf16* qr1 = reinterpret_cast<const __bf16*>(lds + L::Q1_QR);
         const __bf16* dr1 = reinterpret_cast<const __bf16*>(lds + L::Q1_DR);
-        const __bf16* pt = reinterpret_cast<const __bf16*>(lds + L::Q1_P);
-        const __bf16* st = reinterpret_cast<const __bf16*>(lds + L::Q1_DS);
+        const __bf16* pt = reinterpret_cast<const __bf16*>(lds + L::Q1_P + (kt & 1) * L::PDS);
+        const __bf16* st = reinterpret_cast<const __bf16*>(lds + L::Q1_DS + (kt & 1) * L::PDS);
         const int trq = (8 * (lane >> 5) + ((lane & 15) >> 2)) * RS + 16 * ((lane >> 4) & 1) +
                         4 * (lane & 3);
         const int trp = (8 * (lane >> 5) + ((lane & 15) >> 2)) * L::PS +
                         16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         __bf16* ost = reinterpret_cast<__bf16*>(lds + (kt & 1) * L::STAGE +
-                                                wave * out_stage_bytes<D>());
+                                                kvw * out_stage_bytes<D>());
         const uint32_t kv_bytes = m > 0 ? ((uint32_t)(m - 1) * H + 1) * D * 2 : 0;
-        const uint32_t row0 = (uint32_t)((kb0 + kt) * STEP + 32 * wave) * row_bytes;
+        const uint32_t row0 = (uint32_t)((kb0 + kt) * STEP + 32 * kvw) * row_bytes;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {       // 0: dV = P^T dO, 1: dK = s dS^T Q
           const __bf16* xa = which ? qr1 : dr1;
@@ -1231,7 +1253,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
             for (int kc = 0; kc < BM / 16; ++kc) {
               const __bf16* pa = xa + trq + 16 * kc * RS + db * 32;
-              const __bf16* pb = xb + trp + 16 * kc * L::PS + 32 * wave;
+              const __bf16* pb = xb + trp + 16 * kc * L::PS + 32 * kvw;
               const u32x2 a0 = lds_read_tr16(pa), a1 = lds_read_tr16(pa + 4 * RS);
               const u32x2 b0 = lds_read_tr16(pb), b1 = lds_read_tr16(pb + 4 * L::PS);
               o[db] = mfma_bf16(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}),
@@ -1240,17 +1262,31 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
           }
           const rsrc_t r = make_rsrc((__bf16*)(which ? p.dk : p.dv) + ((int64_t)ko * H + h) * D,
                                      kv_bytes);
-          store_rows_via_lds<D>(o, which ? p.scale : 1.0f, ost, r, row0, row_bytes, lane);
+          const float mul = which ? p.scale : 1.0f;
+          if constexpr (SPLIT) {
+            // lane (key l32, g) holds dims 32 db + 8 jq + 4 g + 0..3 of its key row
+            const uint32_t row = row0 + (uint32_t)l32 * row_bytes;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+              for (int jq = 0; jq < 4; ++jq) {
+                const u32x2 v = {pack2bf(o[db][4 * jq] * mul, o[db][4 * jq + 1] * mul),
+                                 pack2bf(o[db][4 * jq + 2] * mul, o[db][4 * jq + 3] * mul)};
+                st8(v, r, row + 2u * (uint32_t)(db * 32 + 8 * jq + 4 * g));
+              }
+          } else {
+            store_rows_via_lds<D>(o, mul, ost, r, row0, row_bytes, lane);
+          }
         }
       }
     };
 
-    if (steps > 0) load_step(kb0);
+    if (steps > 0 && srole) load_step(kb0);
     if (short_item && wave == 0) pipe.resolve(lane);
-    if (steps > 0) store_step(0, kb0);
+    if (steps > 0 && srole) store_step(0, kb0);
     // the query fragments (loaded with the first tiles) are complete before the key loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (L::Q1 && one_q) {
+    if (L::Q1 && one_q && qrole) {
       // the tile's Q and dO rows for the dK / dV steps: lane (query, g) holds head dims
       // 16 ks + 8g + 0..7
       __bf16* q1 = reinterpret_cast<__bf16*>(lds + L::Q1_QR) + qil * RS;
@@ -1264,22 +1300,41 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     __syncthreads();
     const int claim_it = short_item ? -1 : steps - CLAIM_AHEAD;
     const int resolve_it = short_item ? -1 : steps - 2;
-    for (int it = 0; it + 1 < steps; ++it) {
-      if (it == claim_it && wave == 0) pipe.claim(lane);
-      if (it == resolve_it && wave == 0) pipe.resolve(lane);
-      load_step(kb0 + it + 1);
-      compute_step(it);
-      if (one_q) {
+    if constexpr (SPLIT) {
+      // step it: the query waves compute it from LDS stage it&1 and write its P / dS; the key
+      // waves stage step it + 1 into the other stage and turn the P / dS of step it - 1 into
+      // dK, dV rows
+      for (int it = 0; it < steps; ++it) {
+        if (it == claim_it && wave == 0) pipe.claim(lane);
+        if (it == resolve_it && wave == 0) pipe.resolve(lane);
+        if (qrole) {
+          compute_step(it);
+        } else {
+          if (it + 1 < steps) load_step(kb0 + it + 1);
+          if (one_q && it > 0) dkdv_step(it - 1);
+          if (it + 1 < steps) store_step((it + 1) & 1, kb0 + it + 1);
+        }
         __syncthreads();
-        dkdv_step(it);
       }
-      store_step((it + 1) & 1, kb0 + it + 1);
-      __syncthreads();
-    }
-    if (steps > 0) compute_step(steps - 1);
-    if (one_q && steps > 0) {
-      __syncthreads();
-      dkdv_step(steps - 1);
+      if (!qrole && one_q && steps > 0) dkdv_step(steps - 1);
+    } else {
+      for (int it = 0; it + 1 < steps; ++it) {
+        if (it == claim_it && wave == 0) pipe.claim(lane);
+        if (it == resolve_it && wave == 0) pipe.resolve(lane);
+        load_step(kb0 + it + 1);
+        compute_step(it);
+        if (one_q) {
+          __syncthreads();
+          dkdv_step(it);
+        }
+        store_step((it + 1) & 1, kb0 + it + 1);
+        __syncthreads();
+      }
+      if (steps > 0) compute_step(steps - 1);
+      if (one_q && steps > 0) {
+        __syncthreads();
+        dkdv_step(steps - 1);
+      }
     }
     // publish the next descriptor before the epilogue's stores (see the forward kernel)
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
@@ -1298,11 +1353,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
         for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
       }
     }
-    const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
-    // through the stage that the last key step left free (rows of this wave only)
-    __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
-                                            wave * out_stage_bytes<D>());
-    store_rows_via_lds<D>(acc, p.scale, ost, rdq, (uint32_t)qw0 * row_bytes, row_bytes, lane);
+    if (qrole) {
+      const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
+      // through the stage that the last key step left free (rows of this wave only)
+      __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
+                                              wave * out_stage_bytes<D>());
+      store_rows_via_lds<D>(acc, p.scale, ost, rdq, (uint32_t)qw0 * row_bytes, row_bytes, lane);
+    }
     __syncthreads();
   }
 }
@@ -1317,6 +1374,13 @@ template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_kernel(BwdParams p) {
   q_pass<D, NW, MODE, BIAS, true, false, WIN, FP8>(p);
+}
+
+// The query-stationary pass for 64-row tiles on 4 waves (see q_pass, SPLIT).
+template <int D, int MODE, int BIAS, bool WIN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_q1_kernel(BwdParams p) {
+  q_pass<D, 4, MODE, BIAS, true, false, WIN, false, true>(p);
 }
 
 // Both passes in one persistent launch (they are independent): every workgroup first works
@@ -1419,8 +1483,14 @@ hipError_t run_bk(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) 
 }
 template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8 = false>
 hipError_t run_bq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS, WIN, FP8>, QLds<D, NW, BIAS>::TOTAL,
-                           NW * 64, max_items, cu, p, FP8 ? "jfa_bwd_dq_mxfp8" : "jfa_bwd_dq", s);
+  // 64-row tiles of bf16 inputs without a dense bias: the 4-wave variant
+  if constexpr (NW == 2 && !FP8 && BIAS != B_DENSE)
+    return launch_persistent(bwd_q1_kernel<D, MODE, BIAS, WIN>, QLds<D, 2, BIAS, true>::TOTAL,
+                             256, max_items, cu, p, "jfa_bwd_dq", s);
+  else
+    return launch_persistent(bwd_q_kernel<D, NW, MODE, BIAS, WIN, FP8>, QLds<D, NW, BIAS>::TOTAL,
+                             NW * 64, max_items, cu, p, FP8 ? "jfa_bwd_dq_mxfp8" : "jfa_bwd_dq",
+                             s);
 }
 
 template <int D, int NW, int MODE, int BIAS, bool WIN, bool FP8 = false>
