@@ -297,14 +297,21 @@ def kernel_times(w, steps, flush=None):
         w.step()
         jfa.jfa_set_kernel_timing(False)
     torch.cuda.synchronize()
+    names = ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
+             "jfa_fwd_bf16", "jfa_fwd_mxfp8", "jfa_fwd_f32", "jfa_fwd_combine",
+             "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq",
+             "jfa_bwd_kvq_mxfp8", "jfa_bwd_dkdv_mxfp8", "jfa_bwd_dq_mxfp8",
+             "jfa_bwd_dkdv_f32", "jfa_bwd_dq_f32",
+             "jfa_dbias_zero", "jfa_dbias_dq", "jfa_dbias_reduce")
+    # the library matches names by prefix: take the longer names' launches out of each total
+    raw = {name: jfa.jfa_kernel_timing(name) for name in names}
     out = {}
-    for name in ("jfa_offsets", "jfa_block_offsets", "jfa_schedule", "jfa_quant_mxfp8",
-                 "jfa_fwd_bf16", "jfa_fwd_mxfp8",
-                 "jfa_fwd_f32",
-                 "jfa_fwd_combine", "jfa_bwd_kvq", "jfa_bwd_dkdv", "jfa_bwd_dq",
-                 "jfa_bwd_kvq_mxfp8", "jfa_bwd_dkdv_mxfp8", "jfa_bwd_dq_mxfp8",
-                 "jfa_dbias_zero", "jfa_dbias_dq", "jfa_dbias_reduce"):
-        ms, n = jfa.jfa_kernel_timing(name)
+    for name in names:
+        ms, n = raw[name]
+        for other in names:
+            if other != name and other.startswith(name):
+                ms -= raw[other][0]
+                n -= raw[other][1]
         if n:
             out[name] = dict(avg_ms=ms / n, launches=n)
     jfa.jfa_kernel_timing_reset()
@@ -447,24 +454,93 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None
                    passes="fwd" if not w.with_backward else "fwd+bwd")
 
 
+def kernel_work(w):
+    """Per-launch work of each attention kernel of the step: {kernel: (useful flops, executed
+    flops, algorithmic HBM bytes)}.  The backward's samples fall into three classes (the
+    scheduler's test, from the tile configuration): one query tile (the query-stationary pass
+    also writes dK, dV: 10 d useful per pair), else one key tile at d = 64 (the key-stationary
+    pass also writes dQ: 10 d), else both passes (8 d + 2 d useful, 8 d + 6 d executed).  Bytes
+    count every tensor a kernel must read or write once (per class: Q, dO, LSE and D, K, V, the
+    dense bias; the gradients it writes)."""
+    import jagged_attention_amd as jfa
+    c = w.case
+    d, H = c.head_dim, c.heads
+    if w.block:
+        ql = np.array([min(w.block, n - s) for n in c.q_lens for s in range(0, n, w.block)],
+                      dtype=np.int64)
+        kl = ql.copy()
+    else:
+        ql = c.q_lens.astype(np.int64)
+        kl = c.kv_lens.astype(np.int64)
+    pairs = visible_pairs(ql, kl, c.causal, w.window).astype(np.float64) * H
+    tc = jfa.jfa_tile_config(w.problem)
+    fuse = 0 if w.want_dbias else tc["fuse"]           # the bias-gradient call runs both passes
+    one_q = bool(fuse & 1) & (ql > 0) & (ql <= tc["bq_bm"])
+    one_k = ~one_q & bool(fuse & 2) & (kl > 0) & (kl <= tc["bk_bn"])
+    two = ~one_q & ~one_k
+    es = (1 + 1 / 32) if c.dtype == "mxfp8" else (4 if c.dtype == "f32" else 2)
+    gs = 4 if c.dtype == "f32" else 2                  # output / gradient element size
+    qb = ql * H * d * es
+    kb = kl * H * d * es
+    rows = ql * H * 8 if c.mode == "softmax" else 0    # LSE and D (fp32)
+    bias = ql * kl * H * 2 if c.bias_kind == "dense" else 0
+    dq, dkv = ql * H * d * gs, 2 * kl * H * d * gs
+    if w.want_dbias:
+        dq = dq + bias                                 # the dense bias gradient, written once
+    reads = 2 * qb + 2 * kb + rows + bias              # Q, dO, LSE / D, K, V, bias
+    q_cls = one_q | two
+    k_cls = one_k | two
+    work = {
+        "fwd": (4 * d * pairs.sum(), 4 * d * pairs.sum(),
+                (qb + 2 * kb + bias + ql * H * d * gs + (ql * H * 4 if c.mode == "softmax"
+                                                         else 0)).sum()),
+        "dq": ((10 * d * pairs[one_q]).sum() + (2 * d * pairs[two]).sum(),
+               (10 * d * pairs[one_q]).sum() + (6 * d * pairs[two]).sum(),
+               np.sum(np.where(q_cls, reads + dq, 0) + np.where(one_q, dkv, 0))),
+        "dkdv": ((10 * d * pairs[one_k]).sum() + (8 * d * pairs[two]).sum(),
+                 (10 * d * pairs[one_k]).sum() + (8 * d * pairs[two]).sum(),
+                 np.sum(np.where(k_cls, reads + dkv, 0) + np.where(one_k, dq, 0))),
+    }
+    kvq = (work["dq"][0] + work["dkdv"][0], work["dq"][1] + work["dkdv"][1],
+           work["dq"][2] + work["dkdv"][2])
+    work["kvq"] = kvq
+    out = {}
+    for name in USEFUL_FLOPS_PER_PAIR:
+        part = ("fwd" if "fwd" in name else "kvq" if "kvq" in name
+                else "dkdv" if "dkdv" in name else "dq")
+        out[name] = work[part]
+    return out
+
+
 def roofline_of(w, kt):
-    """Roofline record of the dominant MFMA kernel of the step (largest total time)."""
+    """Roofline record of the dominant attention kernel of the step (largest total time):
+    useful FLOP/s against the MFMA peak of its dtype, or algorithmic HBM GB/s against 8 TB/s
+    when its useful flops per algorithmic byte are below the ridge point (peak / 8 TB/s)."""
     cand = {k: v for k, v in kt.items() if k in USEFUL_FLOPS_PER_PAIR}
     if not cand:
         return None
     dom = max(cand, key=lambda k: cand[k]["avg_ms"] * cand[k]["launches"])
-    d = w.case.head_dim
-    useful = USEFUL_FLOPS_PER_PAIR[dom] * d * w.pairs
-    executed = EXECUTED_FLOPS_PER_PAIR[dom] * d * w.pairs
+    useful, executed, nbytes = kernel_work(w)[dom]
+    nbytes = max(float(nbytes), 1.0)
     sec = cand[dom]["avg_ms"] * 1e-3
-    achieved = useful / sec / 1e12
     peak = PEAK_FP8_TFLOPS if dom in FP8_MFMA_KERNELS else PEAK_BF16_TFLOPS
-    return dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak,
-                unit="TFLOP/s", frac=round(achieved / peak, 4),
-                traffic=traffic_for(dom, w.case.name), flops_per_launch=useful,
-                executed_flops_per_launch=executed,
-                executed_frac=round(executed / sec / 1e12 / peak, 4),
-                avg_ms=cand[dom]["avg_ms"])
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    rec = dict(kernel=dom, traffic=traffic_for(dom, w.case.name),
+               flops_per_launch=int(useful), executed_flops_per_launch=int(executed),
+               bytes_per_launch=int(nbytes), flops_per_byte=round(useful / nbytes, 1),
+               mfma_frac=round(useful / sec / 1e12 / peak, 4),
+               executed_frac=round(executed / sec / 1e12 / peak, 4),
+               hbm_frac=round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+               avg_ms=cand[dom]["avg_ms"])
+    if useful / nbytes < ridge:
+        gbs = nbytes / sec / 1e9
+        rec.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                   frac=round(gbs / PEAK_HBM_GBS, 4))
+    else:
+        tf = useful / sec / 1e12
+        rec.update(bound="mfma", achieved=round(tf, 2), peak=peak, unit="TFLOP/s",
+                   frac=round(tf / peak, 4))
+    return {k: rec[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")} | rec
 
 
 def bench_norm_quant(cfg=5, reps=10):

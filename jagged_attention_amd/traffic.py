@@ -29,6 +29,8 @@ ROOT = os.path.dirname(HERE)
 # timing name -> the source file that defines the kernel
 KERNEL_SOURCE = {"jfa_bwd_kvq": "bwd_inst.hip", "jfa_bwd_dkdv": "bwd_inst.hip",
                  "jfa_bwd_dq": "bwd_inst.hip", "jfa_dbias_dq": "bwd_inst.hip",
+                 "jfa_bwd_kvq_mxfp8": "bwd_inst.hip", "jfa_bwd_dkdv_mxfp8": "bwd_inst.hip",
+                 "jfa_bwd_dq_mxfp8": "bwd_inst.hip",
                  "jfa_fwd_bf16": "fwd.hip",
                  "jfa_fwd_mxfp8": "fwd.hip", "jfa_fwd_combine": "fwd.hip",
                  "jfa_schedule": "sched.hip", "jfa_offsets": "sched.hip",
@@ -58,25 +60,36 @@ def source_hash(kernel: str | None = None) -> str:
 
 
 # device kernel name -> the timing name bench.py reports
+def _targs(kernel: str, name: str) -> list:
+    m = re.search(name + r"<([^>]*)>", kernel)
+    return [x.strip() for x in m.group(1).split(",")] if m else []
+
+
 def timing_name(kernel: str) -> str | None:
     k = kernel
-    if "bwd_kvq_kernel" in k:
-        return "jfa_bwd_kvq"
-    if "bwd_kv_kernel" in k:
-        return "jfa_bwd_dkdv"
-    if "bwd_q_db_kernel" in k:
-        return "jfa_dbias_dq"
-    if "bwd_q_kernel" in k:
-        return "jfa_bwd_dq"
+    for base, tname in (("bwd_kvq_kernel", "jfa_bwd_kvq"), ("bwd_kv_kernel", "jfa_bwd_dkdv"),
+                        ("bwd_q_db_kernel", "jfa_dbias_dq"), ("bwd_q_kernel", "jfa_bwd_dq"),
+                        ("bwd_q1_kernel", "jfa_bwd_dq")):
+        if base in k:
+            a = _targs(k, base)          # <D, NW, MODE, BIAS, WIN, FP8>
+            return tname + ("_mxfp8" if len(a) >= 6 and a[5] == "true" else "")
     if "combine_kernel" in k:
         return "jfa_fwd_combine"
     if "fwd_kernel" in k:
-        m = re.search(r"fwd_kernel<[^>]*(true|false)>", k)
-        return "jfa_fwd_mxfp8" if (m and m.group(1) == "true") else "jfa_fwd_bf16"
+        a = _targs(k, "fwd_kernel")      # <D, NW, MODE, BIAS, FP8, WIN>
+        return "jfa_fwd_mxfp8" if len(a) >= 5 and a[4] == "true" else "jfa_fwd_bf16"
     if "schedule_kernel" in k:
         return "jfa_schedule"
+    if "lengths_to_offsets" in k:
+        return "jfa_offsets"
+    if "rmsnorm_quant" in k:
+        return "jfa_norm_quant_mxfp8"
     if "quantize" in k or "quant" in k:
         return "jfa_quant_mxfp8"
+    if "dbias_rows" in k or "dbias_chunks" in k:
+        return "jfa_dbias_reduce"
+    if "zero_u16" in k:
+        return "jfa_dbias_zero"
     if "copyBuffer" in k:
         return "copy"
     return None

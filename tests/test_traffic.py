@@ -21,6 +21,14 @@ def test_timing_names():
         "jfa_fwd_mxfp8"
     assert traffic.timing_name("void jfa::(anonymous namespace)::bwd_kvq_kernel<128, 4, 0, 1>"
                                "(jfa::BwdParams)") == "jfa_bwd_kvq"
+    assert traffic.timing_name("jfa::(anonymous namespace)::fwd_kernel<128, 4, 0, 1, true, false>"
+                               ) == "jfa_fwd_mxfp8"
+    assert traffic.timing_name("jfa::(anonymous namespace)::bwd_kvq_kernel<128, 4, 0, 0, false, "
+                               "true>(jfa::BwdParams)") == "jfa_bwd_kvq_mxfp8"
+    assert traffic.timing_name("jfa::(anonymous namespace)::bwd_q1_kernel<128, 1, 0, false>"
+                               "(jfa::BwdParams)") == "jfa_bwd_dq"
+    assert traffic.timing_name("jfa::(anonymous namespace)::bwd_q_db_kernel<64, 2, 2, 2, false>"
+                               ) == "jfa_dbias_dq"
     assert traffic.timing_name("__amd_rocclr_copyBuffer") == "copy"
     assert traffic.timing_name("something_else") is None
 
