@@ -372,7 +372,9 @@ struct ItemPipeT {
   int n_items;
   int H;
   int cx = 0;                // XCD list being drawn from (wave 0, uniform)
-  int v = 0;                 // lane L < IF_WORDS: dword L of the next item's descriptor
+  int v = 0;                 // lane L < IF_W: dword L of the next item's record
+  int wn = 0;                // the next item's index (uniform), published as dword IF_W
+  int grid = 0;              // workgroups of the launch (read once: the dispatch packet is memory)
   uint32_t t = 0;            // lane 0: the claimed ticket of list cx
 
   __device__ __forceinline__ int len(int x) const {
@@ -380,11 +382,13 @@ struct ItemPipeT {
   }
   // workgroups that start on XCD x's list (they take its first entries without a ticket)
   __device__ __forceinline__ int homed(int x) const {
-    return HOME ? ((int)gridDim.x - x + XCDS - 1) / XCDS : 0;
+    return HOME ? (grid - x + XCDS - 1) / XCDS : 0;
   }
+  // The record load is left in flight (nothing else is written to v before publish, which would
+  // otherwise wait for it).
   __device__ __forceinline__ void load_record(int w, int lane) {
-    if (lane == IF_W) v = w;
-    else if (lane < IF_W && w < n_items) v = reinterpret_cast<const int*>(items + w / H)[lane];
+    wn = w;
+    if (lane < IF_W && w < n_items) v = reinterpret_cast<const int*>(items + w / H)[lane];
   }
   __device__ __forceinline__ void claim(int lane) {
     if (lane == 0) t = atomicAdd(ctr + XCD_TICKET_STRIDE * cx, 1u);
@@ -419,10 +423,11 @@ struct ItemPipeT {
     load_record(k >= 0 ? XCDS * k + cx : n_items, lane);
   }
   __device__ __forceinline__ void publish(int* dst, int lane) {
-    if (lane < IF_WORDS) dst[lane] = v;
+    if (lane < IF_WORDS) dst[lane] = lane == IF_W ? wn : v;
   }
   // first descriptor into dst (wave 0; the caller then synchronises the workgroup)
   __device__ __forceinline__ void start(int* dst, int lane) {
+    grid = (int)__builtin_amdgcn_readfirstlane(gridDim.x);
     cx = blockIdx.x % XCDS;
     if constexpr (HOME) {
       load_record(blockIdx.x, lane);
