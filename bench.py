@@ -149,8 +149,9 @@ class Workload:
                     (self.v, self.vc, self.vs)]
             if self.with_backward:
                 todo.append((self.dout, self.doc, self.dos))
-            for x, c, sc in todo:
-                jfa.jfa_quantize_mxfp8(x, x.numel() // d, d, c, sc)
+            # one launch for all of them
+            jfa.jfa_quantize_mxfp8_batch([t[0] for t in todo], [t[0].numel() // d for t in todo],
+                                         d, [t[1] for t in todo], [t[2] for t in todo])
             jfa.jfa_forward(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks, self.vs,
                             self.qo, ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
             if self.with_backward:

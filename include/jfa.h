@@ -237,6 +237,17 @@ jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t bloc
 jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
                               uint8_t* scales, void* stream);
 
+/* jfa_quantize_mxfp8 on 1 to 4 tensors in one launch (Q, K, V and dO of an MXFP8 step):
+ * "Meta GEM Training Efficiency: ...", section "Bottleneck move 2" (scale generation and
+ * casting must not eat the low-precision gain).  xs_bf16[t] (bf16 [rows[t], d]), codes[t] and
+ * scales[t] are device pointers as for jfa_quantize_mxfp8; the arrays themselves are HOST
+ * arrays of `count` entries.  Results are bit-identical to one jfa_quantize_mxfp8 call per
+ * tensor.  count outside [1, 4], d % 32 != 0, a negative row count, NULL or misaligned pointers
+ * (x 16 B, codes 8 B) of a tensor with rows are JFA_ERR_INVALID_ARG. */
+jfa_status jfa_quantize_mxfp8_batch(int32_t count, const void* const* xs_bf16,
+                                    const int64_t* rows, int32_t d, uint8_t* const* codes,
+                                    uint8_t* const* scales, void* stream);
+
 /* RMS normalisation fused with the MXFP8 quantiser, producing MXFP8 attention inputs in one pass
  * over memory ("Meta GEM Training Efficiency: ...", section "Bottleneck move 2": quantisation
  * fused into the preceding normalisation, so that scale generation and casting cost no extra

@@ -14,7 +14,7 @@ from ._lib import (BIAS_KINDS, DTYPES, JFA_OK, MODES, JfaError, JfaProblem,  # n
                    jfa_forward_noalloc, jfa_backward_mxfp8,
                    jfa_kernel_timing,
                    jfa_kernel_timing_reset, jfa_lengths_to_offsets, jfa_quantize_mxfp8,
-                   jfa_rmsnorm_quantize_mxfp8,
+                   jfa_quantize_mxfp8_batch, jfa_rmsnorm_quantize_mxfp8,
                    jfa_read_device_status, jfa_set_kernel_timing, jfa_tile_config,
                    jfa_workspace_bytes, load, status_string)
 

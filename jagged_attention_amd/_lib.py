@@ -31,7 +31,7 @@ EXPORTS = ("jfa_workspace_bytes", "jfa_forward", "jfa_forward_noalloc", "jfa_bac
            "jfa_backward_mxfp8", "jfa_backward_dbias",
            "jfa_tile_config",
            "jfa_build_schedule", "jfa_lengths_to_offsets", "jfa_block_offsets",
-           "jfa_quantize_mxfp8", "jfa_rmsnorm_quantize_mxfp8",
+           "jfa_quantize_mxfp8", "jfa_quantize_mxfp8_batch", "jfa_rmsnorm_quantize_mxfp8",
            "jfa_read_device_status", "jfa_status_string", "jfa_set_kernel_timing",
            "jfa_kernel_timing", "jfa_kernel_timing_reset")
 
@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_block_offsets.restype = ctypes.c_int
     lib.jfa_quantize_mxfp8.argtypes = [P, I64, I32, P, P, P]
     lib.jfa_quantize_mxfp8.restype = ctypes.c_int
+    lib.jfa_quantize_mxfp8_batch.argtypes = [I32, P, P, I32, P, P, P]
+    lib.jfa_quantize_mxfp8_batch.restype = ctypes.c_int
     lib.jfa_rmsnorm_quantize_mxfp8.argtypes = [P, P, I64, I32, ctypes.c_float, P, P, P]
     lib.jfa_rmsnorm_quantize_mxfp8.restype = ctypes.c_int
     lib.jfa_read_device_status.argtypes = [P, P, ctypes.POINTER(I32)]
@@ -219,6 +221,16 @@ def jfa_quantize_mxfp8(x, rows: int, d: int, codes, scales, stream=None) -> None
     st = load().jfa_quantize_mxfp8(_ptr(x), int(rows), int(d), _ptr(codes), _ptr(scales),
                                    _stream(stream))
     _check("jfa_quantize_mxfp8", st)
+
+
+def jfa_quantize_mxfp8_batch(xs, rows, d: int, codes, scales, stream=None) -> None:
+    """xs, codes, scales: lists of device tensors (1 to 4); rows: their row counts."""
+    n = len(xs)
+    arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+    rws = (ctypes.c_int64 * n)(*[int(r) for r in rows])
+    st = load().jfa_quantize_mxfp8_batch(n, arr(xs), rws, int(d), arr(codes), arr(scales),
+                                         _stream(stream))
+    _check("jfa_quantize_mxfp8_batch", st)
 
 
 def jfa_rmsnorm_quantize_mxfp8(x, weight, groups: int, n: int, eps: float, codes, scales,

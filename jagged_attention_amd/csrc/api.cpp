@@ -559,9 +559,28 @@ jfa_status jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t bloc
 
 jfa_status jfa_quantize_mxfp8(const void* x_bf16, int64_t rows, int32_t d, uint8_t* codes,
                               uint8_t* scales, void* stream) {
-  if (!x_bf16 || !codes || !scales || rows < 0 || d <= 0 || d % 32 != 0) return JFA_ERR_INVALID_ARG;
+  if (rows < 0 || d <= 0 || d % 32 != 0) return JFA_ERR_INVALID_ARG;
+  if (rows == 0) return JFA_OK;            // an empty tensor may have null pointers
+  if (!x_bf16 || !codes || !scales) return JFA_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(codes, 8)) return JFA_ERR_INVALID_ARG;
   return from_hip(launch_quantize_mxfp8(x_bf16, rows, d, codes, scales, (hipStream_t)stream));
+}
+
+jfa_status jfa_quantize_mxfp8_batch(int32_t count, const void* const* xs_bf16,
+                                    const int64_t* rows, int32_t d, uint8_t* const* codes,
+                                    uint8_t* const* scales, void* stream) {
+  if (count < 1 || count > 4 || !xs_bf16 || !rows || !codes || !scales || d <= 0 || d % 32 != 0)
+    return JFA_ERR_INVALID_ARG;
+  for (int t = 0; t < count; ++t) {
+    if (rows[t] < 0) return JFA_ERR_INVALID_ARG;
+    if (rows[t] == 0) continue;           // an empty tensor may have null pointers
+    if (!xs_bf16[t] || !codes[t] || !scales[t]) return JFA_ERR_INVALID_ARG;
+    if (!aligned(xs_bf16[t], 16) || !aligned(codes[t], 8)) return JFA_ERR_INVALID_ARG;
+  }
+  const int cu = cu_count_of_current_device();
+  if (cu <= 0) return JFA_ERR_LAUNCH;
+  return from_hip(launch_quantize_mxfp8_batch(count, xs_bf16, rows, d, codes, scales, cu,
+                                              (hipStream_t)stream));
 }
 
 jfa_status jfa_rmsnorm_quantize_mxfp8(const void* x_bf16, const float* weight, int64_t groups,

@@ -290,6 +290,9 @@ hipError_t ensure_dyn_lds(const void* kernel, size_t bytes);
 
 hipError_t launch_block_offsets(const int32_t* off, int32_t B, int32_t W, int32_t* out,
                                 int32_t out_batch, int32_t* status, hipStream_t s);
+hipError_t launch_quantize_mxfp8_batch(int32_t count, const void* const* xs,
+                                       const int64_t* rows, int32_t d, uint8_t* const* codes,
+                                       uint8_t* const* scales, int cu_count, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int32_t d, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);
 hipError_t launch_rmsnorm_quantize_mxfp8(const void* x, const float* w, int64_t groups, int32_t n,

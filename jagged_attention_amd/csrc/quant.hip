@@ -11,6 +11,8 @@
 // Four lanes own one 32-element block (16 bytes each): a two-step shuffle gives the block max,
 // every lane scales its 8 elements by 2^-e, encodes them with the hardware's pack conversion
 // and stores 8 code bytes.
+#include <algorithm>
+
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -36,10 +38,9 @@ __device__ __forceinline__ int e4m3_pair(float y0, float y1, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, old, W);
 }
 
-__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restrict__ x,
-                                                          int64_t nblocks, uint8_t* codes,
-                                                          uint8_t* scales) {
-  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Thread tid's quarter (8 elements) of block tid / 4; the block's four lanes are consecutive.
+__device__ __forceinline__ void quant_block(const __bf16* __restrict__ x, int64_t nblocks,
+                                            uint8_t* codes, uint8_t* scales, int64_t tid) {
   const int64_t blk = tid >> 2;
   const int sub = (int)(tid & 3);
   const bool ok = blk < nblocks;
@@ -72,6 +73,29 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restri
   }
   *(u32x2*)(codes + blk * 32 + sub * 8) = out;
   if (sub == 0) scales[blk] = (uint8_t)sc;
+}
+
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const __bf16* __restrict__ x,
+                                                          int64_t nblocks, uint8_t* codes,
+                                                          uint8_t* scales) {
+  quant_block(x, nblocks, codes, scales, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// Up to four tensors in one launch: blockIdx.y picks the tensor, and each thread takes one
+// quarter-block exactly as quant_mxfp8_kernel does.
+constexpr int QB_MAX = 4;
+struct QuantBatch {
+  const __bf16* x[QB_MAX];
+  uint8_t* codes[QB_MAX];
+  uint8_t* scales[QB_MAX];
+  int64_t nblocks[QB_MAX];
+};
+
+__global__ __launch_bounds__(256) void quant_mxfp8_batch_kernel(QuantBatch b) {
+  const int t = blockIdx.y;
+  if ((int64_t)blockIdx.x * 64 >= b.nblocks[t]) return;    // this tensor ends before the block
+  quant_block(b.x[t], b.nblocks[t], b.codes[t], b.scales[t],
+              (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // RMS normalisation fused with the MXFP8 quantiser: quantisation folded into the normalisation
@@ -155,6 +179,29 @@ hipError_t launch_rmsnorm_quantize_mxfp8(const void* x, const float* w, int64_t 
     case 512: hipLaunchKernelGGL(rmsnorm_quant_mxfp8_kernel<64>, grid, dim3(256), 0, s, (const __bf16*)x, w, eps, groups, codes, scales); break;
     default: timing_end(s); return hipErrorInvalidValue;
   }
+  timing_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_batch(int32_t count, const void* const* xs,
+                                       const int64_t* rows, int32_t d, uint8_t* const* codes,
+                                       uint8_t* const* scales, int cu_count, hipStream_t s) {
+  if (count < 1 || count > QB_MAX) return hipErrorInvalidValue;
+  QuantBatch b{};
+  int64_t most = 0;
+  for (int t = 0; t < count; ++t) {
+    b.x[t] = (const __bf16*)xs[t];
+    b.codes[t] = codes[t];
+    b.scales[t] = scales[t];
+    b.nblocks[t] = rows[t] * (d / 32);
+    most = std::max(most, b.nblocks[t]);
+  }
+  if (most == 0) return hipSuccess;
+  (void)cu_count;
+  const int64_t need = (most * 4 + 255) / 256;        // one thread per quarter-block
+  timing_begin("jfa_quant_mxfp8", s);
+  hipLaunchKernelGGL(quant_mxfp8_batch_kernel, dim3((unsigned)need, (unsigned)count), dim3(256),
+                     0, s, b);
   timing_end(s);
   return hipGetLastError();
 }

@@ -158,6 +158,21 @@ def test_other_entry_points_host_errors():
     assert lib.jfa_block_offsets(FAKE, 4, 4, FAKE + 2, 8, None, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_quantize_mxfp8(FAKE, 10, 48, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
     assert lib.jfa_quantize_mxfp8(FAKE + 2, 10, 64, FAKE, FAKE, None) == _lib.JFA_ERR_INVALID_ARG
+    # the batched quantiser: 1 to 4 tensors, d % 32 == 0, rows >= 0, aligned non-null pointers
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    rows = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    q = lib.jfa_quantize_mxfp8_batch
+    assert q(0, arr(FAKE), rows(10), 64, arr(FAKE), arr(FAKE), None) == _lib.JFA_ERR_INVALID_ARG
+    assert q(5, arr(*[FAKE] * 5), rows(*[10] * 5), 64, arr(*[FAKE] * 5), arr(*[FAKE] * 5),
+             None) == _lib.JFA_ERR_INVALID_ARG
+    assert q(2, arr(FAKE, FAKE), rows(10, 10), 48, arr(FAKE, FAKE), arr(FAKE, FAKE), None) == \
+        _lib.JFA_ERR_INVALID_ARG
+    assert q(2, arr(FAKE, FAKE + 2), rows(10, 10), 64, arr(FAKE, FAKE), arr(FAKE, FAKE),
+             None) == _lib.JFA_ERR_INVALID_ARG
+    assert q(2, arr(FAKE, FAKE), rows(10, -1), 64, arr(FAKE, FAKE), arr(FAKE, FAKE), None) == \
+        _lib.JFA_ERR_INVALID_ARG
+    assert q(2, arr(FAKE, None), rows(10, 10), 64, arr(FAKE, FAKE), arr(FAKE, FAKE), None) == \
+        _lib.JFA_ERR_INVALID_ARG
     out = ctypes.c_int32(0)
     assert lib.jfa_read_device_status(None, None, ctypes.byref(out)) == _lib.JFA_ERR_INVALID_ARG
     ms, n = ctypes.c_double(), ctypes.c_int64()

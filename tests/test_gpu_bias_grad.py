@@ -114,7 +114,7 @@ def test_bias_grad_parity(mode, causal, bias_kind, d):
     compare("dV", dv, dv_ref, "bf16")
 
 
-@pytest.mark.parametrize("num_buckets", [1, 17, 64, 65, 300])
+@pytest.mark.parametrize("num_buckets", [1, 17, 64, 65, 300, 1500])
 @pytest.mark.parametrize("causal", [True, False])
 def test_bias_grad_table_widths(num_buckets, causal):
     """Tables of at most 64 buckets are summed in LDS, wider ones in memory (two lane halves per

@@ -238,6 +238,28 @@ def test_mxfp8_quantizer_bitexact():
     assert np.array_equal(codes.cpu().numpy(), want_c)
 
 
+def test_mxfp8_quantizer_batch_matches_single():
+    import jagged_attention_amd as jfa
+    rng = np.random.default_rng(31)
+    shapes = [(1000, 4, 128), (3, 4, 128), (0, 4, 128), (40000, 4, 128)]   # the last: two
+    # grid-stride iterations (the grid is capped at 8 workgroups per CU)
+    xs = [torch.from_numpy((rng.standard_normal(s) * np.exp(rng.normal(0, 3, s[:2] + (1,))))
+                           .astype(np.float32)).to(torch.bfloat16).cuda() for s in shapes]
+    d = 128
+    codes = [torch.full(x.shape, 0x5A, dtype=torch.uint8, device="cuda") for x in xs]
+    scales = [torch.full(tuple(x.shape[:-1]) + (d // 32,), 0x5A, dtype=torch.uint8,
+                         device="cuda") for x in xs]
+    jfa.jfa_quantize_mxfp8_batch(xs, [x.numel() // d for x in xs], d, codes, scales)
+    torch.cuda.synchronize()
+    for x, c, s in zip(xs, codes, scales):
+        wc, ws = jfa.quantize_mxfp8(x)
+        assert torch.equal(c, wc) and torch.equal(s, ws)
+    # and against the oracle on one of them
+    want_c, want_s = oracle.mxfp8_quantize(xs[0].cpu().double().numpy())
+    assert np.array_equal(codes[0].cpu().numpy(), want_c)
+    assert np.array_equal(scales[0].cpu().numpy(), want_s)
+
+
 def test_mxfp8_quantizer_golden():
     """The hand-derived cases (ties to even, smallest subnormal, saturation, zero block) on the
     GPU quantiser: one 32-element block per case holding amax and x."""
