@@ -7,8 +7,9 @@ workload is causal jagged self-attention over user histories with a relative-pos
 Inputs are resident in HBM before the timed region.  Every step is timed with HIP events on
 the stream, after a 512 MB write that flushes the 256 MB MALL; the median over the steps is the
 reported time (p10 and p90 beside it, and back-to-back steps as a secondary).  The same step
-captured once as a HIP graph (checked bit-exact against an eager step) is timed too.  Prints
-ONE JSON line.
+captured once as a HIP graph (checked bit-exact against an eager step) is timed too, and so are
+the forward and the backward on their own.  Defaults: 10 warm-up steps, 50 timed.  Prints ONE
+JSON line.
 
 Useful FLOPs count only visible (query, key) pairs: 4*d per pair forward, 10*d backward.
 """
@@ -125,6 +126,13 @@ class Workload:
         self.bwd_flops = 10.0 * d * self.pairs if self.with_backward else 0.0
 
     def step(self):
+        self.step_forward()
+        if self.with_backward:
+            self.step_backward()
+
+    def step_forward(self):
+        """Offsets (and the BlockAttention refinement), the MXFP8 quantiser (with dO when the
+        step has a backward: one launch for all), and the forward."""
         import jagged_attention_amd as jfa
         jfa.jfa_lengths_to_offsets(self.q_lens, self.case.batch, self.qo, status=self.status[0:1])
         if self.block:
@@ -133,10 +141,6 @@ class Workload:
                                   self.status[1:2])
             jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.boff,
                             self.boff, self.bias, self.o, self.lse, self.ws_f, self.nf)
-            if self.with_backward:
-                jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse,
-                                 self.dout, self.boff, self.boff, self.bias, self.dq, self.dk,
-                                 self.dv, self.ws_b, self.nb)
             return
         ko = self.qo
         if not self.self_attn:
@@ -154,19 +158,29 @@ class Workload:
                                          d, [t[1] for t in todo], [t[2] for t in todo])
             jfa.jfa_forward(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks, self.vs,
                             self.qo, ko, self.bias, self.o, self.lse, self.ws_f, self.nf)
-            if self.with_backward:
-                jfa.jfa_backward_mxfp8(self.problem, self.qc, self.kc, self.vc, self.qs,
-                                       self.ks, self.vs, self.o, self.lse, self.doc, self.dos,
-                                       self.qo, ko, self.bias, self.dq, self.dk, self.dv,
-                                       self.ws_b, self.nb)
             return
         jfa.jfa_forward(self.problem, self.q, self.k, self.v, None, None, None, self.qo, ko,
                         self.bias, self.o, self.lse, self.ws_f, self.nf)
-        if self.with_backward and self.want_dbias:
+
+    def step_backward(self):
+        """The backward (scheduler with D, both passes; the bias gradient when asked), on the
+        offsets and forward outputs of the last step_forward."""
+        import jagged_attention_amd as jfa
+        if self.block:
+            jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse, self.dout,
+                             self.boff, self.boff, self.bias, self.dq, self.dk, self.dv,
+                             self.ws_b, self.nb)
+            return
+        ko = self.qo if self.self_attn else self.ko
+        if self.fp8:
+            jfa.jfa_backward_mxfp8(self.problem, self.qc, self.kc, self.vc, self.qs, self.ks,
+                                   self.vs, self.o, self.lse, self.doc, self.dos, self.qo, ko,
+                                   self.bias, self.dq, self.dk, self.dv, self.ws_b, self.nb)
+        elif self.want_dbias:
             jfa.jfa_backward_dbias(self.problem, self.q, self.k, self.v, self.o, self.lse,
                                    self.dout, self.qo, ko, self.bias, self.dq, self.dk, self.dv,
                                    self.dbias, self.ws_b, self.nb)
-        elif self.with_backward:
+        else:
             jfa.jfa_backward(self.problem, self.q, self.k, self.v, self.o, self.lse, self.dout,
                              self.qo, ko, self.bias, self.dq, self.dk, self.dv, self.ws_b,
                              self.nb)
@@ -425,6 +439,10 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None
     w = Workload(case, block=block, dbias=dbias, window=window)
     t_fl = stats(time_steps(w, steps, warmup, flush))          # MALL flushed before every step
     t_hot = stats(time_steps(w, steps, 1))                     # back to back (secondary)
+    # the forward and the backward on their own (each flushed; the backward reuses the last
+    # forward's outputs)
+    t_fwd = stats(_timed(w.step_forward, steps, 1, flush))
+    t_bwd = stats(_timed(w.step_backward, steps, 1, flush)) if w.with_backward else None
     # the same step replayed as one HIP graph (no per-launch host work): reported beside it
     w.graph = capture_step(w)
     t_graph = stats(time_graph(w.graph, steps, 1, flush))
@@ -446,6 +464,10 @@ def bench_config(cfg, steps, warmup, seed=None, block=0, dbias=False, flush=None
     return w, dict(workload=name, seed=case.seed, ms_per_step=t_fl["median"],
                    ms_p10=t_fl["p10"], ms_p90=t_fl["p90"],
                    unflushed_ms_per_step=t_hot["median"],
+                   fwd_ms=t_fwd["median"], bwd_ms=None if t_bwd is None else t_bwd["median"],
+                   fwd_tflops=w.fwd_flops / (t_fwd["median"] * 1e-3) / 1e12,
+                   bwd_tflops=None if t_bwd is None else
+                   w.bwd_flops / (t_bwd["median"] * 1e-3) / 1e12,
                    graph_ms_per_step=t_graph["median"], tflops=tf,
                    frac_of_mfma_peak=tf / peak, roofline_ceiling_tflops=ceiling,
                    frac_of_roofline=tf / ceiling, useful_gflop=flops / 1e9,
@@ -591,8 +613,8 @@ def bench_norm_quant(cfg=5, reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
@@ -723,9 +745,15 @@ def main():
         "ms_p90": round(head["ms_p90"], 4),
         "unflushed_ms_per_step": round(head["unflushed_ms_per_step"], 4),
         "graph_ms_per_step": round(head["graph_ms_per_step"], 4),
+        "fwd_ms": round(head["fwd_ms"], 4),
+        "bwd_ms": None if head["bwd_ms"] is None else round(head["bwd_ms"], 4),
+        "fwd_tflops": round(head["fwd_tflops"], 3),
+        "bwd_tflops": None if head["bwd_tflops"] is None else round(head["bwd_tflops"], 3),
         "timing": "median of per-step HIP events, a 512 MB write flushing the MALL before each "
                   "step; unflushed_ms_per_step: back-to-back steps; graph_ms_per_step: the step "
-                  "replayed as one HIP graph (checked bit-exact against an eager step)",
+                  "replayed as one HIP graph (checked bit-exact against an eager step); fwd_ms "
+                  "and bwd_ms: the forward (with the offsets) and the backward (scheduler "
+                  "included) timed on their own, each flushed",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
