@@ -965,7 +965,10 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     };
     if constexpr (MODE == MODE_SOFTMAX) {
       if (qrole && qi < n) {
-        lse2 = p.lse[(int64_t)h * p.total_q + qo + qi] * LOG2E;
+        // a row without a visible key has lse = -inf and all its pairs at the -inf sentinel:
+        // any finite value keeps exp2(-inf - lse2) = 0
+        const float l = p.lse[(int64_t)h * p.total_q + qo + qi];
+        lse2 = l == NEG_INF ? 0.f : l * LOG2E;
         dlt = p.delta[(int64_t)h * p.total_q + qo + qi];
       }
     }
@@ -1088,22 +1091,33 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
       }
+      // softmax: dP starts at -delta, so that dS = P dP with no subtraction per pair
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[blk][i] = 0.f;
+        for (int i = 0; i < 16; ++i) pacc[blk][i] = MODE == MODE_SOFTMAX ? -dlt : 0.f;
       const bool need_mask = (j0 + STEP > m) || (p.causal && j0 + STEP - 1 > qw0 + delta) ||
                              (qw0 + 32 > n) ||
                              (WIN && (j0 <= qw0 + 31 + delta - W ||
                                       (!p.causal && j0 + STEP - 1 >= qw0 + delta + W)));
-      // keys [kbeg, kend) are visible to query qi: offsets [lo, lim) of this lane's elements
-      int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
-      int lo = 0;
-      if constexpr (WIN) {
-        if (qi < n && !p.causal) kend = min(m, qi + delta + W);
-        lo = qi + delta - W + 1 - j0 - 4 * g;
+      if (need_mask) {
+        // keys [kbeg, kend) are visible to query qi: offsets [lo, lim) of this lane's elements;
+        // the others start at -inf, so that P = 0 and dS = 0 with no per-element test later
+        int kend = qi < n ? (p.causal ? min(m, qi + delta + 1) : m) : 0;
+        int lo = 0;
+        if constexpr (WIN) {
+          if (qi < n && !p.causal) kend = min(m, qi + delta + W);
+          lo = qi + delta - W + 1 - j0 - 4 * g;
+        }
+        const int lim = kend - j0 - 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = blk * 32 + 8 * (i >> 2) + (i & 3);
+            if (off >= lim || (WIN && off < lo)) sacc[blk][i] = NEG_INF;
+          }
       }
-      const int lim = kend - j0 - 4 * g;
       uint32_t dd[2][8], pq2[2][8];
       // B(blk) pair pi: dS and P of elements 2 pi, 2 pi + 1 of block blk
       auto valu_b = [&](int blk, int pi) {
@@ -1111,16 +1125,15 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int ii = 2 * pi + e;
-          const int off = blk * 32 + 8 * (ii >> 2) + (ii & 3);
-          const bool valid = !need_mask || (off < lim && (!WIN || off >= lo));
-          const float x = sacc[blk][ii] * c_log;
+          // a pair is visible iff its logit is not the -inf sentinel (the bias is finite)
+          const bool valid = sacc[blk][ii] != NEG_INF;
           if constexpr (MODE == MODE_SOFTMAX) {
-            const float pr = valid ? fast_exp2(x - lse2) : 0.f;
-            d2[e] = pr * (pacc[blk][ii] - dlt);
+            const float pr = fast_exp2(fmaf(sacc[blk][ii], c_log, -lse2));
+            d2[e] = pr * pacc[blk][ii];
             p2[e] = pr;
           } else {
             float a, da;
-            act_pair<MODE>(x, a, da);
+            act_pair<MODE>(sacc[blk][ii] * c_log, a, da);
             d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
             p2[e] = valid ? a * wn : 0.f;
           }
@@ -1199,8 +1212,16 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
             valu_b(0, decltype(pc)::value);
           });
         }
-        if constexpr (st >= 2 * NA && st < 2 * NA + 2 * NCB) {   // B(1) under C(0)
-          static_for<(st - 2 * NA) * 8 / (2 * NCB), (st - 2 * NA + 1) * 8 / (2 * NCB)>([&](auto pc) {
+        // B(1): pairs 0..3 (dS of key chunk 2) under chunks 0 and 1, pairs 4..7 (chunk 3)
+        // under chunk 2
+        if constexpr (st >= 2 * NA && st < 2 * NA + 2 * NCB) {
+          static_for<(st - 2 * NA) * 4 / (2 * NCB), (st - 2 * NA + 1) * 4 / (2 * NCB)>([&](auto pc) {
+            valu_b(1, decltype(pc)::value);
+          });
+        }
+        if constexpr (st >= 2 * NA + 2 * NCB && st < 2 * NA + 3 * NCB) {
+          static_for<4 + (st - 2 * NA - 2 * NCB) * 4 / NCB,
+                     4 + (st - 2 * NA - 2 * NCB + 1) * 4 / NCB>([&](auto pc) {
             valu_b(1, decltype(pc)::value);
           });
         }
