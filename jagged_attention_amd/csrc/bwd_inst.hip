@@ -628,11 +628,13 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
           pv = fast_exp2(fmaf(sacc[h][i], c_log, -lq[h][i >> 2][i & 3]));
           dsv = pv * pacc[h][i];
         } else {
-          const bool vis = sacc[h][i] != NEG_INF;
-          float a, da;
-          act_pair<MODE>(sacc[h][i] * c_log, a, da);
-          pv = vis ? a * wn : 0.f;
-          dsv = vis ? da * pacc[h][i] * wn : 0.f;
+          // masked pairs hold -inf: clamped to -1e30, the activation and its derivative are
+          // exactly zero (the exponential and the reciprocal saturate) and a NaN logit still
+          // propagates; the weight 1 / kv_len is applied to dK and dV as a whole
+          float x = sacc[h][i] * c_log;
+          x = x < -1e30f ? -1e30f : x;
+          act_pair<MODE>(x, pv, dsv);
+          dsv *= pacc[h][i];
         }
         if (i & 1) {
           pp[h][i >> 1] = pack2bf(pv_t, pv);
@@ -734,8 +736,9 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
           const uint32_t row = (uint32_t)(qs * STEP + 32 * half + l32) * row_bytes;
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
-            const u32x2 v = {pack2bf(qa[4 * jq] * p.scale, qa[4 * jq + 1] * p.scale),
-                             pack2bf(qa[4 * jq + 2] * p.scale, qa[4 * jq + 3] * p.scale)};
+            const float sw = p.scale * wn;
+            const u32x2 v = {pack2bf(qa[4 * jq] * sw, qa[4 * jq + 1] * sw),
+                             pack2bf(qa[4 * jq + 2] * sw, qa[4 * jq + 3] * sw)};
             st8(v, rdq, row + 2u * (uint32_t)(db * 32 + 8 * jq + 4 * g));
           }
         }
@@ -781,9 +784,9 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
     const rsrc_t rdv = make_rsrc((__bf16*)p.dv + ((int64_t)ko * H + h) * D, kv_bytes);
     // through the stage that the last query step left free (rows of this wave only)
     unsigned char* ost = lds + (nsteps & 1) * L::STAGE + wave * 2 * out_stage_bytes<D>();
-    store_rows_via_lds<D>(dk, p.scale, reinterpret_cast<__bf16*>(ost), rdk,
+    store_rows_via_lds<D>(dk, p.scale * wn, reinterpret_cast<__bf16*>(ost), rdk,
                           (uint32_t)jw0 * row_bytes, row_bytes, lane);
-    store_rows_via_lds<D>(dv, 1.0f, reinterpret_cast<__bf16*>(ost + out_stage_bytes<D>()), rdv,
+    store_rows_via_lds<D>(dv, wn, reinterpret_cast<__bf16*>(ost + out_stage_bytes<D>()), rdv,
                           (uint32_t)jw0 * row_bytes, row_bytes, lane);
     __syncthreads();
   }
@@ -903,6 +906,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     const bool one_q = L::Q1 && (p.fuse & 1) && n > 0 && n <= BM;
     const int delta = m - n;
     const float wn = (MODE != MODE_SOFTMAX && p.normalize && m > 0) ? 1.0f / (float)m : 1.0f;
+    // the weight 1 / kv_len per pair (the bias gradient) or on the item's outputs as a whole
+    const float wpair = DB ? wn : 1.0f, wout = DB ? 1.0f : wn;
     const int q0 = t * BM, qw0 = q0 + wave * 32;
     const int qil = wave * 32 + l32, qi = q0 + qil;
     // keys [wave_kbeg, wave_kend) hold every pair this wave's rows can see
@@ -1132,10 +1137,14 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
             d2[e] = pr * pacc[blk][ii];
             p2[e] = pr;
           } else {
+            // masked pairs hold -inf: clamped to -1e30, the activation and its derivative are
+            // exactly zero and a NaN logit still propagates
+            float x = sacc[blk][ii] * c_log;
+            x = x < -1e30f ? -1e30f : x;
             float a, da;
-            act_pair<MODE>(sacc[blk][ii] * c_log, a, da);
-            d2[e] = valid ? da * pacc[blk][ii] * wn : 0.f;
-            p2[e] = valid ? a * wn : 0.f;
+            act_pair<MODE>(x, a, da);
+            d2[e] = da * pacc[blk][ii] * wpair;
+            p2[e] = a * wpair;
           }
           if constexpr (DB) {
             const int j = j0 + blk * 32 + 8 * (ii >> 2) + 4 * g + (ii & 3);
@@ -1283,7 +1292,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
           }
           const rsrc_t r = make_rsrc((__bf16*)(which ? p.dk : p.dv) + ((int64_t)ko * H + h) * D,
                                      kv_bytes);
-          const float mul = which ? p.scale : 1.0f;
+          const float mul = which ? p.scale * wout : wout;
           if constexpr (SPLIT) {
             // lane (key l32, g) holds dims 32 db + 8 jq + 4 g + 0..3 of its key row
             const uint32_t row = row0 + (uint32_t)l32 * row_bytes;
@@ -1379,7 +1388,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       // through the stage that the last key step left free (rows of this wave only)
       __bf16* ost = reinterpret_cast<__bf16*>(lds + (steps & 1) * L::STAGE +
                                               wave * out_stage_bytes<D>());
-      store_rows_via_lds<D>(acc, p.scale, ost, rdq, (uint32_t)qw0 * row_bytes, row_bytes, lane);
+      store_rows_via_lds<D>(acc, p.scale * wout, ost, rdq, (uint32_t)qw0 * row_bytes, row_bytes,
+                            lane);
     }
     __syncthreads();
   }
