@@ -714,6 +714,13 @@ def main():
         r["kernels"] = kernel_times(wx, 3, flush)
         extra["bias_gradient"] = r
         del wx
+        # the short-KV GELU workload with its dense bias trained (both passes: the bias gradient
+        # is formed in the query-stationary pass)
+        log("[bench] dense bias gradient")
+        wx, r = bench_config(4, max(3, args.steps // 2), 2, dbias=True, flush=flush)
+        r["kernels"] = kernel_times(wx, 3, flush)
+        extra["bias_gradient_dense"] = r
+        del wx
         torch.cuda.empty_cache()
 
     cpu = None

@@ -39,87 +39,19 @@ namespace {
 
 enum BiasT { B_NONE = 0, B_RELPOS = 1, B_DENSE = 2 };
 constexpr int STEP = 64;   // rows per step of either kernel's inner loop
-constexpr int TS = STEP + 8;   // stride (bf16) of a transposed tile row
 
 constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 
 // --------------------------------------------------------------- tile staging
 // The NT threads that stage a tile are the first NT of the workgroup or, in a workgroup of more
 // threads, any NT consecutive ones (thread index taken modulo NT).
-// A STEP x D bf16 tile is moved as blocks of 4 rows x 8 dims (one 16-byte load per row).
+// An MXFP8 STEP x D tile is moved as blocks of 4 rows x 8 dims (one load per row).
 // Block id -> (row block rb, dim block cb): within each 16 ids, 4 row blocks x 4 dim blocks,
 // so that a quarter wave's row-major writes cover all banks.
 __device__ __forceinline__ void blk_of(int id, int& rb, int& cb) {
   rb = ((id >> 2) & 3) | (((id >> 4) & 3) << 2);
   cb = (id & 3) | ((id >> 6) << 2);
 }
-
-template <int D, int NT>
-struct Tile {
-  static constexpr int NBLK = (STEP / 4) * (D / 8);
-  static constexpr int NB = (NBLK + NT - 1) / NT;
-  u32x4 v[NB][4];
-
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t row_bytes, int r0) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int id = (int)(threadIdx.x % NT) + i * NT;
-      if (NBLK % NT != 0 && id >= NBLK) break;
-      int rb, cb;
-      blk_of(id, rb, cb);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        v[i][rr] = ld16(r, (uint32_t)(r0 + 4 * rb + rr) * row_bytes + 16 * cb);
-    }
-  }
-  // One sixth of block I's stores: PART 0, 1 write rows 2*PART, 2*PART+1 row-major; PART 2..5
-  // write dims 8cb + 2(PART-2) and + 1 transposed (so the stores can be spread out).
-  static constexpr int PARTS = 6 * NB;
-  template <int P>
-  __device__ __forceinline__ void store_part(__bf16* rows, __bf16* tr) const {
-    constexpr int i = P / 6, part = P % 6;
-    const int id = (int)(threadIdx.x % NT) + i * NT;
-    if (NBLK % NT != 0 && id >= NBLK) return;
-    int rb, cb;
-    blk_of(id, rb, cb);
-    if constexpr (part < 2) {
-#pragma unroll
-      for (int rr = 2 * part; rr < 2 * part + 2; ++rr)
-        *(u32x4*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) = v[i][rr];
-    } else {
-      constexpr int e2 = part - 2;
-      const int pos = vt_pos(4 * rb);
-      const u32x2 lo = {lo_halves(v[i][0][e2], v[i][1][e2]), lo_halves(v[i][2][e2], v[i][3][e2])};
-      const u32x2 hi = {hi_halves(v[i][0][e2], v[i][1][e2]), hi_halves(v[i][2][e2], v[i][3][e2])};
-      *(u32x2*)(tr + (8 * cb + 2 * e2) * TS + pos) = lo;
-      *(u32x2*)(tr + (8 * cb + 2 * e2 + 1) * TS + pos) = hi;
-    }
-  }
-  // rows: [STEP][tile_row_stride] row-major (may be null); tr: [D][TS] transposed, rows permuted
-  __device__ __forceinline__ void store(__bf16* rows, __bf16* tr) const {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int id = (int)(threadIdx.x % NT) + i * NT;
-      if (NBLK % NT != 0 && id >= NBLK) break;
-      int rb, cb;
-      blk_of(id, rb, cb);
-      if (rows) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) *(u32x4*)(rows + (4 * rb + rr) * tile_row_stride<D>() + 8 * cb) = v[i][rr];
-      }
-      if (tr) {
-        const int pos = vt_pos(4 * rb);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const u32x2 lo = {lo_halves(v[i][0][e2], v[i][1][e2]), lo_halves(v[i][2][e2], v[i][3][e2])};
-          const u32x2 hi = {hi_halves(v[i][0][e2], v[i][1][e2]), hi_halves(v[i][2][e2], v[i][3][e2])};
-          *(u32x2*)(tr + (8 * cb + 2 * e2) * TS + pos) = lo;
-          *(u32x2*)(tr + (8 * cb + 2 * e2 + 1) * TS + pos) = hi;
-        }
-      }
-    }
-  }
-};
 
 // Row-major-only staging of a STEP x D tile: 16-byte chunks, consecutive lanes along a row.
 template <int D, int NT>
@@ -304,7 +236,8 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
   const uint32_t in_row = (uint32_t)H * D * ES;             // input row stride
   const uint32_t sc_row = (uint32_t)H * (D / 32);           // MXFP8 scale row stride
 
-  std::conditional_t<FP8, Fp8Tile<D, NT>, Tile<D, NT>> tq, tdo;
+  // bf16 tiles are staged row-major, consecutive lanes along a row (full cache lines per load)
+  std::conditional_t<FP8, Fp8Tile<D, NT>, RowTile<D, NT>> tq, tdo;
   float lsv = 0.f, dlv = 0.f;       // lse / delta entry staged by threads < STEP
   float rpv = 0.f;                  // relpos table entry
   // Dense bias: NDB units per thread and step, each two 16-byte chunks (8 keys of queries q and
@@ -431,22 +364,30 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
           }
       }
     };
-    // tile stores, piece P of 2 * Tile::PARTS (Q then dO), into LDS stage st
-    constexpr int TP = decltype(tq)::PARTS;
-    auto store_tile_piece = [&](auto pc, int st) {
-      constexpr int P = decltype(pc)::value;
+    // the Q and dO rows of a step into LDS stage st
+    auto store_tiles = [&](int st) {
       unsigned char* base = lds + st * L::STAGE;
-      if constexpr (P % 6 < 2) {   // row stores only: no transposed copies
-        if constexpr (P < TP)
-          tq.template store_part<P>(reinterpret_cast<__bf16*>(base + L::QR), nullptr);
-        else
-          tdo.template store_part<P - TP>(reinterpret_cast<__bf16*>(base + L::DR), nullptr);
+      if constexpr (FP8) {
+        // row stores only (pieces 0, 1 of every 6): no transposed copies
+        constexpr int TP = decltype(tq)::PARTS;
+        static_for<0, 2 * TP>([&](auto pc) {
+          constexpr int P = decltype(pc)::value;
+          if constexpr (P % 6 < 2) {
+            if constexpr (P < TP)
+              tq.template store_part<P>(reinterpret_cast<__bf16*>(base + L::QR), nullptr);
+            else
+              tdo.template store_part<P - TP>(reinterpret_cast<__bf16*>(base + L::DR), nullptr);
+          }
+        });
+      } else {
+        tq.store(reinterpret_cast<__bf16*>(base + L::QR));
+        tdo.store(reinterpret_cast<__bf16*>(base + L::DR));
       }
     };
     auto store_step = [&](int st, int qs, bool tiles) {
       unsigned char* base = lds + st * L::STAGE;
       const int q0 = qs * STEP;
-      if (tiles) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, st); });
+      if (tiles) store_tiles(st);
       if constexpr (MODE == MODE_SOFTMAX) {
         if (tid < STEP) {
           // rows without a visible key have lse = -inf; all their pairs are masked to -inf,
@@ -493,9 +434,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
     // VALU work B(h) that turns S_h, dP_h into P_h, dS_h is spread one element per MFMA over the
     // next phase (B(0) under A(1), B(1) under C(0)), so the matrix cores stay busy in this
     // one-wave-per-SIMD kernel.  sched_barrier pins that order against the compiler's scheduler.
-    // `nst` >= 0: the LDS stage that the prefetched next tiles go to; their stores are spread
-    // over the last phase C(1), whose MFMAs need no VALU work.
-    auto compute_step = [&](int it, int qs, int nst) {
+    auto compute_step = [&](int it, int qs) {
       const int q0 = qs * STEP;
       const unsigned char* sb = lds + (it & 1) * L::STAGE;
       // nothing visible between this step's queries and the wave's keys (past the sample,
@@ -504,7 +443,6 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       if (jw0 >= m || (p.causal && q0 + STEP - 1 + delta < jw0) ||
           (WIN && (q0 > jw0 + 31 - delta + W - 1 ||
                    (!p.causal && q0 + STEP - 1 < jw0 - delta - W + 1)))) {
-        if (nst >= 0) static_for<0, 2 * TP>([&](auto pc) { store_tile_piece(pc, nst); });
         if (L::K1 && one_k) {     // these keys contribute nothing to this step's dQ
           uint32_t* ds = reinterpret_cast<uint32_t*>(
               reinterpret_cast<__bf16*>(lds + L::K1_DS) + kvl * L::QS);
@@ -679,15 +617,6 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
         if constexpr (s >= 2 * NA && s < 3 * NA) {
           static_for<0, EPM>([&](auto e) { valu_b(1, (s - 2 * NA) * EPM + e); });
         }
-        // next tiles' stores: piece k of 2 * TP goes with MFMA 3 NA + k NA / (2 TP)
-        if constexpr (s >= 3 * NA) {
-          if (nst >= 0) {
-            static_for<0, 2 * TP>([&](auto pc) {
-              constexpr int P = decltype(pc)::value;
-              if constexpr (3 * NA + P * NA / (2 * TP) == s) store_tile_piece(pc, nst);
-            });
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
       });
       if (L::K1 && one_k) {
@@ -763,7 +692,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       if (it == claim_it && wave == 0) pipe.claim(lane);
       if (it == resolve_it && wave == 0) pipe.resolve(lane);
       load_step(qs_first + it + 1);
-      compute_step(it, qs_first + it, -1);
+      compute_step(it, qs_first + it);
       if (one_k) {
         __syncthreads();
         dq_step(qs_first + it);
@@ -771,7 +700,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       store_step((it + 1) & 1, qs_first + it + 1, true);
       __syncthreads();
     }
-    if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1, -1);
+    if (nsteps > 0) compute_step(nsteps - 1, qs_end - 1);
     if (one_k && nsteps > 0) {
       __syncthreads();
       dq_step(qs_end - 1);
@@ -872,7 +801,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   const uint32_t in_row = (uint32_t)H * D * ES;             // input row stride
   const uint32_t sc_row = (uint32_t)H * (D / 32);           // MXFP8 scale row stride
 
-  std::conditional_t<FP8, Fp8Tile<D, NT>, Tile<D, NT>> tk;
+  // bf16 tiles are staged row-major, consecutive lanes along a row (full cache lines per load)
+  std::conditional_t<FP8, Fp8Tile<D, NT>, RowTile<D, NT>> tk;
   std::conditional_t<FP8, Fp8RowTile<D, NT>, RowTile<D, NT>> tv;
   float rpv = 0.f;
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
@@ -1025,8 +955,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     auto store_step = [&](int st, int kt) {
       unsigned char* base = lds + st * L::STAGE;
       const int j0 = kt * STEP;
-      if constexpr (FP8) tk.store(reinterpret_cast<__bf16*>(base + L::KR));
-      else tk.store(reinterpret_cast<__bf16*>(base + L::KR), nullptr);
+      tk.store(reinterpret_cast<__bf16*>(base + L::KR));
       tv.store(reinterpret_cast<__bf16*>(base + L::VR));
       if constexpr (BIAS == B_RELPOS) {
         if (tid < BM + STEP - 1)

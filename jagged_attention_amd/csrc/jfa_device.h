@@ -162,14 +162,6 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(u32x2 c, uint32_t s) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Position of row k (0..63) of a tile stored transposed for the contraction of a 32x32x16
-// MFMA whose other operand comes from a 32x32 accumulator: within each group of 16, row
-// 8a + 4g + b sits at 8g + 4a + b, so the 8 contraction indices of MFMA lane half g (the
-// accumulator rows 8a + 4g + b that lane half holds) are one contiguous 16-byte read.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
-
 // Length (floats) of one copy of a four-copy diagonal bias table: at least `len`, and 16 mod 64,
 // so that the 16 lanes reading 16 consecutive diagonals from rotating copies hit 16 distinct
 // 16-byte bank groups.
