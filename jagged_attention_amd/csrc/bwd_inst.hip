@@ -1223,15 +1223,26 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                                      kv_bytes);
           const float mul = which ? p.scale * wout : wout;
           if constexpr (SPLIT) {
-            // lane (key l32, g) holds dims 32 db + 8 jq + 4 g + 0..3 of its key row
+            // lane (key l32, g) holds dims 32 db + 8 jq + 4 g + 0..3 of its key row; lanes l and
+            // l + 32 (same key) trade halves so that each stores 8 consecutive dims (16 bytes):
+            // g = 0 the group 32 db + 16 jp, g = 1 the group 32 db + 16 jp + 8.  Half as many
+            // stores, so that waiting for the next tiles' loads never waits for these stores.
             const uint32_t row = row0 + (uint32_t)l32 * row_bytes;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-              for (int jq = 0; jq < 4; ++jq) {
-                const u32x2 v = {pack2bf(o[db][4 * jq] * mul, o[db][4 * jq + 1] * mul),
-                                 pack2bf(o[db][4 * jq + 2] * mul, o[db][4 * jq + 3] * mul)};
-                st8(v, r, row + 2u * (uint32_t)(db * 32 + 8 * jq + 4 * g));
+              for (int jp = 0; jp < 2; ++jp) {
+                const int j0 = 8 * jp, j1 = 8 * jp + 4;       // o[] elements of jq = 2 jp, 2 jp + 1
+                const u32x2 e = {pack2bf(o[db][j0] * mul, o[db][j0 + 1] * mul),
+                                 pack2bf(o[db][j0 + 2] * mul, o[db][j0 + 3] * mul)};
+                const u32x2 f = {pack2bf(o[db][j1] * mul, o[db][j1 + 1] * mul),
+                                 pack2bf(o[db][j1 + 2] * mul, o[db][j1 + 3] * mul)};
+                const u32x2 send = g ? e : f;                 // what the partner lane needs
+                const u32x2 got = {(uint32_t)__shfl_xor((int)send[0], 32),
+                                   (uint32_t)__shfl_xor((int)send[1], 32)};
+                const u32x4 v = g ? u32x4{got[0], got[1], f[0], f[1]}
+                                  : u32x4{e[0], e[1], got[0], got[1]};
+                st16(v, r, row + 2u * (uint32_t)(db * 32 + 16 * jp + 8 * g));
               }
           } else {
             store_rows_via_lds<D>(o, mul, ost, r, row0, row_bytes, lane);
