@@ -558,22 +558,26 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
             lq[h][qd] = *(const f32x4*)(lsl + h * 32 + 8 * qd + 4 * g);
         }
       };
-      // B(h) element i (query offset blk*32 + 8(i/4) + i%4 with blk = h)
+      // B(h) element i (query offset blk*32 + 8(i/4) + i%4 with blk = h), in two stages one MFMA
+      // apart, so that no dependent chain of an element waits inside one MFMA slot: b_front
+      // forms P (and the activation's derivative) from S, b_back forms dS and packs the pair.
       float pv_t = 0.f, ds_t = 0.f;
-      auto valu_b = [&](int h, int i) {
-        float pv, dsv;
+      float fr_p[2] = {0.f, 0.f}, fr_d[2] = {0.f, 0.f};   // front results by element parity
+      auto b_front = [&](int h, int i) {
         if constexpr (MODE == MODE_SOFTMAX) {
-          pv = fast_exp2(fmaf(sacc[h][i], c_log, -lq[h][i >> 2][i & 3]));
-          dsv = pv * pacc[h][i];
+          fr_p[i & 1] = fast_exp2(fmaf(sacc[h][i], c_log, -lq[h][i >> 2][i & 3]));
         } else {
           // masked pairs hold -inf: clamped to -1e30, the activation and its derivative are
           // exactly zero (the exponential and the reciprocal saturate) and a NaN logit still
           // propagates; the weight 1 / kv_len is applied to dK and dV as a whole
           float x = sacc[h][i] * c_log;
           x = x < -1e30f ? -1e30f : x;
-          act_pair<MODE>(x, pv, dsv);
-          dsv *= pacc[h][i];
+          act_pair<MODE>(x, fr_p[i & 1], fr_d[i & 1]);
         }
+      };
+      auto b_back = [&](int h, int i) {
+        const float pv = fr_p[i & 1];
+        const float dsv = (MODE == MODE_SOFTMAX ? pv : fr_d[i & 1]) * pacc[h][i];
         if (i & 1) {
           pp[h][i >> 1] = pack2bf(pv_t, pv);
           dd[h][i >> 1] = pack2bf(ds_t, dsv);
@@ -609,13 +613,22 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
         if constexpr (s == NA / 2) load_lse(0);
         if constexpr (s == NA + NA / 2) load_lse(1);
         mfma_s(s, ring[s % RING]);
-        // B(0) under A(1), B(1) under C(0): one element per MFMA (16 elements per half)
+        // B(0) under A(1), B(1) under C(0): one element per MFMA (16 elements per half), each
+        // element's back stage under the MFMA after its front stage (B(0)'s last back stages
+        // under the first MFMA of C(0), B(1)'s under the first of C(1): the chunks they feed
+        // start later)
         constexpr int EPM = 16 / NA;     // elements per MFMA (1 at d = 128, 2 at d = 64)
+        if constexpr (s >= NA + 1 && s <= 2 * NA) {
+          static_for<0, EPM>([&](auto e) { b_back(0, (s - NA - 1) * EPM + e); });
+        }
+        if constexpr (s >= 2 * NA + 1 && s <= 3 * NA) {
+          static_for<0, EPM>([&](auto e) { b_back(1, (s - 2 * NA - 1) * EPM + e); });
+        }
         if constexpr (s >= NA && s < 2 * NA) {
-          static_for<0, EPM>([&](auto e) { valu_b(0, (s - NA) * EPM + e); });
+          static_for<0, EPM>([&](auto e) { b_front(0, (s - NA) * EPM + e); });
         }
         if constexpr (s >= 2 * NA && s < 3 * NA) {
-          static_for<0, EPM>([&](auto e) { valu_b(1, (s - 2 * NA) * EPM + e); });
+          static_for<0, EPM>([&](auto e) { b_front(1, (s - 2 * NA) * EPM + e); });
         }
         __builtin_amdgcn_sched_barrier(0);
       });
