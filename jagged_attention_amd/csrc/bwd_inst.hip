@@ -1067,26 +1067,37 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       }
       uint32_t dd[2][8], pq2[2][8];
       // B(blk) pair pi: dS and P of elements 2 pi, 2 pi + 1 of block blk
-      auto valu_b = [&](int blk, int pi) {
-        float d2[2], p2[2];
+      // The VALU work of one pair runs in two stages one MFMA apart: the front (exp or the
+      // activation) and the back (times dP, the packing, the bias gradient), so that no
+      // dependent chain waits inside one MFMA slot.  Front results are kept by pair parity.
+      float fr_p[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, fr_d[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+      auto b_front = [&](int blk, int pi) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int ii = 2 * pi + e;
-          // a pair is visible iff its logit is not the -inf sentinel (the bias is finite)
-          const bool valid = sacc[blk][ii] != NEG_INF;
           if constexpr (MODE == MODE_SOFTMAX) {
-            const float pr = fast_exp2(fmaf(sacc[blk][ii], c_log, -lse2));
-            d2[e] = pr * pacc[blk][ii];
-            p2[e] = pr;
+            fr_p[pi & 1][e] = fast_exp2(fmaf(sacc[blk][ii], c_log, -lse2));
           } else {
             // masked pairs hold -inf: clamped to -1e30, the activation and its derivative are
             // exactly zero and a NaN logit still propagates
             float x = sacc[blk][ii] * c_log;
             x = x < -1e30f ? -1e30f : x;
-            float a, da;
-            act_pair<MODE>(x, a, da);
-            d2[e] = da * pacc[blk][ii] * wpair;
-            p2[e] = a * wpair;
+            act_pair<MODE>(x, fr_p[pi & 1][e], fr_d[pi & 1][e]);
+          }
+        }
+      };
+      auto b_back = [&](int blk, int pi) {
+        float d2[2], p2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ii = 2 * pi + e;
+          if constexpr (MODE == MODE_SOFTMAX) {
+            const float pr = fr_p[pi & 1][e];
+            d2[e] = pr * pacc[blk][ii];
+            p2[e] = pr;
+          } else {
+            d2[e] = fr_d[pi & 1][e] * pacc[blk][ii] * wpair;
+            p2[e] = fr_p[pi & 1][e] * wpair;
           }
           if constexpr (DB) {
             const int j = j0 + blk * 32 + 8 * (ii >> 2) + 4 * g + (ii & 3);
@@ -1097,8 +1108,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                 reinterpret_cast<__bf16*>(p.dbias)[(int64_t)H * boff + (int64_t)h * n * m +
                                                    (int64_t)qi * m + j] = (__bf16)d2[e];
             } else if constexpr (BIAS == B_RELPOS) {
-              // `valid` is exactly qi < n, j < m and (causal) j <= qi + delta
-              if (valid) {
+              // a pair is visible iff its logit is not the -inf sentinel (the bias is finite),
+              // which is exactly qi < n, j < m and (causal) j <= qi + delta
+              if (sacc[blk][ii] != NEG_INF) {
                 const int k = relpos_bucket(qi + delta - j, p.num_buckets);
                 if (k != db_k) {
                   db_flush();
@@ -1158,23 +1170,25 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
         constexpr int st = decltype(sc)::value;
         if constexpr (st + PF < NS) ring[(st + PF) % RING] = opnd(st + PF);
         mfma_s(st, ring[st % RING]);
-        if constexpr (st >= NA && st < 2 * NA) {          // B(0) under A(1)
-          static_for<(st - NA) * 8 / NA, (st - NA + 1) * 8 / NA>([&](auto pc) {
-            valu_b(0, decltype(pc)::value);
-          });
+        // B(0) under A(1): the front of pair k in slot NA + ceil(k NA / 8), its back one slot
+        // later.  B(1) under C: the front of pair k in slot 2 NA + floor(k NA / 16), its back
+        // one slot later, so pairs 0..3 (dS of key chunk 2) are done before chunk 2 and
+        // pairs 4..7 before chunk 3.  In each slot the backs come before the fronts.
+        if constexpr (st >= NA + 1 && st <= 2 * NA) {
+          static_for<((st - 1 - NA) * 8 + NA - 1) / NA, ((st - NA) * 8 + NA - 1) / NA>(
+              [&](auto pc) { b_back(0, decltype(pc)::value); });
         }
-        // B(1): pairs 0..3 (dS of key chunk 2) under chunks 0 and 1, pairs 4..7 (chunk 3)
-        // under chunk 2
-        if constexpr (st >= 2 * NA && st < 2 * NA + 2 * NCB) {
-          static_for<(st - 2 * NA) * 4 / (2 * NCB), (st - 2 * NA + 1) * 4 / (2 * NCB)>([&](auto pc) {
-            valu_b(1, decltype(pc)::value);
-          });
+        if constexpr (st >= 2 * NA + 1 && st <= 2 * NA + NA / 2) {
+          static_for<(st - 1 - 2 * NA) * 16 / NA, (st - 2 * NA) * 16 / NA>(
+              [&](auto pc) { b_back(1, decltype(pc)::value); });
         }
-        if constexpr (st >= 2 * NA + 2 * NCB && st < 2 * NA + 3 * NCB) {
-          static_for<4 + (st - 2 * NA - 2 * NCB) * 4 / NCB,
-                     4 + (st - 2 * NA - 2 * NCB + 1) * 4 / NCB>([&](auto pc) {
-            valu_b(1, decltype(pc)::value);
-          });
+        if constexpr (st >= NA && st < 2 * NA) {
+          static_for<((st - NA) * 8 + NA - 1) / NA, ((st - NA + 1) * 8 + NA - 1) / NA>(
+              [&](auto pc) { b_front(0, decltype(pc)::value); });
+        }
+        if constexpr (st >= 2 * NA && st < 2 * NA + NA / 2) {
+          static_for<(st - 2 * NA) * 16 / NA, (st - 2 * NA + 1) * 16 / NA>(
+              [&](auto pc) { b_front(1, decltype(pc)::value); });
         }
         __builtin_amdgcn_sched_barrier(0);
       });
