@@ -777,15 +777,16 @@ struct QLds {
 // The query-stationary pass over the q-stationary list (HOME as for kv_pass).  DB: also the
 // bias gradient, from each pair's dS as it is formed (dense: dS stored in the bias layout;
 // relative-position table: per-lane running sums by bucket, flushed on a change of bucket into
-// the lane's own slots, in LDS for at most DB_NB buckets and else in its partial row in memory;
-// later kernels reduce the rows in a fixed order).  DB runs without the single-pass classes.
+// the lane's own slots, in LDS for at most DB_NB buckets and else (DBG) in its partial row in
+// memory; later kernels reduce the rows in a fixed order).  DB runs without the single-pass
+// classes.
 //
 // SPLIT: a workgroup of 4 waves for 64-row tiles.  Waves 0, 1 own the query rows (S, dP, dS, dQ
 // as above); waves 2, 3 stage the K / V tiles and, for a one-query-tile sample, compute the dK,
 // dV rows of the previous key step from its P / dS while the query waves work on the current
 // one, so every SIMD has a wave.
 template <int D, int NW, int MODE, int BIAS, bool HOME, bool DB, bool WIN, bool FP8,
-          bool SPLIT = false>
+          bool SPLIT = false, bool DBG = false>
 __device__ __forceinline__ void q_pass(const BwdParams& p) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int QW = SPLIT ? 2 : NW;                 // waves that own query rows
@@ -825,9 +826,9 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   ItemPipeT<HOME> pipe{p.xtk_q, p.bq, (int)n_items, H};
   if (wave == 0) pipe.start(s_desc[0], lane);
   // relative-position gradient in LDS: this lane's slot of bucket k is dbl[64 k]
-  const bool db_lds = DB && BIAS == B_RELPOS && p.num_buckets <= DB_NB;
+  constexpr bool DBL = DB && BIAS == B_RELPOS && !DBG;
   float* dbl = reinterpret_cast<float*>(lds + L::DBA) + wave * DB_NB * 64 + lane;
-  if (db_lds)
+  if constexpr (DBL)
     for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
   __syncthreads();
   for (int buf = 0;; buf ^= 1) {
@@ -893,21 +894,22 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     }
     float lse2 = 0.f, dlt = 0.f;
     // bias gradient, relative-position table: the bucket being summed and its running sum
-    int db_k = -1;
+    // (bucket 0 with a zero sum to begin with: flushing it adds nothing)
+    int db_k = 0;
     float db_sum = 0.f;
     auto db_flush = [&]() {
       if constexpr (DB && BIAS == B_RELPOS) {
-        if (db_k >= 0) {
-          if (db_lds) {
-            // an LDS add with no result (ds_add_f32): no wait inside the loop; the slot is this
-            // lane's own and a wave's LDS operations apply in program order, so the sum's order
-            // is fixed
-            __hip_atomic_fetch_add(dbl + 64 * db_k, db_sum, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-          } else {
-            float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
-            pr[db_k] += db_sum;
-          }
+        if constexpr (DBL) {
+          // an LDS add with no result (ds_add_f32): no wait inside the loop; the slot is this
+          // lane's own and a wave's LDS operations apply in program order, so the sum's order
+          // is fixed
+          __hip_atomic_fetch_add(dbl + 64 * db_k, db_sum, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else if (qi < n) {
+          // the row's own partial row in memory (a row past the sample's end belongs to the
+          // next one, and has nothing to add)
+          float* pr = p.dbias_part + (((int64_t)(qo + qi) * H + h) * 2 + g) * p.num_buckets;
+          pr[db_k] += db_sum;
         }
       }
     };
@@ -1109,16 +1111,17 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
                                                    (int64_t)qi * m + j] = (__bf16)d2[e];
             } else if constexpr (BIAS == B_RELPOS) {
               // a pair is visible iff its logit is not the -inf sentinel (the bias is finite),
-              // which is exactly qi < n, j < m and (causal) j <= qi + delta
-              if (sacc[blk][ii] != NEG_INF) {
-                const int k = relpos_bucket(qi + delta - j, p.num_buckets);
-                if (k != db_k) {
-                  db_flush();
-                  db_k = k;
-                  db_sum = 0.f;
-                }
-                db_sum += d2[e];
-              }
+              // which is exactly qi < n, j < m and (causal) j <= qi + delta.  A pair that is not
+              // adds zero to the current bucket (selects, not a branch), so the only branch is
+              // the flush on a change of bucket.
+              const bool vis = sacc[blk][ii] != NEG_INF;
+              const int kb = relpos_bucket(qi + delta - j, p.num_buckets);
+              const int k = vis ? kb : db_k;
+              const float dv = vis ? d2[e] : 0.f;
+              const bool chg = k != db_k;
+              if (chg) db_flush();
+              db_sum = chg ? dv : db_sum + dv;
+              db_k = k;
             }
           }
         }
@@ -1337,18 +1340,16 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     if (wave == 0) pipe.publish(s_desc[buf ^ 1], lane);
 
     db_flush();
-    if constexpr (DB && BIAS == B_RELPOS) {
-      if (db_lds) {
-        // the row's two lane halves, summed in that order, into its partial row [H][buckets];
-        // then the slots start again from zero
-        __syncthreads();
-        if (g == 0 && qi < n) {
-          float* pr = p.dbias_part + ((int64_t)(qo + qi) * H + h) * p.num_buckets;
-          for (int k = 0; k < p.num_buckets; ++k) pr[k] = dbl[64 * k] + dbl[64 * k + 32];
-        }
-        __syncthreads();
-        for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
+    if constexpr (DBL) {
+      // the row's two lane halves, summed in that order, into its partial row [H][buckets];
+      // then the slots start again from zero
+      __syncthreads();
+      if (g == 0 && qi < n) {
+        float* pr = p.dbias_part + ((int64_t)(qo + qi) * H + h) * p.num_buckets;
+        for (int k = 0; k < p.num_buckets; ++k) pr[k] = dbl[64 * k] + dbl[64 * k + 32];
       }
+      __syncthreads();
+      for (int k = 0; k < p.num_buckets; ++k) dbl[64 * k] = 0.f;
     }
     if (qrole) {
       const rsrc_t rdq = make_rsrc((__bf16*)p.dq + ((int64_t)qo * H + h) * D, q_bytes);
@@ -1393,10 +1394,11 @@ void bwd_kvq_kernel(BwdParams p) {
 }
 
 // The query-stationary pass with the bias gradient (DB); the single-pass classes are off.
-template <int D, int NW, int MODE, int BIAS, bool WIN>
+// DBG: a relative-position table wider than DB_NB buckets.
+template <int D, int NW, int MODE, int BIAS, bool WIN, bool DBG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_q_db_kernel(BwdParams p) {
-  q_pass<D, NW, MODE, BIAS, true, true, WIN, false>(p);
+  q_pass<D, NW, MODE, BIAS, true, true, WIN, false, false, DBG>(p);
 }
 
 // Zeroes `count` 16-bit elements of x; with count_from (a dense bias's block offsets), the
@@ -1501,8 +1503,15 @@ hipError_t run_bkq(const BwdParams& p, int64_t max_items, int cu, hipStream_t s)
 
 template <int D, int NW, int MODE, int BIAS, bool WIN>
 hipError_t run_bq_db(const BwdParams& p, int64_t max_items, int cu, hipStream_t s) {
-  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS, WIN>, QLds<D, NW, BIAS>::TOTAL_DB, NW * 64,
-                           max_items, cu, p, "jfa_dbias_dq", s);
+  if constexpr (BIAS == B_RELPOS) {
+    if (p.num_buckets > DB_NB)
+      return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS, WIN, true>,
+                               QLds<D, NW, BIAS>::TOTAL_DB, NW * 64, max_items, cu, p,
+                               "jfa_dbias_dq", s);
+  }
+  return launch_persistent(bwd_q_db_kernel<D, NW, MODE, BIAS, WIN, false>,
+                           QLds<D, NW, BIAS>::TOTAL_DB, NW * 64, max_items, cu, p, "jfa_dbias_dq",
+                           s);
 }
 
 // Backward with the bias gradient: zero dbias (dense) or the partials (relative positions),
