@@ -768,8 +768,13 @@ struct QLds {
   // [DB_NB][64] floats per wave (bucket-major, so the 64 lanes hit 64 banks), in place of the
   // single-pass class's area, which that pass does not use
   static constexpr int DBA = 2 * STAGE;
-  static constexpr int TOTAL_DB = BIAS == B_RELPOS ? (TOTAL > DBA + NW * DB_NB * 64 * 4
-                                                          ? TOTAL : DBA + NW * DB_NB * 64 * 4)
+  // and, after them, each step's bucket of every diagonal as a byte table (four copies shifted
+  // by one byte, like the bias values: a run of 4 keys is one aligned 4-byte read), one table
+  // per stage parity
+  static constexpr int RPB = (BM + STEP + 4 + 3) / 4 * 4;
+  static constexpr int BKT = DBA + NW * DB_NB * 64 * 4;
+  static constexpr int TOTAL_DB = BIAS == B_RELPOS ? (TOTAL > BKT + 2 * 4 * RPB
+                                                          ? TOTAL : BKT + 2 * 4 * RPB)
                                                    : TOTAL;
   static_assert(TOTAL_DB <= 160 * 1024, "LDS of the bias-gradient pass");
 };
@@ -819,6 +824,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
   std::conditional_t<FP8, Fp8Tile<D, NT>, RowTile<D, NT>> tk;
   std::conditional_t<FP8, Fp8RowTile<D, NT>, RowTile<D, NT>> tv;
   float rpv = 0.f;
+  int rpk = 0;                      // its bucket (the bias gradient's byte table)
   constexpr int NDB = BIAS == B_DENSE ? BM * (STEP / 8) / NT : 1;
   BiasRaw dbr[NDB];                 // dense bias chunks (8 keys of one query) of the next step
   constexpr bool BIAS_RAW = !(D == 128 && (DB || WIN));
@@ -942,8 +948,8 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       if constexpr (BIAS == B_RELPOS) {
         if (tid < BM + STEP - 1) {
           const int dist = q0 + delta - j0 + BM - 1 - tid;
-          rpv = ((const float*)p.bias)[(int64_t)h * p.num_buckets +
-                                       relpos_bucket(dist, p.num_buckets)];
+          rpk = relpos_bucket(dist, p.num_buckets);
+          rpv = ((const float*)p.bias)[(int64_t)h * p.num_buckets + rpk];
         }
       }
       if constexpr (FP8) {
@@ -973,8 +979,14 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       tk.store(reinterpret_cast<__bf16*>(base + L::KR));
       tv.store(reinterpret_cast<__bf16*>(base + L::VR));
       if constexpr (BIAS == B_RELPOS) {
-        if (tid < BM + STEP - 1)
+        if (tid < BM + STEP - 1) {
           store_diag<L::RP>(reinterpret_cast<float*>(base + L::BO), tid, rpv * inv_scale);
+          if constexpr (DBL) {
+            unsigned char* bt = lds + L::BKT + st * 4 * L::RPB;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bt[k * L::RPB + tid + k] = (unsigned char)rpk;
+          }
+        }
       } else if constexpr (BIAS == B_DENSE) {
         __bf16* bt = reinterpret_cast<__bf16*>(base + L::BO);
 #pragma unroll
@@ -1009,6 +1021,19 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       const __bf16* kr = reinterpret_cast<const __bf16*>(sb + L::KR);
       const __bf16* vr = reinterpret_cast<const __bf16*>(sb + L::VR);
       // element (blk, i): key j0 + blk*32 + 8(i/4) + 4g + i%4, query qi
+      // the bias gradient's buckets of this lane's pairs: byte e of bkw[blk][qd] is the bucket
+      // of element (blk, 4 qd + e)
+      uint32_t bkw[DBL ? 2 : 1][4];
+      if constexpr (DBL) {
+        const unsigned char* bt = lds + L::BKT + (it & 1) * 4 * L::RPB;
+        const int k = (1 + qil) & 3;
+        const unsigned char* src = bt + k * L::RPB + k + BM - 1 - qil + 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            bkw[blk][qd] = *(const uint32_t*)(src + blk * 32 + 8 * qd);
+      }
       f32x16 sacc[2], pacc[2];
       if constexpr (BIAS == B_RELPOS) {
         const float* rp = reinterpret_cast<const float*>(sb + L::BO);
@@ -1115,7 +1140,11 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
               // adds zero to the current bucket (selects, not a branch), so the only branch is
               // the flush on a change of bucket.
               const bool vis = sacc[blk][ii] != NEG_INF;
-              const int kb = relpos_bucket(qi + delta - j, p.num_buckets);
+              int kb;
+              if constexpr (DBL)
+                kb = (int)((bkw[blk][ii >> 2] >> (8 * (ii & 3))) & 255u);
+              else
+                kb = relpos_bucket(qi + delta - j, p.num_buckets);
               const int k = vis ? kb : db_k;
               const float dv = vis ? d2[e] : 0.f;
               const bool chg = k != db_k;
