@@ -889,6 +889,13 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
     if constexpr (BIAS == B_DENSE)
       rb = make_rsrc((const __bf16*)p.bias + (int64_t)H * boff + (int64_t)h * n * m,
                      (uint32_t)n * (uint32_t)m * 2u);
+    // dense bias gradient: the item's [n][m] block, and this lane's row in it (a row past the
+    // sample's end lies past the block, where stores are dropped)
+    const uint32_t db_size = (uint32_t)n * (uint32_t)m * 2u;
+    const uint32_t db_row = (uint32_t)qi * (uint32_t)m * 2u;
+    rsrc_t rdb = rq;
+    if constexpr (DB && BIAS == B_DENSE)
+      rdb = make_rsrc((const __bf16*)p.dbias + (int64_t)H * boff + (int64_t)h * n * m, db_size);
 
     bf16x8 qf[D / 16], dof[D / 16];
     if (qrole) {
@@ -1129,11 +1136,10 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
           if constexpr (DB) {
             const int j = j0 + blk * 32 + 8 * (ii >> 2) + 4 * g + (ii & 3);
             if constexpr (BIAS == B_DENSE) {
-              // masked pairs store their zero; keys past the sample's end would wrap into the
-              // next row and are skipped
-              if (qi < n && j < m)
-                reinterpret_cast<__bf16*>(p.dbias)[(int64_t)H * boff + (int64_t)h * n * m +
-                                                   (int64_t)qi * m + j] = (__bf16)d2[e];
+              // masked pairs store their zero; a key past the sample's end would wrap into the
+              // next row and is sent past the block instead (a dropped store, no branch)
+              st2(__builtin_bit_cast(uint16_t, (__bf16)d2[e]), rdb,
+                  j < m ? db_row + 2u * (uint32_t)j : db_size);
             } else if constexpr (BIAS == B_RELPOS) {
               // a pair is visible iff its logit is not the -inf sentinel (the bias is finite),
               // which is exactly qi < n, j < m and (causal) j <= qi + delta.  A pair that is not

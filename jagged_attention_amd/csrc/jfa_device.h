@@ -203,6 +203,9 @@ __device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void st16(u32x4 v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void st2(uint16_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
 __device__ __forceinline__ void st4(uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
