@@ -28,24 +28,38 @@ constexpr int BITONIC_MAX = 1024;
 
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// One DPP move of a 64-bit value (both halves with the same control; lanes without a source
+// read 0).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ int64_t dpp64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROW_MASK,
+                                                            0xf, BOUND_ZERO);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+      0, (int)(uint32_t)((uint64_t)x >> 32), CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive scan over the 64 lanes of a wave with DPP: shifts by 1, 2, 4 and 8 lanes within each
+// row of 16 (a row's first lanes read 0), then lane 15's sum broadcast into rows 1 and 3 and
+// lane 31's into rows 2 and 3.
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
+  x += dpp64<0x111, 0xf, true>(x);     // row_shr:1
+  x += dpp64<0x112, 0xf, true>(x);     // row_shr:2
+  x += dpp64<0x114, 0xf, true>(x);     // row_shr:4
+  x += dpp64<0x118, 0xf, true>(x);     // row_shr:8
+  x += dpp64<0x142, 0xa, false>(x);    // row_bcast:15 into rows 1, 3
+  x += dpp64<0x143, 0xc, false>(x);    // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Exclusive scan of one value per thread over the workgroup; *total receives the sum.
 __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* total, int64_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int64_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int64_t x = wave_incl_scan(v);
   if (lane == 63) red[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int64_t w = lane < SW ? red[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < SW; o <<= 1) {
-      int64_t y = __shfl_up(w, o, 64);
-      if (lane >= o) w += y;
-    }
+    const int64_t w = wave_incl_scan(lane < SW ? red[lane] : 0);
     if (lane < SW) red[lane] = w;
   }
   __syncthreads();
