@@ -99,19 +99,18 @@ __device__ __forceinline__ float act_grad_f(float x) {
 
 // Branch-free activations for the bf16 / MXFP8 kernels (errors far below bf16 rounding).
 // GELU: Phi(x) from the erfc approximation of Abramowitz & Stegun, Handbook of Mathematical
-// Functions, formula 7.1.26 (|error of erf| <= 1.5e-7): with z = |x|/sqrt 2, t = 1/(1 + p z),
-// erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2).  exp(-z^2) = exp(-x^2/2) is
-// also the Gaussian density factor of the derivative, so value and derivative share one exp
+// Functions, formula 7.1.25 (|error of erf| <= 2.5e-5, far below bf16's rounding of the
+// activation): with z = |x|/sqrt 2, t = 1/(1 + p z), erfc(z) ~ t (a1 + t (a2 + t a3)) exp(-z^2);
+// the coefficients here are halved, giving (1 - erf(z)) / 2 directly.  exp(-z^2) = exp(-x^2/2)
+// is also the Gaussian density factor of the derivative, so value and derivative share one exp
 // and one reciprocal.  Returns Phi(x) and writes exp(-x^2/2) to e.
 __device__ __forceinline__ float gelu_cdf(float x, float& e) {
   const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = fast_rcp(fmaf(0.3275911f, z, 1.0f));
+  const float t = fast_rcp(fmaf(0.47047f, z, 1.0f));
   e = fast_exp2(-z * z * 1.4426950408889634f);
-  float poly = fmaf(t, 1.061405429f, -1.453152027f);
-  poly = fmaf(t, poly, 1.421413741f);
-  poly = fmaf(t, poly, -0.284496736f);
-  poly = fmaf(t, poly, 0.254829592f);
-  const float half_erfc = 0.5f * t * poly * e;            // (1 - erf(z)) / 2
+  float poly = fmaf(t, 0.5f * 0.7478556f, 0.5f * -0.0958798f);
+  poly = fmaf(t, poly, 0.5f * 0.3480242f);
+  const float half_erfc = t * poly * e;                   // (1 - erf(z)) / 2
   return x >= 0.f ? 1.0f - half_erfc : half_erfc;
 }
 template <int MODE>
