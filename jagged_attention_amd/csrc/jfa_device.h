@@ -105,9 +105,9 @@ __device__ __forceinline__ float act_grad_f(float x) {
 // is also the Gaussian density factor of the derivative, so value and derivative share one exp
 // and one reciprocal.  Returns Phi(x) and writes exp(-x^2/2) to e.
 __device__ __forceinline__ float gelu_cdf(float x, float& e) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = fast_rcp(fmaf(0.47047f, z, 1.0f));
-  e = fast_exp2(-z * z * 1.4426950408889634f);
+  // t = 1 / (1 + p |x| / sqrt 2), exp(-z^2) = 2^(x^2 (-log2(e) / 2))
+  const float t = fast_rcp(fmaf(0.47047f * 0.70710678118654752f, fabsf(x), 1.0f));
+  e = fast_exp2(x * x * -0.72134752044448170f);
   float poly = fmaf(t, 0.5f * 0.7478556f, 0.5f * -0.0958798f);
   poly = fmaf(t, poly, 0.5f * 0.3480242f);
   const float half_erfc = t * poly * e;                   // (1 - erf(z)) / 2
