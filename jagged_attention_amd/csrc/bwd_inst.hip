@@ -571,7 +571,7 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
           // exactly zero (the exponential and the reciprocal saturate) and a NaN logit still
           // propagates; the weight 1 / kv_len is applied to dK and dV as a whole
           float x = sacc[h][i] * c_log;
-          x = x < -1e30f ? -1e30f : x;
+          x = act_clamp(x);
           act_pair<MODE>(x, fr_p[i & 1], fr_d[i & 1]);
         }
       };
@@ -1115,7 +1115,7 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
             // masked pairs hold -inf: clamped to -1e30, the activation and its derivative are
             // exactly zero and a NaN logit still propagates
             float x = sacc[blk][ii] * c_log;
-            x = x < -1e30f ? -1e30f : x;
+            x = act_clamp(x);
             act_pair<MODE>(x, fr_p[pi & 1][e], fr_d[pi & 1][e]);
           }
         }

@@ -502,10 +502,10 @@ void fwd_kernel(FwdParams p) {
           for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
-              // masked scores are -inf: act(-inf) is NaN for SiLU/GELU, so select zero
-              const float x0 = sacc[blk][i], x1 = sacc[blk][i + 1];
-              const float a0 = x0 == NEG_INF ? 0.f : act_fast<MODE>(x0 * c_log);
-              const float a1 = x1 == NEG_INF ? 0.f : act_fast<MODE>(x1 * c_log);
+              // masked scores are -inf, where SiLU and GELU would give NaN: clamped to -1e30,
+              // both are exactly zero (a NaN score still propagates)
+              const float a0 = act_fast<MODE>(act_clamp(sacc[blk][i] * c_log));
+              const float a1 = act_fast<MODE>(act_clamp(sacc[blk][i + 1] * c_log));
               pk[blk][i >> 1] = pack2bf(a0, a1);
             }
         }

@@ -100,24 +100,30 @@ __device__ __forceinline__ float act_grad_f(float x) {
 // Branch-free activations for the bf16 / MXFP8 kernels (errors far below bf16 rounding).
 // GELU: Phi(x) from the erfc approximation of Abramowitz & Stegun, Handbook of Mathematical
 // Functions, formula 7.1.25 (|error of erf| <= 2.5e-5, far below bf16's rounding of the
-// activation): with z = |x|/sqrt 2, t = 1/(1 + p z), erfc(z) ~ t (a1 + t (a2 + t a3)) exp(-z^2);
-// the coefficients here are halved, giving (1 - erf(z)) / 2 directly.  exp(-z^2) = exp(-x^2/2)
-// is also the Gaussian density factor of the derivative, so value and derivative share one exp
-// and one reciprocal.  Returns Phi(x) and writes exp(-x^2/2) to e.
-__device__ __forceinline__ float gelu_cdf(float x, float& e) {
-  // t = 1 / (1 + p |x| / sqrt 2), exp(-z^2) = 2^(x^2 (-log2(e) / 2))
+// activation): with z = |x|/sqrt 2, t = 1/(1 + p z), erfc(z) ~ t (a1 + t (a2 + t a3)) exp(-z^2).
+// exp(-z^2) = exp(-x^2/2) is also the Gaussian density's factor, so the density
+// phi(x) = exp(-x^2/2) / sqrt(2 pi) is computed once, and the coefficients here are
+// b_i = a_i sqrt(2 pi) / 2, so that t (b1 + t (b2 + t b3)) phi(x) = (1 - erf(z)) / 2.  Value and
+// derivative share one exp and one reciprocal.  Returns Phi(x) and writes phi(x) to pdf.
+__device__ __forceinline__ float gelu_cdf(float x, float& pdf) {
   const float t = fast_rcp(fmaf(0.47047f * 0.70710678118654752f, fabsf(x), 1.0f));
-  e = fast_exp2(x * x * -0.72134752044448170f);
-  float poly = fmaf(t, 0.5f * 0.7478556f, 0.5f * -0.0958798f);
-  poly = fmaf(t, poly, 0.5f * 0.3480242f);
-  const float half_erfc = t * poly * e;                   // (1 - erf(z)) / 2
+  // phi(x) = 2^(x^2 (-log2(e) / 2) - log2(sqrt(2 pi)))
+  pdf = fast_exp2(fmaf(x * x, -0.72134752044448170f, -1.3257480647361593f));
+  float poly = fmaf(t, 0.7478556f * 1.2533141373155001f, -0.0958798f * 1.2533141373155001f);
+  poly = fmaf(t, poly, 0.3480242f * 1.2533141373155001f);
+  const float half_erfc = t * poly * pdf;                 // (1 - erf(z)) / 2
   return x >= 0.f ? 1.0f - half_erfc : half_erfc;
+}
+// x, or -1e30 where x is below it (a masked pair's -inf): every activation and derivative here
+// is then exactly zero, while a NaN stays NaN (IEEE maximum: one instruction on gfx950).
+__device__ __forceinline__ float act_clamp(float x) {
+  return __builtin_elementwise_maximum(x, -1e30f);
 }
 template <int MODE>
 __device__ __forceinline__ float act_fast(float x) {
   if (MODE == MODE_SILU) return x * fast_rcp(1.0f + fast_exp2(-x * 1.4426950408889634f));
-  float e;
-  return x * gelu_cdf(x, e);
+  float pdf;
+  return x * gelu_cdf(x, pdf);
 }
 // Activation and its derivative at x.
 template <int MODE>
@@ -127,10 +133,10 @@ __device__ __forceinline__ void act_pair(float x, float& a, float& da) {
     a = x * sg;
     da = sg * (1.0f + x * (1.0f - sg));
   } else {
-    float e;
-    const float cdf = gelu_cdf(x, e);
+    float pdf;
+    const float cdf = gelu_cdf(x, pdf);
     a = x * cdf;
-    da = fmaf(x * 0.39894228040143268f, e, cdf);
+    da = fmaf(x, pdf, cdf);
   }
 }
 
