@@ -111,8 +111,8 @@ __device__ __forceinline__ float gelu_cdf(float x, float& pdf) {
   pdf = fast_exp2(fmaf(x * x, -0.72134752044448170f, -1.3257480647361593f));
   float poly = fmaf(t, 0.7478556f * 1.2533141373155001f, -0.0958798f * 1.2533141373155001f);
   poly = fmaf(t, poly, 0.3480242f * 1.2533141373155001f);
-  const float half_erfc = t * poly * pdf;                 // (1 - erf(z)) / 2
-  return x >= 0.f ? 1.0f - half_erfc : half_erfc;
+  // (1 - erf(z)) / 2 = t poly pdf lies in [0, 1/2]; Phi(x) = 1/2 + sign(x) (1/2 - that)
+  return __builtin_copysignf(fmaf(-t * poly, pdf, 0.5f), x) + 0.5f;
 }
 // x, or -1e30 where x is below it (a masked pair's -inf): every activation and derivative here
 // is then exactly zero, while a NaN stays NaN (IEEE maximum: one instruction on gfx950).
