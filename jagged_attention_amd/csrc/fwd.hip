@@ -438,7 +438,11 @@ void fwd_kernel(FwdParams p) {
         // ---- mask (only tiles that cross the sample end, the causal diagonal or a window
         //      edge): element (blk, i) is visible iff its key offset blk*32 + 8(i/4) + i%4
         //      lies in [lo, lim)
-        const bool need_mask = (j0 + BN > m) || (p.causal && j0 + BN - 1 > qw0 + delta) ||
+        // (GDPA needs no mask at the sample's end: a key past it has K and V rows that read as
+        // zero and dense-bias entries that load as zero, so its activation times V is exactly
+        // zero; softmax needs it for the row sum)
+        const bool need_mask = (MODE == MODE_SOFTMAX && j0 + BN > m) ||
+                               (p.causal && j0 + BN - 1 > qw0 + delta) ||
                                (WIN && (j0 <= qw0 + 31 + delta - W ||
                                         (!p.causal && j0 + BN - 1 >= qw0 + delta + W)));
         if (need_mask) {
