@@ -489,7 +489,11 @@ __device__ __forceinline__ void kv_pass(const BwdParams& p) {
       }
       // pairs that are not visible start at -inf, so P = 0 and dS = 0 with no per-element test
       // later: query offset o = blk*32 + 8(i/4) + i%4 (+4g) is visible iff qlo <= o < qhi
-      const bool need_mask = (q0 + STEP > n) || (jw0 + 32 > m) ||
+      // (GDPA needs no mask at the sample's ends: a query row past them has Q and dO rows that
+      // read as zero, a key past them K and V rows that do, and dense-bias entries there load
+      // as zero, so such a pair's terms in dK, dV and dQ vanish; softmax keeps the mask, since
+      // its P there would not be zero)
+      const bool need_mask = (MODE == MODE_SOFTMAX && (q0 + STEP > n || jw0 + 32 > m)) ||
                              (p.causal && q0 + delta < jw0 + 31) ||
                              (WIN && (q0 + STEP - 1 >= jw0 - delta + W ||
                                       (!p.causal && q0 <= jw0 + 31 - delta - W)));
@@ -1077,8 +1081,11 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pacc[blk][i] = MODE == MODE_SOFTMAX ? -dlt : 0.f;
-      const bool need_mask = (j0 + STEP > m) || (p.causal && j0 + STEP - 1 > qw0 + delta) ||
-                             (qw0 + 32 > n) ||
+      // (GDPA without the bias gradient needs no mask at the sample's ends, as in the dK/dV
+      // pass; the bias gradient keeps it, since its relative-position sums test each pair's
+      // visibility)
+      const bool need_mask = ((MODE == MODE_SOFTMAX || DB) && (j0 + STEP > m || qw0 + 32 > n)) ||
+                             (p.causal && j0 + STEP - 1 > qw0 + delta) ||
                              (WIN && (j0 <= qw0 + 31 + delta - W ||
                                       (!p.causal && j0 + STEP - 1 >= qw0 + delta + W)));
       if (need_mask) {
