@@ -1161,8 +1161,12 @@ __device__ __forceinline__ void q_pass(const BwdParams& p) {
               const int k = vis ? kb : db_k;
               const float dv = vis ? d2[e] : 0.f;
               const bool chg = k != db_k;
+              // the new sum as a select ahead of the flush (the empty asm keeps the compiler from
+              // moving the add into an else branch around it)
+              float nsum = chg ? dv : db_sum + dv;
+              asm volatile("" : "+v"(nsum));
               if (chg) db_flush();
-              db_sum = chg ? dv : db_sum + dv;
+              db_sum = nsum;
               db_k = k;
             }
           }
